@@ -1,0 +1,323 @@
+/*
+ * oracle/decode_ref.c -- plain, slow, float64 CPU reference for single-query
+ * GQA decode attention over a contiguous or a paged K/V cache.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or call
+ * this file: only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg use it.  It shares no code, header, table or helper with the HIP library.
+ *
+ * What it computes (for every request b and query/output head h):
+ *   g      = h / (Hq / Hkv)                      -- consecutive query heads share a
+ *                                                   KV head (ferrox-cuda 0.15.2
+ *                                                   src/attn.rs, kernel source
+ *                                                   gqa_decode: the group index)
+ *   x_j    = scale * <q[b,h,:], K_b[g,j,:]>       j = 0 .. L_b-1
+ *   o      = sum_j softmax(x)_j * V_b[g,j,:]      (ferrum-kernels 0.7.7
+ *                                                   src/backend/cuda/decode_attention.rs,
+ *                                                   module doc: scores, stable
+ *                                                   softmax, weighted sum of V)
+ *   lse    = ln sum_j exp(x_j)                    (baracuda-kernels 0.0.1-alpha.68
+ *                                                   src/attention/batch_paged_decode.rs,
+ *                                                   module doc "Query / output": a
+ *                                                   per-row log-sum-exp kept in f32)
+ * The softmax is evaluated in the textbook two-pass way: pass 1 finds the max
+ * score M, pass 2 sums w_j = exp(x_j - M) and the w_j-weighted V rows.
+ *
+ * Readings taken where the pages are silent:
+ *   - lse is the natural log of the sum of exp of the *scaled* scores.
+ *   - a request with no valid rows yields o = 0 and lse = -inf (the ferrox-cuda
+ *     page returns zeros for an empty sequence; log of an empty sum is -inf).
+ *   - paged: request b owns pages indices[indptr[b] .. indptr[b+1]); all but the
+ *     last are full, the last holds last_page_len[b] rows, so
+ *     L_b = (n_b - 1) * page_size + last_page_len[b] for n_b >= 1, and 0 for n_b = 0
+ *     (baracuda-kernels page, module doc "Layout").
+ *   - K/V rows outside [0, L_b) are excluded, never down-weighted.
+ *
+ * Element decoding is exact: f32 is widened, bf16 is the high half of an f32,
+ * f16 is decoded from its sign / exponent / mantissa fields by hand.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2 };
+
+enum {
+  OR_OK = 0,
+  OR_BAD_ARG = 1,
+  OR_BAD_INDPTR = 2,
+  OR_BAD_INDEX = 3,
+  OR_BAD_LAST_PAGE_LEN = 4,
+  OR_NO_MEMORY = 5
+};
+
+/* ---------------------------------------------------------------- decoders */
+
+double oracle_f16_to_f64(uint16_t h) {
+  int neg = (h >> 15) & 1;
+  int e = (h >> 10) & 0x1f;
+  int m = h & 0x3ff;
+  double v;
+  if (e == 0) {
+    v = ldexp((double)m, -24); /* subnormal: m * 2^-24 */
+  } else if (e == 31) {
+    v = m ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(1024 + m), e - 25); /* (1 + m/1024) * 2^(e-15) */
+  }
+  return neg ? -v : v;
+}
+
+double oracle_bf16_to_f64(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+static size_t elem_size(int dtype) { return dtype == OR_F32 ? 4 : 2; }
+
+static double load_elem(int dtype, const void *base, int64_t idx) {
+  if (dtype == OR_F32) return (double)((const float *)base)[idx];
+  uint16_t bits = ((const uint16_t *)base)[idx];
+  return dtype == OR_F16 ? oracle_f16_to_f64(bits) : oracle_bf16_to_f64(bits);
+}
+
+/* ------------------------------------------------------------ page tables */
+
+/* Checks the device-side contract of a page table.  Returns OR_OK or the first
+ * violation found. */
+int oracle_validate_table(int batch, int page_size, int num_total_pages,
+                          int total_used_pages, const int32_t *indices,
+                          const int32_t *indptr, const int32_t *last_page_len) {
+  if (batch <= 0 || page_size <= 0 || num_total_pages <= 0 || total_used_pages < 0)
+    return OR_BAD_ARG;
+  if (indptr[0] != 0) return OR_BAD_INDPTR;
+  for (int b = 0; b < batch; ++b)
+    if (indptr[b + 1] < indptr[b]) return OR_BAD_INDPTR;
+  if (indptr[batch] > total_used_pages) return OR_BAD_INDPTR;
+  for (int i = 0; i < indptr[batch]; ++i)
+    if (indices[i] < 0 || indices[i] >= num_total_pages) return OR_BAD_INDEX;
+  for (int b = 0; b < batch; ++b)
+    if (last_page_len[b] < 0 || last_page_len[b] > page_size) return OR_BAD_LAST_PAGE_LEN;
+  return OR_OK;
+}
+
+/* L_b for every request (reading stated in the header). */
+void oracle_seq_lens(int batch, int page_size, const int32_t *indptr,
+                     const int32_t *last_page_len, int64_t *out_len) {
+  for (int b = 0; b < batch; ++b) {
+    int64_t n = (int64_t)indptr[b + 1] - indptr[b];
+    out_len[b] = n == 0 ? 0 : (n - 1) * page_size + last_page_len[b];
+  }
+}
+
+/* Element offset of row j of request b, kv head g, in a paged store laid out
+ * [num_pages, num_kv_heads, page_size, head_dim] (heads-major inside a page). */
+static int64_t paged_row_offset(int num_kv_heads, int page_size, int head_dim,
+                                const int32_t *indices, const int32_t *indptr, int b,
+                                int g, int64_t j) {
+  int64_t page = indices[indptr[b] + j / page_size];
+  int64_t r = j % page_size;
+  return ((page * num_kv_heads + g) * page_size + r) * head_dim;
+}
+
+/* Copies the page-table-resolved rows of K (or V), as raw element bits, into
+ * out laid out [sum_b L_b, num_kv_heads, head_dim] (requests in order, rows in
+ * order).  out must hold sum_b L_b * num_kv_heads * head_dim elements. */
+int oracle_gather_paged(int dtype, int batch, int num_kv_heads, int head_dim,
+                        int page_size, const void *data, const int32_t *indices,
+                        const int32_t *indptr, const int32_t *last_page_len, void *out) {
+  size_t es = elem_size(dtype);
+  int64_t row_out = 0;
+  for (int b = 0; b < batch; ++b) {
+    int64_t n = (int64_t)indptr[b + 1] - indptr[b];
+    int64_t L = n == 0 ? 0 : (n - 1) * page_size + last_page_len[b];
+    for (int64_t j = 0; j < L; ++j, ++row_out) {
+      for (int g = 0; g < num_kv_heads; ++g) {
+        int64_t src = paged_row_offset(num_kv_heads, page_size, head_dim, indices, indptr,
+                                       b, g, j);
+        int64_t dst = (row_out * num_kv_heads + g) * head_dim;
+        memcpy((char *)out + dst * es, (const char *)data + src * es, head_dim * es);
+      }
+    }
+  }
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------ attention */
+
+/* One query row against L explicit K/V rows given by element offsets into k and
+ * v.  q_off is the element offset of the query row.  Two-pass softmax in f64.
+ * o gets head_dim values; *lse the natural-log log-sum-exp. */
+static void attend_rows(int dtype, int head_dim, double scale, const void *q, int64_t q_off,
+                        const void *k, const void *v, const int64_t *row_off, int64_t L,
+                        double *x, double *o, double *lse) {
+  for (int d = 0; d < head_dim; ++d) o[d] = 0.0;
+  if (L == 0) {
+    *lse = -INFINITY;
+    return;
+  }
+  /* scores */
+  for (int64_t j = 0; j < L; ++j) {
+    double dot = 0.0;
+    for (int d = 0; d < head_dim; ++d)
+      dot += load_elem(dtype, q, q_off + d) * load_elem(dtype, k, row_off[j] + d);
+    x[j] = scale * dot;
+  }
+  /* pass 1: max */
+  double M = x[0];
+  for (int64_t j = 1; j < L; ++j)
+    if (x[j] > M) M = x[j];
+  /* pass 2: weights, normaliser, weighted V */
+  double l = 0.0;
+  for (int64_t j = 0; j < L; ++j) {
+    double w = exp(x[j] - M);
+    l += w;
+    for (int d = 0; d < head_dim; ++d) o[d] += w * load_elem(dtype, v, row_off[j] + d);
+  }
+  for (int d = 0; d < head_dim; ++d) o[d] /= l;
+  *lse = M + log(l);
+}
+
+/* Paged decode.  q [batch, Hq, D], k/v [num_pages, Hkv, P, D] in dtype; outputs
+ * o [batch, Hq, D] and lse [batch, Hq] in f64.  If n_sample > 0 only the listed
+ * (sample_b[i], sample_h[i]) pairs are computed, into o[i*D ..] and lse[i].
+ * threads <= 0 uses the OpenMP default. */
+int oracle_decode_paged(int dtype, int batch, int num_qo_heads, int num_kv_heads,
+                        int head_dim, int page_size, double scale, const void *q,
+                        const void *k, const void *v, const int32_t *indices,
+                        const int32_t *indptr, const int32_t *last_page_len, int n_sample,
+                        const int32_t *sample_b, const int32_t *sample_h, double *o,
+                        double *lse, int threads) {
+  if (batch <= 0 || num_qo_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      page_size <= 0 || num_qo_heads % num_kv_heads != 0)
+    return OR_BAD_ARG;
+  int group = num_qo_heads / num_kv_heads;
+  int64_t n_items = n_sample > 0 ? n_sample : (int64_t)batch * num_qo_heads;
+  int status = OR_OK;
+#ifdef _OPENMP
+  if (threads <= 0) threads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(threads)
+#endif
+  for (int64_t it = 0; it < n_items; ++it) {
+    int b = n_sample > 0 ? sample_b[it] : (int)(it / num_qo_heads);
+    int h = n_sample > 0 ? sample_h[it] : (int)(it % num_qo_heads);
+    int g = h / group;
+    int64_t n = (int64_t)indptr[b + 1] - indptr[b];
+    int64_t L = n == 0 ? 0 : (n - 1) * page_size + last_page_len[b];
+    int64_t *row_off = (int64_t *)malloc(sizeof(int64_t) * (size_t)(L > 0 ? L : 1));
+    double *x = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+    if (!row_off || !x) {
+      status = OR_NO_MEMORY;
+    } else {
+      for (int64_t j = 0; j < L; ++j)
+        row_off[j] = paged_row_offset(num_kv_heads, page_size, head_dim, indices, indptr,
+                                      b, g, j);
+      int64_t q_off = ((int64_t)b * num_qo_heads + h) * head_dim;
+      attend_rows(dtype, head_dim, scale, q, q_off, k, v, row_off, L, x,
+                  o + it * head_dim, lse + it);
+    }
+    free(row_off);
+    free(x);
+  }
+  return status;
+}
+
+/* Contiguous decode.  q [Hq, D], k/v [Hkv, max_kv_len, D]; only rows
+ * [0, valid_kv_len) take part (ferrum-kernels page, decode_attention argument
+ * list).  o [Hq, D] and lse [Hq] in f64. */
+int oracle_decode_contig(int dtype, int num_qo_heads, int num_kv_heads, int head_dim,
+                         int max_kv_len, int valid_kv_len, double scale, const void *q,
+                         const void *k, const void *v, double *o, double *lse,
+                         int threads) {
+  if (num_qo_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_kv_len < 0 ||
+      valid_kv_len < 0 || valid_kv_len > max_kv_len || num_qo_heads % num_kv_heads != 0)
+    return OR_BAD_ARG;
+  int group = num_qo_heads / num_kv_heads;
+  int status = OR_OK;
+#ifdef _OPENMP
+  if (threads <= 0) threads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(threads)
+#endif
+  for (int h = 0; h < num_qo_heads; ++h) {
+    int g = h / group;
+    int64_t L = valid_kv_len;
+    int64_t *row_off = (int64_t *)malloc(sizeof(int64_t) * (size_t)(L > 0 ? L : 1));
+    double *x = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+    if (!row_off || !x) {
+      status = OR_NO_MEMORY;
+    } else {
+      for (int64_t j = 0; j < L; ++j)
+        row_off[j] = ((int64_t)g * max_kv_len + j) * head_dim;
+      attend_rows(dtype, head_dim, scale, q, (int64_t)h * head_dim, k, v, row_off, L, x,
+                  o + (int64_t)h * head_dim, lse + h);
+    }
+    free(row_off);
+    free(x);
+  }
+  return status;
+}
+
+/* One query row (f64) against L explicit f64 K/V rows [L, D]: the partial that
+ * a split of the KV range produces.  Same two-pass definition as above. */
+void oracle_attend_f64(int head_dim, int64_t L, double scale, const double *q,
+                       const double *k, const double *v, double *o, double *lse) {
+  for (int d = 0; d < head_dim; ++d) o[d] = 0.0;
+  if (L <= 0) {
+    *lse = -INFINITY;
+    return;
+  }
+  double *x = (double *)malloc(sizeof(double) * (size_t)L);
+  if (!x) {
+    *lse = NAN;
+    return;
+  }
+  for (int64_t j = 0; j < L; ++j) {
+    double dot = 0.0;
+    for (int d = 0; d < head_dim; ++d) dot += q[d] * k[j * head_dim + d];
+    x[j] = scale * dot;
+  }
+  double M = x[0];
+  for (int64_t j = 1; j < L; ++j)
+    if (x[j] > M) M = x[j];
+  double l = 0.0;
+  for (int64_t j = 0; j < L; ++j) {
+    double w = exp(x[j] - M);
+    l += w;
+    for (int d = 0; d < head_dim; ++d) o[d] += w * v[j * head_dim + d];
+  }
+  for (int d = 0; d < head_dim; ++d) o[d] /= l;
+  *lse = M + log(l);
+  free(x);
+}
+
+/* Merge of S partial results (o_s normalised over its own rows, lse_s) of one
+ * query row over a partition of its KV rows into the result over the union:
+ *   lse = ln sum_s exp(lse_s),  o = sum_s exp(lse_s - lse) * o_s.
+ * Evaluated with the max shift M = max_s lse_s.  Partials with lse_s = -inf
+ * (empty parts) contribute nothing; if every part is empty, o = 0, lse = -inf. */
+void oracle_merge(int head_dim, int n_parts, const double *o_parts, const double *lse_parts,
+                  double *o, double *lse) {
+  double M = -INFINITY;
+  for (int s = 0; s < n_parts; ++s)
+    if (lse_parts[s] > M) M = lse_parts[s];
+  for (int d = 0; d < head_dim; ++d) o[d] = 0.0;
+  if (M == -INFINITY) {
+    *lse = -INFINITY;
+    return;
+  }
+  double sum = 0.0;
+  for (int s = 0; s < n_parts; ++s) sum += exp(lse_parts[s] - M);
+  double out_lse = M + log(sum);
+  for (int s = 0; s < n_parts; ++s) {
+    if (lse_parts[s] == -INFINITY) continue;
+    double w = exp(lse_parts[s] - out_lse);
+    for (int d = 0; d < head_dim; ++d) o[d] += w * o_parts[(int64_t)s * head_dim + d];
+  }
+  *lse = out_lse;
+}

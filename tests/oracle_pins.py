@@ -1,0 +1,428 @@
+"""Pins of the float64 oracle to facts that do not come from the oracle itself.
+
+Each pin_* function raises AssertionError when the oracle (whichever build the
+`oracle` module currently routes through) disagrees with:
+  * library routines: numpy's float16 and torch's bfloat16 widening, scipy's
+    logsumexp, torch's float64 scaled_dot_product_attention with GQA;
+  * closed forms: identical V rows, identical K rows, a single row, scale 0,
+    the worked example printed on the ferrox-cuda page, the merge of two
+    partials with equal lse;
+  * brute force: a 50-digit mpmath evaluation of the definition on tiny inputs,
+    without the max shift, over logical rows the test lays out in pages itself;
+  * invariants: row permutation, poisoned excluded rows, paged vs contiguous,
+    the page-table gather as the inverse of the test's own scatter.
+The same functions run against deliberately broken copies of the oracle
+(test_oracle_mutants.py) to show each plausible mistake fails at least one pin.
+"""
+import json
+import math
+import os
+
+import mpmath
+import numpy as np
+import scipy.special
+import torch
+
+import oracle as O
+import workloads as W
+from _helpers import contig_from_rows, f64, rand_t, scatter_paged
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+DTYPES = ("f32", "f16", "bf16")
+
+
+def _paged_problem(rng, dtype, lens, hkv, group, d, page_size, pool_extra=3,
+                   empty_last_page=(), k_rows=None, v_rows=None, q=None):
+    """Random logical rows -> paged layout.  Returns a dict with both views."""
+    hq = hkv * group
+    batch = len(lens)
+    if k_rows is None:
+        k_rows = [rand_t(rng, (L, hkv, d), dtype) for L in lens]
+    if v_rows is None:
+        v_rows = [rand_t(rng, (L, hkv, d), dtype) for L in lens]
+    if q is None:
+        q = rand_t(rng, (batch, hq, d), dtype)
+    seed = int(rng.integers(1 << 30))
+    kd, ind, ptr, lpl = scatter_paged(k_rows, page_size, np.random.default_rng(seed),
+                                      pool_extra, empty_last_page, fill=1.0e4)
+    vd, ind2, ptr2, lpl2 = scatter_paged(v_rows, page_size, np.random.default_rng(seed),
+                                         pool_extra, empty_last_page, fill=1.0e4)
+    assert np.array_equal(ind, ind2) and np.array_equal(lpl, lpl2)
+    return dict(dtype=dtype, q=q, k_rows=k_rows, v_rows=v_rows, k_data=kd, v_data=vd,
+                indices=ind, indptr=ptr, last_page_len=lpl, hq=hq, hkv=hkv, group=group,
+                d=d, page_size=page_size)
+
+
+def _oracle_paged(p, scale):
+    return O.decode_paged(p["dtype"], W.bits(p["q"]), W.bits(p["k_data"]), W.bits(p["v_data"]),
+                          p["indices"], p["indptr"], p["last_page_len"], scale)
+
+
+# ------------------------------------------------------------------ decoders
+
+def pin_f16_decoder():
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = pats.view(np.float16).astype(np.float64)
+    got = np.array([O.f16_to_f64(int(p)) for p in pats])
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got)), "f16 NaN patterns"
+    assert np.array_equal(ref[~nan], got[~nan]), "f16 values"
+    assert np.array_equal(np.signbit(ref[~nan]), np.signbit(got[~nan])), "f16 signs"
+
+
+def pin_bf16_decoder():
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(pats.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([O.bf16_to_f64(int(p)) for p in pats])
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got)), "bf16 NaN patterns"
+    assert np.array_equal(ref[~nan], got[~nan]), "bf16 values"
+    assert np.array_equal(np.signbit(ref[~nan]), np.signbit(got[~nan])), "bf16 signs"
+
+
+# ------------------------------------------------------------- worked example
+
+def pin_worked_example():
+    """The ferrox-cuda page's hardware test inputs; closed-form outputs."""
+    g = json.load(open(os.path.join(GOLDEN, "ferrox_gqa_decode_hw_example.json")))
+    hq, hkv, d, L = g["n_heads"], g["n_kv_heads"], g["head_dim"], g["seq_len"]
+    qv, kv, vv = (np.float32(g["q_fill_f32"]), np.float32(g["k_fill_f32"]),
+                  np.float32(g["v_fill_f32"]))
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    q = np.full((hq, d), qv, dtype=np.float32)
+    k = np.full((hkv, L, d), kv, dtype=np.float32)
+    v = np.full((hkv, L, d), vv, dtype=np.float32)
+    o, lse = O.decode_contig("f32", q, k, v, L, scale)
+    score = d * float(qv) * float(kv) * scale
+    assert np.all(o == float(vv)), "worked example: o must equal the V row"
+    assert np.allclose(lse, score + math.log(3.0), rtol=0, atol=1e-15), "worked example lse"
+    # the same rows through a paged store with a ragged last page
+    rng = np.random.default_rng(7)
+    rows_k = torch.full((L, hkv, d), float(kv), dtype=torch.float32)
+    rows_v = torch.full((L, hkv, d), float(vv), dtype=torch.float32)
+    p = _paged_problem(rng, "f32", [L], hkv, hq // hkv, d, 2, k_rows=[rows_k],
+                       v_rows=[rows_v], q=torch.from_numpy(q[None].copy()))
+    o2, lse2 = _oracle_paged(p, scale)
+    assert np.all(o2 == float(vv)) and np.allclose(lse2, score + math.log(3.0), atol=1e-15)
+
+
+# ----------------------------------------------------------------- closed forms
+
+def pin_identical_v_rows():
+    rng = np.random.default_rng(11)
+    for dtype in DTYPES:
+        lens = [5, 17, 1, 33]
+        vstar = rand_t(rng, (1, 2, 64), dtype)
+        v_rows = [vstar.expand(L, 2, 64).contiguous() for L in lens]
+        p = _paged_problem(rng, dtype, lens, 2, 3, 64, 4, v_rows=v_rows)
+        o, _ = _oracle_paged(p, 0.125)
+        want = f64(vstar)[0]
+        for b in range(len(lens)):
+            for h in range(p["hq"]):
+                np.testing.assert_allclose(o[b, h], want[h // 3], rtol=1e-14, atol=0)
+
+
+def pin_identical_k_rows():
+    rng = np.random.default_rng(12)
+    for dtype in DTYPES:
+        lens = [3, 16, 40]
+        kstar = rand_t(rng, (1, 2, 32), dtype)
+        k_rows = [kstar.expand(L, 2, 32).contiguous() for L in lens]
+        p = _paged_problem(rng, dtype, lens, 2, 2, 32, 5, k_rows=k_rows)
+        scale = 0.3
+        o, lse = _oracle_paged(p, scale)
+        qf, kf = f64(p["q"]), f64(kstar)[0]
+        for b, L in enumerate(lens):
+            vmean = f64(p["v_rows"][b]).mean(axis=0)
+            for h in range(p["hq"]):
+                g = h // 2
+                np.testing.assert_allclose(o[b, h], vmean[g], rtol=1e-12, atol=1e-14)
+                x = scale * float(np.dot(qf[b, h], kf[g]))
+                assert abs(lse[b, h] - (x + math.log(L))) < 1e-12
+
+
+def pin_single_row():
+    rng = np.random.default_rng(13)
+    for dtype in DTYPES:
+        p = _paged_problem(rng, dtype, [1, 1], 2, 4, 128, 16)
+        scale = 0.0884
+        o, lse = _oracle_paged(p, scale)
+        qf = f64(p["q"])
+        for b in range(2):
+            v0, k0 = f64(p["v_rows"][b])[0], f64(p["k_rows"][b])[0]
+            for h in range(p["hq"]):
+                assert np.array_equal(o[b, h], v0[h // 4]), "L=1 must return V[0]"
+                assert abs(lse[b, h] - scale * float(np.dot(qf[b, h], k0[h // 4]))) < 1e-12
+
+
+def pin_scale_zero():
+    rng = np.random.default_rng(14)
+    lens = [7, 64, 2]
+    p = _paged_problem(rng, "bf16", lens, 1, 4, 64, 8)
+    o, lse = _oracle_paged(p, 0.0)
+    for b, L in enumerate(lens):
+        vmean = f64(p["v_rows"][b]).mean(axis=0)[0]
+        for h in range(4):
+            np.testing.assert_allclose(o[b, h], vmean, rtol=1e-12, atol=1e-14)
+            assert abs(lse[b, h] - math.log(L)) < 1e-13
+
+
+def pin_empty_requests():
+    """n_b = 0, and a single allocated page with last_page_len 0: o = 0, lse = -inf."""
+    rng = np.random.default_rng(15)
+    k_rows = [rand_t(rng, (L, 2, 64), "f16") for L in (0, 0, 9)]
+    v_rows = [rand_t(rng, (L, 2, 64), "f16") for L in (0, 0, 9)]
+    p = _paged_problem(rng, "f16", [0, 0, 9], 2, 2, 64, 4, empty_last_page=(1,),
+                       k_rows=k_rows, v_rows=v_rows)
+    assert list(np.diff(p["indptr"])) == [0, 1, 3] and p["last_page_len"][1] == 0
+    o, lse = _oracle_paged(p, 0.125)
+    for b in (0, 1):
+        assert np.all(o[b] == 0.0) and np.all(np.isneginf(lse[b]))
+    assert np.all(np.isfinite(lse[2]))
+    qc = rand_t(rng, (4, 64), "f32")
+    kc = rand_t(rng, (2, 8, 64), "f32")
+    o, lse = O.decode_contig("f32", W.bits(qc), W.bits(kc), W.bits(kc), 0, 0.125)
+    assert np.all(o == 0.0) and np.all(np.isneginf(lse))
+
+
+# -------------------------------------------------------- library routines
+
+def pin_lse_logsumexp():
+    rng = np.random.default_rng(16)
+    lens = [100, 1, 37, 256]
+    p = _paged_problem(rng, "f32", lens, 4, 2, 64, 16)
+    scale = 0.125
+    _, lse = _oracle_paged(p, scale)
+    qf = f64(p["q"])
+    for b in range(len(lens)):
+        kf = f64(p["k_rows"][b])  # [L, Hkv, D]
+        for h in range(p["hq"]):
+            x = scale * (kf[:, h // 2, :] @ qf[b, h])
+            assert abs(lse[b, h] - scipy.special.logsumexp(x)) < 1e-12
+
+
+def pin_sdpa_float64():
+    rng = np.random.default_rng(17)
+    for dtype, (hq, hkv, d, L, maxlen) in [("f32", (8, 2, 64, 128, 256)),
+                                           ("f16", (12, 4, 128, 300, 301)),
+                                           ("bf16", (6, 1, 256, 77, 80))]:
+        q = rand_t(rng, (hq, d), dtype)
+        rows_k = rand_t(rng, (L, hkv, d), dtype)
+        rows_v = rand_t(rng, (L, hkv, d), dtype)
+        kc, vc = contig_from_rows(rows_k, maxlen), contig_from_rows(rows_v, maxlen)
+        scale = float(np.float32(1.0 / math.sqrt(d)))
+        o, _ = O.decode_contig(dtype, W.bits(q), W.bits(kc), W.bits(vc), L, scale)
+        tq = torch.from_numpy(f64(q))[None, :, None, :]
+        tk = torch.from_numpy(f64(rows_k)).permute(1, 0, 2)[None].contiguous()
+        tv = torch.from_numpy(f64(rows_v)).permute(1, 0, 2)[None].contiguous()
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=scale,
+                                                               enable_gqa=True)
+        np.testing.assert_allclose(o, ref[0, :, 0, :].numpy(), rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------ brute force
+
+def _mp_attend(qrow, krows, vrows, scale):
+    """50-digit evaluation of the definition, one pass, no max shift."""
+    mpmath.mp.dps = 50
+    L = len(krows)
+    if L == 0:
+        return [mpmath.mpf(0)] * len(qrow), -mpmath.inf
+    w = []
+    for j in range(L):
+        x = mpmath.mpf(scale) * mpmath.fsum(mpmath.mpf(a) * mpmath.mpf(b)
+                                            for a, b in zip(qrow, krows[j]))
+        w.append(mpmath.e ** x)
+    z = mpmath.fsum(w)
+    o = [mpmath.fsum(w[j] * mpmath.mpf(vrows[j][d]) for j in range(L)) / z
+         for d in range(len(qrow))]
+    return o, mpmath.log(z)
+
+
+def pin_bruteforce_mpmath():
+    rng = np.random.default_rng(18)
+    for d in (1, 2, 4):
+        for page_size in (1, 2, 3, 4):
+            for group in (1, 2, 3):
+                hkv = 1 + int(rng.integers(2))
+                dtype = DTYPES[int(rng.integers(3))]
+                lens = [int(x) for x in rng.integers(0, 7, size=3)]
+                empty = tuple(b for b in range(3) if lens[b] % page_size == 0
+                              and rng.random() < 0.5)
+                p = _paged_problem(rng, dtype, lens, hkv, group, d, page_size,
+                                   pool_extra=int(rng.integers(4)), empty_last_page=empty)
+                scale = float(rng.uniform(0.1, 2.0))
+                o, lse = _oracle_paged(p, scale)
+                qf = f64(p["q"])
+                for b, L in enumerate(lens):
+                    kf, vf = f64(p["k_rows"][b]), f64(p["v_rows"][b])
+                    for h in range(p["hq"]):
+                        g = h // group
+                        mo, ml = _mp_attend(qf[b, h], kf[:, g, :], vf[:, g, :], scale)
+                        if L == 0:
+                            assert np.all(o[b, h] == 0) and np.isneginf(lse[b, h])
+                            continue
+                        for dd in range(d):
+                            ref = float(mo[dd])
+                            assert abs(o[b, h, dd] - ref) <= 1e-13 * max(1.0, abs(ref)), \
+                                (d, page_size, group, b, h, dd)
+                        assert abs(lse[b, h] - float(ml)) <= 1e-13 * max(1.0, abs(float(ml)))
+
+
+# ------------------------------------------------------------- head mapping
+
+def pin_head_mapping():
+    """Distinct constant V per KV head: query head h must see KV head h // G."""
+    rng = np.random.default_rng(19)
+    hkv, group, d = 3, 4, 64
+    lens = [6, 21]
+    consts = [0.25, -1.5, 3.0]
+    v_rows = []
+    for L in lens:
+        t = torch.empty((L, hkv, d), dtype=torch.float16)
+        for g in range(hkv):
+            t[:, g, :] = consts[g]
+        v_rows.append(t)
+    p = _paged_problem(rng, "f16", lens, hkv, group, d, 4, v_rows=v_rows)
+    o, _ = _oracle_paged(p, 0.125)
+    for b in range(len(lens)):
+        for h in range(hkv * group):
+            np.testing.assert_allclose(o[b, h], consts[h // group], rtol=1e-14, atol=0)
+
+
+# -------------------------------------------------------------- split / merge
+
+def pin_merge_closed_form():
+    """Two parts with equal lse: weights 1/2 each, lse grows by ln 2."""
+    rng = np.random.default_rng(20)
+    o1, o2 = rng.standard_normal(16), rng.standard_normal(16)
+    o, lse = O.merge(np.stack([o1, o2]), np.array([0.7, 0.7]))
+    np.testing.assert_allclose(o, 0.5 * (o1 + o2), rtol=1e-15, atol=1e-15)
+    assert abs(lse - (0.7 + math.log(2.0))) < 1e-15
+    # an empty part (lse = -inf) changes nothing; all parts empty gives 0 / -inf
+    o, lse = O.merge(np.stack([o1, np.full(16, np.nan)]), np.array([1.25, -np.inf]))
+    assert np.array_equal(o, o1) and lse == 1.25
+    o, lse = O.merge(np.zeros((3, 16)), np.full(3, -np.inf))
+    assert np.all(o == 0) and np.isneginf(lse)
+
+
+def pin_merge_partition():
+    """Merging the partials of any partition of the rows gives the whole."""
+    rng = np.random.default_rng(21)
+    for trial in range(20):
+        L = int(rng.integers(1, 200))
+        d = 32
+        q = rng.standard_normal(d)
+        k = rng.standard_normal((L, d)) * 2.0
+        v = rng.standard_normal((L, d))
+        scale = float(rng.uniform(0.05, 1.0))
+        o_all, lse_all = O.attend_f64(q, k, v, scale)
+        cuts = np.sort(rng.integers(0, L + 1, size=int(rng.integers(0, 6))))
+        bounds = [0, *cuts.tolist(), L]
+        parts = [O.attend_f64(q, k[a:b], v[a:b], scale) for a, b in zip(bounds, bounds[1:])]
+        o, lse = O.merge(np.stack([p[0] for p in parts]), np.array([p[1] for p in parts]))
+        np.testing.assert_allclose(o, o_all, rtol=0, atol=1e-12)
+        assert abs(lse - lse_all) < 1e-12
+
+
+# -------------------------------------------------------------- invariants
+
+def pin_permutation_invariance():
+    rng = np.random.default_rng(22)
+    lens = [50, 129]
+    p = _paged_problem(rng, "bf16", lens, 2, 4, 128, 16)
+    o, lse = _oracle_paged(p, 0.0884)
+    perms = [rng.permutation(L) for L in lens]
+    p2 = _paged_problem(rng, "bf16", lens, 2, 4, 128, 16, q=p["q"],
+                        k_rows=[r[pp] for r, pp in zip(p["k_rows"], perms)],
+                        v_rows=[r[pp] for r, pp in zip(p["v_rows"], perms)])
+    o2, lse2 = _oracle_paged(p2, 0.0884)
+    np.testing.assert_allclose(o2, o, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse2, lse, rtol=0, atol=1e-13)
+
+
+def pin_masking_poison():
+    """Rows outside [0, L_b) and unreferenced pages never change a bit."""
+    rng = np.random.default_rng(23)
+    lens = [13, 31, 8]
+    p = _paged_problem(rng, "f16", lens, 2, 2, 64, 8, pool_extra=5)
+    o, lse = _oracle_paged(p, 0.125)
+    used = np.zeros(p["k_data"].shape[0], dtype=bool)
+    used[p["indices"]] = True
+    for poison in (float("nan"), -1.0e4, 6.0e4):
+        kd, vd = p["k_data"].clone(), p["v_data"].clone()
+        kd[torch.from_numpy(~used)] = poison
+        vd[torch.from_numpy(~used)] = poison
+        for b in range(len(lens)):
+            last = int(p["indices"][p["indptr"][b + 1] - 1])
+            r0 = int(p["last_page_len"][b])
+            kd[last, :, r0:, :] = poison
+            vd[last, :, r0:, :] = poison
+        o2, lse2 = O.decode_paged("f16", W.bits(p["q"]), W.bits(kd), W.bits(vd), p["indices"],
+                                  p["indptr"], p["last_page_len"], 0.125)
+        assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+    # contiguous: slots past valid_kv_len
+    q = rand_t(rng, (8, 64), "f32")
+    rows_k, rows_v = rand_t(rng, (40, 2, 64), "f32"), rand_t(rng, (40, 2, 64), "f32")
+    ref = O.decode_contig("f32", W.bits(q), W.bits(contig_from_rows(rows_k, 64)),
+                          W.bits(contig_from_rows(rows_v, 64)), 40, 0.125)
+    for poison in (float("nan"), 1.0e4):
+        got = O.decode_contig("f32", W.bits(q), W.bits(contig_from_rows(rows_k, 64, poison)),
+                              W.bits(contig_from_rows(rows_v, 64, poison)), 40, 0.125)
+        assert np.array_equal(ref[0], got[0]) and np.array_equal(ref[1], got[1])
+
+
+def pin_paged_equals_contig():
+    rng = np.random.default_rng(24)
+    for dtype in DTYPES:
+        L, hkv, group, d = 97, 2, 4, 128
+        q = rand_t(rng, (hkv * group, d), dtype)
+        rows_k, rows_v = rand_t(rng, (L, hkv, d), dtype), rand_t(rng, (L, hkv, d), dtype)
+        oc, lc = O.decode_contig(dtype, W.bits(q), W.bits(contig_from_rows(rows_k, 128)),
+                                 W.bits(contig_from_rows(rows_v, 128)), L, 0.0884)
+        for page_size in (1, 16, 97, 128):
+            p = _paged_problem(rng, dtype, [L], hkv, group, d, page_size, k_rows=[rows_k],
+                               v_rows=[rows_v], q=q[None].contiguous())
+            op, lp = _oracle_paged(p, 0.0884)
+            assert np.array_equal(op[0], oc) and np.array_equal(lp[0], lc), (dtype, page_size)
+
+
+def pin_gather_inverse():
+    rng = np.random.default_rng(25)
+    for dtype in DTYPES:
+        lens = [0, 1, 16, 17, 45]
+        p = _paged_problem(rng, dtype, lens, 3, 1, 64, 16, pool_extra=4,
+                           empty_last_page=(2,))
+        for which in ("k", "v"):
+            got = O.gather_paged(dtype, W.bits(p[which + "_data"]), p["indices"], p["indptr"],
+                                 p["last_page_len"])
+            want = np.concatenate([W.bits(r) for r in p[which + "_rows"] if r.shape[0]])
+            assert got.shape == want.shape and np.array_equal(got.view(np.uint8),
+                                                              want.view(np.uint8))
+
+
+def pin_seq_lens():
+    """The oracle's L_b equals the row count the test scattered."""
+    rng = np.random.default_rng(26)
+    for page_size in (1, 5, 16):
+        lens = [int(x) for x in rng.integers(0, 80, size=9)]
+        empty = tuple(b for b, L in enumerate(lens) if L % page_size == 0)
+        p = _paged_problem(rng, "bf16", lens, 1, 1, 64, page_size, empty_last_page=empty)
+        assert list(O.seq_lens(page_size, p["indptr"], p["last_page_len"])) == lens
+
+
+def pin_validate_table():
+    ind = np.array([3, 0, 2], dtype=np.int32)
+    ptr = np.array([0, 2, 3], dtype=np.int32)
+    lpl = np.array([4, 1], dtype=np.int32)
+    assert O.validate_table(2, 4, 4, ind, ptr, lpl) == "OK"
+    assert O.validate_table(2, 4, 3, ind, ptr, lpl) == "BAD_INDEX"
+    assert O.validate_table(2, 4, 4, np.array([3, -1, 2]), ptr, lpl) == "BAD_INDEX"
+    assert O.validate_table(2, 4, 4, ind, np.array([1, 2, 3]), lpl) == "BAD_INDPTR"
+    assert O.validate_table(2, 4, 4, ind, np.array([0, 3, 2]), lpl) == "BAD_INDPTR"
+    assert O.validate_table(2, 4, 4, ind, np.array([0, 2, 4]), lpl) == "BAD_INDPTR"
+    assert O.validate_table(2, 4, 4, ind, ptr, np.array([5, 1])) == "BAD_LAST_PAGE_LEN"
+    assert O.validate_table(2, 4, 4, ind, ptr, np.array([4, -1])) == "BAD_LAST_PAGE_LEN"
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

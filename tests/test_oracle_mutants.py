@@ -1,0 +1,85 @@
+"""Each plausible mistake planted in a copy of the oracle fails at least one pin.
+
+The mistake is planted in a temporary copy of oracle/decode_ref.c on the CPU;
+the copy is built with gcc and the pins of oracle_pins.py run against it.  This
+shows the pins have teeth: a dropped term, a wrong sign or index or a
+transposed layout in the oracle would not go unnoticed.
+"""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "decode_ref.c")
+
+# (name, text in decode_ref.c, replacement)
+MUTANTS = [
+    ("drop_scale", "x[j] = scale * dot;", "x[j] = dot;"),
+    ("head_map_modulo", "int g = h / group;", "int g = h % num_kv_heads;"),
+    ("max_shift_sign", "double w = exp(x[j] - M);", "double w = exp(M - x[j]);"),
+    ("lse_drops_max", "*lse = M + log(l);", "*lse = log(l);"),
+    ("no_normalise", "o[d] /= l;", "o[d] /= 1.0;"),
+    ("kv_len_ignores_last_page_len",
+     "(n - 1) * page_size + last_page_len[b]", "n * page_size"),
+    ("token_major_layout",
+     "((page * num_kv_heads + g) * page_size + r) * head_dim",
+     "((page * page_size + r) * num_kv_heads + g) * head_dim"),
+    ("page_order_reversed", "indices[indptr[b] + j / page_size]",
+     "indices[indptr[b + 1] - 1 - j / page_size]"),
+    ("f16_exponent_bias", "e - 25", "e - 24"),
+    ("f16_subnormal_scale", "ldexp((double)m, -24)", "ldexp((double)m, -25)"),
+    ("bf16_shift", "(uint32_t)b << 16", "(uint32_t)b << 15"),
+    ("merge_weight_unshifted", "double w = exp(lse_parts[s] - out_lse);",
+     "double w = exp(lse_parts[s] - M);"),
+    ("merge_lse_no_log", "double out_lse = M + log(sum);", "double out_lse = M + sum - 1.0;"),
+    ("empty_seq_lse_zero", "*lse = -INFINITY;\n    return;\n  }\n  /* scores */",
+     "*lse = 0.0;\n    return;\n  }\n  /* scores */"),
+    ("contig_row_stride", "((int64_t)g * max_kv_len + j) * head_dim",
+     "((int64_t)g * valid_kv_len + j) * head_dim"),
+    ("validate_skips_upper_bound", "indices[i] >= num_total_pages", "indices[i] > num_total_pages"),
+]
+
+
+def _build_variant(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert old in src, f"mutation anchor not found: {name}"
+    mutated = src.replace(old, new)
+    path = tmp_path / f"{name}.c"
+    path.write_text(mutated)
+    lib = tmp_path / f"lib{name}.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-o", str(lib),
+                    str(path), "-lm"], check=True)
+    return str(lib)
+
+
+_RUNNER = """
+import json, sys
+sys.path[:0] = [{root!r}, {tests!r}]
+import oracle, oracle_pins
+oracle.use_library({lib!r})
+caught = []
+for pin in oracle_pins.ALL_PINS:
+    try:
+        pin()
+    except Exception as e:
+        caught.append(pin.__name__)
+print(json.dumps(caught))
+"""
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    lib = _build_variant(tmp_path, name, old, new)
+    tests = os.path.dirname(os.path.abspath(__file__))
+    code = _RUNNER.format(root=os.path.dirname(tests), tests=tests, lib=lib)
+    # a separate process, so that a mutant that reads out of bounds cannot take
+    # the test session down with it
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       timeout=600, env=dict(os.environ, OMP_NUM_THREADS="4"))
+    assert r.returncode == 0, f"mutant {name} crashed the pin run: {r.stderr[-2000:]}"
+    caught = json.loads(r.stdout.strip().splitlines()[-1])
+    assert caught, f"no pin caught the planted mistake {name}"
