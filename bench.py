@@ -1,0 +1,184 @@
+"""Benchmark: batched paged bf16 GQA decode on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3|c4|c5|c2|c1]
+
+One step is one call of the library's decode entry point over the whole batch
+(split plan, attention kernel and split merge), with inputs resident in HBM.
+Prints one JSON line.  value = algorithmic bytes per call / wall time per call
+(GB/s, 1e9 B/s), where the algorithmic bytes are the valid K and V rows, q, o,
+lse and the page table, counted once each.  roofline.achieved divides the same
+bytes by the attention kernel's own average duration, timed with HIP events the
+library records on its stream during the timed steps.  cpu_baseline runs the
+float64 oracle on the host over the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import decode_attention_query_amd as fad  # noqa: E402
+import workloads as W  # noqa: E402
+
+METRIC = "achieved HBM GB/s (% of peak) + µs/call, batched paged bf16 GQA decode"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def algorithmic_bytes(p):
+    """Valid K/V rows + q + o + lse + page table, each counted once."""
+    es = W.ELEM_BYTES[p.dtype]
+    if isinstance(p, W.ContigProblem):
+        kv = p.valid_kv_len * p.num_kv_heads * p.head_dim * es * 2
+        return kv + 2 * p.num_qo_heads * p.head_dim * es + 4 * p.num_qo_heads
+    lens = np.asarray(p.kv_lens, dtype=np.int64)
+    kv = int(lens.sum()) * p.num_kv_heads * p.head_dim * es * 2
+    qo = 2 * p.batch * p.num_qo_heads * p.head_dim * es
+    lse = 4 * p.batch * p.num_qo_heads
+    table = 4 * (p.total_used_pages + 2 * p.batch + 1)
+    return kv + qo + lse + table
+
+
+def describe(p):
+    if isinstance(p, W.ContigProblem):
+        return {"workload": p.name, "layout": "contiguous", "num_qo_heads": p.num_qo_heads,
+                "num_kv_heads": p.num_kv_heads, "head_dim": p.head_dim,
+                "max_kv_len": p.max_kv_len, "valid_kv_len": p.valid_kv_len}
+    lens = np.asarray(p.kv_lens)
+    return {"workload": p.name, "layout": "paged", "batch": p.batch,
+            "num_qo_heads": p.num_qo_heads, "num_kv_heads": p.num_kv_heads,
+            "head_dim": p.head_dim, "page_size": p.page_size,
+            "num_total_pages": p.num_total_pages, "total_used_pages": p.total_used_pages,
+            "sum_kv_len": int(lens.sum()), "max_kv_len": int(lens.max())}
+
+
+def cpu_baseline(p, nbytes):
+    """The float64 oracle over the whole workload on this host's cores."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    if isinstance(p, W.ContigProblem):
+        oracle.decode_contig(p.dtype, W.bits(p.q), W.bits(p.k_cache), W.bits(p.v_cache),
+                             p.valid_kv_len, p.scale, threads=threads)
+    else:
+        oracle.decode_paged(p.dtype, W.bits(p.q), W.bits(p.k_data), W.bits(p.v_data),
+                            p.indices.numpy(), p.indptr.numpy(), p.last_page_len.numpy(),
+                            p.scale, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "seconds_per_call": round(dt, 3),
+            "sample": f"the whole {p.name} call (every request and head), one run"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c3", choices=sorted(W.FULL))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requests and KV heads shard across GPUs with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fad.load_library()
+    dev = torch.device("cuda:0")
+
+    t0 = time.perf_counter()
+    p = W.FULL[args.workload]()
+    print(f"[bench] generated {p.name} in {time.perf_counter() - t0:.1f}s", file=sys.stderr,
+          flush=True)
+    nbytes = algorithmic_bytes(p)
+
+    if isinstance(p, W.ContigProblem):
+        q, k, v = p.q.to(dev), p.k_cache.to(dev), p.v_cache.to(dev)
+        o = torch.empty_like(q)
+        lse = torch.empty(p.num_qo_heads, dtype=torch.float32, device=dev)
+        ws = fad.workspace_paged(1, p.num_qo_heads, p.num_kv_heads, p.head_dim, p.max_kv_len, 1,
+                                 dev)
+
+        def step():
+            fad.decode_contig(q, k, v, p.valid_kv_len, p.scale, o=o, lse=lse, workspace=ws)
+    else:
+        q, k, v = p.q.to(dev), p.k_data.to(dev), p.v_data.to(dev)
+        ind, ptr, lpl = p.indices.to(dev), p.indptr.to(dev), p.last_page_len.to(dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((p.batch, p.num_qo_heads), dtype=torch.float32, device=dev)
+        ws = fad.workspace_paged(p.batch, p.num_qo_heads, p.num_kv_heads, p.head_dim,
+                                 p.page_size, p.total_used_pages, dev)
+
+        def step():
+            fad.decode_paged(q, k, v, ind, ptr, lpl, p.scale, o=o, lse=lse, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} calls)", file=sys.stderr, flush=True)
+
+    fad.fa_debug_timing_enable(1)
+    fad.fa_debug_timing_read()  # reset
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    main_ms, call_ms, calls = fad.fa_debug_timing_read()
+    fad.fa_debug_timing_enable(0)
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    kernel_ms = main_ms / max(calls, 1)
+    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    chunk, bound, gt, kind = fad.fa_debug_plan(fad.DTYPE_CODES[p.dtype],
+                                               getattr(p, "batch", 1), p.num_qo_heads,
+                                               p.num_kv_heads, p.head_dim,
+                                               getattr(p, "page_size", getattr(p, "max_kv_len", 1)),
+                                               getattr(p, "total_used_pages", 1))
+    print(f"[bench] {args.steps} calls: {ms_per_step * 1e3:.1f} us/call, attention kernel "
+          f"{kernel_ms * 1e3:.1f} us, {value:.0f} GB/s call, {achieved:.0f} GB/s kernel",
+          file=sys.stderr, flush=True)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_call": round(ms_per_step * 1e3, 2),
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.dtype,
+        "data": "synthetic (seeded N(0,1) values, seeded page tables; no dataset)",
+        "config": {**describe(p), "algorithmic_bytes_per_call": int(nbytes),
+                   "chunk_rows": chunk, "heads_per_workgroup": gt,
+                   "attention_kernel": "valu" if kind == 0 else "mfma"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel_us": round(kernel_ms * 1e3, 2),
+                     "kernel": "decode attention (fa::decode_*_kernel)"},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the float64 oracle on the host", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(p, nbytes)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,73 @@
+"""MI355X-native single-query GQA decode attention.
+
+The computation runs in libfadecode.so (hand-written HIP kernels for gfx950);
+this package is its binding.  The C entry points are available under their
+own names (fa_decode_contig, fa_decode_paged, fa_decode_workspace_size, and
+the fa_debug_* hooks); decode_contig and decode_paged below are conveniences
+that read the dimensions off the tensors and allocate outputs and workspace.
+"""
+import torch
+
+from ._binding import (CODE_TORCH_DTYPES, DTYPE_CODES, EXPORTED, FA_DTYPE_BF16, FA_DTYPE_F16,
+                       FA_DTYPE_F32, FA_ERR_INVALID_PROBLEM, FA_ERR_LAUNCH, FA_ERR_UNSUPPORTED,
+                       FA_ERR_WORKSPACE_TOO_SMALL, FA_OK, LIB_PATH, STATUS_NAMES,
+                       TORCH_DTYPE_CODES, FaError, fa_debug_gather_paged, fa_debug_plan,
+                       fa_debug_timing_enable, fa_debug_timing_read, fa_decode_contig,
+                       fa_decode_paged, fa_decode_workspace_size, fa_status_string,
+                       load_library)
+
+
+def _code(t):
+    try:
+        return TORCH_DTYPE_CODES[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported element type {t.dtype}") from None
+
+
+def workspace_paged(batch, num_qo_heads, num_kv_heads, head_dim, page_size, total_used_pages,
+                    device="cuda"):
+    n = fa_decode_workspace_size(batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                                 total_used_pages)
+    if n == 0:
+        raise FaError("fa_decode_workspace_size", FA_ERR_INVALID_PROBLEM)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def decode_paged(q, k_data, v_data, indices, indptr, last_page_len, sm_scale, o=None, lse=None,
+                 workspace=None, stream=None):
+    """q [B, Hq, D]; k_data/v_data [pages, Hkv, P, D]; int32 page table.
+    Returns (o [B, Hq, D] in q's dtype, lse [B, Hq] f32)."""
+    batch, hq, d = q.shape
+    pages, hkv, page_size, d2 = k_data.shape
+    if d2 != d or tuple(v_data.shape) != tuple(k_data.shape):
+        raise ValueError("q, k_data and v_data disagree on shape")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((batch, hq), dtype=torch.float32, device=q.device)
+    used = indices.numel()
+    if workspace is None:
+        workspace = workspace_paged(batch, hq, hkv, d, page_size, used, q.device)
+    fa_decode_paged(_code(q), batch, hq, hkv, d, page_size, pages, used, sm_scale, q, k_data,
+                    v_data, indices if used else None, indptr, last_page_len, o, lse,
+                    workspace, stream)
+    return o, lse
+
+
+def decode_contig(q, k_cache, v_cache, valid_kv_len, scale, o=None, lse=None, workspace=None,
+                  stream=None):
+    """q [Hq, D]; k_cache/v_cache [Hkv, max_kv_len, D].
+    Returns (o [Hq, D] in q's dtype, lse [Hq] f32)."""
+    hq, d = q.shape
+    hkv, max_kv_len, d2 = k_cache.shape
+    if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("q, k_cache and v_cache disagree on shape")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((hq,), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = workspace_paged(1, hq, hkv, d, max_kv_len, 1, q.device)
+    fa_decode_contig(_code(q), hq, hkv, d, max_kv_len, valid_kv_len, scale, q, k_cache,
+                     v_cache, o, lse, workspace, stream)
+    return o, lse

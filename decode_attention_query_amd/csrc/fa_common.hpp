@@ -1,0 +1,170 @@
+// fa_common.hpp -- launch parameters and device helpers shared by the decode
+// kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kWave = 64;
+
+// Division of a 32-bit unsigned n by a divisor d fixed at launch, by the
+// round-up multiply method: with s = ceil(log2 d) and
+// magic = floor(2^32 (2^s - d) / d) + 1, the quotient is (umulhi(n, magic) + n) >> s
+// (Granlund & Montgomery, "Division by invariant integers using
+// multiplication", PLDI 1994).  Valid for 1 <= d < 2^31 and every n < 2^32.
+struct FastDiv {
+  uint32_t d;
+  uint32_t magic;
+  uint32_t shift;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  f.shift = s;
+  f.magic = (uint32_t)(((1ull << 32) * ((1ull << s) - d)) / d + 1);
+  return f;
+}
+
+__host__ __device__ inline uint32_t fastdiv(uint32_t n, FastDiv f) {
+#ifdef __HIP_DEVICE_COMPILE__
+  uint32_t hi = __umulhi(n, f.magic);
+#else
+  uint32_t hi = (uint32_t)(((uint64_t)n * f.magic) >> 32);
+#endif
+  return (uint32_t)(((uint64_t)hi + n) >> f.shift);
+}
+
+// Everything a decode launch needs.  Passed by value as the kernel argument.
+struct DecodeParams {
+  // tensors
+  const void *q;                  // [B, Hq, D] (contiguous: B = 1)
+  const void *k;                  // paged [pages, Hkv, P, D]; contiguous [Hkv, max_kv_len, D]
+  const void *v;
+  void *o;                        // [B, Hq, D]
+  float *lse;                     // [B, Hq] or null (contiguous only)
+  const int32_t *indices;         // [total_used_pages]
+  const int32_t *indptr;          // [B + 1]
+  const int32_t *last_page_len;   // [B]
+  // geometry
+  int batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_total_pages;
+  int total_used_pages;
+  int group;          // Hq / Hkv
+  int n_gblocks;      // workgroups per KV head along the query group
+  float scale_log2;   // scale * log2(e): scores live in the base-2 domain
+  FastDiv page_div;   // row -> (page slot, row in page)
+  // split-KV plan
+  int chunk;          // KV rows per split unit
+  int units_bound;    // grid.x; units past the real count exit at once
+  int contig;         // 1: contiguous cache (a single page of max_kv_len rows)
+  int contig_len;     // contiguous: valid_kv_len
+  int contig_units;   // contiguous: ceil(valid_kv_len / chunk), at least 1
+  // workspace regions
+  int32_t *seq_len;       // [B]       L_b
+  int32_t *page_base;     // [B]       first index of request b's pages in indices
+  int32_t *unit_prefix;   // [B + 1]   first split unit of each request
+  int64_t *row_prefix;    // [B + 1]   first output row of each request (gather hook)
+  int32_t *unit_req;      // [units_bound] request of each split unit
+  float *part_lse;        // [units_bound, Hq]     base-2 lse of each split's partial
+  float *part_o;          // [units_bound, Hq, D]  normalised partial outputs
+};
+
+// ---------------------------------------------------------------- elements
+//
+// Each element type knows how to widen a 16-byte vector to f32 and how to
+// round an f32 back to itself (round-to-nearest-even).
+
+struct F32 {
+  static constexpr int kBytes = 4;
+  using raw = float;
+  __device__ static inline void widen(const uint4 &r, float *out) {
+    out[0] = __uint_as_float(r.x);
+    out[1] = __uint_as_float(r.y);
+    out[2] = __uint_as_float(r.z);
+    out[3] = __uint_as_float(r.w);
+  }
+  __device__ static inline raw narrow(float f) { return f; }
+};
+
+struct BF16 {
+  static constexpr int kBytes = 2;
+  using raw = uint16_t;
+  __device__ static inline void widen(const uint4 &r, float *out) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static inline raw narrow(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+  }
+};
+
+struct F16 {
+  static constexpr int kBytes = 2;
+  using raw = uint16_t;
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  __device__ static inline void widen(const uint4 &r, float *out) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h2 h = __builtin_bit_cast(h2, w[i]);
+      out[2 * i] = (float)h[0];
+      out[2 * i + 1] = (float)h[1];
+    }
+  }
+  __device__ static inline raw narrow(float f) {
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+  }
+};
+
+// ------------------------------------------------------------ loads
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load with the streaming (non-temporal) hint: K/V rows are read once.
+__device__ inline uint4 load16_stream(const void *ptr) {
+  const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4 *>(ptr));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// ------------------------------------------------------------ math helpers
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// The shift used for an online-softmax rescale: the running max, or 0 while no
+// valid score has been seen (keeps -inf - -inf out of the exponent).
+__device__ inline float safe_ref(float m) { return m == -INFINITY ? 0.0f : m; }
+
+// Element offset of KV row t (of request b, KV head kvh), lane vector vi
+// excluded.  Paged: page = indices[page_base + t / P], row = t % P, layout
+// [pages, Hkv, P, D]; contiguous: the single page 0 of P = max_kv_len rows.
+// Page ids are clamped into the pool so that a table breaking its contract
+// cannot make a kernel read outside the K/V buffers.
+__device__ inline int64_t kv_row_offset(const DecodeParams &p, int32_t page_base, int kvh,
+                                        int t) {
+  int64_t page = 0;
+  uint32_t row = (uint32_t)t;
+  if (!p.contig) {
+    const uint32_t slot = fastdiv((uint32_t)t, p.page_div);
+    row = (uint32_t)t - slot * (uint32_t)p.page_size;
+    int32_t id = p.indices[page_base + slot];
+    id = min(max(id, 0), p.num_total_pages - 1);
+    page = id;
+  }
+  return ((page * p.num_kv_heads + kvh) * (int64_t)p.page_size + row) * p.head_dim;
+}
+
+}  // namespace fa

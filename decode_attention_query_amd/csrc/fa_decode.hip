@@ -1,0 +1,430 @@
+// fa_decode.hip -- the C ABI of the decode library: argument checks, the
+// launch plan, workspace carve-up and kernel dispatch.  See include/fa_decode.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <array>
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+#include <vector>
+
+#include "../../include/fa_decode.h"
+#include "../../include/fa_decode_debug.h"
+#include "fa_common.hpp"
+#include "fa_kernels.hpp"
+
+namespace {
+
+using fa::DecodeParams;
+
+// Split sizing: aim for about this many decode workgroups per call, so the
+// 256 CUs each get several and the tail is short.
+constexpr int64_t kTargetWorkgroups = 2048;
+constexpr int64_t kChunkQuantum = 256;  // KV rows; a multiple of every kernel's tile
+constexpr int64_t kMaxChunk = int64_t(1) << 30;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int heads_per_unit(int group) {
+  for (int gt : {8, 4, 2})
+    if (group % gt == 0) return gt;
+  return 1;
+}
+
+struct HostPlan {
+  int group = 0, gt = 0, n_gblocks = 0, planes = 0;
+  int chunk = 0, units_bound = 0, kind = 0;
+  // workspace byte offsets
+  size_t seq_len = 0, page_base = 0, unit_prefix = 0, row_prefix = 0, unit_req = 0,
+         part_lse = 0, part_o = 0, total = 0;
+};
+
+bool extents_ok(int batch, int hq, int hkv, int page_size) {
+  return batch > 0 && hq > 0 && hkv > 0 && page_size > 0 && hq % hkv == 0;
+}
+
+bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
+
+// grid.y is Hkv * (workgroups per KV head) and must stay within the launch limit
+bool grid_ok(int hq, int hkv) { return hq / hkv > 0 && hkv * (hq / hkv) <= 65535; }
+
+// The plan for a call; `page_size` is max_kv_len and total_used_pages 1 for a
+// contiguous cache.  Pure host arithmetic.
+HostPlan make_plan(int batch, int hq, int hkv, int d, int page_size, int total_used_pages,
+                   bool contig) {
+  HostPlan hp;
+  hp.group = hq / hkv;
+  hp.gt = heads_per_unit(hp.group);
+  hp.n_gblocks = hp.group / hp.gt;
+  hp.planes = hkv * hp.n_gblocks;
+  hp.kind = 0;
+  const int64_t rows_ub = int64_t(std::max(total_used_pages, 0)) * page_size;
+  int64_t want = (rows_ub * hp.planes + kTargetWorkgroups - 1) / kTargetWorkgroups;
+  want = std::max<int64_t>(want, kChunkQuantum);
+  int64_t chunk = (want + kChunkQuantum - 1) / kChunkQuantum * kChunkQuantum;
+  chunk = std::min(chunk, kMaxChunk);
+  hp.chunk = int(chunk);
+  // Units: a request of L rows has max(1, ceil(L / chunk)) of them, which is at
+  // most 1 + floor(L / chunk); summed, at most batch + floor(sum L / chunk).
+  if (contig)
+    hp.units_bound = int(std::max<int64_t>(1, (int64_t(page_size) + chunk - 1) / chunk));
+  else
+    hp.units_bound = int(batch + rows_ub / chunk);
+  size_t off = 0;
+  hp.seq_len = off;     off = align_up(off + sizeof(int32_t) * batch);
+  hp.page_base = off;   off = align_up(off + sizeof(int32_t) * batch);
+  hp.unit_prefix = off; off = align_up(off + sizeof(int32_t) * (batch + 1));
+  hp.row_prefix = off;  off = align_up(off + sizeof(int64_t) * (batch + 1));
+  hp.unit_req = off;    off = align_up(off + sizeof(int32_t) * hp.units_bound);
+  hp.part_lse = off;    off = align_up(off + sizeof(float) * size_t(hp.units_bound) * hq);
+  hp.part_o = off;      off = align_up(off + sizeof(float) * size_t(hp.units_bound) * hq * d);
+  hp.total = off;
+  return hp;
+}
+
+void carve(DecodeParams &p, const HostPlan &hp, void *ws) {
+  char *w = static_cast<char *>(ws);
+  p.seq_len = reinterpret_cast<int32_t *>(w + hp.seq_len);
+  p.page_base = reinterpret_cast<int32_t *>(w + hp.page_base);
+  p.unit_prefix = reinterpret_cast<int32_t *>(w + hp.unit_prefix);
+  p.row_prefix = reinterpret_cast<int64_t *>(w + hp.row_prefix);
+  p.unit_req = reinterpret_cast<int32_t *>(w + hp.unit_req);
+  p.part_lse = reinterpret_cast<float *>(w + hp.part_lse);
+  p.part_o = reinterpret_cast<float *>(w + hp.part_o);
+}
+
+// ------------------------------------------------------------------ timing
+
+struct Timing {
+  std::mutex mu;
+  bool enabled = false;
+  std::vector<std::array<hipEvent_t, 4>> recorded;  // call start, main start, main end, call end
+  std::vector<hipEvent_t> pool;
+
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+
+Timing &timing() {
+  static Timing t;
+  return t;
+}
+
+// Event quad of one call while timing is on (all null otherwise).
+struct CallEvents {
+  std::array<hipEvent_t, 4> ev{};
+  bool on = false;
+  explicit CallEvents(hipStream_t s) {
+    Timing &t = timing();
+    std::lock_guard<std::mutex> lk(t.mu);
+    if (!t.enabled) return;
+    for (auto &e : ev) e = t.get();
+    on = std::all_of(ev.begin(), ev.end(), [](hipEvent_t e) { return e != nullptr; });
+    if (on) (void)hipEventRecord(ev[0], s);
+  }
+  void mark(int i, hipStream_t s) {
+    if (on) (void)hipEventRecord(ev[i], s);
+  }
+  void finish(hipStream_t s) {
+    if (!on) return;
+    (void)hipEventRecord(ev[3], s);
+    Timing &t = timing();
+    std::lock_guard<std::mutex> lk(t.mu);
+    t.recorded.push_back(ev);
+  }
+};
+
+// --------------------------------------------------------------- dispatch
+
+template <class E, int D, int GT>
+hipError_t launch_valu(const DecodeParams &p, const HostPlan &hp, hipStream_t s) {
+  dim3 grid(hp.units_bound, hp.planes);
+  hipLaunchKernelGGL((fa::decode_valu_kernel<E, D, GT>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <class E, int D>
+hipError_t launch_valu_gt(const DecodeParams &p, const HostPlan &hp, hipStream_t s) {
+  switch (hp.gt) {
+    case 8: return launch_valu<E, D, 8>(p, hp, s);
+    case 4: return launch_valu<E, D, 4>(p, hp, s);
+    case 2: return launch_valu<E, D, 2>(p, hp, s);
+    default: return launch_valu<E, D, 1>(p, hp, s);
+  }
+}
+
+template <class E>
+hipError_t launch_decode(const DecodeParams &p, const HostPlan &hp, hipStream_t s) {
+  switch (p.head_dim) {
+    case 64: return launch_valu_gt<E, 64>(p, hp, s);
+    case 128: return launch_valu_gt<E, 128>(p, hp, s);
+    default: return launch_valu_gt<E, 256>(p, hp, s);
+  }
+}
+
+template <class E>
+hipError_t launch_merge(const DecodeParams &p, hipStream_t s) {
+  const int items = p.batch * p.num_qo_heads;
+  hipLaunchKernelGGL((fa::merge_kernel<E>), dim3((items + 3) / 4), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t dispatch_decode(fa_dtype_t dt, const DecodeParams &p, const HostPlan &hp,
+                           hipStream_t s) {
+  switch (dt) {
+    case FA_DTYPE_F32: return launch_decode<fa::F32>(p, hp, s);
+    case FA_DTYPE_F16: return launch_decode<fa::F16>(p, hp, s);
+    default: return launch_decode<fa::BF16>(p, hp, s);
+  }
+}
+
+hipError_t dispatch_merge(fa_dtype_t dt, const DecodeParams &p, hipStream_t s) {
+  switch (dt) {
+    case FA_DTYPE_F32: return launch_merge<fa::F32>(p, s);
+    case FA_DTYPE_F16: return launch_merge<fa::F16>(p, s);
+    default: return launch_merge<fa::BF16>(p, s);
+  }
+}
+
+bool dtype_ok(fa_dtype_t dt) {
+  return dt == FA_DTYPE_F32 || dt == FA_DTYPE_F16 || dt == FA_DTYPE_BF16;
+}
+
+// Elements of a [pages, Hkv, P, D] pool must stay far inside int64 offsets.
+bool pool_size_ok(int pages, int hkv, int page_size, int d) {
+  const double n = double(pages) * hkv * page_size * d;
+  return n < 1.0e15;
+}
+
+DecodeParams base_params(int batch, int hq, int hkv, int d, int page_size, int pages,
+                         int total_used_pages, float scale, const HostPlan &hp) {
+  DecodeParams p{};
+  p.batch = batch;
+  p.num_qo_heads = hq;
+  p.num_kv_heads = hkv;
+  p.head_dim = d;
+  p.page_size = page_size;
+  p.num_total_pages = pages;
+  p.total_used_pages = total_used_pages;
+  p.group = hp.group;
+  p.n_gblocks = hp.n_gblocks;
+  p.scale_log2 = scale * fa::kLog2e;
+  p.page_div = fa::make_fastdiv(uint32_t(page_size));
+  p.chunk = hp.chunk;
+  p.units_bound = hp.units_bound;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_decode_workspace_size(int batch, int num_qo_heads, int num_kv_heads, int head_dim,
+                                int page_size, int total_used_pages) {
+  if (!extents_ok(batch, num_qo_heads, num_kv_heads, page_size) || !head_dim_ok(head_dim) ||
+      total_used_pages < 0)
+    return 0;
+  if (int64_t(total_used_pages) * page_size >= (int64_t(1) << 31)) return 0;
+  return make_plan(batch, num_qo_heads, num_kv_heads, head_dim, page_size, total_used_pages,
+                   false)
+      .total;
+}
+
+fa_status_t fa_decode_contig(fa_dtype_t dtype, int num_qo_heads, int num_kv_heads,
+                             int head_dim, int max_kv_len, int valid_kv_len, float scale,
+                             const void *q, const void *k_cache, const void *v_cache, void *o,
+                             float *lse, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  if (!dtype_ok(dtype)) return FA_ERR_UNSUPPORTED;
+  if (!extents_ok(1, num_qo_heads, num_kv_heads, max_kv_len)) return FA_ERR_INVALID_PROBLEM;
+  if (!head_dim_ok(head_dim)) return FA_ERR_UNSUPPORTED;
+  if (!grid_ok(num_qo_heads, num_kv_heads)) return FA_ERR_UNSUPPORTED;
+  if (!q || !k_cache || !v_cache || !o) return FA_ERR_INVALID_PROBLEM;
+  if (valid_kv_len < 0 || valid_kv_len > max_kv_len) return FA_ERR_INVALID_PROBLEM;
+  if (!pool_size_ok(1, num_kv_heads, max_kv_len, head_dim)) return FA_ERR_UNSUPPORTED;
+  const size_t need =
+      fa_decode_workspace_size(1, num_qo_heads, num_kv_heads, head_dim, max_kv_len, 1);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
+
+  // Sized like the workspace query (a single page of max_kv_len rows) so the
+  // split units fit what the caller allocated.
+  const HostPlan hp =
+      make_plan(1, num_qo_heads, num_kv_heads, head_dim, max_kv_len, 1, /*contig=*/true);
+  DecodeParams p = base_params(1, num_qo_heads, num_kv_heads, head_dim, max_kv_len, 1, 1,
+                               scale, hp);
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.o = o;
+  p.lse = lse;
+  p.contig = 1;
+  p.contig_len = valid_kv_len;
+  p.contig_units =
+      valid_kv_len == 0 ? 1 : int((int64_t(valid_kv_len) + hp.chunk - 1) / hp.chunk);
+  carve(p, hp, workspace);
+
+  CallEvents ev(stream);
+  ev.mark(1, stream);
+  if (dispatch_decode(dtype, p, hp, stream) != hipSuccess) return FA_ERR_LAUNCH;
+  ev.mark(2, stream);
+  if (p.contig_units > 1 && dispatch_merge(dtype, p, stream) != hipSuccess)
+    return FA_ERR_LAUNCH;
+  ev.finish(stream);
+  return FA_OK;
+}
+
+fa_status_t fa_decode_paged(fa_dtype_t dtype, int batch, int num_qo_heads, int num_kv_heads,
+                            int head_dim, int page_size, int num_total_pages,
+                            int total_used_pages, float sm_scale, const void *q,
+                            const void *k_data, const void *v_data, const int32_t *indices,
+                            const int32_t *indptr, const int32_t *last_page_len, void *o,
+                            float *lse, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  if (!dtype_ok(dtype)) return FA_ERR_UNSUPPORTED;
+  if (!extents_ok(batch, num_qo_heads, num_kv_heads, page_size) || num_total_pages <= 0)
+    return FA_ERR_INVALID_PROBLEM;
+  if (!head_dim_ok(head_dim)) return FA_ERR_UNSUPPORTED;
+  if (total_used_pages < 0) return FA_ERR_INVALID_PROBLEM;
+  if (!grid_ok(num_qo_heads, num_kv_heads)) return FA_ERR_UNSUPPORTED;
+  if (!q || !k_data || !v_data || !indptr || !last_page_len || !o || !lse ||
+      (!indices && total_used_pages > 0))
+    return FA_ERR_INVALID_PROBLEM;
+  if (int64_t(total_used_pages) * page_size >= (int64_t(1) << 31)) return FA_ERR_UNSUPPORTED;
+  if (!pool_size_ok(num_total_pages, num_kv_heads, page_size, head_dim))
+    return FA_ERR_UNSUPPORTED;
+  const size_t need = fa_decode_workspace_size(batch, num_qo_heads, num_kv_heads, head_dim,
+                                               page_size, total_used_pages);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
+
+  const HostPlan hp = make_plan(batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                                total_used_pages, false);
+  DecodeParams p = base_params(batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                               num_total_pages, total_used_pages, sm_scale, hp);
+  p.q = q;
+  p.k = k_data;
+  p.v = v_data;
+  p.o = o;
+  p.lse = lse;
+  p.indices = indices;
+  p.indptr = indptr;
+  p.last_page_len = last_page_len;
+  carve(p, hp, workspace);
+
+  CallEvents ev(stream);
+  hipLaunchKernelGGL(fa::plan_kernel, dim3(1), dim3(fa::kPlanThreads), 0, stream, p);
+  if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+  ev.mark(1, stream);
+  if (dispatch_decode(dtype, p, hp, stream) != hipSuccess) return FA_ERR_LAUNCH;
+  ev.mark(2, stream);
+  if (dispatch_merge(dtype, p, stream) != hipSuccess) return FA_ERR_LAUNCH;
+  ev.finish(stream);
+  return FA_OK;
+}
+
+const char *fa_status_string(fa_status_t status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_PROBLEM: return "FA_ERR_INVALID_PROBLEM";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_WORKSPACE_TOO_SMALL: return "FA_ERR_WORKSPACE_TOO_SMALL";
+    case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH";
+  }
+  return "FA_ERR_UNKNOWN";
+}
+
+// ------------------------------------------------------------------- hooks
+
+fa_status_t fa_debug_gather_paged(fa_dtype_t dtype, int batch, int num_kv_heads, int head_dim,
+                                  int page_size, int num_total_pages, int total_used_pages,
+                                  const void *data, const int32_t *indices,
+                                  const int32_t *indptr, const int32_t *last_page_len,
+                                  void *out, int64_t out_rows, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return FA_ERR_UNSUPPORTED;
+  if (!extents_ok(batch, num_kv_heads, num_kv_heads, page_size) || num_total_pages <= 0)
+    return FA_ERR_INVALID_PROBLEM;
+  if (!head_dim_ok(head_dim)) return FA_ERR_UNSUPPORTED;
+  if (total_used_pages < 0 || out_rows < 0) return FA_ERR_INVALID_PROBLEM;
+  if (!data || !indptr || !last_page_len || !out || (!indices && total_used_pages > 0))
+    return FA_ERR_INVALID_PROBLEM;
+  if (int64_t(total_used_pages) * page_size >= (int64_t(1) << 31)) return FA_ERR_UNSUPPORTED;
+  if (!pool_size_ok(num_total_pages, num_kv_heads, page_size, head_dim))
+    return FA_ERR_UNSUPPORTED;
+  const size_t need = fa_decode_workspace_size(batch, num_kv_heads, num_kv_heads, head_dim,
+                                               page_size, total_used_pages);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
+  const HostPlan hp = make_plan(batch, num_kv_heads, num_kv_heads, head_dim, page_size,
+                                total_used_pages, false);
+  DecodeParams p = base_params(batch, num_kv_heads, num_kv_heads, head_dim, page_size,
+                               num_total_pages, total_used_pages, 1.0f, hp);
+  p.k = data;
+  p.indices = indices;
+  p.indptr = indptr;
+  p.last_page_len = last_page_len;
+  carve(p, hp, workspace);
+  const int elem = dtype == FA_DTYPE_F32 ? 4 : 2;
+  hipLaunchKernelGGL(fa::plan_kernel, dim3(1), dim3(fa::kPlanThreads), 0, stream, p);
+  if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+  hipLaunchKernelGGL(fa::gather_kernel, dim3(hp.units_bound, num_kv_heads), dim3(256), 0,
+                     stream, p, out, out_rows, elem);
+  if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+  return FA_OK;
+}
+
+fa_status_t fa_debug_timing_enable(int enable) {
+  Timing &t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  t.enabled = enable != 0;
+  return FA_OK;
+}
+
+fa_status_t fa_debug_timing_read(double *main_kernel_ms, double *whole_call_ms, int *calls) {
+  Timing &t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  double main_ms = 0.0, call_ms = 0.0;
+  bool ok = true;
+  for (auto &ev : t.recorded) {
+    float a = 0.0f, b = 0.0f;
+    if (hipEventSynchronize(ev[3]) != hipSuccess ||
+        hipEventElapsedTime(&a, ev[1], ev[2]) != hipSuccess ||
+        hipEventElapsedTime(&b, ev[0], ev[3]) != hipSuccess)
+      ok = false;
+    main_ms += a;
+    call_ms += b;
+    for (hipEvent_t e : ev) t.pool.push_back(e);
+  }
+  const int n = int(t.recorded.size());
+  t.recorded.clear();
+  if (main_kernel_ms) *main_kernel_ms = main_ms;
+  if (whole_call_ms) *whole_call_ms = call_ms;
+  if (calls) *calls = n;
+  return ok ? FA_OK : FA_ERR_LAUNCH;
+}
+
+fa_status_t fa_debug_plan(fa_dtype_t dtype, int batch, int num_qo_heads, int num_kv_heads,
+                          int head_dim, int page_size, int total_used_pages, int *chunk_rows,
+                          int *units_bound, int *heads_per_unit_out, int *kernel_kind) {
+  if (!dtype_ok(dtype)) return FA_ERR_UNSUPPORTED;
+  if (!extents_ok(batch, num_qo_heads, num_kv_heads, page_size) || total_used_pages < 0)
+    return FA_ERR_INVALID_PROBLEM;
+  if (!head_dim_ok(head_dim)) return FA_ERR_UNSUPPORTED;
+  const HostPlan hp = make_plan(batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                                total_used_pages, false);
+  if (chunk_rows) *chunk_rows = hp.chunk;
+  if (units_bound) *units_bound = hp.units_bound;
+  if (heads_per_unit_out) *heads_per_unit_out = hp.gt;
+  if (kernel_kind) *kernel_kind = hp.kind;
+  return FA_OK;
+}
+
+}  // extern "C"

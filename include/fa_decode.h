@@ -1,0 +1,163 @@
+/*
+ * fa_decode.h -- single-query GQA decode attention for MI355X (gfx950).
+ *
+ * One query token per request attends over that request's K/V history.  For a
+ * request b and query/output head h the KV head is g = h / (Hq / Hkv): runs of
+ * Hq/Hkv consecutive query heads share one KV head (ferrox-cuda 0.15.2,
+ * src/attn.rs, kernel source gqa_decode: the group-size and KV-head index).
+ * With L_b valid K/V rows,
+ *
+ *     x_j      = scale * <q[b,h,:], K_b[g,j,:]>          j = 0 .. L_b - 1
+ *     o[b,h,:] = sum_j softmax(x)_j * V_b[g,j,:]
+ *     lse[b,h] = ln sum_j exp(x_j)                        (natural log, f32)
+ *
+ * (ferrum-kernels 0.7.7, src/backend/cuda/decode_attention.rs, module doc: the
+ * scores, a numerically stable softmax, and the score-weighted sum of V;
+ * baracuda-kernels 0.0.1-alpha.68, src/attention/batch_paged_decode.rs, module
+ * doc "Query / output": the per-row log-sum-exp, always f32.)
+ * A request with L_b = 0 gets o = 0 and lse = -inf.
+ *
+ * Conventions common to every entry point:
+ *   - All buffer pointers are DEVICE pointers to dense, row-major (C-order)
+ *     arrays with no padding between rows.  Element type T is given by dtype;
+ *     indices, indptr and last_page_len are int32; lse is always f32.
+ *   - Arithmetic: products and sums in f32, o rounded once to T
+ *     (round-to-nearest-even).
+ *   - Ownership: the caller allocates and frees every buffer (inputs, outputs,
+ *     workspace).  The library allocates no device memory and keeps no state
+ *     between calls.
+ *   - Streams: work is enqueued on `stream` (0 = the null stream) and the call
+ *     returns without synchronising; outputs are ready when the stream reaches
+ *     that point.  No host<->device copies are made.
+ *   - Determinism: for a fixed argument set, results are bit-identical from
+ *     run to run on one device (fixed reduction order, no atomics).
+ *   - Errors: arguments are checked on the host in the order listed for each
+ *     entry point; any status other than FA_OK means nothing was enqueued,
+ *     except FA_ERR_LAUNCH, which reports a failed kernel launch.
+ *   - o and lse must not overlap any input or the workspace.
+ *   - Concurrent calls on different streams must use different workspaces.
+ */
+#ifndef FA_DECODE_H
+#define FA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, K, V and o (baracuda-kernels page, module doc
+ * "Constraints": f16, bf16 or f32). */
+typedef enum { FA_DTYPE_F32 = 0, FA_DTYPE_F16 = 1, FA_DTYPE_BF16 = 2 } fa_dtype_t;
+
+/* Status codes.  The three problem classes follow the error kinds the
+ * baracuda-kernels plan returns (BatchPagedDecodePlan::select, can_implement
+ * and run): an invalid problem, an unsupported one, and a workspace that is too
+ * small; FA_ERR_LAUNCH mirrors the launch-failure error of the ferrum-kernels
+ * and ferrox-cuda host wrappers. */
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_PROBLEM = 1,
+  FA_ERR_UNSUPPORTED = 2,
+  FA_ERR_WORKSPACE_TOO_SMALL = 3,
+  FA_ERR_LAUNCH = 4
+} fa_status_t;
+
+/* Bytes of device workspace a call needs (baracuda-kernels page,
+ * BatchPagedDecodePlan::workspace_size: auxiliary buffers the launcher fills on
+ * every call; ours also hold the split-KV partial results).
+ *
+ * A pure function of its arguments; it makes no device query.
+ *   paged calls:       fa_decode_workspace_size(batch, Hq, Hkv, D, page_size, total_used_pages)
+ *   contiguous calls:  fa_decode_workspace_size(1, Hq, Hkv, D, max_kv_len, 1)
+ * Returns 0 when the arguments are not a valid problem (the entry point then
+ * reports why); otherwise a positive size.  The workspace needs no
+ * initialisation and is overwritten by each call. */
+size_t fa_decode_workspace_size(int batch, int num_qo_heads, int num_kv_heads, int head_dim,
+                                int page_size, int total_used_pages);
+
+/* Decode against a contiguous cache (ferrum-kernels page, decode_attention and
+ * its argument list).
+ *
+ *   q        [Hq, D]              T   the single query token's heads
+ *   k_cache  [Hkv, max_kv_len, D] T   heads-major cache; rows >= valid_kv_len
+ *   v_cache  [Hkv, max_kv_len, D] T   are never read into the result
+ *   o        [Hq, D]              T   output
+ *   lse      [Hq]                 f32 output; may be NULL (not written)
+ *   scale    the score multiplier, usually 1/sqrt(D)
+ *   workspace, workspace_bytes   >= fa_decode_workspace_size(1, Hq, Hkv, D, max_kv_len, 1)
+ *
+ * Checks, in order:
+ *   dtype not one of fa_dtype_t                              -> FA_ERR_UNSUPPORTED
+ *   num_qo_heads, num_kv_heads or max_kv_len <= 0            -> FA_ERR_INVALID_PROBLEM
+ *   num_qo_heads % num_kv_heads != 0                         -> FA_ERR_INVALID_PROBLEM
+ *   head_dim not 64, 128 or 256                              -> FA_ERR_UNSUPPORTED
+ *   q, k_cache, v_cache or o NULL                            -> FA_ERR_INVALID_PROBLEM
+ *   valid_kv_len < 0 or > max_kv_len                         -> FA_ERR_INVALID_PROBLEM
+ *   workspace NULL or workspace_bytes short                  -> FA_ERR_WORKSPACE_TOO_SMALL
+ *   a kernel launch fails                                    -> FA_ERR_LAUNCH */
+fa_status_t fa_decode_contig(fa_dtype_t dtype, int num_qo_heads, int num_kv_heads,
+                             int head_dim, int max_kv_len, int valid_kv_len, float scale,
+                             const void *q, const void *k_cache, const void *v_cache,
+                             void *o, float *lse, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/* Batched decode against a paged K/V store (baracuda-kernels page: module doc
+ * "Layout" and "Query / output", the descriptor structs and
+ * BatchPagedDecodePlan::run).  Every request contributes one query row.
+ *
+ *   q              [batch, Hq, D]                   T
+ *   k_data, v_data [num_total_pages, Hkv, page_size, D] T  heads-major inside a page
+ *   indices        [total_used_pages]               int32 physical page ids,
+ *                                                   in [0, num_total_pages)
+ *   indptr         [batch + 1]                      int32 request b owns pages
+ *                                                   indices[indptr[b] .. indptr[b+1])
+ *   last_page_len  [batch]                          int32 rows used in the last page,
+ *                                                   in [0, page_size]
+ *   o              [batch, Hq, D]                   T   output
+ *   lse            [batch, Hq]                      f32 output (required)
+ *   sm_scale       the score multiplier, usually 1/sqrt(D)
+ *   workspace, workspace_bytes   >= fa_decode_workspace_size(batch, Hq, Hkv, D,
+ *                                                            page_size, total_used_pages)
+ *
+ * Request b has L_b = (n_b - 1) * page_size + last_page_len[b] rows, where
+ * n_b = indptr[b+1] - indptr[b]; L_b = 0 when n_b = 0.  Only row positions
+ * inside those L_b rows are read into the result.
+ *
+ * The page table lives in device memory and is not checked here: indptr[0] = 0,
+ * indptr non-decreasing, indptr[batch] <= total_used_pages, page ids in range
+ * and last_page_len in [0, page_size] are the caller's contract (the
+ * baracuda-kernels plan checks shapes only).  A table that breaks it gives
+ * unspecified results but never reads or writes outside the buffers described
+ * above.  The page table and its allocator stay with the caller.
+ *
+ * Checks, in order:
+ *   dtype not one of fa_dtype_t                               -> FA_ERR_UNSUPPORTED
+ *   batch, Hq, Hkv, page_size or num_total_pages <= 0         -> FA_ERR_INVALID_PROBLEM
+ *   num_qo_heads % num_kv_heads != 0                          -> FA_ERR_INVALID_PROBLEM
+ *   head_dim not 64, 128 or 256                               -> FA_ERR_UNSUPPORTED
+ *   total_used_pages < 0                                      -> FA_ERR_INVALID_PROBLEM
+ *   q, k_data, v_data, indptr, last_page_len, o or lse NULL,
+ *     or indices NULL with total_used_pages > 0               -> FA_ERR_INVALID_PROBLEM
+ *   total_used_pages * page_size >= 2^31 (row index range)    -> FA_ERR_UNSUPPORTED
+ *   workspace NULL or workspace_bytes short                   -> FA_ERR_WORKSPACE_TOO_SMALL
+ *   a kernel launch fails                                     -> FA_ERR_LAUNCH */
+fa_status_t fa_decode_paged(fa_dtype_t dtype, int batch, int num_qo_heads, int num_kv_heads,
+                            int head_dim, int page_size, int num_total_pages,
+                            int total_used_pages, float sm_scale, const void *q,
+                            const void *k_data, const void *v_data, const int32_t *indices,
+                            const int32_t *indptr, const int32_t *last_page_len, void *o,
+                            float *lse, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *fa_status_string(fa_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_DECODE_H */

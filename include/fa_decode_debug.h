@@ -1,0 +1,61 @@
+/*
+ * fa_decode_debug.h -- test and measurement hooks of the decode library.
+ *
+ * Not needed to run attention.  The gather hook exposes the page-table address
+ * generation of the decode kernels so a test can compare it bit for bit with an
+ * independent gather; the timing hooks let a benchmark time the dominant
+ * kernel with HIP events on the stream it is launched on.
+ */
+#ifndef FA_DECODE_DEBUG_H
+#define FA_DECODE_DEBUG_H
+
+#include "fa_decode.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Resolve a paged store through its page table (baracuda-kernels 0.0.1-alpha.68,
+ * src/attention/batch_paged_decode.rs, module doc "Layout") with the same
+ * row-address code the decode kernels use, and write the valid rows, as raw
+ * element bits, to out laid out [sum_b L_b, Hkv, D]: request 0's rows first,
+ * each request's rows in order.
+ *
+ *   data           [num_total_pages, Hkv, page_size, D]  element size from dtype
+ *   indices, indptr, last_page_len   as for fa_decode_paged (same contract)
+ *   out            [out_rows, Hkv, D]; rows past out_rows are not written
+ *   workspace      >= fa_decode_workspace_size(batch, Hkv, Hkv, D, page_size,
+ *                                              total_used_pages)
+ * Checks are those of fa_decode_paged that apply (dtype, extents, head_dim,
+ * NULL pointers, row range, workspace), plus out_rows < 0 -> FA_ERR_INVALID_PROBLEM.
+ * Asynchronous on stream, like the decode calls. */
+fa_status_t fa_debug_gather_paged(fa_dtype_t dtype, int batch, int num_kv_heads, int head_dim,
+                                  int page_size, int num_total_pages, int total_used_pages,
+                                  const void *data, const int32_t *indices,
+                                  const int32_t *indptr, const int32_t *last_page_len,
+                                  void *out, int64_t out_rows, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/* Kernel timing.  While enabled, every decode call records a HIP event pair on
+ * its stream around its main attention kernel (the one that streams K and V),
+ * and another around the whole call.  fa_debug_timing_read waits for the
+ * recorded events, returns the summed milliseconds and the number of calls
+ * since the last reset, and resets.  Process-wide; meant for one benchmarking
+ * thread.  Returns FA_ERR_LAUNCH if a HIP event call fails. */
+fa_status_t fa_debug_timing_enable(int enable);
+fa_status_t fa_debug_timing_read(double *main_kernel_ms, double *whole_call_ms, int *calls);
+
+/* The launch plan a decode call with these arguments would use (host-side
+ * arithmetic only): KV rows per split unit, the bound on split units, query
+ * heads per workgroup, and which attention kernel runs (0 = vector ALU,
+ * 1 = matrix-core).  Returns FA_ERR_INVALID_PROBLEM for arguments the entry
+ * points would reject on extents. */
+fa_status_t fa_debug_plan(fa_dtype_t dtype, int batch, int num_qo_heads, int num_kv_heads,
+                          int head_dim, int page_size, int total_used_pages, int *chunk_rows,
+                          int *units_bound, int *heads_per_unit, int *kernel_kind);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_DECODE_DEBUG_H */

@@ -1,0 +1,180 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+The library must load and export every function the public headers declare.
+Argument checks happen on the host before any HIP call, so each rejection path
+can be exercised here with placeholder pointers that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_attention_query_amd as fad
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INCLUDE = os.path.join(ROOT, "include")
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below is rejected first
+
+
+def _declared_functions():
+    names = set()
+    for fn in os.listdir(INCLUDE):
+        if fn.endswith(".h"):
+            text = open(os.path.join(INCLUDE, fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fad.load_library()
+    declared = _declared_functions()
+    assert declared, "no declarations found"
+    assert declared == set(fad.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code, name in fad.STATUS_NAMES.items():
+        assert fad.fa_status_string(code) == name
+
+
+def test_workspace_size():
+    ws = fad.fa_decode_workspace_size
+    assert ws(64, 32, 8, 128, 16, 17408) > 0
+    assert ws(1, 8, 2, 64, 256, 1) > 0
+    # invalid problems report 0
+    assert ws(0, 32, 8, 128, 16, 10) == 0
+    assert ws(4, 30, 8, 128, 16, 10) == 0       # group not integral
+    assert ws(4, 32, 8, 96, 16, 10) == 0        # head_dim unsupported
+    assert ws(4, 32, 8, 128, 0, 10) == 0
+    assert ws(4, 32, 8, 128, 16, -1) == 0
+    assert ws(4, 32, 8, 128, 1 << 20, 1 << 12) == 0  # 2^32 rows
+    # grows with the problem
+    assert ws(64, 32, 8, 128, 16, 40000) >= ws(64, 32, 8, 128, 16, 1000)
+    assert ws(64, 32, 8, 256, 16, 1000) >= ws(64, 32, 8, 128, 16, 1000)
+
+
+def test_plan_covers_units():
+    """The unit bound covers any request lengths the page table allows."""
+    for dtype, b, hq, hkv, d, p, used in [(2, 64, 32, 8, 128, 16, 17408),
+                                          (2, 32, 64, 8, 128, 32, 32768),
+                                          (1, 128, 16, 4, 256, 16, 33000),
+                                          (0, 1, 8, 2, 64, 256, 1),
+                                          (2, 3, 12, 4, 64, 3, 7)]:
+        chunk, bound, gt, kind = fad.fa_debug_plan(dtype, b, hq, hkv, d, p, used)
+        assert chunk > 0 and chunk % 256 == 0
+        assert (hq // hkv) % gt == 0 and gt in (1, 2, 4, 8)
+        # worst case: every row in one request, or spread so each request wastes a unit
+        rows = used * p
+        assert bound >= -(-rows // chunk) + (b - 1)
+
+
+def _paged(*, dtype=2, batch=2, hq=8, hkv=2, d=128, page=16, pages=10, used=4,
+           ptrs=None, ws=FAKE, ws_bytes=1 << 30):
+    lib = fad.load_library()
+    q = k = v = ind = ptr = lpl = o = lse = FAKE
+    if ptrs:
+        q, k, v, ind, ptr, lpl, o, lse = [ptrs.get(n, FAKE) for n in
+                                          ("q", "k", "v", "ind", "ptr", "lpl", "o", "lse")]
+    return lib.fa_decode_paged(dtype, batch, hq, hkv, d, page, pages, used, 0.125, q, k, v, ind,
+                               ptr, lpl, o, lse, ws, ws_bytes, None)
+
+
+def _contig(*, dtype=1, hq=8, hkv=2, d=64, max_len=256, valid=128, ptrs=None, ws=FAKE,
+            ws_bytes=1 << 30):
+    lib = fad.load_library()
+    q = k = v = o = lse = FAKE
+    if ptrs:
+        q, k, v, o, lse = [ptrs.get(n, FAKE) for n in ("q", "k", "v", "o", "lse")]
+    return lib.fa_decode_contig(dtype, hq, hkv, d, max_len, valid, 0.125, q, k, v, o, lse, ws,
+                                ws_bytes, None)
+
+
+INV, UNS, WS = fad.FA_ERR_INVALID_PROBLEM, fad.FA_ERR_UNSUPPORTED, fad.FA_ERR_WORKSPACE_TOO_SMALL
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=3), UNS),
+    (dict(dtype=-1), UNS),
+    (dict(batch=0), INV),
+    (dict(hq=0), INV),
+    (dict(hkv=0), INV),
+    (dict(page=0), INV),
+    (dict(pages=0), INV),
+    (dict(hq=12, hkv=8), INV),
+    (dict(d=96), UNS),
+    (dict(d=512), UNS),
+    (dict(used=-1), INV),
+    (dict(ptrs={"q": None}), INV),
+    (dict(ptrs={"k": None}), INV),
+    (dict(ptrs={"v": None}), INV),
+    (dict(ptrs={"ind": None}), INV),
+    (dict(ptrs={"ptr": None}), INV),
+    (dict(ptrs={"lpl": None}), INV),
+    (dict(ptrs={"o": None}), INV),
+    (dict(ptrs={"lse": None}), INV),
+    (dict(page=1 << 20, used=1 << 11, pages=1 << 11), UNS),
+    (dict(ws=None), WS),
+    (dict(ws_bytes=16), WS),
+    # order: the dtype is checked before the extents, the extents before head_dim
+    (dict(dtype=7, batch=0), UNS),
+    (dict(batch=0, d=96), INV),
+    (dict(d=96, ptrs={"q": None}), UNS),
+    (dict(ptrs={"q": None}, ws=None), INV),
+])
+def test_paged_rejects(kw, status):
+    assert _paged(**kw) == status
+
+
+def test_paged_workspace_exact_boundary():
+    need = fad.fa_decode_workspace_size(2, 8, 2, 128, 16, 4)
+    assert _paged(ws_bytes=need - 1) == WS
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=5), UNS),
+    (dict(hq=0), INV),
+    (dict(hkv=0), INV),
+    (dict(max_len=0, valid=0), INV),
+    (dict(hq=6, hkv=4), INV),
+    (dict(d=32), UNS),
+    (dict(ptrs={"q": None}), INV),
+    (dict(ptrs={"k": None}), INV),
+    (dict(ptrs={"v": None}), INV),
+    (dict(ptrs={"o": None}), INV),
+    (dict(valid=-1), INV),
+    (dict(valid=257), INV),
+    (dict(ws=None), WS),
+    (dict(ws_bytes=0), WS),
+])
+def test_contig_rejects(kw, status):
+    assert _contig(**kw) == status
+
+
+def test_gather_rejects():
+    lib = fad.load_library()
+    args = [2, 2, 2, 128, 16, 10, 4, FAKE, FAKE, FAKE, FAKE, FAKE]
+    assert lib.fa_debug_gather_paged(*args, -1, FAKE, 1 << 30, None) == INV
+    assert lib.fa_debug_gather_paged(*args, 10, None, 0, None) == WS
+    bad = list(args)
+    bad[3] = 100
+    assert lib.fa_debug_gather_paged(*bad, 10, FAKE, 1 << 30, None) == UNS
+
+
+def test_binding_rejects_host_tensors():
+    """The binding refuses buffers that are not device memory before calling in."""
+    import torch
+    q = torch.zeros(8, 64)
+    with pytest.raises(ValueError):
+        fad.fa_decode_contig(0, 8, 2, 64, 16, 8, 0.125, q, q, q, q, None, q)
+
+
+def test_timing_hooks_without_calls():
+    fad.fa_debug_timing_enable(1)
+    main_ms, call_ms, n = fad.fa_debug_timing_read()
+    fad.fa_debug_timing_enable(0)
+    assert (main_ms, call_ms, n) == (0.0, 0.0, 0)
