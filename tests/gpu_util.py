@@ -12,6 +12,18 @@ import workloads as W
 # tolerances (absolute): o per element type, lse always f32 against f64
 O_TOL = {"f32": 1e-5, "f16": 4e-3, "bf16": 4e-3}
 LSE_TOL = 1e-4
+MANT_BITS = {"f32": 23, "f16": 10, "bf16": 7}
+
+
+def o_tolerance(dtype, o_ref):
+    """Per-element bound on |o - o_ref|: the stated tolerance, or one unit in
+    the last place of the element type at |o_ref| where that is larger.  Even
+    the correctly rounded exact result is half an ulp away from o_ref, and for
+    |o| >= 1 half a bf16 ulp already exceeds 4e-3; below 1 (every configured
+    workload) the bound is the stated tolerance itself."""
+    mag = np.maximum(np.abs(o_ref), np.finfo(np.float64).tiny)
+    ulp = np.exp2(np.floor(np.log2(mag)) - MANT_BITS[dtype])
+    return np.maximum(O_TOL[dtype], ulp)
 
 
 def device():
@@ -53,18 +65,22 @@ def oracle_of(p, samples=None):
                                 p.valid_kv_len, p.scale)
 
 
-def compare(dtype, o_gpu, lse_gpu, o_ref, lse_ref, what=""):
-    """Element-by-element check; returns (max |do|, max |dlse|)."""
+def compare(dtype, o_gpu, lse_gpu, o_ref, lse_ref, what="", strict=False):
+    """Element-by-element check; returns (max |do|, max |dlse|).  strict: the
+    stated tolerance alone, with no one-ulp allowance for |o| >= 1."""
     go = o_gpu.float().cpu().numpy().astype(np.float64).reshape(o_ref.shape)
     gl = lse_gpu.cpu().numpy().astype(np.float64).reshape(lse_ref.shape)
     empty = np.isneginf(lse_ref)
     assert np.array_equal(np.isneginf(gl), empty), f"{what}: -inf lse pattern differs"
     assert np.all(go[empty] == 0.0), f"{what}: empty rows must give o = 0"
     assert np.all(np.isfinite(go)), f"{what}: non-finite o"
-    err_o = float(np.max(np.abs(go - o_ref))) if go.size else 0.0
+    diff = np.abs(go - o_ref)
+    err_o = float(np.max(diff)) if go.size else 0.0
     fin = ~empty
     err_l = float(np.max(np.abs(gl[fin] - lse_ref[fin]))) if fin.any() else 0.0
-    assert err_o <= O_TOL[dtype], f"{what}: max |o - oracle| = {err_o:.3e} > {O_TOL[dtype]}"
+    tol = O_TOL[dtype] if strict else o_tolerance(dtype, o_ref)
+    worst = float(np.max(diff - tol)) if go.size else -1.0
+    assert worst <= 0.0, f"{what}: max |o - oracle| = {err_o:.3e} exceeds its bound by {worst:.3e}"
     assert err_l <= LSE_TOL, f"{what}: max |lse - oracle| = {err_l:.3e} > {LSE_TOL}"
     return err_o, err_l
 

@@ -61,7 +61,7 @@ def test_full_config_parity(dev, name):
     torch.cuda.synchronize()
     if isinstance(p, W.ContigProblem):
         ro, rl = oracle_of(p)
-        eo, el = compare(p.dtype, o, lse, ro, rl, p.name)
+        eo, el = compare(p.dtype, o, lse, ro, rl, p.name, strict=True)
     else:
         pairs = sample_pairs(p, 96, np.random.default_rng(5))
         ro, rl = oracle_of(p, samples=pairs)
@@ -69,7 +69,7 @@ def test_full_config_parity(dev, name):
             torch.from_numpy(pairs[:, 1].astype(np.int64))
         o_s = o.cpu()[idx[0], idx[1]]
         l_s = lse.cpu()[idx[0], idx[1]]
-        eo, el = compare(p.dtype, o_s, l_s, ro, rl, p.name)
+        eo, el = compare(p.dtype, o_s, l_s, ro, rl, p.name, strict=True)
         # every output: finite, and -inf lse exactly for the empty requests
         lens = oracle.seq_lens(p.page_size, p.indptr.numpy(), p.last_page_len.numpy())
         lse_all = lse.cpu().numpy()
