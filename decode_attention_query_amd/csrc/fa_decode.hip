@@ -13,6 +13,7 @@
 #include "../../include/fa_decode_debug.h"
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
+#include "fa_mfma.hpp"
 
 namespace {
 
@@ -27,11 +28,17 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-int heads_per_unit(int group) {
-  for (int gt : {8, 4, 2})
+// Query heads per workgroup: the largest power of two dividing the group that
+// the kernel's head block holds (8 for the vector-ALU kernel, 16 for the
+// matrix-core kernel's 16-wide MFMA column block).
+int heads_per_unit(int group, int max_heads) {
+  for (int gt = max_heads; gt > 1; gt /= 2)
     if (group % gt == 0) return gt;
   return 1;
 }
+
+// 0: vector-ALU kernel (f32); 1: matrix-core kernel (f16, bf16)
+int kernel_kind(fa_dtype_t dt) { return dt == FA_DTYPE_F32 ? 0 : 1; }
 
 struct HostPlan {
   int group = 0, gt = 0, n_gblocks = 0, planes = 0;
@@ -52,16 +59,18 @@ bool grid_ok(int hq, int hkv) { return hq / hkv > 0 && hkv * (hq / hkv) <= 65535
 
 // The plan for a call; `page_size` is max_kv_len and total_used_pages 1 for a
 // contiguous cache.  Pure host arithmetic.
-HostPlan make_plan(int batch, int hq, int hkv, int d, int page_size, int total_used_pages,
-                   bool contig) {
+HostPlan make_plan(fa_dtype_t dt, int batch, int hq, int hkv, int d, int page_size,
+                   int total_used_pages, bool contig) {
   HostPlan hp;
+  hp.kind = kernel_kind(dt);
   hp.group = hq / hkv;
-  hp.gt = heads_per_unit(hp.group);
+  hp.gt = heads_per_unit(hp.group, hp.kind == 0 ? 8 : 16);
   hp.n_gblocks = hp.group / hp.gt;
   hp.planes = hkv * hp.n_gblocks;
-  hp.kind = 0;
+  // The split size depends on the KV heads only (not on the kernel's head
+  // blocking), so the workspace size is the same for every element type.
   const int64_t rows_ub = int64_t(std::max(total_used_pages, 0)) * page_size;
-  int64_t want = (rows_ub * hp.planes + kTargetWorkgroups - 1) / kTargetWorkgroups;
+  int64_t want = (rows_ub * hkv + kTargetWorkgroups - 1) / kTargetWorkgroups;
   want = std::max<int64_t>(want, kChunkQuantum);
   int64_t chunk = (want + kChunkQuantum - 1) / kChunkQuantum * kChunkQuantum;
   chunk = std::min(chunk, kMaxChunk);
@@ -172,6 +181,22 @@ hipError_t launch_decode(const DecodeParams &p, const HostPlan &hp, hipStream_t 
   }
 }
 
+template <class E, int D>
+hipError_t launch_mfma(const DecodeParams &p, const HostPlan &hp, hipStream_t s) {
+  dim3 grid(hp.units_bound, hp.planes);
+  hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <class E>
+hipError_t launch_decode_mfma(const DecodeParams &p, const HostPlan &hp, hipStream_t s) {
+  switch (p.head_dim) {
+    case 64: return launch_mfma<E, 64>(p, hp, s);
+    case 128: return launch_mfma<E, 128>(p, hp, s);
+    default: return launch_mfma<E, 256>(p, hp, s);
+  }
+}
+
 template <class E>
 hipError_t launch_merge(const DecodeParams &p, hipStream_t s) {
   const int items = p.batch * p.num_qo_heads;
@@ -183,8 +208,8 @@ hipError_t dispatch_decode(fa_dtype_t dt, const DecodeParams &p, const HostPlan 
                            hipStream_t s) {
   switch (dt) {
     case FA_DTYPE_F32: return launch_decode<fa::F32>(p, hp, s);
-    case FA_DTYPE_F16: return launch_decode<fa::F16>(p, hp, s);
-    default: return launch_decode<fa::BF16>(p, hp, s);
+    case FA_DTYPE_F16: return launch_decode_mfma<fa::F16>(p, hp, s);
+    default: return launch_decode_mfma<fa::BF16>(p, hp, s);
   }
 }
 
@@ -218,6 +243,7 @@ DecodeParams base_params(int batch, int hq, int hkv, int d, int page_size, int p
   p.total_used_pages = total_used_pages;
   p.group = hp.group;
   p.n_gblocks = hp.n_gblocks;
+  p.heads_per_unit = hp.gt;
   p.scale_log2 = scale * fa::kLog2e;
   p.page_div = fa::make_fastdiv(uint32_t(page_size));
   p.chunk = hp.chunk;
@@ -235,8 +261,8 @@ size_t fa_decode_workspace_size(int batch, int num_qo_heads, int num_kv_heads, i
       total_used_pages < 0)
     return 0;
   if (int64_t(total_used_pages) * page_size >= (int64_t(1) << 31)) return 0;
-  return make_plan(batch, num_qo_heads, num_kv_heads, head_dim, page_size, total_used_pages,
-                   false)
+  return make_plan(FA_DTYPE_BF16, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                   total_used_pages, false)
       .total;
 }
 
@@ -258,8 +284,8 @@ fa_status_t fa_decode_contig(fa_dtype_t dtype, int num_qo_heads, int num_kv_head
 
   // Sized like the workspace query (a single page of max_kv_len rows) so the
   // split units fit what the caller allocated.
-  const HostPlan hp =
-      make_plan(1, num_qo_heads, num_kv_heads, head_dim, max_kv_len, 1, /*contig=*/true);
+  const HostPlan hp = make_plan(dtype, 1, num_qo_heads, num_kv_heads, head_dim, max_kv_len, 1,
+                                /*contig=*/true);
   DecodeParams p = base_params(1, num_qo_heads, num_kv_heads, head_dim, max_kv_len, 1, 1,
                                scale, hp);
   p.q = q;
@@ -306,7 +332,7 @@ fa_status_t fa_decode_paged(fa_dtype_t dtype, int batch, int num_qo_heads, int n
                                                page_size, total_used_pages);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
 
-  const HostPlan hp = make_plan(batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+  const HostPlan hp = make_plan(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
                                 total_used_pages, false);
   DecodeParams p = base_params(batch, num_qo_heads, num_kv_heads, head_dim, page_size,
                                num_total_pages, total_used_pages, sm_scale, hp);
@@ -363,7 +389,7 @@ fa_status_t fa_debug_gather_paged(fa_dtype_t dtype, int batch, int num_kv_heads,
   const size_t need = fa_decode_workspace_size(batch, num_kv_heads, num_kv_heads, head_dim,
                                                page_size, total_used_pages);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
-  const HostPlan hp = make_plan(batch, num_kv_heads, num_kv_heads, head_dim, page_size,
+  const HostPlan hp = make_plan(dtype, batch, num_kv_heads, num_kv_heads, head_dim, page_size,
                                 total_used_pages, false);
   DecodeParams p = base_params(batch, num_kv_heads, num_kv_heads, head_dim, page_size,
                                num_total_pages, total_used_pages, 1.0f, hp);
@@ -418,7 +444,7 @@ fa_status_t fa_debug_plan(fa_dtype_t dtype, int batch, int num_qo_heads, int num
   if (!extents_ok(batch, num_qo_heads, num_kv_heads, page_size) || total_used_pages < 0)
     return FA_ERR_INVALID_PROBLEM;
   if (!head_dim_ok(head_dim)) return FA_ERR_UNSUPPORTED;
-  const HostPlan hp = make_plan(batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+  const HostPlan hp = make_plan(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
                                 total_used_pages, false);
   if (chunk_rows) *chunk_rows = hp.chunk;
   if (units_bound) *units_bound = hp.units_bound;

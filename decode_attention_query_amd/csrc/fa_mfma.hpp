@@ -1,0 +1,307 @@
+// fa_mfma.hpp -- matrix-core (MFMA) decode kernel for f16 / bf16 K/V on gfx950.
+//
+// One workgroup = one split unit of one KV head and a block of up to 16 query
+// heads of its group (the whole group when G <= 16), so K and V are read from
+// HBM once for all those heads.  Four waves; each wave streams its own 32-row
+// tiles of the unit and keeps its own online-softmax state; the waves are
+// merged through LDS at the end.
+//
+// Per 32-row tile, with n = lane % 16 and grp = lane / 16:
+//   scores   S^T[t][g] = sum_d K[t][d] Q[g][d]        v_mfma_f32_16x16x32 (bf16|f16)
+//            A = K rows (lane: row n of a 16-row block, 8 features at 32kk + 8grp,
+//            straight from a 16-byte global load), B = Q^T (lane: head n).
+//            Result: lane holds S for head g = n and rows 4grp + i (i < 4) of
+//            each of the two 16-row blocks.
+//   softmax  per head (column): the tile max over the 32 rows (in-lane max of
+//            8, then across the four lane groups), one rescale of the running
+//            state, p = 2^(s - m).
+//   P.V      O^T[d][g] += sum_t V[t][d] P[t][g]      v_mfma_f32_16x16x32
+//            B = P^T is exactly the lane's 8 probabilities (row order below),
+//            A = V^T is read transposed from LDS, where the wave stored its
+//            V tile.  bf16 P keeps 8 bits, so P is split into hi + lo bf16
+//            parts (two MFMAs) to keep P.V at ~16-bit accuracy; f16 P is used
+//            as is.
+// The contraction index k of both P.V operands is mapped to tile rows as
+// row(k = 8 grp + i) = 16 (i / 4) + 4 grp + (i % 4), which is where the score
+// MFMA left each lane's probabilities; any k order works as long as A and B
+// agree, which they do by construction.
+#pragma once
+
+#include "fa_common.hpp"
+#include "fa_kernels.hpp"
+
+namespace fa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+template <class E>
+struct Mfma;
+
+template <>
+struct Mfma<BF16> {
+  typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+  typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+  static constexpr bool kSplitP = true;
+  __device__ static inline f32x4 mma(v8 a, v8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline __bf16 from_bits(uint16_t u) { return __builtin_bit_cast(__bf16, u); }
+};
+
+template <>
+struct Mfma<F16> {
+  typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+  typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+  static constexpr bool kSplitP = false;
+  __device__ static inline f32x4 mma(v8 a, v8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline _Float16 from_bits(uint16_t u) {
+    return __builtin_bit_cast(_Float16, u);
+  }
+};
+
+// 8 probabilities -> MFMA operand(s), round-to-nearest-even; with kSplitP the
+// residual p - hi is rounded into lo, so hi + lo carries ~16 significant bits.
+template <class E>
+__device__ inline void pack_probs(const float *p, typename Mfma<E>::v8 &hi,
+                                  typename Mfma<E>::v8 &lo) {
+  using M = Mfma<E>;
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const f32x2 f = {p[e], p[e + 1]};
+    const typename M::v2 h = __builtin_convertvector(f, typename M::v2);
+    hi[e] = h[0];
+    hi[e + 1] = h[1];
+    if constexpr (M::kSplitP) {
+      const f32x2 back = __builtin_convertvector(h, f32x2);
+      const f32x2 r = {f[0] - back[0], f[1] - back[1]};
+      const typename M::v2 l = __builtin_convertvector(r, typename M::v2);
+      lo[e] = l[0];
+      lo[e + 1] = l[1];
+    }
+  }
+}
+
+// K and V of one 32-row tile in the MFMA A-operand order: [block j][k step kk].
+template <int KK>
+struct KVTile {
+  uint4 k[2][KK];
+  uint4 v[2][KK];
+};
+
+template <class E, int D>
+struct MfmaGeom {
+  static constexpr int NW = 4;           // waves per workgroup
+  static constexpr int TT = 32;          // rows per wave tile
+  static constexpr int KK = D / 32;      // score k-steps per 16-row block
+  static constexpr int MB = D / 16;      // 16-feature blocks of O^T
+  static constexpr int ROW = D * 2 + 16; // LDS bytes per V row (16-byte pad)
+  static constexpr int WAVE_LDS = TT * ROW;
+  static constexpr int LDS_V = NW * WAVE_LDS;
+  static constexpr int LDS_ACC = NW * 16 * D * 4;  // merge area (reuses the V area)
+  static constexpr int LDS = LDS_V > LDS_ACC ? LDS_V : LDS_ACC;
+  static constexpr bool kPipelined = D <= 128;   // prefetch one tile ahead
+};
+
+// Issues the global loads of the tile whose first row is t0 (rows past t_end
+// are clamped to t_end - 1: in bounds, and masked out of the softmax later).
+template <class E, int D>
+__device__ inline void issue_tile(KVTile<D / 32> &T, const DecodeParams &p, int32_t page_base,
+                                  int kvh, int t0, int t_end, int n, int grp) {
+  constexpr int KK = D / 32;
+  const char *kb = static_cast<const char *>(p.k) + (int64_t)(8 * grp) * 2;
+  const char *vb = static_cast<const char *>(p.v) + (int64_t)(8 * grp) * 2;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int t = min(t0 + 16 * j + n, t_end - 1);
+    const int64_t off = kv_row_offset(p, page_base, kvh, t) * 2;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      T.k[j][kk] = load16_stream(kb + off + kk * 64);
+      T.v[j][kk] = load16_stream(vb + off + kk * 64);
+    }
+  }
+}
+
+template <class E, int D>
+__global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) {
+  using G = MfmaGeom<E, D>;
+  using M = Mfma<E>;
+  using v8 = typename M::v8;
+  constexpr int KK = G::KK, MB = G::MB, NW = G::NW, TT = G::TT;
+
+  __shared__ __attribute__((aligned(16))) char lds[G::LDS];
+  __shared__ float s_m[NW][16];
+  __shared__ float s_l[NW][16];
+
+  UnitInfo u;
+  if (!resolve_unit(p, blockIdx.x, u)) return;
+  const int gt = p.heads_per_unit;  // valid columns of the 16-wide head block
+  const int kvh = blockIdx.y / p.n_gblocks;
+  const int h0 = kvh * p.group + (blockIdx.y % p.n_gblocks) * gt;
+  const int t_begin = u.c * p.chunk;
+  const int t_end = min(u.L, t_begin + p.chunk);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 15;
+  const int grp = lane >> 4;
+
+  // B operand of the score MFMA: Q^T, head n, features 32kk + 8grp .. +8.
+  v8 qb[KK];
+  {
+    const bool live = n < gt;
+    const char *qrow = static_cast<const char *>(p.q) +
+                       (((int64_t)u.b * p.num_qo_heads + h0 + (live ? n : 0)) * D + 8 * grp) * 2;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      uint4 r = *reinterpret_cast<const uint4 *>(qrow + kk * 64);
+      if (!live) r = make_uint4(0, 0, 0, 0);
+      qb[kk] = __builtin_bit_cast(v8, r);
+    }
+  }
+
+  f32x4 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = -INFINITY;  // running max (base 2) of head n; same in all 4 lane groups
+  float l_run = 0.0f;       // this lane's share of the normaliser of head n
+
+  char *wl = lds + wave * G::WAVE_LDS;
+  const uint16_t *vl = reinterpret_cast<const uint16_t *>(wl);
+  const float c = p.scale_log2;
+
+  auto compute = [&](const KVTile<KK> &T, int t0) {
+    // V tile to LDS: row 16j + n, features 32kk + 8grp .. +8
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        *reinterpret_cast<uint4 *>(wl + (16 * j + n) * G::ROW + (32 * kk + 8 * grp) * 2) =
+            T.v[j][kk];
+    // scores
+    f32x4 s[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      s[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        s[j] = M::mma(__builtin_bit_cast(v8, T.k[j][kk]), qb[kk], s[j]);
+    }
+    // online softmax for head n over the tile's rows 16j + 4grp + i
+    float x[8];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 16 * j + 4 * grp + i;
+        const float v = t < t_end ? s[j][i] * c : -INFINITY;
+        x[4 * j + i] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);
+    const float ref = safe_ref(m_new);
+    const float alpha = fast_exp2(m_run - ref);
+    float pr[8];
+    float psum = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pr[e] = fast_exp2(x[e] - ref);
+      psum += pr[e];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] *= alpha;
+    v8 ph, pl;
+    pack_probs<E>(pr, ph, pl);
+    // this wave's LDS stores before its transposed reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      v8 a;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = 16 * (i >> 2) + 4 * grp + (i & 3);
+        a[i] = M::from_bits(vl[row * (G::ROW / 2) + 16 * mb + n]);
+      }
+      acc[mb] = M::mma(a, ph, acc[mb]);
+      if constexpr (M::kSplitP) acc[mb] = M::mma(a, pl, acc[mb]);
+    }
+    // the reads above complete before the next tile overwrites the area
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  const int stride = NW * TT;
+  int t0 = t_begin + wave * TT;
+  if (t0 < t_end) {
+    KVTile<KK> A;
+    issue_tile<E, D>(A, p, u.page_base, kvh, t0, t_end, n, grp);
+    if constexpr (G::kPipelined) {
+      KVTile<KK> B;
+      while (true) {
+        issue_tile<E, D>(B, p, u.page_base, kvh, t0 + stride, t_end, n, grp);
+        compute(A, t0);
+        t0 += stride;
+        if (t0 >= t_end) break;
+        issue_tile<E, D>(A, p, u.page_base, kvh, t0 + stride, t_end, n, grp);
+        compute(B, t0);
+        t0 += stride;
+        if (t0 >= t_end) break;
+      }
+    } else {
+      while (true) {
+        compute(A, t0);
+        t0 += stride;
+        if (t0 >= t_end) break;
+        issue_tile<E, D>(A, p, u.page_base, kvh, t0, t_end, n, grp);
+      }
+    }
+  }
+
+  // ---- merge the four lane groups' normalisers, then the waves
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  __syncthreads();  // every wave is done with its V area; reuse it for the merge
+  float *s_acc = reinterpret_cast<float *>(lds);  // [NW][16][D]
+  if (n < gt) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        s_acc[(wave * 16 + n) * D + 16 * mb + 4 * grp + i] = acc[mb][i];
+    if (grp == 0) {
+      s_m[wave][n] = m_run;
+      s_l[wave][n] = l_run;
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < gt * D; idx += NW * 64) {
+    const int g = idx / D;
+    const int d = idx % D;
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) Mx = fmaxf(Mx, s_m[w][g]);
+    const float ref = safe_ref(Mx);
+    float lsum = 0.0f, a = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float sw = fast_exp2(s_m[w][g] - ref);
+      lsum += s_l[w][g] * sw;
+      a += s_acc[(w * 16 + g) * D + d] * sw;
+    }
+    emit<E>(p, u, blockIdx.x, h0 + g, d, Mx, lsum, a);
+  }
+}
+
+}  // namespace fa
