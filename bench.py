@@ -76,6 +76,28 @@ def cpu_baseline(p, nbytes):
             "sample": f"the whole {p.name} call (every request and head), one run"}
 
 
+def hbm_probe(dev, nbytes=2 << 30, reps=10):
+    """Achievable bandwidth on this GPU, for context: torch's copy kernel
+    (reads and writes nbytes each) and a full reduction (reads nbytes)."""
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).normal_()
+    dst = torch.empty_like(src)
+    out = {}
+    for name, fn, moved in (("copy", lambda: dst.copy_(src), 2 * nbytes),
+                            ("read", lambda: src.sum(dtype=torch.float32), nbytes)):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        out[name + "_GBps"] = round(moved * reps / (a.elapsed_time(b) * 1e-3) / 1e9, 1)
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -83,6 +105,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c3", choices=sorted(W.FULL))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--probe", action="store_true",
+                    help="also measure torch copy / read bandwidth for context")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -172,8 +196,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None, "kernel_us": round(kernel_ms * 1e3, 2),
-                     "kernel": "decode attention (fa::decode_*_kernel)"},
+                     "kernel": "decode attention with fused split merge (fa::decode_*_kernel)"},
     }
+    if args.probe:
+        line["hbm_probe"] = hbm_probe(dev)
     if not args.no_cpu_baseline:
         print("[bench] timing the float64 oracle on the host", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(p, nbytes)

@@ -41,6 +41,17 @@ __host__ __device__ inline uint32_t fastdiv(uint32_t n, FastDiv f) {
   return (uint32_t)(((uint64_t)hi + n) >> f.shift);
 }
 
+// One split unit, as the plan kernel describes it (32 bytes, one scalar load).
+struct UnitDesc {
+  int32_t b;          // request; -1 for units past the real count
+  int32_t c;          // index of the unit within its request
+  int32_t n_units;    // units of the request
+  int32_t L;          // L_b
+  int32_t page_base;  // first index of the request's pages in indices
+  int32_t u0;         // first unit of the request
+  int32_t pad0, pad1;
+};
+
 // Everything a decode launch needs.  Passed by value as the kernel argument.
 struct DecodeParams {
   // tensors
@@ -64,16 +75,15 @@ struct DecodeParams {
   int chunk;          // KV rows per split unit
   int units_bound;    // grid.x; units past the real count exit at once
   int contig;         // 1: contiguous cache (a single page of max_kv_len rows)
+  int uniform_blocks; // 1: every 16-row block starting at a multiple of 16 lies in one page
   int contig_len;     // contiguous: valid_kv_len
   int contig_units;   // contiguous: ceil(valid_kv_len / chunk), at least 1
   // workspace regions
-  int32_t *seq_len;       // [B]       L_b
-  int32_t *page_base;     // [B]       first index of request b's pages in indices
-  int32_t *unit_prefix;   // [B + 1]   first split unit of each request
   int64_t *row_prefix;    // [B + 1]   first output row of each request (gather hook)
-  int32_t *unit_req;      // [units_bound] request of each split unit
+  struct UnitDesc *unit_desc;  // [units_bound]
   float *part_lse;        // [units_bound, Hq]     base-2 lse of each split's partial
   float *part_o;          // [units_bound, Hq, D]  normalised partial outputs
+  int32_t *arrivals;      // [B, Hq]   finished split units per (request, head block)
 };
 
 // ---------------------------------------------------------------- elements
@@ -166,6 +176,36 @@ __device__ inline int64_t kv_row_offset(const DecodeParams &p, int32_t page_base
     page = id;
   }
   return ((page * p.num_kv_heads + kvh) * (int64_t)p.page_size + row) * p.head_dim;
+}
+
+// Element offset of the first row of the 16-row block starting at row tb
+// (wave-uniform), for blocks that lie in one page.  The page id is read with a
+// scalar load, so it does not queue behind the wave's outstanding K/V loads.
+__device__ inline int64_t block_row_offset(const DecodeParams &p, int32_t page_base, int kvh,
+                                           int tb) {
+  int64_t page = 0;
+  uint32_t row = (uint32_t)tb;
+  if (!p.contig) {
+    const uint32_t slot = fastdiv((uint32_t)tb, p.page_div);
+    row = (uint32_t)tb - slot * (uint32_t)p.page_size;
+    typedef const __attribute__((address_space(4))) int32_t cint32;
+    int32_t id = ((cint32 *)p.indices)[page_base + slot];
+    id = min(max(id, 0), p.num_total_pages - 1);
+    page = id;
+  }
+  return ((page * p.num_kv_heads + kvh) * (int64_t)p.page_size + row) * p.head_dim;
+}
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
 }
 
 }  // namespace fa

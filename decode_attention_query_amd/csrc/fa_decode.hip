@@ -44,8 +44,7 @@ struct HostPlan {
   int group = 0, gt = 0, n_gblocks = 0, planes = 0;
   int chunk = 0, units_bound = 0, kind = 0;
   // workspace byte offsets
-  size_t seq_len = 0, page_base = 0, unit_prefix = 0, row_prefix = 0, unit_req = 0,
-         part_lse = 0, part_o = 0, total = 0;
+  size_t row_prefix = 0, unit_desc = 0, part_lse = 0, part_o = 0, arrivals = 0, total = 0;
 };
 
 bool extents_ok(int batch, int hq, int hkv, int page_size) {
@@ -82,26 +81,23 @@ HostPlan make_plan(fa_dtype_t dt, int batch, int hq, int hkv, int d, int page_si
   else
     hp.units_bound = int(batch + rows_ub / chunk);
   size_t off = 0;
-  hp.seq_len = off;     off = align_up(off + sizeof(int32_t) * batch);
-  hp.page_base = off;   off = align_up(off + sizeof(int32_t) * batch);
-  hp.unit_prefix = off; off = align_up(off + sizeof(int32_t) * (batch + 1));
   hp.row_prefix = off;  off = align_up(off + sizeof(int64_t) * (batch + 1));
-  hp.unit_req = off;    off = align_up(off + sizeof(int32_t) * hp.units_bound);
+  hp.unit_desc = off;   off = align_up(off + sizeof(fa::UnitDesc) * hp.units_bound);
   hp.part_lse = off;    off = align_up(off + sizeof(float) * size_t(hp.units_bound) * hq);
   hp.part_o = off;      off = align_up(off + sizeof(float) * size_t(hp.units_bound) * hq * d);
+  // one counter per (request, head block); Hq per request bounds the blocks
+  hp.arrivals = off;    off = align_up(off + sizeof(int32_t) * size_t(batch) * hq);
   hp.total = off;
   return hp;
 }
 
 void carve(DecodeParams &p, const HostPlan &hp, void *ws) {
   char *w = static_cast<char *>(ws);
-  p.seq_len = reinterpret_cast<int32_t *>(w + hp.seq_len);
-  p.page_base = reinterpret_cast<int32_t *>(w + hp.page_base);
-  p.unit_prefix = reinterpret_cast<int32_t *>(w + hp.unit_prefix);
   p.row_prefix = reinterpret_cast<int64_t *>(w + hp.row_prefix);
-  p.unit_req = reinterpret_cast<int32_t *>(w + hp.unit_req);
+  p.unit_desc = reinterpret_cast<fa::UnitDesc *>(w + hp.unit_desc);
   p.part_lse = reinterpret_cast<float *>(w + hp.part_lse);
   p.part_o = reinterpret_cast<float *>(w + hp.part_o);
+  p.arrivals = reinterpret_cast<int32_t *>(w + hp.arrivals);
 }
 
 // ------------------------------------------------------------------ timing
@@ -197,27 +193,12 @@ hipError_t launch_decode_mfma(const DecodeParams &p, const HostPlan &hp, hipStre
   }
 }
 
-template <class E>
-hipError_t launch_merge(const DecodeParams &p, hipStream_t s) {
-  const int items = p.batch * p.num_qo_heads;
-  hipLaunchKernelGGL((fa::merge_kernel<E>), dim3((items + 3) / 4), dim3(256), 0, s, p);
-  return hipGetLastError();
-}
-
 hipError_t dispatch_decode(fa_dtype_t dt, const DecodeParams &p, const HostPlan &hp,
                            hipStream_t s) {
   switch (dt) {
     case FA_DTYPE_F32: return launch_decode<fa::F32>(p, hp, s);
     case FA_DTYPE_F16: return launch_decode_mfma<fa::F16>(p, hp, s);
     default: return launch_decode_mfma<fa::BF16>(p, hp, s);
-  }
-}
-
-hipError_t dispatch_merge(fa_dtype_t dt, const DecodeParams &p, hipStream_t s) {
-  switch (dt) {
-    case FA_DTYPE_F32: return launch_merge<fa::F32>(p, s);
-    case FA_DTYPE_F16: return launch_merge<fa::F16>(p, s);
-    default: return launch_merge<fa::BF16>(p, s);
   }
 }
 
@@ -246,6 +227,7 @@ DecodeParams base_params(int batch, int hq, int hkv, int d, int page_size, int p
   p.heads_per_unit = hp.gt;
   p.scale_log2 = scale * fa::kLog2e;
   p.page_div = fa::make_fastdiv(uint32_t(page_size));
+  p.uniform_blocks = page_size % 16 == 0;
   p.chunk = hp.chunk;
   p.units_bound = hp.units_bound;
   return p;
@@ -294,17 +276,20 @@ fa_status_t fa_decode_contig(fa_dtype_t dtype, int num_qo_heads, int num_kv_head
   p.o = o;
   p.lse = lse;
   p.contig = 1;
+  p.uniform_blocks = 1;
   p.contig_len = valid_kv_len;
   p.contig_units =
       valid_kv_len == 0 ? 1 : int((int64_t(valid_kv_len) + hp.chunk - 1) / hp.chunk);
   carve(p, hp, workspace);
 
   CallEvents ev(stream);
+  if (p.contig_units > 1) {  // split: the plan kernel zeroes the merge counters
+    hipLaunchKernelGGL(fa::plan_kernel, dim3(1), dim3(fa::kPlanThreads), 0, stream, p);
+    if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+  }
   ev.mark(1, stream);
   if (dispatch_decode(dtype, p, hp, stream) != hipSuccess) return FA_ERR_LAUNCH;
   ev.mark(2, stream);
-  if (p.contig_units > 1 && dispatch_merge(dtype, p, stream) != hipSuccess)
-    return FA_ERR_LAUNCH;
   ev.finish(stream);
   return FA_OK;
 }
@@ -352,7 +337,6 @@ fa_status_t fa_decode_paged(fa_dtype_t dtype, int batch, int num_qo_heads, int n
   ev.mark(1, stream);
   if (dispatch_decode(dtype, p, hp, stream) != hipSuccess) return FA_ERR_LAUNCH;
   ev.mark(2, stream);
-  if (dispatch_merge(dtype, p, stream) != hipSuccess) return FA_ERR_LAUNCH;
   ev.finish(stream);
   return FA_OK;
 }

@@ -5,8 +5,9 @@
 // unit for one KV head and a block of GT query heads of that head's group, so
 // every K/V byte of the unit is read from HBM once for all GT heads.  A request
 // with one unit writes o and lse directly; otherwise each unit writes a
-// normalised partial output and its base-2 log-sum-exp, and the merge kernel
-// combines them in a fixed order.
+// normalised partial output and its base-2 log-sum-exp, and the workgroup that
+// finishes last for that (request, head block) merges all of them, in unit
+// order, so the result does not depend on which workgroup that is.
 #pragma once
 
 #include "fa_common.hpp"
@@ -17,14 +18,18 @@ namespace fa {
 //
 // One workgroup.  For every request: L_b from the page table (clamped so a
 // table that breaks its contract cannot send a later kernel outside the
-// buffers), its number of split units, and the prefix sums that map a split
-// unit back to its request.  baracuda-kernels 0.0.1-alpha.68,
-// src/attention/batch_paged_decode.rs, module doc "Layout": request b owns
-// pages indices[indptr[b] .. indptr[b+1]), its last page holds
+// buffers) and its number of split units; then one descriptor per split unit
+// (request, index, count, L_b, page base, first unit), so a decode workgroup
+// finds everything about its unit with a single scalar load.  baracuda-kernels
+// 0.0.1-alpha.68, src/attention/batch_paged_decode.rs, module doc "Layout":
+// request b owns pages indices[indptr[b] .. indptr[b+1]), its last page holds
 // last_page_len[b] rows.
 constexpr int kPlanThreads = 1024;
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const DecodeParams p) {
+  // split-merge arrival counters start every call at zero
+  for (int i = threadIdx.x; i < p.batch * p.num_qo_heads; i += kPlanThreads) p.arrivals[i] = 0;
+  if (p.contig) return;  // a contiguous cache's single length is known on the host
   __shared__ int s_units[kPlanThreads];
   __shared__ long long s_rows[kPlanThreads];
   __shared__ int s_carry_units;
@@ -46,8 +51,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const DecodeParams p
       const int lpl = min(max(p.last_page_len[b], 0), p.page_size);
       L = n == 0 ? 0 : (n - 1) * p.page_size + lpl;  // < 2^31: host checks T * P
       units = L == 0 ? 1 : (L + p.chunk - 1) / p.chunk;
-      p.seq_len[b] = L;
-      p.page_base[b] = p0;
     }
     // inclusive scans (Hillis-Steele) of the unit counts and row counts
     s_units[tid] = units;
@@ -64,11 +67,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const DecodeParams p
     const int first_unit = s_carry_units + s_units[tid] - units;
     const long long first_row = s_carry_rows + s_rows[tid] - L;
     if (b < p.batch) {
-      p.unit_prefix[b] = min(first_unit, p.units_bound);
       p.row_prefix[b] = first_row;
       for (int i = 0; i < units; ++i) {
         const int u = first_unit + i;
-        if (u < p.units_bound) p.unit_req[u] = b;
+        if (u < p.units_bound) p.unit_desc[u] = UnitDesc{b, i, units, L, p0, first_unit, 0, 0};
       }
     }
     __syncthreads();
@@ -78,37 +80,41 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const DecodeParams p
     }
     __syncthreads();
   }
-  if (tid == 0) {
-    p.unit_prefix[p.batch] = min(s_carry_units, p.units_bound);
-    p.row_prefix[p.batch] = s_carry_rows;
-  }
+  // units past the real count exit at once
+  for (int u = s_carry_units + tid; u < p.units_bound; u += kPlanThreads)
+    p.unit_desc[u] = UnitDesc{-1, 0, 0, 0, 0, 0, 0, 0};
+  if (tid == 0) p.row_prefix[p.batch] = s_carry_rows;
 }
 
-// Resolves split unit blockIdx.x to (request, unit within request, units of
-// the request, L_b, page base).  Returns false for units past the real count.
+// Split unit blockIdx.x: (request, unit within request, units of the request,
+// L_b, first unit of the request, page base).
 struct UnitInfo {
   int b, c, n_units, L;
+  int u0;
   int32_t page_base;
 };
 
+// Returns false for units past the real count.
 __device__ inline bool resolve_unit(const DecodeParams &p, int unit, UnitInfo &u) {
   if (p.contig) {
     if (unit >= p.contig_units) return false;
     u.b = 0;
     u.c = unit;
+    u.u0 = 0;
     u.n_units = p.contig_units;
     u.L = p.contig_len;
     u.page_base = 0;
     return true;
   }
-  if (unit >= p.unit_prefix[p.batch]) return false;
-  u.b = p.unit_req[unit];
-  const int u0 = p.unit_prefix[u.b];
-  u.c = unit - u0;
-  u.n_units = p.unit_prefix[u.b + 1] - u0;
-  u.L = p.seq_len[u.b];
-  u.page_base = p.page_base[u.b];
-  return true;
+  typedef const __attribute__((address_space(4))) UnitDesc cdesc;
+  const cdesc *d = (cdesc *)p.unit_desc + unit;  // written by the plan kernel
+  u.b = d->b;
+  u.c = d->c;
+  u.n_units = d->n_units;
+  u.L = d->L;
+  u.page_base = d->page_base;
+  u.u0 = d->u0;
+  return u.b >= 0;
 }
 
 // Writes the combined result of one (request, query head, feature) of a unit:
@@ -122,10 +128,97 @@ __device__ inline void emit(const DecodeParams &p, const UnitInfo &u, int unit, 
     static_cast<typename E::raw *>(p.o)[row * p.head_dim + d] = E::narrow(any ? a / l : 0.0f);
     if (d == 0 && p.lse) p.lse[row] = any ? (m2 + fast_log2(l)) * kLn2 : -INFINITY;
   } else {
+    // Partials are read by whichever workgroup merges the request, possibly on
+    // another XCD: store them device-coherent (agent-scope atomic stores write
+    // through to memory) so no L2 write-back of the whole cache is needed.
     const int64_t row = (int64_t)unit * p.num_qo_heads + h;
-    p.part_o[row * p.head_dim + d] = any ? a / l : 0.0f;
-    if (d == 0) p.part_lse[row] = any ? m2 + fast_log2(l) : -INFINITY;
+    __hip_atomic_store(p.part_o + row * p.head_dim + d, any ? a / l : 0.0f, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    if (d == 0)
+      __hip_atomic_store(p.part_lse + row, any ? m2 + fast_log2(l) : -INFINITY,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+}
+
+// ------------------------------------------------------------- LSE merge
+
+// Device-coherent load of data another workgroup wrote (see finish_split).
+__device__ inline float coherent_load(const float *ptr) {
+  return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+//
+// Combines request b's split partials (o_s normalised over its rows, lse_s in
+// base 2) for query heads h0 .. h0 + gt - 1; every thread of the 256-thread
+// workgroup takes part.  Per head:
+//   M = max_s lse_s,  W = sum_s 2^(lse_s - M),
+//   o = sum_s 2^(lse_s - M) o_s / W,  lse = (M + log2 W) * ln 2,
+// with s running over the request's units in order (one wave per head for M
+// and W, fixed butterfly order), so the result is reproducible bit for bit.
+template <class E>
+__device__ void merge_partials(const DecodeParams &p, int b, int u0, int n, int h0, int gt,
+                               float *s_stat /* LDS [32] */) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int hq = p.num_qo_heads;
+  for (int g = wave; g < gt; g += 4) {
+    float mx = -INFINITY;
+    for (int s = lane; s < n; s += kWave) mx = fmaxf(mx, coherent_load(p.part_lse + (int64_t)(u0 + s) * hq + h0 + g));
+    mx = wave_max(mx);
+    const float ref = safe_ref(mx);
+    float w = 0.0f;
+    for (int s = lane; s < n; s += kWave)
+      w += fast_exp2(coherent_load(p.part_lse + (int64_t)(u0 + s) * hq + h0 + g) - ref);
+    w = wave_sum(w);
+    if (lane == 0) {
+      s_stat[g] = mx;
+      s_stat[16 + g] = w;
+    }
+  }
+  __syncthreads();
+  const int D = p.head_dim;
+  for (int idx = tid; idx < gt * D; idx += 4 * kWave) {
+    const int g = idx / D;
+    const int d = idx % D;
+    const int h = h0 + g;
+    const float mx = s_stat[g];
+    const float W = s_stat[16 + g];
+    const float ref = safe_ref(mx);
+    float a = 0.0f;
+#pragma unroll 8
+    for (int s = 0; s < n; ++s) {
+      const int64_t row = (int64_t)(u0 + s) * hq + h;
+      a = fmaf(fast_exp2(coherent_load(p.part_lse + row) - ref), coherent_load(p.part_o + row * D + d), a);
+    }
+    const bool any = W > 0.0f;
+    const int64_t orow = (int64_t)b * hq + h;
+    static_cast<typename E::raw *>(p.o)[orow * D + d] = E::narrow(any ? a / W : 0.0f);
+    if (d == 0 && p.lse) p.lse[orow] = any ? (mx + fast_log2(W)) * kLn2 : -INFINITY;
+  }
+}
+
+// After a split unit has written its partials: count it in, and if it is the
+// last unit of its (request, head block) to finish, merge them all.
+//
+// Ordering: every wave waits until its device-coherent partial stores have
+// completed (s_waitcnt 0), the barrier gathers the waves, and only then does
+// one thread count the unit in with a device-scope atomic.  The workgroup that
+// sees the final count reads the partials with device-coherent loads, which
+// go to memory rather than to a possibly stale L2 line.  No cache-wide
+// write-back or invalidate (what a device-scope fence would emit, once per
+// workgroup) is needed, because no non-coherent data crosses workgroups.
+template <class E>
+__device__ void finish_split(const DecodeParams &p, const UnitInfo &u, int h0, int gt,
+                             float *s_stat, int *s_last) {
+  if (u.n_units <= 1) return;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int32_t *counter = p.arrivals + (int64_t)u.b * p.num_qo_heads + blockIdx.y;
+  if (threadIdx.x == 0) *s_last = atomicAdd(counter, 1) == u.n_units - 1;
+  __syncthreads();
+  if (!*s_last) return;
+  merge_partials<E>(p, u.b, u.u0, u.n_units, h0, gt, s_stat);
+  if (threadIdx.x == 0) *counter = 0;
 }
 
 // ------------------------------------------------------ vector-ALU decode
@@ -299,59 +392,9 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
     }
     emit<E>(p, u, blockIdx.x, h0 + g, d, M, lsum, a);
   }
-}
-
-// ------------------------------------------------------------- LSE merge
-//
-// One wave per (request, query head).  Combines the request's split partials
-// (o_s normalised over its rows, lse_s in base 2):
-//   M = max_s lse_s,  w_s = 2^(lse_s - M),  o = sum_s w_s o_s / sum_s w_s,
-//   lse = (M + log2 sum_s w_s) * ln 2,
-// summing over s in increasing order (fixed, so the result is reproducible).
-// Requests with a single unit were written by the decode kernel and are left.
-template <class E>
-__global__ __launch_bounds__(256) void merge_kernel(const DecodeParams p) {
-  const int item = blockIdx.x * 4 + threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
-  if (item >= p.batch * p.num_qo_heads) return;
-  const int b = item / p.num_qo_heads;
-  const int h = item % p.num_qo_heads;
-  int u0, n;
-  if (p.contig) {
-    u0 = 0;
-    n = p.contig_units;
-  } else {
-    u0 = p.unit_prefix[b];
-    n = p.unit_prefix[b + 1] - u0;
-  }
-  if (n <= 1) return;
-  float M = -INFINITY;
-  for (int s = 0; s < n; ++s) M = fmaxf(M, p.part_lse[(int64_t)(u0 + s) * p.num_qo_heads + h]);
-  const float ref = safe_ref(M);
-  constexpr int kMaxPerLane = 256 / kWave;
-  float a[kMaxPerLane] = {0.0f, 0.0f, 0.0f, 0.0f};
-  float wsum = 0.0f;
-  for (int s = 0; s < n; ++s) {
-    const int64_t row = (int64_t)(u0 + s) * p.num_qo_heads + h;
-    const float w = fast_exp2(p.part_lse[row] - ref);
-    wsum += w;
-    const float *po = p.part_o + row * p.head_dim;
-#pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
-      const int d = lane + j * kWave;
-      if (d < p.head_dim) a[j] = fmaf(w, po[d], a[j]);
-    }
-  }
-  const int64_t out_row = (int64_t)b * p.num_qo_heads + h;
-  const bool any = wsum > 0.0f;
-#pragma unroll
-  for (int j = 0; j < kMaxPerLane; ++j) {
-    const int d = lane + j * kWave;
-    if (d < p.head_dim)
-      static_cast<typename E::raw *>(p.o)[out_row * p.head_dim + d] =
-          E::narrow(any ? a[j] / wsum : 0.0f);
-  }
-  if (lane == 0 && p.lse) p.lse[out_row] = any ? (M + fast_log2(wsum)) * kLn2 : -INFINITY;
+  __shared__ float s_stat[32];
+  __shared__ int s_last;
+  finish_split<E>(p, u, h0, GT, s_stat, &s_last);
 }
 
 // ------------------------------------------------------------ gather hook

@@ -17,10 +17,12 @@
 //            state, p = 2^(s - m).
 //   P.V      O^T[d][g] += sum_t V[t][d] P[t][g]      v_mfma_f32_16x16x32
 //            B = P^T is exactly the lane's 8 probabilities (row order below),
-//            A = V^T is read transposed from LDS, where the wave stored its
-//            V tile.  bf16 P keeps 8 bits, so P is split into hi + lo bf16
-//            parts (two MFMAs) to keep P.V at ~16-bit accuracy; f16 P is used
-//            as is.
+//            A = V^T is read from the wave's LDS copy of its V tile with
+//            ds_read_b64_tr_b16: in each 16-lane group, lane 4r + b names row r,
+//            features 4b .. 4b + 3 of a 4 x 16 block and lane L receives column
+//            L, i.e. 4 rows of one feature -- half an A operand per read.
+//            bf16 P keeps 8 bits, so P is split into hi + lo bf16 parts (two
+//            MFMAs) to keep P.V at ~16-bit accuracy; f16 P is used as is.
 // The contraction index k of both P.V operands is mapped to tile rows as
 // row(k = 8 grp + i) = 16 (i / 4) + 4 grp + (i % 4), which is where the score
 // MFMA left each lane's probabilities; any k order works as long as A and B
@@ -46,7 +48,6 @@ struct Mfma<BF16> {
   __device__ static inline f32x4 mma(v8 a, v8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
-  __device__ static inline __bf16 from_bits(uint16_t u) { return __builtin_bit_cast(__bf16, u); }
 };
 
 template <>
@@ -56,9 +57,6 @@ struct Mfma<F16> {
   static constexpr bool kSplitP = false;
   __device__ static inline f32x4 mma(v8 a, v8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-  }
-  __device__ static inline _Float16 from_bits(uint16_t u) {
-    return __builtin_bit_cast(_Float16, u);
   }
 };
 
@@ -97,7 +95,9 @@ struct MfmaGeom {
   static constexpr int TT = 32;          // rows per wave tile
   static constexpr int KK = D / 32;      // score k-steps per 16-row block
   static constexpr int MB = D / 16;      // 16-feature blocks of O^T
-  static constexpr int ROW = D * 2 + 16; // LDS bytes per V row (16-byte pad)
+  // LDS bytes per V row: the 32-byte pad puts any 8 consecutive rows' 32-byte
+  // slices of one transposed read in disjoint banks.
+  static constexpr int ROW = D * 2 + 32;
   static constexpr int WAVE_LDS = TT * ROW;
   static constexpr int LDS_V = NW * WAVE_LDS;
   static constexpr int LDS_ACC = NW * 16 * D * 4;  // merge area (reuses the V area)
@@ -107,6 +107,10 @@ struct MfmaGeom {
 
 // Issues the global loads of the tile whose first row is t0 (rows past t_end
 // are clamped to t_end - 1: in bounds, and masked out of the softmax later).
+// t0, t_end and page_base are wave-uniform.  When every 16-row block lies in
+// one page, the block's page is resolved once per wave with a scalar load;
+// otherwise (page sizes that are not multiples of 16) every lane resolves its
+// own row.
 template <class E, int D>
 __device__ inline void issue_tile(KVTile<D / 32> &T, const DecodeParams &p, int32_t page_base,
                                   int kvh, int t0, int t_end, int n, int grp) {
@@ -116,7 +120,13 @@ __device__ inline void issue_tile(KVTile<D / 32> &T, const DecodeParams &p, int3
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int t = min(t0 + 16 * j + n, t_end - 1);
-    const int64_t off = kv_row_offset(p, page_base, kvh, t) * 2;
+    int64_t off;
+    if (p.uniform_blocks) {
+      const int tb = min(t0 + 16 * j, t_end - 1);
+      off = (block_row_offset(p, page_base, kvh, tb) + (int64_t)(t - tb) * D) * 2;
+    } else {
+      off = kv_row_offset(p, page_base, kvh, t) * 2;
+    }
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       T.k[j][kk] = load16_stream(kb + off + kk * 64);
@@ -135,18 +145,22 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
   __shared__ __attribute__((aligned(16))) char lds[G::LDS];
   __shared__ float s_m[NW][16];
   __shared__ float s_l[NW][16];
+  __shared__ float s_stat[32];
+  __shared__ int s_last;
 
   UnitInfo u;
   if (!resolve_unit(p, blockIdx.x, u)) return;
   const int gt = p.heads_per_unit;  // valid columns of the 16-wide head block
   const int kvh = blockIdx.y / p.n_gblocks;
   const int h0 = kvh * p.group + (blockIdx.y % p.n_gblocks) * gt;
-  const int t_begin = u.c * p.chunk;
-  const int t_end = min(u.L, t_begin + p.chunk);
+  // workgroup-uniform values, kept in scalar registers
+  const int t_begin = __builtin_amdgcn_readfirstlane(u.c * p.chunk);
+  const int t_end = __builtin_amdgcn_readfirstlane(min(u.L, u.c * p.chunk + p.chunk));
+  const int32_t page_base = __builtin_amdgcn_readfirstlane(u.page_base);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15;
   const int grp = lane >> 4;
 
@@ -171,8 +185,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
   float l_run = 0.0f;       // this lane's share of the normaliser of head n
 
   char *wl = lds + wave * G::WAVE_LDS;
-  const uint16_t *vl = reinterpret_cast<const uint16_t *>(wl);
   const float c = p.scale_log2;
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  // this lane's address in each transposed read: row 4 grp + (n / 4) of the
+  // 16-row half, features 4 (n % 4) .. + 3 of the 16-feature block
+  const char *vt = wl + (4 * grp + (n >> 2)) * G::ROW + (4 * (n & 3)) * 2;
 
   auto compute = [&](const KVTile<KK> &T, int t0) {
     // V tile to LDS: row 16j + n, features 32kk + 8grp .. +8
@@ -227,12 +245,14 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      v8 a;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = 16 * (i >> 2) + 4 * grp + (i & 3);
-        a[i] = M::from_bits(vl[row * (G::ROW / 2) + 16 * mb + n]);
-      }
+      // A = V^T: rows 16h + 4grp + r (r < 4) of feature 16mb + n, for h = 0, 1
+      const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4 *)(vt + 32 * mb));
+      const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4 *)(vt + 16 * G::ROW + 32 * mb));
+      typedef short s16x8 __attribute__((ext_vector_type(8)));
+      const s16x8 a16 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      const v8 a = __builtin_bit_cast(v8, a16);
       acc[mb] = M::mma(a, ph, acc[mb]);
       if constexpr (M::kSplitP) acc[mb] = M::mma(a, pl, acc[mb]);
     }
@@ -246,15 +266,15 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
   int t0 = t_begin + wave * TT;
   if (t0 < t_end) {
     KVTile<KK> A;
-    issue_tile<E, D>(A, p, u.page_base, kvh, t0, t_end, n, grp);
+    issue_tile<E, D>(A, p, page_base, kvh, t0, t_end, n, grp);
     if constexpr (G::kPipelined) {
       KVTile<KK> B;
       while (true) {
-        issue_tile<E, D>(B, p, u.page_base, kvh, t0 + stride, t_end, n, grp);
+        issue_tile<E, D>(B, p, page_base, kvh, t0 + stride, t_end, n, grp);
         compute(A, t0);
         t0 += stride;
         if (t0 >= t_end) break;
-        issue_tile<E, D>(A, p, u.page_base, kvh, t0 + stride, t_end, n, grp);
+        issue_tile<E, D>(A, p, page_base, kvh, t0 + stride, t_end, n, grp);
         compute(B, t0);
         t0 += stride;
         if (t0 >= t_end) break;
@@ -264,7 +284,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
         compute(A, t0);
         t0 += stride;
         if (t0 >= t_end) break;
-        issue_tile<E, D>(A, p, u.page_base, kvh, t0, t_end, n, grp);
+        issue_tile<E, D>(A, p, page_base, kvh, t0, t_end, n, grp);
       }
     }
   }
@@ -302,6 +322,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
     }
     emit<E>(p, u, blockIdx.x, h0 + g, d, Mx, lsum, a);
   }
+  finish_split<E>(p, u, h0, gt, s_stat, &s_last);
 }
 
 }  // namespace fa
