@@ -82,27 +82,37 @@ __device__ inline void pack_probs(const float *p, typename Mfma<E>::v8 &hi,
   }
 }
 
-// K and V of one 32-row tile in the MFMA A-operand order: [block j][k step kk].
-template <int KK>
-struct KVTile {
-  uint4 k[2][KK];
-  uint4 v[2][KK];
-};
-
 template <class E, int D>
 struct MfmaGeom {
   static constexpr int NW = 4;           // waves per workgroup
   static constexpr int TT = 32;          // rows per wave tile
   static constexpr int KK = D / 32;      // score k-steps per 16-row block
   static constexpr int MB = D / 16;      // 16-feature blocks of O^T
-  // LDS bytes per V row: the 32-byte pad puts any 8 consecutive rows' 32-byte
-  // slices of one transposed read in disjoint banks.
-  static constexpr int ROW = D * 2 + 32;
-  static constexpr int WAVE_LDS = TT * ROW;
-  static constexpr int LDS_V = NW * WAVE_LDS;
-  static constexpr int LDS_ACC = NW * 16 * D * 4;  // merge area (reuses the V area)
-  static constexpr int LDS = LDS_V > LDS_ACC ? LDS_V : LDS_ACC;
+  // Global loads: each instruction reads whole rows, 1 KiB contiguous per
+  // wave (LPR lanes per row, RPI rows per instruction, NI instructions per
+  // 32-row tile of K, and as many of V).  An instruction shaped like the MFMA
+  // operand instead (16 rows x 64 bytes) streams ~13% slower from HBM.
+  static constexpr int LPR = D * 2 / 16;
+  static constexpr int RPI = 64 / LPR;
+  static constexpr int NI = TT / RPI;
+  // LDS row strides.  K is read back 16 bytes per lane from 16 rows at once:
+  // a 16-byte pad puts those rows in distinct banks.  V is read with
+  // transposed 8-byte reads spanning 8 rows: a 32-byte pad does the same.
+  static constexpr int ROWK = D * 2 + 16;
+  static constexpr int ROWV = D * 2 + 32;
+  static constexpr int WAVE_LDS = TT * (ROWK + ROWV);
+  static constexpr int LDS_KV = NW * WAVE_LDS;
+  static constexpr int LDS_ACC = NW * 16 * D * 4;  // merge area (reuses the K/V area)
+  static constexpr int LDS = LDS_KV > LDS_ACC ? LDS_KV : LDS_ACC;
   static constexpr bool kPipelined = D <= 128;   // prefetch one tile ahead
+};
+
+// K and V of one 32-row tile as loaded: instruction i, lane l holds row
+// RPI * i + l / LPR, bytes 16 (l % LPR) .. + 16.
+template <int NI>
+struct KVTile {
+  uint4 k[NI];
+  uint4 v[NI];
 };
 
 // Issues the global loads of the tile whose first row is t0 (rows past t_end
@@ -110,28 +120,36 @@ struct MfmaGeom {
 // t0, t_end and page_base are wave-uniform.  When every 16-row block lies in
 // one page, the block's page is resolved once per wave with a scalar load;
 // otherwise (page sizes that are not multiples of 16) every lane resolves its
-// own row.
+// own rows.
 template <class E, int D>
-__device__ inline void issue_tile(KVTile<D / 32> &T, const DecodeParams &p, int32_t page_base,
-                                  int kvh, int t0, int t_end, int n, int grp) {
-  constexpr int KK = D / 32;
-  const char *kb = static_cast<const char *>(p.k) + (int64_t)(8 * grp) * 2;
-  const char *vb = static_cast<const char *>(p.v) + (int64_t)(8 * grp) * 2;
+__device__ inline void issue_tile(KVTile<MfmaGeom<E, D>::NI> &T, const DecodeParams &p,
+                                  int32_t page_base, int kvh, int t0, int t_end, int lane) {
+  using G = MfmaGeom<E, D>;
+  const int r0 = lane / G::LPR;           // row within an instruction
+  const int col = (lane % G::LPR) * 16;   // byte within the row
+  const char *kb = static_cast<const char *>(p.k) + col;
+  const char *vb = static_cast<const char *>(p.v) + col;
+  int64_t blk[2];
+  if (p.uniform_blocks) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int t = min(t0 + 16 * j + n, t_end - 1);
+    for (int j = 0; j < 2; ++j) {
+      const int tb = min(t0 + 16 * j, t_end - 1);
+      blk[j] = block_row_offset(p, page_base, kvh, tb) - (int64_t)tb * D;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < G::NI; ++i) {
+    const int r = G::RPI * i + r0;  // row within the tile
+    const int t = min(t0 + r, t_end - 1);
     int64_t off;
     if (p.uniform_blocks) {
-      const int tb = min(t0 + 16 * j, t_end - 1);
-      off = (block_row_offset(p, page_base, kvh, tb) + (int64_t)(t - tb) * D) * 2;
+      // rows of block j = r / 16 share its page: offset = block base + row * D
+      off = (blk[(G::RPI * i) / 16] + (int64_t)t * D) * 2;
     } else {
       off = kv_row_offset(p, page_base, kvh, t) * 2;
     }
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      T.k[j][kk] = load16_stream(kb + off + kk * 64);
-      T.v[j][kk] = load16_stream(vb + off + kk * 64);
-    }
+    T.k[i] = load16_stream(kb + off);
+    T.v[i] = load16_stream(vb + off);
   }
 }
 
@@ -184,30 +202,39 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
   float m_run = -INFINITY;  // running max (base 2) of head n; same in all 4 lane groups
   float l_run = 0.0f;       // this lane's share of the normaliser of head n
 
-  char *wl = lds + wave * G::WAVE_LDS;
+  char *wk = lds + wave * G::WAVE_LDS;   // this wave's K tile
+  char *wv = wk + TT * G::ROWK;           // and V tile
   const float c = p.scale_log2;
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
   // this lane's address in each transposed read: row 4 grp + (n / 4) of the
   // 16-row half, features 4 (n % 4) .. + 3 of the 16-feature block
-  const char *vt = wl + (4 * grp + (n >> 2)) * G::ROW + (4 * (n & 3)) * 2;
+  const char *vt = wv + (4 * grp + (n >> 2)) * G::ROWV + (4 * (n & 3)) * 2;
+  // where this lane's loaded 16 bytes go: row RPI * i + lane / LPR
+  const int st_row = lane / G::LPR, st_col = (lane % G::LPR) * 16;
 
-  auto compute = [&](const KVTile<KK> &T, int t0) {
-    // V tile to LDS: row 16j + n, features 32kk + 8grp .. +8
+  auto compute = [&](const KVTile<G::NI> &T, int t0) {
+    // K and V tiles to LDS
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        *reinterpret_cast<uint4 *>(wl + (16 * j + n) * G::ROW + (32 * kk + 8 * grp) * 2) =
-            T.v[j][kk];
-    // scores
+    for (int i = 0; i < G::NI; ++i) {
+      const int r = G::RPI * i + st_row;
+      *reinterpret_cast<uint4 *>(wk + r * G::ROWK + st_col) = T.k[i];
+      *reinterpret_cast<uint4 *>(wv + r * G::ROWV + st_col) = T.v[i];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // scores; A = K rows 16j + n, features 32kk + 8grp .. + 8
     f32x4 s[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       s[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        s[j] = M::mma(__builtin_bit_cast(v8, T.k[j][kk]), qb[kk], s[j]);
+      for (int kk = 0; kk < KK; ++kk) {
+        const uint4 ka =
+            *reinterpret_cast<const uint4 *>(wk + (16 * j + n) * G::ROWK + (32 * kk + 8 * grp) * 2);
+        s[j] = M::mma(__builtin_bit_cast(v8, ka), qb[kk], s[j]);
+      }
     }
     // online softmax for head n over the tile's rows 16j + 4grp + i
     float x[8];
@@ -239,17 +266,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
     for (int mb = 0; mb < MB; ++mb) acc[mb] *= alpha;
     v8 ph, pl;
     pack_probs<E>(pr, ph, pl);
-    // this wave's LDS stores before its transposed reads
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       // A = V^T: rows 16h + 4grp + r (r < 4) of feature 16mb + n, for h = 0, 1
       const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_s16x4 *)(vt + 32 * mb));
       const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4 *)(vt + 16 * G::ROW + 32 * mb));
+          (lds_s16x4 *)(vt + 16 * G::ROWV + 32 * mb));
       typedef short s16x8 __attribute__((ext_vector_type(8)));
       const s16x8 a16 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
       const v8 a = __builtin_bit_cast(v8, a16);
@@ -265,16 +288,16 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
   const int stride = NW * TT;
   int t0 = t_begin + wave * TT;
   if (t0 < t_end) {
-    KVTile<KK> A;
-    issue_tile<E, D>(A, p, page_base, kvh, t0, t_end, n, grp);
+    KVTile<G::NI> A;
+    issue_tile<E, D>(A, p, page_base, kvh, t0, t_end, lane);
     if constexpr (G::kPipelined) {
-      KVTile<KK> B;
+      KVTile<G::NI> B;
       while (true) {
-        issue_tile<E, D>(B, p, page_base, kvh, t0 + stride, t_end, n, grp);
+        issue_tile<E, D>(B, p, page_base, kvh, t0 + stride, t_end, lane);
         compute(A, t0);
         t0 += stride;
         if (t0 >= t_end) break;
-        issue_tile<E, D>(A, p, page_base, kvh, t0 + stride, t_end, n, grp);
+        issue_tile<E, D>(A, p, page_base, kvh, t0 + stride, t_end, lane);
         compute(B, t0);
         t0 += stride;
         if (t0 >= t_end) break;
@@ -284,7 +307,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
         compute(A, t0);
         t0 += stride;
         if (t0 >= t_end) break;
-        issue_tile<E, D>(A, p, page_base, kvh, t0, t_end, n, grp);
+        issue_tile<E, D>(A, p, page_base, kvh, t0, t_end, lane);
       }
     }
   }
