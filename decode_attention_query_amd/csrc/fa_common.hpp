@@ -48,7 +48,7 @@ struct UnitDesc {
   int32_t n_units;    // units of the request
   int32_t L;          // L_b
   int32_t page_base;  // first index of the request's pages in indices
-  int32_t u0;         // first unit of the request
+  int32_t u0;         // first partial-result slot of the request
   int32_t pad0, pad1;
 };
 
@@ -69,6 +69,7 @@ struct DecodeParams {
   int group;          // Hq / Hkv
   int n_gblocks;      // workgroups per KV head along the query group
   int heads_per_unit; // query heads per workgroup (group / n_gblocks)
+  int planes;         // Hkv * n_gblocks: head blocks per split unit
   float scale_log2;   // scale * log2(e): scores live in the base-2 domain
   FastDiv page_div;   // row -> (page slot, row in page)
   // split-KV plan

@@ -179,7 +179,7 @@ hipError_t launch_decode(const DecodeParams &p, const HostPlan &hp, hipStream_t 
 
 template <class E, int D>
 hipError_t launch_mfma(const DecodeParams &p, const HostPlan &hp, hipStream_t s) {
-  dim3 grid(hp.units_bound, hp.planes);
+  dim3 grid(unsigned(hp.units_bound) * unsigned(hp.planes));
   hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
@@ -225,6 +225,7 @@ DecodeParams base_params(int batch, int hq, int hkv, int d, int page_size, int p
   p.group = hp.group;
   p.n_gblocks = hp.n_gblocks;
   p.heads_per_unit = hp.gt;
+  p.planes = hp.planes;
   p.scale_log2 = scale * fa::kLog2e;
   p.page_div = fa::make_fastdiv(uint32_t(page_size));
   p.uniform_blocks = page_size % 16 == 0;

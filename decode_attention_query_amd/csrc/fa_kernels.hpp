@@ -30,64 +30,88 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const DecodeParams p
   // split-merge arrival counters start every call at zero
   for (int i = threadIdx.x; i < p.batch * p.num_qo_heads; i += kPlanThreads) p.arrivals[i] = 0;
   if (p.contig) return;  // a contiguous cache's single length is known on the host
-  __shared__ int s_units[kPlanThreads];
+  // Work order: every request's full-length units first, then the shorter
+  // last units, so the short work fills the tail of the launch (longest
+  // first).  Partial results use a separate numbering, contiguous per request
+  // (slot = first slot of the request + index of the unit).
+  __shared__ int s_full[kPlanThreads];
+  __shared__ int s_part[kPlanThreads];
   __shared__ long long s_rows[kPlanThreads];
-  __shared__ int s_carry_units;
+  __shared__ int s_carry_full, s_carry_part;
   __shared__ long long s_carry_rows;
   const int tid = threadIdx.x;
-  if (tid == 0) {
-    s_carry_units = 0;
-    s_carry_rows = 0;
-  }
-  __syncthreads();
   const int T = p.total_used_pages;
-  for (int base = 0; base < p.batch; base += kPlanThreads) {
-    const int b = base + tid;
-    int L = 0, units = 0, p0 = 0;
-    if (b < p.batch) {
-      p0 = min(max(p.indptr[b], 0), T);
-      const int p1 = min(max(p.indptr[b + 1], p0), T);
-      const int n = p1 - p0;
-      const int lpl = min(max(p.last_page_len[b], 0), p.page_size);
-      L = n == 0 ? 0 : (n - 1) * p.page_size + lpl;  // < 2^31: host checks T * P
-      units = L == 0 ? 1 : (L + p.chunk - 1) / p.chunk;
+  // pass 0 counts the full units of the whole batch (where the partial ones
+  // start); pass 1 writes the descriptors
+  int total_full = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    if (tid == 0) {
+      s_carry_full = 0;
+      s_carry_part = 0;
+      s_carry_rows = 0;
     }
-    // inclusive scans (Hillis-Steele) of the unit counts and row counts
-    s_units[tid] = units;
-    s_rows[tid] = L;
     __syncthreads();
-    for (int off = 1; off < kPlanThreads; off <<= 1) {
-      const int u = tid >= off ? s_units[tid - off] : 0;
-      const long long r = tid >= off ? s_rows[tid - off] : 0;
-      __syncthreads();
-      s_units[tid] += u;
-      s_rows[tid] += r;
-      __syncthreads();
-    }
-    const int first_unit = s_carry_units + s_units[tid] - units;
-    const long long first_row = s_carry_rows + s_rows[tid] - L;
-    if (b < p.batch) {
-      p.row_prefix[b] = first_row;
-      for (int i = 0; i < units; ++i) {
-        const int u = first_unit + i;
-        if (u < p.units_bound) p.unit_desc[u] = UnitDesc{b, i, units, L, p0, first_unit, 0, 0};
+    for (int base = 0; base < p.batch; base += kPlanThreads) {
+      const int b = base + tid;
+      int L = 0, full = 0, part = 0, p0 = 0;
+      if (b < p.batch) {
+        p0 = min(max(p.indptr[b], 0), T);
+        const int p1 = min(max(p.indptr[b + 1], p0), T);
+        const int n = p1 - p0;
+        const int lpl = min(max(p.last_page_len[b], 0), p.page_size);
+        L = n == 0 ? 0 : (n - 1) * p.page_size + lpl;  // < 2^31: host checks T * P
+        full = L / p.chunk;
+        part = (L % p.chunk != 0 || L == 0) ? 1 : 0;  // an empty request is one empty unit
       }
+      // inclusive scans (Hillis-Steele)
+      s_full[tid] = full;
+      s_part[tid] = part;
+      s_rows[tid] = L;
+      __syncthreads();
+      for (int off = 1; off < kPlanThreads; off <<= 1) {
+        const int f = tid >= off ? s_full[tid - off] : 0;
+        const int q = tid >= off ? s_part[tid - off] : 0;
+        const long long r = tid >= off ? s_rows[tid - off] : 0;
+        __syncthreads();
+        s_full[tid] += f;
+        s_part[tid] += q;
+        s_rows[tid] += r;
+        __syncthreads();
+      }
+      if (pass == 1 && b < p.batch) {
+        const int first_full = s_carry_full + s_full[tid] - full;
+        const int first_part = s_carry_part + s_part[tid] - part;
+        const int units = full + part;
+        const int slot0 = first_full + first_part;  // units of earlier requests
+        p.row_prefix[b] = s_carry_rows + s_rows[tid] - L;
+        for (int i = 0; i < full; ++i) {
+          const int w = first_full + i;
+          if (w < p.units_bound) p.unit_desc[w] = UnitDesc{b, i, units, L, p0, slot0, 0, 0};
+        }
+        if (part) {
+          const int w = total_full + first_part;
+          if (w < p.units_bound) p.unit_desc[w] = UnitDesc{b, full, units, L, p0, slot0, 0, 0};
+        }
+      }
+      __syncthreads();
+      if (tid == kPlanThreads - 1) {
+        s_carry_full += s_full[tid];
+        s_carry_part += s_part[tid];
+        s_carry_rows += s_rows[tid];
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    if (tid == kPlanThreads - 1) {
-      s_carry_units += s_units[tid];
-      s_carry_rows += s_rows[tid];
-    }
-    __syncthreads();
+    total_full = s_carry_full;
+    __syncthreads();  // everyone has read the carry before pass 1 resets it
   }
   // units past the real count exit at once
-  for (int u = s_carry_units + tid; u < p.units_bound; u += kPlanThreads)
-    p.unit_desc[u] = UnitDesc{-1, 0, 0, 0, 0, 0, 0, 0};
+  for (int w = s_carry_full + s_carry_part + tid; w < p.units_bound; w += kPlanThreads)
+    p.unit_desc[w] = UnitDesc{-1, 0, 0, 0, 0, 0, 0, 0};
   if (tid == 0) p.row_prefix[p.batch] = s_carry_rows;
 }
 
-// Split unit blockIdx.x: (request, unit within request, units of the request,
-// L_b, first unit of the request, page base).
+// A split unit: (request, unit within request, units of the request, L_b,
+// first partial-result slot of the request, page base).
 struct UnitInfo {
   int b, c, n_units, L;
   int u0;
@@ -120,8 +144,8 @@ __device__ inline bool resolve_unit(const DecodeParams &p, int unit, UnitInfo &u
 // Writes the combined result of one (request, query head, feature) of a unit:
 // the final o / lse if the request has a single unit, else the partial.
 template <class E>
-__device__ inline void emit(const DecodeParams &p, const UnitInfo &u, int unit, int h, int d,
-                            float m2, float l, float a) {
+__device__ inline void emit(const DecodeParams &p, const UnitInfo &u, int h, int d, float m2,
+                            float l, float a) {
   const bool any = l > 0.0f;
   if (u.n_units == 1) {
     const int64_t row = (int64_t)u.b * p.num_qo_heads + h;
@@ -131,7 +155,7 @@ __device__ inline void emit(const DecodeParams &p, const UnitInfo &u, int unit, 
     // Partials are read by whichever workgroup merges the request, possibly on
     // another XCD: store them device-coherent (agent-scope atomic stores write
     // through to memory) so no L2 write-back of the whole cache is needed.
-    const int64_t row = (int64_t)unit * p.num_qo_heads + h;
+    const int64_t row = (int64_t)(u.u0 + u.c) * p.num_qo_heads + h;
     __hip_atomic_store(p.part_o + row * p.head_dim + d, any ? a / l : 0.0f, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
     if (d == 0)
@@ -208,12 +232,12 @@ __device__ void merge_partials(const DecodeParams &p, int b, int u0, int n, int 
 // write-back or invalidate (what a device-scope fence would emit, once per
 // workgroup) is needed, because no non-coherent data crosses workgroups.
 template <class E>
-__device__ void finish_split(const DecodeParams &p, const UnitInfo &u, int h0, int gt,
+__device__ void finish_split(const DecodeParams &p, const UnitInfo &u, int plane, int h0, int gt,
                              float *s_stat, int *s_last) {
   if (u.n_units <= 1) return;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  int32_t *counter = p.arrivals + (int64_t)u.b * p.num_qo_heads + blockIdx.y;
+  int32_t *counter = p.arrivals + (int64_t)u.b * p.num_qo_heads + plane;
   if (threadIdx.x == 0) *s_last = atomicAdd(counter, 1) == u.n_units - 1;
   __syncthreads();
   if (!*s_last) return;
@@ -390,11 +414,11 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
       lsum += s_l[w][g] * sw;
       a += s_acc[w][g][d] * sw;
     }
-    emit<E>(p, u, blockIdx.x, h0 + g, d, M, lsum, a);
+    emit<E>(p, u, h0 + g, d, M, lsum, a);
   }
   __shared__ float s_stat[32];
   __shared__ int s_last;
-  finish_split<E>(p, u, h0, GT, s_stat, &s_last);
+  finish_split<E>(p, u, blockIdx.y, h0, GT, s_stat, &s_last);
 }
 
 // ------------------------------------------------------------ gather hook

@@ -166,11 +166,15 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
   __shared__ float s_stat[32];
   __shared__ int s_last;
 
+  // work item = unit * planes + head block: a unit's head blocks are adjacent,
+  // so the launch runs the (longest-first) unit order
+  const int unit = blockIdx.x / p.planes;
+  const int plane = blockIdx.x - unit * p.planes;
   UnitInfo u;
-  if (!resolve_unit(p, blockIdx.x, u)) return;
+  if (!resolve_unit(p, unit, u)) return;
   const int gt = p.heads_per_unit;  // valid columns of the 16-wide head block
-  const int kvh = blockIdx.y / p.n_gblocks;
-  const int h0 = kvh * p.group + (blockIdx.y % p.n_gblocks) * gt;
+  const int kvh = plane / p.n_gblocks;
+  const int h0 = kvh * p.group + (plane % p.n_gblocks) * gt;
   // workgroup-uniform values, kept in scalar registers
   const int t_begin = __builtin_amdgcn_readfirstlane(u.c * p.chunk);
   const int t_end = __builtin_amdgcn_readfirstlane(min(u.L, u.c * p.chunk + p.chunk));
@@ -343,9 +347,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
       lsum += s_l[w][g] * sw;
       a += s_acc[(w * 16 + g) * D + d] * sw;
     }
-    emit<E>(p, u, blockIdx.x, h0 + g, d, Mx, lsum, a);
+    emit<E>(p, u, h0 + g, d, Mx, lsum, a);
   }
-  finish_split<E>(p, u, h0, gt, s_stat, &s_last);
+  finish_split<E>(p, u, plane, h0, gt, s_stat, &s_last);
 }
 
 }  // namespace fa
