@@ -73,6 +73,14 @@ HostPlan make_plan(fa_dtype_t dt, int batch, int hq, int hkv, int d, int page_si
   want = std::max<int64_t>(want, kChunkQuantum);
   int64_t chunk = (want + kChunkQuantum - 1) / kChunkQuantum * kChunkQuantum;
   chunk = std::min(chunk, kMaxChunk);
+  if (!contig && page_size % 16 == 0) {
+    // the matrix-core kernel stages a unit's page ids in LDS: at most 1024
+    // whole pages per unit (plus a partial page at each end)
+    static_assert(1024 + 2 <= fa::kPageTable, "page table slice");
+    const int64_t cap = std::max<int64_t>(
+        kChunkQuantum, 1024 * int64_t(page_size) / kChunkQuantum * kChunkQuantum);
+    chunk = std::min(chunk, cap);
+  }
   hp.chunk = int(chunk);
   // Units: a request of L rows has max(1, ceil(L / chunk)) of them, which is at
   // most 1 + floor(L / chunk); summed, at most batch + floor(sum L / chunk).

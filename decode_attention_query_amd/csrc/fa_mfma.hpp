@@ -82,6 +82,10 @@ __device__ inline void pack_probs(const float *p, typename Mfma<E>::v8 &hi,
   }
 }
 
+// Page slots of one split unit staged in LDS (the host caps the split size so
+// a unit spans at most 1024 whole pages plus a partial one at each end).
+constexpr int kPageTable = 1040;
+
 template <class E, int D>
 struct MfmaGeom {
   static constexpr int NW = 4;           // waves per workgroup
@@ -121,9 +125,26 @@ struct KVTile {
 // one page, the block's page is resolved once per wave with a scalar load;
 // otherwise (page sizes that are not multiples of 16) every lane resolves its
 // own rows.
+// Element offset of the first row of the 16-row block starting at row tb
+// (wave-uniform; the block lies in one page).  Page ids come from the unit's
+// slice of the page table, staged in LDS at the start of the workgroup
+// (s_pages[i] = page id of page slot slot0 + i).
+__device__ inline int64_t staged_block_offset(const DecodeParams &p, const int32_t *s_pages,
+                                              int slot0, int kvh, int tb) {
+  int64_t page = 0;
+  uint32_t row = (uint32_t)tb;
+  if (!p.contig) {
+    const uint32_t slot = fastdiv((uint32_t)tb, p.page_div);
+    row = (uint32_t)tb - slot * (uint32_t)p.page_size;
+    page = __builtin_amdgcn_readfirstlane(s_pages[slot - slot0]);
+  }
+  return ((page * p.num_kv_heads + kvh) * (int64_t)p.page_size + row) * p.head_dim;
+}
+
 template <class E, int D>
 __device__ inline void issue_tile(KVTile<MfmaGeom<E, D>::NI> &T, const DecodeParams &p,
-                                  int32_t page_base, int kvh, int t0, int t_end, int lane) {
+                                  int32_t page_base, const int32_t *s_pages, int slot0, int kvh,
+                                  int t0, int t_end, int lane) {
   using G = MfmaGeom<E, D>;
   const int r0 = lane / G::LPR;           // row within an instruction
   const int col = (lane % G::LPR) * 16;   // byte within the row
@@ -134,7 +155,7 @@ __device__ inline void issue_tile(KVTile<MfmaGeom<E, D>::NI> &T, const DecodePar
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int tb = min(t0 + 16 * j, t_end - 1);
-      blk[j] = block_row_offset(p, page_base, kvh, tb) - (int64_t)tb * D;
+      blk[j] = staged_block_offset(p, s_pages, slot0, kvh, tb) - (int64_t)tb * D;
     }
   }
 #pragma unroll
@@ -179,6 +200,21 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
   const int t_begin = __builtin_amdgcn_readfirstlane(u.c * p.chunk);
   const int t_end = __builtin_amdgcn_readfirstlane(min(u.L, u.c * p.chunk + p.chunk));
   const int32_t page_base = __builtin_amdgcn_readfirstlane(u.page_base);
+
+  // The unit's page ids, once, into LDS: later lookups are LDS reads instead
+  // of scalar loads that each tile would wait for.  The host keeps a unit
+  // within kPageTable page slots.
+  __shared__ int32_t s_pages[kPageTable];
+  int slot0 = 0;
+  if (p.uniform_blocks && !p.contig && t_begin < t_end) {
+    slot0 = (int)fastdiv((uint32_t)t_begin, p.page_div);
+    const int count = (int)fastdiv((uint32_t)(t_end - 1), p.page_div) - slot0 + 1;
+    for (int i = threadIdx.x; i < count; i += 256) {
+      const int32_t id = p.indices[page_base + slot0 + i];
+      s_pages[i] = min(max(id, 0), p.num_total_pages - 1);
+    }
+    __syncthreads();
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -293,15 +329,15 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
   int t0 = t_begin + wave * TT;
   if (t0 < t_end) {
     KVTile<G::NI> A;
-    issue_tile<E, D>(A, p, page_base, kvh, t0, t_end, lane);
+    issue_tile<E, D>(A, p, page_base, s_pages, slot0, kvh, t0, t_end, lane);
     if constexpr (G::kPipelined) {
       KVTile<G::NI> B;
       while (true) {
-        issue_tile<E, D>(B, p, page_base, kvh, t0 + stride, t_end, lane);
+        issue_tile<E, D>(B, p, page_base, s_pages, slot0, kvh, t0 + stride, t_end, lane);
         compute(A, t0);
         t0 += stride;
         if (t0 >= t_end) break;
-        issue_tile<E, D>(A, p, page_base, kvh, t0 + stride, t_end, lane);
+        issue_tile<E, D>(A, p, page_base, s_pages, slot0, kvh, t0 + stride, t_end, lane);
         compute(B, t0);
         t0 += stride;
         if (t0 >= t_end) break;
@@ -311,7 +347,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
         compute(A, t0);
         t0 += stride;
         if (t0 >= t_end) break;
-        issue_tile<E, D>(A, p, page_base, kvh, t0, t_end, lane);
+        issue_tile<E, D>(A, p, page_base, s_pages, slot0, kvh, t0, t_end, lane);
       }
     }
   }
