@@ -29,7 +29,7 @@ STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_INVALID_PROBLEM", 2: "FA_ERR_UNSUPPORTED"
 # every symbol the public headers declare
 EXPORTED = ("fa_decode_workspace_size", "fa_decode_contig", "fa_decode_paged",
             "fa_status_string", "fa_debug_gather_paged", "fa_debug_timing_enable",
-            "fa_debug_timing_read", "fa_debug_plan")
+            "fa_debug_timing_read", "fa_debug_plan", "fa_debug_schedule")
 
 
 class FaError(RuntimeError):
@@ -76,6 +76,8 @@ def load_library():
     lib.fa_debug_timing_read.restype = _I
     lib.fa_debug_plan.argtypes = [_I, _I, _I, _I, _I, _I, _I] + [ctypes.POINTER(_I)] * 4
     lib.fa_debug_plan.restype = _I
+    lib.fa_debug_schedule.argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I64, _P]
+    lib.fa_debug_schedule.restype = _I
     _lib = lib
     return lib
 
@@ -219,6 +221,20 @@ def fa_debug_plan(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
         dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size, total_used_pages,
         *[ctypes.byref(x) for x in out]))
     return tuple(x.value for x in out)
+
+
+def fa_debug_schedule(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                      total_used_pages, indptr, last_page_len, out, stream=None):
+    """Fills out (device int32, 8 per work index) with the split-unit schedule."""
+    lib = load_library()
+    if not isinstance(out, torch.Tensor) or out.device.type != "cuda" or \
+            out.dtype != torch.int32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous int32 device tensor")
+    _check("fa_debug_schedule", lib.fa_debug_schedule(
+        dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size, total_used_pages,
+        _dev_buf(indptr, "indptr", batch + 1, torch.int32),
+        _dev_buf(last_page_len, "last_page_len", batch, torch.int32),
+        out.data_ptr(), out.numel(), _stream(stream)))
 
 
 def fa_status_string(status):

@@ -41,17 +41,6 @@ __host__ __device__ inline uint32_t fastdiv(uint32_t n, FastDiv f) {
   return (uint32_t)(((uint64_t)hi + n) >> f.shift);
 }
 
-// One split unit, as the plan kernel describes it (32 bytes, one scalar load).
-struct UnitDesc {
-  int32_t b;          // request; -1 for units past the real count
-  int32_t c;          // index of the unit within its request
-  int32_t n_units;    // units of the request
-  int32_t L;          // L_b
-  int32_t page_base;  // first index of the request's pages in indices
-  int32_t u0;         // first partial-result slot of the request
-  int32_t pad0, pad1;
-};
-
 // Everything a decode launch needs.  Passed by value as the kernel argument.
 struct DecodeParams {
   // tensors
@@ -73,19 +62,23 @@ struct DecodeParams {
   float scale_log2;   // scale * log2(e): scores live in the base-2 domain
   FastDiv page_div;   // row -> (page slot, row in page)
   // split-KV plan
-  int chunk;          // KV rows per split unit
-  int units_bound;    // grid.x; units past the real count exit at once
+  int chunk;          // KV rows per split unit (a multiple of 256)
+  int units_bound;    // work indices launched; those past the real unit count exit at once
   int contig;         // 1: contiguous cache (a single page of max_kv_len rows)
   int uniform_blocks; // 1: every 16-row block starting at a multiple of 16 lies in one page
   int contig_len;     // contiguous: valid_kv_len
   int contig_units;   // contiguous: ceil(valid_kv_len / chunk), at least 1
   // workspace regions
-  int64_t *row_prefix;    // [B + 1]   first output row of each request (gather hook)
-  struct UnitDesc *unit_desc;  // [units_bound]
   float *part_lse;        // [units_bound, Hq]     base-2 lse of each split's partial
   float *part_o;          // [units_bound, Hq, D]  normalised partial outputs
-  int32_t *arrivals;      // [B, Hq]   finished split units per (request, head block)
+  uint64_t *arrivals;     // [B, Hq]  per (request, head block): call tag << kCountBits | units done
+  uint64_t call_tag;      // this call's tag (< 2^40), different for every call
 };
+
+// Arrival counters carry the tag of the call that last counted in them, so a
+// counter left by an earlier call (or never written) reads as zero and the
+// workspace needs no clearing between calls.
+constexpr int kCountBits = 24;  // a request has fewer than 2^24 split units
 
 // ---------------------------------------------------------------- elements
 //

@@ -4,9 +4,12 @@
 
 #include <algorithm>
 #include <array>
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdint>
 #include <mutex>
+#include <random>
 #include <vector>
 
 #include "../../include/fa_decode.h"
@@ -44,7 +47,7 @@ struct HostPlan {
   int group = 0, gt = 0, n_gblocks = 0, planes = 0;
   int chunk = 0, units_bound = 0, kind = 0;
   // workspace byte offsets
-  size_t row_prefix = 0, unit_desc = 0, part_lse = 0, part_o = 0, arrivals = 0, total = 0;
+  size_t part_lse = 0, part_o = 0, arrivals = 0, total = 0;
 };
 
 bool extents_ok(int batch, int hq, int hkv, int page_size) {
@@ -89,23 +92,42 @@ HostPlan make_plan(fa_dtype_t dt, int batch, int hq, int hkv, int d, int page_si
   else
     hp.units_bound = int(batch + rows_ub / chunk);
   size_t off = 0;
-  hp.row_prefix = off;  off = align_up(off + sizeof(int64_t) * (batch + 1));
-  hp.unit_desc = off;   off = align_up(off + sizeof(fa::UnitDesc) * hp.units_bound);
   hp.part_lse = off;    off = align_up(off + sizeof(float) * size_t(hp.units_bound) * hq);
   hp.part_o = off;      off = align_up(off + sizeof(float) * size_t(hp.units_bound) * hq * d);
   // one counter per (request, head block); Hq per request bounds the blocks
-  hp.arrivals = off;    off = align_up(off + sizeof(int32_t) * size_t(batch) * hq);
+  hp.arrivals = off;    off = align_up(off + sizeof(uint64_t) * size_t(batch) * hq);
   hp.total = off;
   return hp;
 }
 
+// Work indices (split units times head blocks) must fit a launch and an int.
+bool launch_ok(const HostPlan &hp) {
+  return int64_t(hp.units_bound) * hp.planes < (int64_t(1) << 31);
+}
+
 void carve(DecodeParams &p, const HostPlan &hp, void *ws) {
   char *w = static_cast<char *>(ws);
-  p.row_prefix = reinterpret_cast<int64_t *>(w + hp.row_prefix);
-  p.unit_desc = reinterpret_cast<fa::UnitDesc *>(w + hp.unit_desc);
   p.part_lse = reinterpret_cast<float *>(w + hp.part_lse);
   p.part_o = reinterpret_cast<float *>(w + hp.part_o);
-  p.arrivals = reinterpret_cast<int32_t *>(w + hp.arrivals);
+  p.arrivals = reinterpret_cast<uint64_t *>(w + hp.arrivals);
+}
+
+// Call tags: distinct for every call of the process, in [2^39, 2^40), starting
+// at a random point so that a counter word left in memory by anything else
+// is unlikely to carry a live tag.
+uint64_t first_call_tag() {
+  uint64_t r = uint64_t(std::chrono::steady_clock::now().time_since_epoch().count());
+  try {
+    std::random_device rd;
+    r ^= (uint64_t(rd()) << 32) ^ rd();
+  } catch (...) {
+  }
+  return (uint64_t(1) << 39) | (r & ((uint64_t(1) << 38) - 1));
+}
+
+uint64_t next_call_tag() {
+  static std::atomic<uint64_t> next{first_call_tag()};
+  return next.fetch_add(1, std::memory_order_relaxed) & ((uint64_t(1) << 40) - 1);
 }
 
 // ------------------------------------------------------------------ timing
@@ -290,12 +312,9 @@ fa_status_t fa_decode_contig(fa_dtype_t dtype, int num_qo_heads, int num_kv_head
   p.contig_units =
       valid_kv_len == 0 ? 1 : int((int64_t(valid_kv_len) + hp.chunk - 1) / hp.chunk);
   carve(p, hp, workspace);
+  p.call_tag = next_call_tag();
 
   CallEvents ev(stream);
-  if (p.contig_units > 1) {  // split: the plan kernel zeroes the merge counters
-    hipLaunchKernelGGL(fa::plan_kernel, dim3(1), dim3(fa::kPlanThreads), 0, stream, p);
-    if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
-  }
   ev.mark(1, stream);
   if (dispatch_decode(dtype, p, hp, stream) != hipSuccess) return FA_ERR_LAUNCH;
   ev.mark(2, stream);
@@ -322,12 +341,13 @@ fa_status_t fa_decode_paged(fa_dtype_t dtype, int batch, int num_qo_heads, int n
   if (int64_t(total_used_pages) * page_size >= (int64_t(1) << 31)) return FA_ERR_UNSUPPORTED;
   if (!pool_size_ok(num_total_pages, num_kv_heads, page_size, head_dim))
     return FA_ERR_UNSUPPORTED;
+  const HostPlan hp = make_plan(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                                total_used_pages, false);
+  if (!launch_ok(hp)) return FA_ERR_UNSUPPORTED;
   const size_t need = fa_decode_workspace_size(batch, num_qo_heads, num_kv_heads, head_dim,
                                                page_size, total_used_pages);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
 
-  const HostPlan hp = make_plan(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
-                                total_used_pages, false);
   DecodeParams p = base_params(batch, num_qo_heads, num_kv_heads, head_dim, page_size,
                                num_total_pages, total_used_pages, sm_scale, hp);
   p.q = q;
@@ -339,10 +359,9 @@ fa_status_t fa_decode_paged(fa_dtype_t dtype, int batch, int num_qo_heads, int n
   p.indptr = indptr;
   p.last_page_len = last_page_len;
   carve(p, hp, workspace);
+  p.call_tag = next_call_tag();
 
   CallEvents ev(stream);
-  hipLaunchKernelGGL(fa::plan_kernel, dim3(1), dim3(fa::kPlanThreads), 0, stream, p);
-  if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
   ev.mark(1, stream);
   if (dispatch_decode(dtype, p, hp, stream) != hipSuccess) return FA_ERR_LAUNCH;
   ev.mark(2, stream);
@@ -392,12 +411,31 @@ fa_status_t fa_debug_gather_paged(fa_dtype_t dtype, int batch, int num_kv_heads,
   p.last_page_len = last_page_len;
   carve(p, hp, workspace);
   const int elem = dtype == FA_DTYPE_F32 ? 4 : 2;
-  hipLaunchKernelGGL(fa::plan_kernel, dim3(1), dim3(fa::kPlanThreads), 0, stream, p);
-  if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
   hipLaunchKernelGGL(fa::gather_kernel, dim3(hp.units_bound, num_kv_heads), dim3(256), 0,
                      stream, p, out, out_rows, elem);
   if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
   return FA_OK;
+}
+
+fa_status_t fa_debug_schedule(fa_dtype_t dtype, int batch, int num_qo_heads, int num_kv_heads,
+                              int head_dim, int page_size, int total_used_pages,
+                              const int32_t *indptr, const int32_t *last_page_len,
+                              int32_t *out, int64_t out_entries, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return FA_ERR_UNSUPPORTED;
+  if (!extents_ok(batch, num_qo_heads, num_kv_heads, page_size)) return FA_ERR_INVALID_PROBLEM;
+  if (!head_dim_ok(head_dim)) return FA_ERR_UNSUPPORTED;
+  if (total_used_pages < 0) return FA_ERR_INVALID_PROBLEM;
+  if (!indptr || !last_page_len || !out) return FA_ERR_INVALID_PROBLEM;
+  if (int64_t(total_used_pages) * page_size >= (int64_t(1) << 31)) return FA_ERR_UNSUPPORTED;
+  const HostPlan hp = make_plan(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                                total_used_pages, false);
+  if (out_entries < 8 * int64_t(hp.units_bound)) return FA_ERR_WORKSPACE_TOO_SMALL;
+  DecodeParams p = base_params(batch, num_qo_heads, num_kv_heads, head_dim, page_size, 1,
+                               total_used_pages, 1.0f, hp);
+  p.indptr = indptr;
+  p.last_page_len = last_page_len;
+  hipLaunchKernelGGL(fa::schedule_kernel, dim3(hp.units_bound), dim3(256), 0, stream, p, out);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 fa_status_t fa_debug_timing_enable(int enable) {

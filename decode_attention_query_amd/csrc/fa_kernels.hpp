@@ -1,4 +1,5 @@
-// fa_kernels.hpp -- split plan, vector-ALU decode, LSE merge and the gather hook.
+// fa_kernels.hpp -- split-unit schedule, vector-ALU decode, LSE merge and the
+// gather hook.
 //
 // Work decomposition (all kernels): a *split unit* is one request's KV rows
 // [c * chunk, min(L_b, (c + 1) * chunk)).  A decode workgroup handles one split
@@ -14,131 +15,205 @@
 
 namespace fa {
 
-// ------------------------------------------------------------------ plan
+// -------------------------------------------------------------- schedule
 //
-// One workgroup.  For every request: L_b from the page table (clamped so a
-// table that breaks its contract cannot send a later kernel outside the
-// buffers) and its number of split units; then one descriptor per split unit
-// (request, index, count, L_b, page base, first unit), so a decode workgroup
-// finds everything about its unit with a single scalar load.  baracuda-kernels
-// 0.0.1-alpha.68, src/attention/batch_paged_decode.rs, module doc "Layout":
-// request b owns pages indices[indptr[b] .. indptr[b+1]), its last page holds
+// No separate plan launch: every wave derives its workgroup's split unit from
+// the page table on its own (all four waves reach the same answer), with
+// cross-lane operations only -- no LDS, no barrier, so a starting workgroup
+// does not queue behind the LDS traffic of the workgroup already running on
+// its compute unit.  It recomputes every request's length and unit count (a
+// few hundred bytes, served by the cache after the first workgroups) and
+// selects the unit its work index names.  baracuda-kernels 0.0.1-alpha.68,
+// src/attention/batch_paged_decode.rs, module doc "Layout": request b owns
+// pages indices[indptr[b] .. indptr[b+1]), its last page holds
 // last_page_len[b] rows.
-constexpr int kPlanThreads = 1024;
+//
+// Work order (longest processing time first, so short work fills the tail of
+// the launch): every request's full-length units, in request order; then the
+// last, shorter units, longest first by length class (kClasses classes of
+// chunk / kClasses rows each; request order inside a class).  The order only
+// decides which workgroup runs what: partial results have their own
+// numbering, contiguous per request (slot = first slot of the request + index
+// of the unit), and are merged in that order.
+constexpr int kClasses = 16;   // length classes of last units
+constexpr int kRegChunks = 4;  // 64-request chunks held in registers at once
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const DecodeParams p) {
-  // split-merge arrival counters start every call at zero
-  for (int i = threadIdx.x; i < p.batch * p.num_qo_heads; i += kPlanThreads) p.arrivals[i] = 0;
-  if (p.contig) return;  // a contiguous cache's single length is known on the host
-  // Work order: every request's full-length units first, then the shorter
-  // last units, so the short work fills the tail of the launch (longest
-  // first).  Partial results use a separate numbering, contiguous per request
-  // (slot = first slot of the request + index of the unit).
-  __shared__ int s_full[kPlanThreads];
-  __shared__ int s_part[kPlanThreads];
-  __shared__ long long s_rows[kPlanThreads];
-  __shared__ int s_carry_full, s_carry_part;
-  __shared__ long long s_carry_rows;
-  const int tid = threadIdx.x;
-  const int T = p.total_used_pages;
-  // pass 0 counts the full units of the whole batch (where the partial ones
-  // start); pass 1 writes the descriptors
-  int total_full = 0;
-  for (int pass = 0; pass < 2; ++pass) {
-    if (tid == 0) {
-      s_carry_full = 0;
-      s_carry_part = 0;
-      s_carry_rows = 0;
-    }
-    __syncthreads();
-    for (int base = 0; base < p.batch; base += kPlanThreads) {
-      const int b = base + tid;
-      int L = 0, full = 0, part = 0, p0 = 0;
-      if (b < p.batch) {
-        p0 = min(max(p.indptr[b], 0), T);
-        const int p1 = min(max(p.indptr[b + 1], p0), T);
-        const int n = p1 - p0;
-        const int lpl = min(max(p.last_page_len[b], 0), p.page_size);
-        L = n == 0 ? 0 : (n - 1) * p.page_size + lpl;  // < 2^31: host checks T * P
-        full = L / p.chunk;
-        part = (L % p.chunk != 0 || L == 0) ? 1 : 0;  // an empty request is one empty unit
-      }
-      // inclusive scans (Hillis-Steele)
-      s_full[tid] = full;
-      s_part[tid] = part;
-      s_rows[tid] = L;
-      __syncthreads();
-      for (int off = 1; off < kPlanThreads; off <<= 1) {
-        const int f = tid >= off ? s_full[tid - off] : 0;
-        const int q = tid >= off ? s_part[tid - off] : 0;
-        const long long r = tid >= off ? s_rows[tid - off] : 0;
-        __syncthreads();
-        s_full[tid] += f;
-        s_part[tid] += q;
-        s_rows[tid] += r;
-        __syncthreads();
-      }
-      if (pass == 1 && b < p.batch) {
-        const int first_full = s_carry_full + s_full[tid] - full;
-        const int first_part = s_carry_part + s_part[tid] - part;
-        const int units = full + part;
-        const int slot0 = first_full + first_part;  // units of earlier requests
-        p.row_prefix[b] = s_carry_rows + s_rows[tid] - L;
-        for (int i = 0; i < full; ++i) {
-          const int w = first_full + i;
-          if (w < p.units_bound) p.unit_desc[w] = UnitDesc{b, i, units, L, p0, slot0, 0, 0};
-        }
-        if (part) {
-          const int w = total_full + first_part;
-          if (w < p.units_bound) p.unit_desc[w] = UnitDesc{b, full, units, L, p0, slot0, 0, 0};
-        }
-      }
-      __syncthreads();
-      if (tid == kPlanThreads - 1) {
-        s_carry_full += s_full[tid];
-        s_carry_part += s_part[tid];
-        s_carry_rows += s_rows[tid];
-      }
-      __syncthreads();
-    }
-    total_full = s_carry_full;
-    __syncthreads();  // everyone has read the carry before pass 1 resets it
-  }
-  // units past the real count exit at once
-  for (int w = s_carry_full + s_carry_part + tid; w < p.units_bound; w += kPlanThreads)
-    p.unit_desc[w] = UnitDesc{-1, 0, 0, 0, 0, 0, 0, 0};
-  if (tid == 0) p.row_prefix[p.batch] = s_carry_rows;
-}
-
-// A split unit: (request, unit within request, units of the request, L_b,
-// first partial-result slot of the request, page base).
+// A split unit: request, unit within the request, units of the request, L_b,
+// first partial-result slot of the request, page base, and (gather hook) the
+// request's first row in a concatenation of all requests' rows (sum L < 2^31).
 struct UnitInfo {
   int b, c, n_units, L;
   int u0;
   int32_t page_base;
+  int row0;
 };
 
-// Returns false for units past the real count.
-__device__ inline bool resolve_unit(const DecodeParams &p, int unit, UnitInfo &u) {
-  if (p.contig) {
-    if (unit >= p.contig_units) return false;
+struct Request {
+  int L, full, part, p0;
+};
+
+// L_b and the unit counts of request b (zeros past the batch).  The page table
+// is clamped so a table that breaks its contract cannot send a kernel outside
+// the buffers.
+__device__ inline Request request_of(const DecodeParams &p, int b) {
+  const int bb = min(b, p.batch - 1);  // loads stay in bounds
+  const int T = p.total_used_pages;
+  const int i0 = p.indptr[bb], i1 = p.indptr[bb + 1], lpl_raw = p.last_page_len[bb];
+  Request r;
+  r.p0 = min(max(i0, 0), T);
+  const int n = min(max(i1, r.p0), T) - r.p0;
+  const int lpl = min(max(lpl_raw, 0), p.page_size);
+  r.L = n == 0 ? 0 : (n - 1) * p.page_size + lpl;  // < 2^31: the host checks T * P
+  r.full = r.L / p.chunk;
+  r.part = (r.L % p.chunk != 0 || r.L == 0) ? 1 : 0;  // an empty request is one empty unit
+  if (b >= p.batch) r = Request{0, 0, 0, 0};
+  return r;
+}
+
+// Length class of a request's last unit, -1 if it has none (chunk is a
+// multiple of kClasses).
+__device__ inline int length_class(const DecodeParams &p, const Request &r) {
+  if (!r.part) return -1;
+  return min((r.L - r.full * p.chunk) / (p.chunk / kClasses), kClasses - 1);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts within each row of
+// 16 lanes, then the row totals broadcast into the following rows (DPP).
+__device__ inline int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
+__device__ inline int lane_value(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+
+__device__ inline int lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+}
+
+// The split unit of work index w; false for indices past the real unit count.
+// Every lane of the calling wave takes part; the result is wave-uniform.
+template <bool kRows>
+__device__ bool find_unit(const DecodeParams &p, int w, UnitInfo &u) {
+  if (p.contig) {  // one request of contig_len rows, known on the host
+    if (w >= p.contig_units) return false;
     u.b = 0;
-    u.c = unit;
+    u.c = w;
     u.u0 = 0;
     u.n_units = p.contig_units;
     u.L = p.contig_len;
     u.page_base = 0;
+    u.row0 = 0;
     return true;
   }
-  typedef const __attribute__((address_space(4))) UnitDesc cdesc;
-  const cdesc *d = (cdesc *)p.unit_desc + unit;  // written by the plan kernel
-  u.b = d->b;
-  u.c = d->c;
-  u.n_units = d->n_units;
-  u.L = d->L;
-  u.page_base = d->page_base;
-  u.u0 = d->u0;
-  return u.b >= 0;
+  const int lane = threadIdx.x & (kWave - 1);
+  constexpr int kGroup = kRegChunks * kWave;  // requests per register group
+  const int groups = (p.batch + kGroup - 1) / kGroup;
+  Request rq[kRegChunks];
+  auto load_group = [&](int g) {
+#pragma unroll
+    for (int j = 0; j < kRegChunks; ++j)
+      if ((g * kRegChunks + j) * kWave < p.batch)
+        rq[j] = request_of(p, (g * kRegChunks + j) * kWave + lane);
+  };
+  auto take = [&](const Request &r, int src, int b0, int c, int n_units, int u0, int row0) {
+    u.b = b0 + src;
+    u.c = c;
+    u.n_units = n_units;
+    u.L = lane_value(r.L, src);
+    u.u0 = u0;
+    u.page_base = lane_value(r.p0, src);
+    u.row0 = row0;
+  };
+
+  // pass 1: the full-length units, in request order
+  int carry_full = 0, carry_units = 0, carry_rows = 0;
+  for (int g = 0; g < groups; ++g) {
+    load_group(g);
+#pragma unroll
+    for (int j = 0; j < kRegChunks; ++j) {
+      const int b0 = (g * kRegChunks + j) * kWave;
+      if (b0 >= p.batch) break;
+      const Request &r = rq[j];
+      const int units = r.full + r.part;
+      const int i_full = wave_incl_scan(r.full);
+      const int i_units = wave_incl_scan(units);
+      const int i_rows = kRows ? wave_incl_scan(r.L) : 0;
+      const int e_full = carry_full + i_full - r.full;
+      const uint64_t own = __ballot(w >= e_full && w < e_full + r.full);
+      if (own) {
+        const int src = (int)__builtin_ctzll(own);
+        take(r, src, b0, w - lane_value(e_full, src), lane_value(units, src),
+             carry_units + lane_value(i_units - units, src),
+             kRows ? carry_rows + lane_value(i_rows - r.L, src) : 0);
+        return true;
+      }
+      carry_full += lane_value(i_full, kWave - 1);
+      carry_units += lane_value(i_units, kWave - 1);
+      if (kRows) carry_rows += lane_value(i_rows, kWave - 1);
+    }
+  }
+  if (w >= carry_units) return false;
+  const int rank = w - carry_full;  // among the last units
+
+  // pass 2: last units per length class; lane kClasses-1-k counts class k, so
+  // the lane order is the work order
+  const bool resident = groups == 1;  // rq[] still holds every request
+  int hist = 0;
+  for (int g = 0; g < groups; ++g) {
+    if (!resident) load_group(g);
+#pragma unroll
+    for (int j = 0; j < kRegChunks; ++j) {
+      if ((g * kRegChunks + j) * kWave >= p.batch) break;
+      const int cls = length_class(p, rq[j]);
+#pragma unroll
+      for (int k = 0; k < kClasses; ++k) {
+        const int cnt = __popcll(__ballot(cls == k));
+        if (lane == kClasses - 1 - k) hist += cnt;
+      }
+    }
+  }
+  const int i_hist = wave_incl_scan(hist);
+  const uint64_t hit = __ballot(rank >= i_hist - hist && rank < i_hist);
+  const int slot = (int)__builtin_ctzll(hit);
+  const int sel_class = kClasses - 1 - slot;
+  const int sel_rank = rank - lane_value(i_hist - hist, slot);
+
+  // pass 3: the request holding that rank within its class
+  int carry_sel = 0;
+  carry_units = 0;
+  carry_rows = 0;
+  for (int g = 0; g < groups; ++g) {
+    if (!resident) load_group(g);
+#pragma unroll
+    for (int j = 0; j < kRegChunks; ++j) {
+      const int b0 = (g * kRegChunks + j) * kWave;
+      if (b0 >= p.batch) break;
+      const Request &r = rq[j];
+      const int units = r.full + r.part;
+      const uint64_t sel = __ballot(length_class(p, r) == sel_class);
+      const int i_units = wave_incl_scan(units);
+      const int i_rows = kRows ? wave_incl_scan(r.L) : 0;
+      const bool mine = ((sel >> lane) & 1) && carry_sel + lanes_below(sel) == sel_rank;
+      const uint64_t own = __ballot(mine);
+      if (own) {
+        const int src = (int)__builtin_ctzll(own);
+        take(r, src, b0, lane_value(r.full, src), lane_value(units, src),
+             carry_units + lane_value(i_units - units, src),
+             kRows ? carry_rows + lane_value(i_rows - r.L, src) : 0);
+        return true;
+      }
+      carry_sel += __popcll(sel);
+      carry_units += lane_value(i_units, kWave - 1);
+      if (kRows) carry_rows += lane_value(i_rows, kWave - 1);
+    }
+  }
+  return false;  // not reached: the class counts hold the rank
 }
 
 // Writes the combined result of one (request, query head, feature) of a unit:
@@ -231,18 +306,40 @@ __device__ void merge_partials(const DecodeParams &p, int b, int u0, int n, int 
 // go to memory rather than to a possibly stale L2 line.  No cache-wide
 // write-back or invalidate (what a device-scope fence would emit, once per
 // workgroup) is needed, because no non-coherent data crosses workgroups.
+//
+// The counter holds (call tag << kCountBits) | units counted.  A compare-and-
+// swap counts the unit in: a counter whose tag is not this call's counts as
+// zero.  The loop ends: each failed swap means another unit of this request
+// was counted, and there are fewer than n_units of those.  The merging
+// workgroup leaves the counter at (tag, 0), so replaying the same launch (a
+// captured graph) also starts from zero.
 template <class E>
 __device__ void finish_split(const DecodeParams &p, const UnitInfo &u, int plane, int h0, int gt,
                              float *s_stat, int *s_last) {
   if (u.n_units <= 1) return;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  int32_t *counter = p.arrivals + (int64_t)u.b * p.num_qo_heads + plane;
-  if (threadIdx.x == 0) *s_last = atomicAdd(counter, 1) == u.n_units - 1;
+  unsigned long long *counter = reinterpret_cast<unsigned long long *>(
+      p.arrivals + (int64_t)u.b * p.num_qo_heads + plane);
+  const unsigned long long mine = (unsigned long long)p.call_tag << kCountBits;
+  if (threadIdx.x == 0) {
+    unsigned long long seen = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    while (true) {
+      const unsigned long long want =
+          ((seen >> kCountBits) == p.call_tag ? seen : mine) + 1;
+      const unsigned long long prev = atomicCAS(counter, seen, want);
+      if (prev == seen) {
+        *s_last = want - mine == (unsigned long long)u.n_units;
+        break;
+      }
+      seen = prev;
+    }
+  }
   __syncthreads();
   if (!*s_last) return;
+  if (threadIdx.x == 0)
+    __hip_atomic_store(counter, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   merge_partials<E>(p, u.b, u.u0, u.n_units, h0, gt, s_stat);
-  if (threadIdx.x == 0) *counter = 0;
 }
 
 // ------------------------------------------------------ vector-ALU decode
@@ -269,7 +366,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   __shared__ float s_l[NW][GT];
 
   UnitInfo u;
-  if (!resolve_unit(p, blockIdx.x, u)) return;
+  if (!find_unit<false>(p, blockIdx.x, u)) return;
   const int kvh = blockIdx.y / p.n_gblocks;
   const int h0 = kvh * p.group + (blockIdx.y % p.n_gblocks) * GT;
   const int t_begin = u.c * p.chunk;
@@ -421,15 +518,40 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   finish_split<E>(p, u, blockIdx.y, h0, GT, s_stat, &s_last);
 }
 
+// ---------------------------------------------------------- schedule hook
+//
+// Test-only: the unit each work index runs, from find_unit, 8 int32 per index:
+// b (-1 past the real count), c, n_units, L, u0, page base, row0 low, row0 high.
+__global__ __launch_bounds__(256) void schedule_kernel(const DecodeParams p, int32_t *out) {
+  UnitInfo u;
+  const bool ok = find_unit<true>(p, blockIdx.x, u);
+  if (threadIdx.x != 0) return;
+  int32_t *o = out + 8 * (int64_t)blockIdx.x;
+  if (!ok) {
+    o[0] = -1;
+    for (int i = 1; i < 8; ++i) o[i] = 0;
+    return;
+  }
+  o[0] = u.b;
+  o[1] = u.c;
+  o[2] = u.n_units;
+  o[3] = u.L;
+  o[4] = u.u0;
+  o[5] = u.page_base;
+  o[6] = u.row0;
+  o[7] = 0;
+}
+
 // ------------------------------------------------------------ gather hook
 //
-// Test-only: copies every valid row of one KV head of one split unit to
-// out[(row_prefix[b] + t) * Hkv + kvh, :], using kv_row_offset, the same
-// address code as the decode kernels.  16 bytes per lane.
+// Test-only: copies every valid row t of one KV head of one split unit of
+// request b to out[(row0_b + t) * Hkv + kvh, :], where row0_b = L_0 + .. +
+// L_{b-1}, using kv_row_offset, the same address code as the decode kernels,
+// and the same unit schedule.  16 bytes per lane.
 __global__ __launch_bounds__(256) void gather_kernel(const DecodeParams p, void *out,
                                                      int64_t out_rows, int elem_bytes) {
   UnitInfo u;
-  if (!resolve_unit(p, blockIdx.x, u)) return;
+  if (!find_unit<true>(p, blockIdx.x, u)) return;
   const int kvh = blockIdx.y;
   const int t_begin = u.c * p.chunk;
   const int t_end = min(u.L, t_begin + p.chunk);
@@ -437,7 +559,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const DecodeParams p, void 
   for (int idx = threadIdx.x; idx < (t_end - t_begin) * vecs; idx += blockDim.x) {
     const int t = t_begin + idx / vecs;
     const int vi = idx % vecs;
-    const int64_t orow = p.row_prefix[u.b] + t;
+    const int64_t orow = u.row0 + t;
     if (orow >= out_rows) continue;
     const int64_t off = kv_row_offset(p, u.page_base, kvh, t);
     const uint4 r =

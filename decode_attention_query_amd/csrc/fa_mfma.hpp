@@ -175,7 +175,8 @@ __device__ inline void issue_tile(KVTile<MfmaGeom<E, D>::NI> &T, const DecodePar
 }
 
 template <class E, int D>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1))) void decode_mfma_kernel(
+    const DecodeParams p) {
   using G = MfmaGeom<E, D>;
   using M = Mfma<E>;
   using v8 = typename M::v8;
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(const DecodeParams p) 
   const int unit = blockIdx.x / p.planes;
   const int plane = blockIdx.x - unit * p.planes;
   UnitInfo u;
-  if (!resolve_unit(p, unit, u)) return;
+  if (!find_unit<false>(p, unit, u)) return;
   const int gt = p.heads_per_unit;  // valid columns of the 16-wide head block
   const int kvh = plane / p.n_gblocks;
   const int h0 = kvh * p.group + (plane % p.n_gblocks) * gt;

@@ -30,7 +30,11 @@
  *     returns without synchronising; outputs are ready when the stream reaches
  *     that point.  No host<->device copies are made.
  *   - Determinism: for a fixed argument set, results are bit-identical from
- *     run to run on one device (fixed reduction order, no atomics).
+ *     run to run on one device.  Long requests are split into units whose
+ *     partial results are combined in unit order, whichever workgroup ends
+ *     last; the only atomics are the counters that find that workgroup.
+ *   - Graph capture: a call may be captured into a HIP graph and replayed;
+ *     replays of one captured call must not overlap each other.
  *   - Errors: arguments are checked on the host in the order listed for each
  *     entry point; any status other than FA_OK means nothing was enqueued,
  *     except FA_ERR_LAUNCH, which reports a failed kernel launch.
@@ -74,8 +78,10 @@ typedef enum {
  *   paged calls:       fa_decode_workspace_size(batch, Hq, Hkv, D, page_size, total_used_pages)
  *   contiguous calls:  fa_decode_workspace_size(1, Hq, Hkv, D, max_kv_len, 1)
  * Returns 0 when the arguments are not a valid problem (the entry point then
- * reports why); otherwise a positive size.  The workspace needs no
- * initialisation and is overwritten by each call. */
+ * reports why); otherwise a positive size.  The workspace holds the split
+ * partial results and one arrival counter per (request, head block); each
+ * counter is tagged with the call that last used it, so the workspace needs no
+ * initialisation and may hold anything between calls. */
 size_t fa_decode_workspace_size(int batch, int num_qo_heads, int num_kv_heads, int head_dim,
                                 int page_size, int total_used_pages);
 
@@ -95,8 +101,10 @@ size_t fa_decode_workspace_size(int batch, int num_qo_heads, int num_kv_heads, i
  *   num_qo_heads, num_kv_heads or max_kv_len <= 0            -> FA_ERR_INVALID_PROBLEM
  *   num_qo_heads % num_kv_heads != 0                         -> FA_ERR_INVALID_PROBLEM
  *   head_dim not 64, 128 or 256                              -> FA_ERR_UNSUPPORTED
+ *   num_qo_heads > 65535                                     -> FA_ERR_UNSUPPORTED
  *   q, k_cache, v_cache or o NULL                            -> FA_ERR_INVALID_PROBLEM
  *   valid_kv_len < 0 or > max_kv_len                         -> FA_ERR_INVALID_PROBLEM
+ *   Hkv * max_kv_len * D >= 10^15 elements                   -> FA_ERR_UNSUPPORTED
  *   workspace NULL or workspace_bytes short                  -> FA_ERR_WORKSPACE_TOO_SMALL
  *   a kernel launch fails                                    -> FA_ERR_LAUNCH */
 fa_status_t fa_decode_contig(fa_dtype_t dtype, int num_qo_heads, int num_kv_heads,
@@ -140,9 +148,14 @@ fa_status_t fa_decode_contig(fa_dtype_t dtype, int num_qo_heads, int num_kv_head
  *   num_qo_heads % num_kv_heads != 0                          -> FA_ERR_INVALID_PROBLEM
  *   head_dim not 64, 128 or 256                               -> FA_ERR_UNSUPPORTED
  *   total_used_pages < 0                                      -> FA_ERR_INVALID_PROBLEM
+ *   num_qo_heads > 65535                                      -> FA_ERR_UNSUPPORTED
  *   q, k_data, v_data, indptr, last_page_len, o or lse NULL,
  *     or indices NULL with total_used_pages > 0               -> FA_ERR_INVALID_PROBLEM
  *   total_used_pages * page_size >= 2^31 (row index range)    -> FA_ERR_UNSUPPORTED
+ *   num_total_pages * Hkv * page_size * D >= 10^15 elements   -> FA_ERR_UNSUPPORTED
+ *   (batch + total_used_pages * page_size / chunk) * Hq / G >= 2^31, where
+ *     chunk and G (query heads per workgroup) are fa_debug_plan's chunk_rows
+ *     and heads_per_unit (more workgroups than a launch takes) -> FA_ERR_UNSUPPORTED
  *   workspace NULL or workspace_bytes short                   -> FA_ERR_WORKSPACE_TOO_SMALL
  *   a kernel launch fails                                     -> FA_ERR_LAUNCH */
 fa_status_t fa_decode_paged(fa_dtype_t dtype, int batch, int num_qo_heads, int num_kv_heads,

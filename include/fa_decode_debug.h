@@ -36,6 +36,25 @@ fa_status_t fa_debug_gather_paged(fa_dtype_t dtype, int batch, int num_kv_heads,
                                   void *out, int64_t out_rows, void *workspace,
                                   size_t workspace_bytes, hipStream_t stream);
 
+/* The split-unit schedule of a paged decode call with these arguments, as the
+ * decode kernels compute it on the device (same code): for every work index
+ * w < units_bound (see fa_debug_plan), 8 int32 values at out[8 w .. 8 w + 7]:
+ * the request b (-1 for indices past the real unit count, the rest 0), the
+ * unit's index c within the request, the request's unit count, L_b, the
+ * request's first partial-result slot, its page base (indptr[b], clamped),
+ * and the low and high 32-bit words of L_0 + .. + L_{b-1}.
+ *   indptr, last_page_len   as for fa_decode_paged (same contract)
+ *   out                     device int32 [out_entries], at least 8 * units_bound
+ * Checks: dtype, extents, head_dim and total_used_pages as fa_decode_paged;
+ * indptr, last_page_len or out NULL -> FA_ERR_INVALID_PROBLEM; rows beyond
+ * the index range -> FA_ERR_UNSUPPORTED; out_entries short ->
+ * FA_ERR_WORKSPACE_TOO_SMALL; a failed launch -> FA_ERR_LAUNCH.
+ * Asynchronous on stream. */
+fa_status_t fa_debug_schedule(fa_dtype_t dtype, int batch, int num_qo_heads, int num_kv_heads,
+                              int head_dim, int page_size, int total_used_pages,
+                              const int32_t *indptr, const int32_t *last_page_len,
+                              int32_t *out, int64_t out_entries, hipStream_t stream);
+
 /* Kernel timing.  While enabled, every decode call records a HIP event pair on
  * its stream around its main attention kernel (the one that streams K and V),
  * and another around the whole call.  fa_debug_timing_read waits for the

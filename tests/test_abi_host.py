@@ -118,6 +118,10 @@ INV, UNS, WS = fad.FA_ERR_INVALID_PROBLEM, fad.FA_ERR_UNSUPPORTED, fad.FA_ERR_WO
     (dict(ptrs={"o": None}), INV),
     (dict(ptrs={"lse": None}), INV),
     (dict(page=1 << 20, used=1 << 11, pages=1 << 11), UNS),
+    (dict(hq=70000, hkv=70000), UNS),                  # more query heads than a launch takes
+    (dict(pages=1 << 30, hkv=64, hq=64, page=1 << 9), UNS),  # pool beyond 10^15 elements
+    (dict(batch=1 << 20, hq=32768, hkv=1), UNS),       # 2^31 workgroups or more
+    (dict(batch=1 << 20, hq=32768, hkv=1, ws=None), UNS),  # ... checked before the workspace
     (dict(ws=None), WS),
     (dict(ws_bytes=16), WS),
     # order: the dtype is checked before the extents, the extents before head_dim

@@ -1,0 +1,171 @@
+"""The split-unit schedule the decode kernels compute on the device, and the
+merge counters that ride on it.
+
+The schedule is checked exactly (integers) against a plain restatement here:
+every split unit of every request appears once, full-length units first in
+request order, then each request's last (shorter) unit by length class,
+longest class first, request order inside a class, then the unused work
+indices.  Request lengths follow the page-table definition (the
+baracuda-kernels batch_paged_decode page, module doc "Layout").
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_query_amd as fad
+import workloads as W
+from gpu_util import announce, compare, device, oracle_of, run, to_dev
+
+pytestmark = pytest.mark.gpu
+
+N_CLASSES = 16
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return device()
+
+
+def expected_schedule(lens, page_size, chunk, units_bound):
+    lens = [int(x) for x in lens]
+    B = len(lens)
+    full = [L // chunk for L in lens]
+    part = [1 if (L % chunk or L == 0) else 0 for L in lens]
+    units = [f + q for f, q in zip(full, part)]
+    u0 = np.concatenate([[0], np.cumsum(units)])[:-1]
+    row0 = np.concatenate([[0], np.cumsum(lens)])[:-1]
+    n_pages, _ = W.pages_for_lens(lens, page_size)
+    base = np.concatenate([[0], np.cumsum(n_pages)])[:-1]
+    order = [(b, c) for b in range(B) for c in range(full[b])]
+    width = chunk // N_CLASSES
+    last = [b for b in range(B) if part[b]]
+    last.sort(key=lambda b: (-min((lens[b] - full[b] * chunk) // width, N_CLASSES - 1), b))
+    order += [(b, full[b]) for b in last]
+    assert len(order) <= units_bound
+    rows = [[b, c, units[b], lens[b], int(u0[b]), int(base[b]), int(row0[b]) & 0xffffffff,
+             int(row0[b]) >> 32] for b, c in order]
+    rows += [[-1, 0, 0, 0, 0, 0, 0, 0]] * (units_bound - len(order))
+    out = np.array(rows, dtype=np.int64)
+    out[:, 6] = out[:, 6].astype(np.uint32).astype(np.int32)  # low word as int32 bits
+    return out.astype(np.int32)
+
+
+def _lens_case(name):
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    if name == "c3-like":      # B=64, L ~ U[512, 8192]
+        return 16, rng.integers(512, 8193, 64), (32, 8, 128)
+    if name == "c4-like":      # B=32, all 32768
+        return 32, np.full(32, 32768), (64, 8, 128)
+    if name == "skew":         # B=128, mostly short, a few empty, one very long
+        lens = rng.integers(1, 600, 128)
+        lens[rng.integers(0, 128, 6)] = 0
+        lens[7] = 42110
+        return 16, lens, (16, 4, 256)
+    if name == "many":         # several scheduling rounds of 1024 requests
+        lens = rng.integers(0, 3000, 3000)
+        lens[rng.integers(0, 3000, 300)] = 0
+        return 16, lens, (32, 8, 128)
+    if name == "round-edge":   # 1025 requests: one past a round
+        return 7, rng.integers(0, 5000, 1025), (8, 2, 64)
+    if name == "one-empty":
+        return 16, np.array([0]), (8, 1, 128)
+    if name == "exact-chunks":  # lengths that are whole multiples of the split
+        return 16, np.array([256 * 16, 0, 256 * 32, 1, 4096]), (32, 8, 128)
+    raise KeyError(name)
+
+
+@pytest.mark.parametrize("name", ["c3-like", "c4-like", "skew", "many", "round-edge",
+                                  "one-empty", "exact-chunks"])
+def test_schedule_matches_definition(dev, name):
+    page_size, lens, (hq, hkv, d) = _lens_case(name)
+    n_pages, lpl = W.pages_for_lens(lens, page_size)
+    indptr = np.concatenate([[0], np.cumsum(n_pages)]).astype(np.int32)
+    used = int(indptr[-1])
+    chunk, bound, _, _ = fad.fa_debug_plan(fad.FA_DTYPE_BF16, len(lens), hq, hkv, d, page_size,
+                                           used)
+    announce(f"schedule {name}: B={len(lens)} chunk={chunk} bound={bound}")
+    out = torch.full((bound * 8,), 12345, dtype=torch.int32, device=dev)
+    fad.fa_debug_schedule(fad.FA_DTYPE_BF16, len(lens), hq, hkv, d, page_size, used,
+                          torch.from_numpy(indptr).to(dev),
+                          torch.from_numpy(lpl.astype(np.int32)).to(dev), out)
+    got = out.cpu().numpy().reshape(bound, 8)
+    want = expected_schedule(lens, page_size, chunk, bound)
+    bad = np.nonzero(np.any(got != want, axis=1))[0]
+    assert bad.size == 0, (f"{bad.size} work indices differ; first {bad[0]}: "
+                           f"got {got[bad[0]].tolist()} want {want[bad[0]].tolist()}")
+
+
+def test_schedule_rejects_short_output(dev):
+    lens = np.array([100, 200])
+    n_pages, lpl = W.pages_for_lens(lens, 16)
+    indptr = np.concatenate([[0], np.cumsum(n_pages)]).astype(np.int32)
+    _, bound, _, _ = fad.fa_debug_plan(fad.FA_DTYPE_BF16, 2, 8, 2, 128, 16, int(indptr[-1]))
+    out = torch.zeros(bound * 8 - 1, dtype=torch.int32, device=dev)
+    with pytest.raises(fad.FaError) as e:
+        fad.fa_debug_schedule(fad.FA_DTYPE_BF16, 2, 8, 2, 128, 16, int(indptr[-1]),
+                              torch.from_numpy(indptr).to(dev),
+                              torch.from_numpy(lpl.astype(np.int32)).to(dev), out)
+    assert e.value.status == fad.FA_ERR_WORKSPACE_TOO_SMALL
+
+
+# ------------------------------------------------------- merge counters
+
+def _split_problem(dtype="bf16", seed=77):
+    """Requests long enough to split into several units, plus short and empty ones."""
+    lens = np.array([9000, 0, 17, 4096, 25000, 300, 12345, 1])
+    return W.make_paged("split-mix", dtype, len(lens), 16, 4, 128, 16, seed, lens=lens,
+                        pool_slack=0.1)
+
+
+def test_garbage_workspace(dev):
+    """The workspace needs no clearing: random bytes in it change nothing."""
+    p = _split_problem()
+    d = to_dev(p, dev)
+    ref_o, ref_l = run(p, d)
+    ws = fad.workspace_paged(p.batch, p.num_qo_heads, p.num_kv_heads, p.head_dim,
+                             p.page_size, p.total_used_pages, dev)
+    for trial in range(3):
+        g = torch.Generator(device="cpu").manual_seed(trial)
+        ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, generator=g))
+        if trial == 2:
+            ws.fill_(255)
+        o, l = run(p, d, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(l, ref_l), f"trial {trial}"
+    ro, rl = oracle_of(p)
+    compare(p.dtype, ref_o, ref_l, ro, rl, p.name)
+
+
+def test_graph_replay(dev):
+    """A captured call replays correctly again and again (the merge counters
+    return to zero for the same call tag), with eager work in between."""
+    p = _split_problem(seed=78)
+    d = to_dev(p, dev)
+    ws = fad.workspace_paged(p.batch, p.num_qo_heads, p.num_kv_heads, p.head_dim,
+                             p.page_size, p.total_used_pages, dev)
+    o = torch.empty_like(d["q"])
+    lse = torch.empty((p.batch, p.num_qo_heads), dtype=torch.float32, device=dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run(p, d, o=o, lse=lse, workspace=ws)  # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(p, d, o=o, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    q0 = d["q"].clone()
+    for r in range(4):
+        # new query values in the captured buffer; eager reference on its own workspace
+        d["q"].copy_(q0 * (1.0 + 0.25 * r))
+        eo, el = run(p, d)
+        torch.cuda.synchronize()
+        o.zero_()
+        lse.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, eo) and torch.equal(lse, el), f"replay {r}"
+    announce("graph replays match eager")
