@@ -210,7 +210,8 @@ hipError_t launch_decode(const DecodeParams &p, const HostPlan &hp, hipStream_t 
 template <class E, int D>
 hipError_t launch_mfma(const DecodeParams &p, const HostPlan &hp, hipStream_t s) {
   dim3 grid(unsigned(hp.units_bound) * unsigned(hp.planes));
-  hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D>), grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D>), grid, dim3(fa::MfmaGeom<E, D>::NW * 64), 0,
+                     s, p);
   return hipGetLastError();
 }
 

@@ -247,20 +247,20 @@ __device__ inline float coherent_load(const float *ptr) {
 }
 //
 // Combines request b's split partials (o_s normalised over its rows, lse_s in
-// base 2) for query heads h0 .. h0 + gt - 1; every thread of the 256-thread
+// base 2) for query heads h0 .. h0 + gt - 1; every thread of the nw-wave
 // workgroup takes part.  Per head:
 //   M = max_s lse_s,  W = sum_s 2^(lse_s - M),
 //   o = sum_s 2^(lse_s - M) o_s / W,  lse = (M + log2 W) * ln 2,
 // with s running over the request's units in order (one wave per head for M
 // and W, fixed butterfly order), so the result is reproducible bit for bit.
 template <class E>
-__device__ void merge_partials(const DecodeParams &p, int b, int u0, int n, int h0, int gt,
+__device__ void merge_partials(const DecodeParams &p, int b, int u0, int n, int h0, int gt, int nw,
                                float *s_stat /* LDS [32] */) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int hq = p.num_qo_heads;
-  for (int g = wave; g < gt; g += 4) {
+  for (int g = wave; g < gt; g += nw) {
     float mx = -INFINITY;
     for (int s = lane; s < n; s += kWave) mx = fmaxf(mx, coherent_load(p.part_lse + (int64_t)(u0 + s) * hq + h0 + g));
     mx = wave_max(mx);
@@ -276,7 +276,7 @@ __device__ void merge_partials(const DecodeParams &p, int b, int u0, int n, int 
   }
   __syncthreads();
   const int D = p.head_dim;
-  for (int idx = tid; idx < gt * D; idx += 4 * kWave) {
+  for (int idx = tid; idx < gt * D; idx += nw * kWave) {
     const int g = idx / D;
     const int d = idx % D;
     const int h = h0 + g;
@@ -314,7 +314,7 @@ __device__ void merge_partials(const DecodeParams &p, int b, int u0, int n, int 
 // workgroup leaves the counter at (tag, 0), so replaying the same launch (a
 // captured graph) also starts from zero.
 template <class E>
-__device__ void finish_split(const DecodeParams &p, const UnitInfo &u, int plane, int h0, int gt,
+__device__ void finish_split(const DecodeParams &p, const UnitInfo &u, int plane, int h0, int gt, int nw,
                              float *s_stat, int *s_last) {
   if (u.n_units <= 1) return;
   __builtin_amdgcn_s_waitcnt(0);
@@ -339,7 +339,7 @@ __device__ void finish_split(const DecodeParams &p, const UnitInfo &u, int plane
   if (!*s_last) return;
   if (threadIdx.x == 0)
     __hip_atomic_store(counter, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  merge_partials<E>(p, u.b, u.u0, u.n_units, h0, gt, s_stat);
+  merge_partials<E>(p, u.b, u.u0, u.n_units, h0, gt, nw, s_stat);
 }
 
 // ------------------------------------------------------ vector-ALU decode
@@ -515,7 +515,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   }
   __shared__ float s_stat[32];
   __shared__ int s_last;
-  finish_split<E>(p, u, blockIdx.y, h0, GT, s_stat, &s_last);
+  finish_split<E>(p, u, blockIdx.y, h0, GT, NW, s_stat, &s_last);
 }
 
 // ---------------------------------------------------------- schedule hook

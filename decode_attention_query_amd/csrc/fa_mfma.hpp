@@ -2,9 +2,9 @@
 //
 // One workgroup = one split unit of one KV head and a block of up to 16 query
 // heads of its group (the whole group when G <= 16), so K and V are read from
-// HBM once for all those heads.  Four waves; each wave streams its own 32-row
-// tiles of the unit and keeps its own online-softmax state; the waves are
-// merged through LDS at the end.
+// HBM once for all those heads.  Four waves (two at D = 256); each wave
+// streams its own 32-row tiles of the unit and keeps its own online-softmax
+// state; the waves are merged through LDS at the end.
 //
 // Per 32-row tile, with n = lane % 16 and grp = lane / 16:
 //   scores   S^T[t][g] = sum_d K[t][d] Q[g][d]        v_mfma_f32_16x16x32 (bf16|f16)
@@ -86,9 +86,14 @@ __device__ inline void pack_probs(const float *p, typename Mfma<E>::v8 &hi,
 // a unit spans at most 1024 whole pages plus a partial one at each end).
 constexpr int kPageTable = 1040;
 
+// Waves per workgroup: four, but two at D = 256, whose K/V tiles would fill
+// 137 KB of LDS at four waves; at two, two workgroups share a compute unit, so
+// one streams while the other starts or finishes.
+constexpr int mfma_waves(int d) { return d <= 128 ? 4 : 2; }
+
 template <class E, int D>
 struct MfmaGeom {
-  static constexpr int NW = 4;           // waves per workgroup
+  static constexpr int NW = mfma_waves(D);
   static constexpr int TT = 32;          // rows per wave tile
   static constexpr int KK = D / 32;      // score k-steps per 16-row block
   static constexpr int MB = D / 16;      // 16-feature blocks of O^T
@@ -175,7 +180,7 @@ __device__ inline void issue_tile(KVTile<MfmaGeom<E, D>::NI> &T, const DecodePar
 }
 
 template <class E, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1))) void decode_mfma_kernel(
+__global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1))) void decode_mfma_kernel(
     const DecodeParams p) {
   using G = MfmaGeom<E, D>;
   using M = Mfma<E>;
@@ -210,7 +215,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 
   if (p.uniform_blocks && !p.contig && t_begin < t_end) {
     slot0 = (int)fastdiv((uint32_t)t_begin, p.page_div);
     const int count = (int)fastdiv((uint32_t)(t_end - 1), p.page_div) - slot0 + 1;
-    for (int i = threadIdx.x; i < count; i += 256) {
+    for (int i = threadIdx.x; i < count; i += NW * 64) {
       const int32_t id = p.indices[page_base + slot0 + i];
       s_pages[i] = min(max(id, 0), p.num_total_pages - 1);
     }
@@ -386,7 +391,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 
     }
     emit<E>(p, u, h0 + g, d, Mx, lsum, a);
   }
-  finish_split<E>(p, u, plane, h0, gt, s_stat, &s_last);
+  finish_split<E>(p, u, plane, h0, gt, NW, s_stat, &s_last);
 }
 
 }  // namespace fa
