@@ -8,7 +8,9 @@ Prints one JSON line.  value = algorithmic bytes per call / wall time per call
 (GB/s, 1e9 B/s), where the algorithmic bytes are the valid K and V rows, q, o,
 lse and the page table, counted once each.  roofline.achieved divides the same
 bytes by the attention kernel's own average duration, timed with HIP events the
-library records on its stream during the timed steps.  cpu_baseline runs the
+library records on its stream during a second run of the same steps.
+per_call gives p10 / median / p90 of single calls, each in its own event pair
+(--flush: with the caches flushed before each call).  cpu_baseline runs the
 float64 oracle on the host over the same workload.
 """
 import argparse
@@ -85,32 +87,41 @@ def describe(p):
             "sum_kv_len": int(lens.sum()), "max_kv_len": int(lens.max())}
 
 
-def cpu_baseline(p, nbytes):
-    """The float64 oracle over the whole workload on this host's cores."""
+def cpu_baseline(p, nbytes, min_seconds=2.0, max_runs=5):
+    """The float64 oracle over the whole workload on this host's cores: whole
+    calls repeated until min_seconds have passed (at most max_runs), median."""
     import oracle
     threads = len(os.sched_getaffinity(0))
-    t0 = time.perf_counter()
-    if isinstance(p, W.ContigProblem):
-        oracle.decode_contig(p.dtype, W.bits(p.q), W.bits(p.k_cache), W.bits(p.v_cache),
-                             p.valid_kv_len, p.scale, threads=threads)
-    else:
-        oracle.decode_paged(p.dtype, W.bits(p.q), W.bits(p.k_data), W.bits(p.v_data),
-                            p.indices.numpy(), p.indptr.numpy(), p.last_page_len.numpy(),
-                            p.scale, threads=threads)
-    dt = time.perf_counter() - t0
+    times = []
+    while len(times) < max_runs and (len(times) < 1 or sum(times) < min_seconds):
+        t0 = time.perf_counter()
+        if isinstance(p, W.ContigProblem):
+            oracle.decode_contig(p.dtype, W.bits(p.q), W.bits(p.k_cache), W.bits(p.v_cache),
+                                 p.valid_kv_len, p.scale, threads=threads)
+        else:
+            oracle.decode_paged(p.dtype, W.bits(p.q), W.bits(p.k_data), W.bits(p.v_data),
+                                p.indices.numpy(), p.indptr.numpy(), p.last_page_len.numpy(),
+                                p.scale, threads=threads)
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "seconds_per_call": round(dt, 3),
-            "sample": f"the whole {p.name} call (every request and head), one run"}
+            "sample": f"the whole {p.name} call (every request and head), "
+                      f"median of {len(times)} runs"}
 
 
-def hbm_probe(dev, nbytes=2 << 30, reps=10):
-    """Achievable bandwidth on this GPU, for context: torch's copy kernel
-    (reads and writes nbytes each) and a full reduction (reads nbytes)."""
-    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).normal_()
-    dst = torch.empty_like(src)
+def hbm_probe(dev, nbytes=4 << 30, reps=10):
+    """Bandwidth context on this GPU: the library's read probe (the attention
+    kernels' load shape over nbytes) and the runtime's device copy (reads and
+    writes nbytes // 2 each; also the calibration kernel of the HBM counters)."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(3)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    half = buf[: nbytes // 2]
+    dst = torch.empty_like(half)
     out = {}
-    for name, fn, moved in (("copy", lambda: dst.copy_(src), 2 * nbytes),
-                            ("read", lambda: src.sum(dtype=torch.float32), nbytes)):
+    for name, fn, moved in (("read_probe", lambda: fad.fa_debug_read_probe(buf, sink), nbytes),
+                            ("copy", lambda: dst.copy_(half), nbytes)):
         fn()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -120,8 +131,32 @@ def hbm_probe(dev, nbytes=2 << 30, reps=10):
         b.record()
         torch.cuda.synchronize()
         out[name + "_GBps"] = round(moved * reps / (a.elapsed_time(b) * 1e-3) / 1e9, 1)
-    del src, dst
+    del buf, dst
     torch.cuda.empty_cache()
+    return out
+
+
+def per_call_times(step, n, dev, flush):
+    """p10 / median / p90 of single calls, each bracketed by its own event pair
+    on the library's stream; with flush, a 512 MiB buffer is written before
+    every call (outside the bracket) so the 256 MiB last-level cache and the
+    L2s hold none of the call's inputs."""
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if flush else None
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(n)]
+    torch.cuda.synchronize()
+    for a, b in pairs:
+        if flush:
+            scratch.fill_(1)
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) * 1e3 for a, b in pairs])
+    out = {"p10_us": round(float(np.percentile(t, 10)), 2),
+           "median_us": round(float(np.median(t)), 2),
+           "p90_us": round(float(np.percentile(t, 90)), 2)}
+    del scratch
     return out
 
 
@@ -133,7 +168,9 @@ def main():
     ap.add_argument("--workload", default="c3", choices=sorted(W.FULL))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe", action="store_true",
-                    help="also measure torch copy / read bandwidth for context")
+                    help="also measure the read probe and a device copy for context")
+    ap.add_argument("--flush", action="store_true",
+                    help="per-call timings with the caches flushed before each call")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -197,6 +234,8 @@ def main():
     torch.cuda.synchronize()
     main_ms, call_ms, calls = fad.fa_debug_timing_read()
     fad.fa_debug_timing_enable(0)
+    per_call = per_call_times(step, args.steps, dev, flush=False)
+    per_call_cold = per_call_times(step, args.steps, dev, flush=True) if args.flush else None
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     kernel_ms = main_ms / max(calls, 1)
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
@@ -236,6 +275,9 @@ def main():
                      "kernel_us": round(kernel_ms * 1e3, 2),
                      "kernel": "decode attention with fused split merge (fa::decode_*_kernel)"},
     }
+    line["per_call"] = per_call
+    if per_call_cold:
+        line["per_call_flushed"] = per_call_cold
     if args.probe:
         line["hbm_probe"] = hbm_probe(dev)
     if not args.no_cpu_baseline:

@@ -12,7 +12,7 @@ from ._binding import (CODE_TORCH_DTYPES, DTYPE_CODES, EXPORTED, FA_DTYPE_BF16, 
                        FA_DTYPE_F32, FA_ERR_INVALID_PROBLEM, FA_ERR_LAUNCH, FA_ERR_UNSUPPORTED,
                        FA_ERR_WORKSPACE_TOO_SMALL, FA_OK, LIB_PATH, STATUS_NAMES,
                        TORCH_DTYPE_CODES, FaError, fa_debug_gather_paged, fa_debug_plan,
-                       fa_debug_schedule, fa_debug_timing_enable, fa_debug_timing_read, fa_decode_contig,
+                       fa_debug_read_probe, fa_debug_schedule, fa_debug_timing_enable, fa_debug_timing_read, fa_decode_contig,
                        fa_decode_paged, fa_decode_workspace_size, fa_status_string,
                        load_library)
 

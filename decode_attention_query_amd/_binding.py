@@ -29,7 +29,8 @@ STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_INVALID_PROBLEM", 2: "FA_ERR_UNSUPPORTED"
 # every symbol the public headers declare
 EXPORTED = ("fa_decode_workspace_size", "fa_decode_contig", "fa_decode_paged",
             "fa_status_string", "fa_debug_gather_paged", "fa_debug_timing_enable",
-            "fa_debug_timing_read", "fa_debug_plan", "fa_debug_schedule")
+            "fa_debug_timing_read", "fa_debug_plan", "fa_debug_schedule",
+            "fa_debug_read_probe")
 
 
 class FaError(RuntimeError):
@@ -78,6 +79,8 @@ def load_library():
     lib.fa_debug_plan.restype = _I
     lib.fa_debug_schedule.argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I64, _P]
     lib.fa_debug_schedule.restype = _I
+    lib.fa_debug_read_probe.argtypes = [_P, _SZ, _P, _P]
+    lib.fa_debug_read_probe.restype = _I
     _lib = lib
     return lib
 
@@ -235,6 +238,18 @@ def fa_debug_schedule(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_s
         _dev_buf(indptr, "indptr", batch + 1, torch.int32),
         _dev_buf(last_page_len, "last_page_len", batch, torch.int32),
         out.data_ptr(), out.numel(), _stream(stream)))
+
+
+def fa_debug_read_probe(buf, sink, stream=None):
+    """Streams every byte of buf (a contiguous device tensor) once."""
+    lib = load_library()
+    for t, name in ((buf, "buf"), (sink, "sink")):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if sink.dtype != torch.int32 or sink.numel() < 1:
+        raise ValueError("sink must be an int32 device tensor")
+    _check("fa_debug_read_probe", lib.fa_debug_read_probe(
+        buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), _stream(stream)))
 
 
 def fa_status_string(status):

@@ -439,6 +439,16 @@ fa_status_t fa_debug_schedule(fa_dtype_t dtype, int batch, int num_qo_heads, int
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+fa_status_t fa_debug_read_probe(const void *buf, size_t bytes, uint32_t *sink,
+                                hipStream_t stream) {
+  if (!buf || !sink || bytes == 0 || bytes % fa::kProbeBlock != 0)
+    return FA_ERR_INVALID_PROBLEM;
+  const int64_t n_blocks = int64_t(bytes / fa::kProbeBlock);
+  hipLaunchKernelGGL(fa::read_probe_kernel, dim3(8192), dim3(256), 0, stream,
+                     static_cast<const char *>(buf), n_blocks, sink);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 fa_status_t fa_debug_timing_enable(int enable) {
   Timing &t = timing();
   std::lock_guard<std::mutex> lk(t.mu);

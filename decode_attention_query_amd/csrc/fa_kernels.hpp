@@ -542,6 +542,32 @@ __global__ __launch_bounds__(256) void schedule_kernel(const DecodeParams p, int
   o[7] = 0;
 }
 
+// ------------------------------------------------------------- read probe
+//
+// Measurement only: streams a buffer of whole 8 KiB blocks with the decode
+// kernels' load shape (each wave instruction reads 1 KiB contiguous, 16 bytes
+// per lane, non-temporal), eight instructions in flight per wave, so a
+// benchmark can state the read bandwidth this shape reaches on the device.
+// The loaded words are folded into one value that is stored only if it equals
+// a fixed constant, which keeps the loads without writing anything.
+constexpr int kProbeBlock = 8192;
+__global__ __launch_bounds__(256) void read_probe_kernel(const char *buf, int64_t n_blocks,
+                                                         uint32_t *sink) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x / kWave);
+  const int64_t n_waves = (int64_t)gridDim.x * 4;
+  uint32_t acc = 0;
+  for (int64_t bi = wave; bi < n_blocks; bi += n_waves) {
+    const char *blk = buf + bi * kProbeBlock + lane * 16;
+    uint4 r[kProbeBlock / 1024];
+#pragma unroll
+    for (int i = 0; i < kProbeBlock / 1024; ++i) r[i] = load16_stream(blk + i * 1024);
+#pragma unroll
+    for (int i = 0; i < kProbeBlock / 1024; ++i) acc ^= r[i].x ^ r[i].y ^ r[i].z ^ r[i].w;
+  }
+  if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+
 // ------------------------------------------------------------ gather hook
 //
 // Test-only: copies every valid row t of one KV head of one split unit of

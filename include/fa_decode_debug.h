@@ -55,6 +55,16 @@ fa_status_t fa_debug_schedule(fa_dtype_t dtype, int batch, int num_qo_heads, int
                               const int32_t *indptr, const int32_t *last_page_len,
                               int32_t *out, int64_t out_entries, hipStream_t stream);
 
+/* Read-bandwidth probe: reads every byte of buf (device memory, bytes > 0 and a
+ * multiple of 8192) once with the load shape of the attention kernels (1 KiB
+ * contiguous per wave instruction, non-temporal), so a benchmark can compare
+ * the attention kernel with what that shape reaches on the device.  sink is a
+ * device uint32 that is left unchanged unless the folded data happen to equal
+ * one fixed 32-bit constant.  NULL pointers or a bad size ->
+ * FA_ERR_INVALID_PROBLEM; a failed launch -> FA_ERR_LAUNCH.  Asynchronous. */
+fa_status_t fa_debug_read_probe(const void *buf, size_t bytes, uint32_t *sink,
+                                hipStream_t stream);
+
 /* Kernel timing.  While enabled, every decode call records a HIP event pair on
  * its stream around its main attention kernel (the one that streams K and V),
  * and another around the whole call.  fa_debug_timing_read waits for the

@@ -169,6 +169,19 @@ def test_gather_rejects():
     assert lib.fa_debug_gather_paged(*bad, 10, FAKE, 1 << 30, None) == UNS
 
 
+def test_schedule_and_probe_reject():
+    lib = fad.load_library()
+    base = [2, 2, 8, 2, 128, 16, 4]
+    assert lib.fa_debug_schedule(7, *base[1:], FAKE, FAKE, FAKE, 1 << 20, None) == UNS
+    assert lib.fa_debug_schedule(*base, None, FAKE, FAKE, 1 << 20, None) == INV
+    assert lib.fa_debug_schedule(*base, FAKE, FAKE, None, 1 << 20, None) == INV
+    assert lib.fa_debug_schedule(*base, FAKE, FAKE, FAKE, 7, None) == WS
+    assert lib.fa_debug_read_probe(None, 8192, FAKE, None) == INV
+    assert lib.fa_debug_read_probe(FAKE, 8192, None, None) == INV
+    assert lib.fa_debug_read_probe(FAKE, 0, FAKE, None) == INV
+    assert lib.fa_debug_read_probe(FAKE, 8192 + 16, FAKE, None) == INV
+
+
 def test_binding_rejects_host_tensors():
     """The binding refuses buffers that are not device memory before calling in."""
     import torch

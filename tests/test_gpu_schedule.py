@@ -169,3 +169,14 @@ def test_graph_replay(dev):
         torch.cuda.synchronize()
         assert torch.equal(o, eo) and torch.equal(lse, el), f"replay {r}"
     announce("graph replays match eager")
+
+
+def test_read_probe_runs(dev):
+    """The bandwidth probe reads the whole buffer and leaves the sink alone."""
+    buf = torch.full((1 << 20,), 3, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    fad.fa_debug_read_probe(buf, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
+    with pytest.raises(fad.FaError):
+        fad.fa_debug_read_probe(buf[:100], sink)
