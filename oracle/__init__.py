@@ -12,10 +12,13 @@ int16 / float16 numpy arrays; numpy has no bf16, so bf16 is always bits).
 Functions and what they follow:
   decode_contig  -- contiguous [Hkv, max_kv_len, D] cache masked to valid_kv_len
                     (ferrum-kernels 0.7.7 src/backend/cuda/decode_attention.rs,
-                    decode_attention argument list and module doc)
+                    decode_attention argument list and module doc); layout="nhd":
+                    token-major [max_kv_len, Hkv, D] (ferrox-cuda 0.15.2
+                    src/attn.rs, gqa_decode kernel source)
   decode_paged   -- paged [pages, Hkv, P, D] store via indptr/indices/last_page_len
                     (baracuda-kernels 0.0.1-alpha.68 src/attention/batch_paged_decode.rs,
-                    module doc "Layout" and "Query / output")
+                    module doc "Layout" and "Query / output"); layout="nhd":
+                    [pages, P, Hkv, D] (reading: the page-level token-major form)
   gather_paged   -- the page-table-resolved rows, raw bits (same page, "Layout")
   seq_lens       -- L_b from the page table (reading: all pages but the last are full)
   validate_table -- the device-side page-table contract (same page, "Layout")
@@ -32,6 +35,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
+LAYOUTS = {"hnd": 0, "nhd": 1}
 
 STATUS = {0: "OK", 1: "BAD_ARG", 2: "BAD_INDPTR", 3: "BAD_INDEX",
           4: "BAD_LAST_PAGE_LEN", 5: "NO_MEMORY"}
@@ -55,13 +59,13 @@ class _Lib:
         lib.oracle_validate_table.restype = _I
         lib.oracle_seq_lens.argtypes = [_I, _I, _P, _P, _P]
         lib.oracle_seq_lens.restype = None
-        lib.oracle_gather_paged.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P]
+        lib.oracle_gather_paged.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I]
         lib.oracle_gather_paged.restype = _I
         lib.oracle_decode_paged.argtypes = [_I, _I, _I, _I, _I, _I, _D, _P, _P, _P, _P, _P,
-                                            _P, _I, _P, _P, _P, _P, _I]
+                                            _P, _I, _P, _P, _P, _P, _I, _I]
         lib.oracle_decode_paged.restype = _I
         lib.oracle_decode_contig.argtypes = [_I, _I, _I, _I, _I, _I, _D, _P, _P, _P, _P, _P,
-                                             _I]
+                                             _I, _I]
         lib.oracle_decode_contig.restype = _I
         lib.oracle_attend_f64.argtypes = [_I, _I64, _D, _P, _P, _P, _P, _P]
         lib.oracle_attend_f64.restype = None
@@ -140,29 +144,41 @@ def seq_lens(page_size, indptr, last_page_len):
     return out
 
 
-def gather_paged(dtype, data, indices, indptr, last_page_len):
-    """Resolved rows of a paged store `data` [pages, Hkv, P, D], raw bits,
-    as [sum L_b, Hkv, D]."""
+def _paged_dims(shape, layout):
+    """(Hkv, P, D) of a paged store's shape in the given layout."""
+    if layout == "nhd":
+        _, page_size, hkv, head_dim = shape
+    elif layout == "hnd":
+        _, hkv, page_size, head_dim = shape
+    else:
+        raise ValueError(f"unknown layout {layout!r}")
+    return hkv, page_size, head_dim
+
+
+def gather_paged(dtype, data, indices, indptr, last_page_len, layout="hnd"):
+    """Resolved rows of a paged store `data` ([pages, Hkv, P, D], or
+    [pages, P, Hkv, D] for layout="nhd"), raw bits, as [sum L_b, Hkv, D]."""
     data = _bits(data, dtype)
-    _, hkv, page_size, head_dim = data.shape
+    hkv, page_size, head_dim = _paged_dims(data.shape, layout)
     indices, indptr, lpl = _i32(indices), _i32(indptr), _i32(last_page_len)
     total = int(seq_lens(page_size, indptr, lpl).sum())
     out = np.empty((total, hkv, head_dim), dtype=data.dtype)
     r = _load().oracle_gather_paged(DTYPES[dtype], int(lpl.size), hkv, head_dim, page_size,
                                     _ptr(data), _ptr(indices), _ptr(indptr), _ptr(lpl),
-                                    _ptr(out))
+                                    _ptr(out), LAYOUTS[layout])
     if r != 0:
         raise RuntimeError(f"oracle_gather_paged: {STATUS[r]}")
     return out
 
 
 def decode_paged(dtype, q, k_data, v_data, indices, indptr, last_page_len, scale,
-                 samples=None, threads=0):
-    """q [B, Hq, D]; k_data/v_data [pages, Hkv, P, D].  Returns (o, lse) in f64:
-    o [B, Hq, D], lse [B, Hq]; with samples=[(b, h), ...] returns o [n, D], lse [n]."""
+                 samples=None, threads=0, layout="hnd"):
+    """q [B, Hq, D]; k_data/v_data [pages, Hkv, P, D] (layout="nhd":
+    [pages, P, Hkv, D]).  Returns (o, lse) in f64: o [B, Hq, D], lse [B, Hq];
+    with samples=[(b, h), ...] returns o [n, D], lse [n]."""
     q, k_data, v_data = _bits(q, dtype), _bits(k_data, dtype), _bits(v_data, dtype)
     batch, hq, head_dim = q.shape
-    _, hkv, page_size, d2 = k_data.shape
+    hkv, page_size, d2 = _paged_dims(k_data.shape, layout)
     assert d2 == head_dim and v_data.shape == k_data.shape
     indices, indptr, lpl = _i32(indices), _i32(indptr), _i32(last_page_len)
     if samples is None:
@@ -180,23 +196,31 @@ def decode_paged(dtype, q, k_data, v_data, indices, indptr, last_page_len, scale
     r = _load().oracle_decode_paged(DTYPES[dtype], batch, hq, hkv, head_dim, page_size,
                                     float(scale), _ptr(q), _ptr(k_data), _ptr(v_data),
                                     _ptr(indices), _ptr(indptr), _ptr(lpl), n_sample,
-                                    _ptr(sb), _ptr(sh), _ptr(o), _ptr(lse), int(threads))
+                                    _ptr(sb), _ptr(sh), _ptr(o), _ptr(lse), int(threads),
+                                    LAYOUTS[layout])
     if r != 0:
         raise RuntimeError(f"oracle_decode_paged: {STATUS[r]}")
     return o, lse
 
 
-def decode_contig(dtype, q, k_cache, v_cache, valid_kv_len, scale, threads=0):
-    """q [Hq, D]; k_cache/v_cache [Hkv, max_kv_len, D].  Returns (o [Hq, D], lse [Hq]) f64."""
+def decode_contig(dtype, q, k_cache, v_cache, valid_kv_len, scale, threads=0, layout="hnd"):
+    """q [Hq, D]; k_cache/v_cache [Hkv, max_kv_len, D] (layout="nhd":
+    [max_kv_len, Hkv, D]).  Returns (o [Hq, D], lse [Hq]) f64."""
     q, k_cache, v_cache = _bits(q, dtype), _bits(k_cache, dtype), _bits(v_cache, dtype)
     hq, head_dim = q.shape
-    hkv, max_kv_len, d2 = k_cache.shape
+    if layout == "nhd":
+        max_kv_len, hkv, d2 = k_cache.shape
+    elif layout == "hnd":
+        hkv, max_kv_len, d2 = k_cache.shape
+    else:
+        raise ValueError(f"unknown layout {layout!r}")
     assert d2 == head_dim and v_cache.shape == k_cache.shape
     o = np.empty((hq, head_dim), dtype=np.float64)
     lse = np.empty((hq,), dtype=np.float64)
     r = _load().oracle_decode_contig(DTYPES[dtype], hq, hkv, head_dim, max_kv_len,
                                      int(valid_kv_len), float(scale), _ptr(q), _ptr(k_cache),
-                                     _ptr(v_cache), _ptr(o), _ptr(lse), int(threads))
+                                     _ptr(v_cache), _ptr(o), _ptr(lse), int(threads),
+                                     LAYOUTS[layout])
     if r != 0:
         raise RuntimeError(f"oracle_decode_contig: {STATUS[r]}")
     return o, lse

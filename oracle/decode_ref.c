@@ -35,6 +35,15 @@
  *
  * Element decoding is exact: f32 is widened, bf16 is the high half of an f32,
  * f16 is decoded from its sign / exponent / mantissa fields by hand.
+ *
+ * Two K/V layouts (argument `layout`):
+ *   OR_HND (0), heads-major: contiguous [Hkv, max_kv_len, D] (ferrum-kernels
+ *     page, decode_attention argument list), paged [pages, Hkv, P, D]
+ *     (baracuda-kernels page, module doc "Layout");
+ *   OR_NHD (1), token-major: contiguous [max_kv_len, Hkv, D], row t of KV head g
+ *     at (t * Hkv + g) * D (ferrox-cuda page, gqa_decode kernel source and the
+ *     k_cache / v_cache shape in its doc comment); paged [pages, P, Hkv, D], the
+ *     same order inside each page (reading: the page-level form of that layout).
  */
 #include <math.h>
 #include <stdint.h>
@@ -45,6 +54,8 @@
 #endif
 
 enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2 };
+
+enum { OR_HND = 0, OR_NHD = 1 };
 
 enum {
   OR_OK = 0,
@@ -117,13 +128,24 @@ void oracle_seq_lens(int batch, int page_size, const int32_t *indptr,
 }
 
 /* Element offset of row j of request b, kv head g, in a paged store laid out
- * [num_pages, num_kv_heads, page_size, head_dim] (heads-major inside a page). */
-static int64_t paged_row_offset(int num_kv_heads, int page_size, int head_dim,
+ * [num_pages, num_kv_heads, page_size, head_dim] (OR_HND, heads-major inside a
+ * page) or [num_pages, page_size, num_kv_heads, head_dim] (OR_NHD). */
+static int64_t paged_row_offset(int layout, int num_kv_heads, int page_size, int head_dim,
                                 const int32_t *indices, const int32_t *indptr, int b,
                                 int g, int64_t j) {
   int64_t page = indices[indptr[b] + j / page_size];
   int64_t r = j % page_size;
+  if (layout == OR_NHD) return ((page * page_size + r) * num_kv_heads + g) * head_dim;
   return ((page * num_kv_heads + g) * page_size + r) * head_dim;
+}
+
+/* Element offset of row j of kv head g in a contiguous cache of max_kv_len rows:
+ * [num_kv_heads, max_kv_len, head_dim] (OR_HND) or [max_kv_len, num_kv_heads,
+ * head_dim] (OR_NHD). */
+static int64_t contig_row_offset(int layout, int num_kv_heads, int max_kv_len, int head_dim,
+                                 int g, int64_t j) {
+  if (layout == OR_NHD) return (j * num_kv_heads + g) * head_dim;
+  return ((int64_t)g * max_kv_len + j) * head_dim;
 }
 
 /* Copies the page-table-resolved rows of K (or V), as raw element bits, into
@@ -131,7 +153,9 @@ static int64_t paged_row_offset(int num_kv_heads, int page_size, int head_dim,
  * order).  out must hold sum_b L_b * num_kv_heads * head_dim elements. */
 int oracle_gather_paged(int dtype, int batch, int num_kv_heads, int head_dim,
                         int page_size, const void *data, const int32_t *indices,
-                        const int32_t *indptr, const int32_t *last_page_len, void *out) {
+                        const int32_t *indptr, const int32_t *last_page_len, void *out,
+                        int layout) {
+  if (layout != OR_HND && layout != OR_NHD) return OR_BAD_ARG;
   size_t es = elem_size(dtype);
   int64_t row_out = 0;
   for (int b = 0; b < batch; ++b) {
@@ -139,8 +163,8 @@ int oracle_gather_paged(int dtype, int batch, int num_kv_heads, int head_dim,
     int64_t L = n == 0 ? 0 : (n - 1) * page_size + last_page_len[b];
     for (int64_t j = 0; j < L; ++j, ++row_out) {
       for (int g = 0; g < num_kv_heads; ++g) {
-        int64_t src = paged_row_offset(num_kv_heads, page_size, head_dim, indices, indptr,
-                                       b, g, j);
+        int64_t src = paged_row_offset(layout, num_kv_heads, page_size, head_dim, indices,
+                                       indptr, b, g, j);
         int64_t dst = (row_out * num_kv_heads + g) * head_dim;
         memcpy((char *)out + dst * es, (const char *)data + src * es, head_dim * es);
       }
@@ -184,7 +208,8 @@ static void attend_rows(int dtype, int head_dim, double scale, const void *q, in
   *lse = M + log(l);
 }
 
-/* Paged decode.  q [batch, Hq, D], k/v [num_pages, Hkv, P, D] in dtype; outputs
+/* Paged decode.  q [batch, Hq, D], k/v [num_pages, Hkv, P, D] (OR_HND) or
+ * [num_pages, P, Hkv, D] (OR_NHD) in dtype; outputs
  * o [batch, Hq, D] and lse [batch, Hq] in f64.  If n_sample > 0 only the listed
  * (sample_b[i], sample_h[i]) pairs are computed, into o[i*D ..] and lse[i].
  * threads <= 0 uses the OpenMP default. */
@@ -193,9 +218,10 @@ int oracle_decode_paged(int dtype, int batch, int num_qo_heads, int num_kv_heads
                         const void *k, const void *v, const int32_t *indices,
                         const int32_t *indptr, const int32_t *last_page_len, int n_sample,
                         const int32_t *sample_b, const int32_t *sample_h, double *o,
-                        double *lse, int threads) {
+                        double *lse, int threads, int layout) {
   if (batch <= 0 || num_qo_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-      page_size <= 0 || num_qo_heads % num_kv_heads != 0)
+      page_size <= 0 || num_qo_heads % num_kv_heads != 0 ||
+      (layout != OR_HND && layout != OR_NHD))
     return OR_BAD_ARG;
   int group = num_qo_heads / num_kv_heads;
   int64_t n_items = n_sample > 0 ? n_sample : (int64_t)batch * num_qo_heads;
@@ -216,8 +242,8 @@ int oracle_decode_paged(int dtype, int batch, int num_qo_heads, int num_kv_heads
       status = OR_NO_MEMORY;
     } else {
       for (int64_t j = 0; j < L; ++j)
-        row_off[j] = paged_row_offset(num_kv_heads, page_size, head_dim, indices, indptr,
-                                      b, g, j);
+        row_off[j] = paged_row_offset(layout, num_kv_heads, page_size, head_dim, indices,
+                                      indptr, b, g, j);
       int64_t q_off = ((int64_t)b * num_qo_heads + h) * head_dim;
       attend_rows(dtype, head_dim, scale, q, q_off, k, v, row_off, L, x,
                   o + it * head_dim, lse + it);
@@ -228,15 +254,17 @@ int oracle_decode_paged(int dtype, int batch, int num_qo_heads, int num_kv_heads
   return status;
 }
 
-/* Contiguous decode.  q [Hq, D], k/v [Hkv, max_kv_len, D]; only rows
+/* Contiguous decode.  q [Hq, D], k/v [Hkv, max_kv_len, D] (OR_HND) or
+ * [max_kv_len, Hkv, D] (OR_NHD); only rows
  * [0, valid_kv_len) take part (ferrum-kernels page, decode_attention argument
  * list).  o [Hq, D] and lse [Hq] in f64. */
 int oracle_decode_contig(int dtype, int num_qo_heads, int num_kv_heads, int head_dim,
                          int max_kv_len, int valid_kv_len, double scale, const void *q,
                          const void *k, const void *v, double *o, double *lse,
-                         int threads) {
+                         int threads, int layout) {
   if (num_qo_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_kv_len < 0 ||
-      valid_kv_len < 0 || valid_kv_len > max_kv_len || num_qo_heads % num_kv_heads != 0)
+      valid_kv_len < 0 || valid_kv_len > max_kv_len || num_qo_heads % num_kv_heads != 0 ||
+      (layout != OR_HND && layout != OR_NHD))
     return OR_BAD_ARG;
   int group = num_qo_heads / num_kv_heads;
   int status = OR_OK;
@@ -253,7 +281,7 @@ int oracle_decode_contig(int dtype, int num_qo_heads, int num_kv_heads, int head
       status = OR_NO_MEMORY;
     } else {
       for (int64_t j = 0; j < L; ++j)
-        row_off[j] = ((int64_t)g * max_kv_len + j) * head_dim;
+        row_off[j] = contig_row_offset(layout, num_kv_heads, max_kv_len, head_dim, g, j);
       attend_rows(dtype, head_dim, scale, q, (int64_t)h * head_dim, k, v, row_off, L, x,
                   o + (int64_t)h * head_dim, lse + h);
     }

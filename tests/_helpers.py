@@ -25,14 +25,15 @@ def f64(t):
 
 
 def scatter_paged(rows, page_size, rng, pool_extra=0, empty_last_page=(), fill=None,
-                  permute=True):
+                  permute=True, layout="hnd"):
     """Lays logical rows out in a paged store.
 
     rows: list over requests of tensors [L_b, Hkv, D] (one dtype).
     empty_last_page: requests that get one more, empty page (last_page_len 0);
       their L_b must be a multiple of page_size.
-    Returns (data [pool, Hkv, P, D], indices, indptr, last_page_len) where
-    unused memory holds `fill` (default NaN)."""
+    Returns (data [pool, Hkv, P, D] -- [pool, P, Hkv, D] for layout "nhd" --,
+    indices, indptr, last_page_len) where unused memory holds `fill` (default
+    NaN)."""
     batch = len(rows)
     hkv, d = rows[0].shape[1], rows[0].shape[2]
     dtype = rows[0].dtype
@@ -50,8 +51,8 @@ def scatter_paged(rows, page_size, rng, pool_extra=0, empty_last_page=(), fill=N
     used = sum(n_pages)
     pool = max(1, used + pool_extra)
     perm = rng.permutation(pool) if permute else np.arange(pool)
-    data = torch.full((pool, hkv, page_size, d), float("nan") if fill is None else fill,
-                      dtype=dtype)
+    shape = (pool, page_size, hkv, d) if layout == "nhd" else (pool, hkv, page_size, d)
+    data = torch.full(shape, float("nan") if fill is None else fill, dtype=dtype)
     indices = np.zeros(used, dtype=np.int32)
     indptr = np.zeros(batch + 1, dtype=np.int32)
     k = 0
@@ -62,7 +63,10 @@ def scatter_paged(rows, page_size, rng, pool_extra=0, empty_last_page=(), fill=N
             indices[k] = page
             lo = p * page_size
             hi = min(r.shape[0], lo + page_size)
-            if hi > lo:
+            if hi > lo and layout == "nhd":
+                # a page is [P, Hkv, D], like the logical rows [L, Hkv, D]
+                data[page, : hi - lo] = r[lo:hi]
+            elif hi > lo:
                 # a page is [Hkv, P, D]; logical rows are [L, Hkv, D]
                 data[page, :, : hi - lo, :] = r[lo:hi].permute(1, 0, 2)
             k += 1
@@ -70,9 +74,14 @@ def scatter_paged(rows, page_size, rng, pool_extra=0, empty_last_page=(), fill=N
     return data, indices, indptr, np.asarray(lpl, dtype=np.int32)
 
 
-def contig_from_rows(rows, max_kv_len, fill=1.0e4):
-    """[L, Hkv, D] logical rows -> [Hkv, max_kv_len, D] cache; slack holds fill."""
+def contig_from_rows(rows, max_kv_len, fill=1.0e4, layout="hnd"):
+    """[L, Hkv, D] logical rows -> [Hkv, max_kv_len, D] cache ([max_kv_len, Hkv, D]
+    for layout "nhd"); slack holds fill."""
     L, hkv, d = rows.shape
+    if layout == "nhd":
+        cache = torch.full((max_kv_len, hkv, d), fill, dtype=rows.dtype)
+        cache[:L] = rows
+        return cache
     cache = torch.full((hkv, max_kv_len, d), fill, dtype=rows.dtype)
     cache[:, :L, :] = rows.permute(1, 0, 2)
     return cache

@@ -32,7 +32,7 @@ DTYPES = ("f32", "f16", "bf16")
 
 
 def _paged_problem(rng, dtype, lens, hkv, group, d, page_size, pool_extra=3,
-                   empty_last_page=(), k_rows=None, v_rows=None, q=None):
+                   empty_last_page=(), k_rows=None, v_rows=None, q=None, layout="hnd"):
     """Random logical rows -> paged layout.  Returns a dict with both views."""
     hq = hkv * group
     batch = len(lens)
@@ -44,18 +44,20 @@ def _paged_problem(rng, dtype, lens, hkv, group, d, page_size, pool_extra=3,
         q = rand_t(rng, (batch, hq, d), dtype)
     seed = int(rng.integers(1 << 30))
     kd, ind, ptr, lpl = scatter_paged(k_rows, page_size, np.random.default_rng(seed),
-                                      pool_extra, empty_last_page, fill=1.0e4)
+                                      pool_extra, empty_last_page, fill=1.0e4, layout=layout)
     vd, ind2, ptr2, lpl2 = scatter_paged(v_rows, page_size, np.random.default_rng(seed),
-                                         pool_extra, empty_last_page, fill=1.0e4)
+                                         pool_extra, empty_last_page, fill=1.0e4,
+                                         layout=layout)
     assert np.array_equal(ind, ind2) and np.array_equal(lpl, lpl2)
     return dict(dtype=dtype, q=q, k_rows=k_rows, v_rows=v_rows, k_data=kd, v_data=vd,
                 indices=ind, indptr=ptr, last_page_len=lpl, hq=hq, hkv=hkv, group=group,
-                d=d, page_size=page_size)
+                d=d, page_size=page_size, layout=layout)
 
 
 def _oracle_paged(p, scale):
     return O.decode_paged(p["dtype"], W.bits(p["q"]), W.bits(p["k_data"]), W.bits(p["v_data"]),
-                          p["indices"], p["indptr"], p["last_page_len"], scale)
+                          p["indices"], p["indptr"], p["last_page_len"], scale,
+                          layout=p["layout"])
 
 
 # ------------------------------------------------------------------ decoders
@@ -240,9 +242,17 @@ def _mp_attend(qrow, krows, vrows, scale):
 
 
 def pin_bruteforce_mpmath():
-    rng = np.random.default_rng(18)
-    for d in (1, 2, 4):
-        for page_size in (1, 2, 3, 4):
+    _bruteforce(np.random.default_rng(18), "hnd", (1, 2, 4), (1, 2, 3, 4))
+
+
+def pin_bruteforce_mpmath_token_major():
+    """The same brute force over token-major pages [pages, P, Hkv, D]."""
+    _bruteforce(np.random.default_rng(28), "nhd", (1, 3), (1, 2, 4))
+
+
+def _bruteforce(rng, layout, dims, page_sizes):
+    for d in dims:
+        for page_size in page_sizes:
             for group in (1, 2, 3):
                 hkv = 1 + int(rng.integers(2))
                 dtype = DTYPES[int(rng.integers(3))]
@@ -250,7 +260,8 @@ def pin_bruteforce_mpmath():
                 empty = tuple(b for b in range(3) if lens[b] % page_size == 0
                               and rng.random() < 0.5)
                 p = _paged_problem(rng, dtype, lens, hkv, group, d, page_size,
-                                   pool_extra=int(rng.integers(4)), empty_last_page=empty)
+                                   pool_extra=int(rng.integers(4)), empty_last_page=empty,
+                                   layout=layout)
                 scale = float(rng.uniform(0.1, 2.0))
                 o, lse = _oracle_paged(p, scale)
                 qf = f64(p["q"])
@@ -385,6 +396,41 @@ def pin_paged_equals_contig():
                                v_rows=[rows_v], q=q[None].contiguous())
             op, lp = _oracle_paged(p, 0.0884)
             assert np.array_equal(op[0], oc) and np.array_equal(lp[0], lc), (dtype, page_size)
+
+
+def pin_token_major_equals_heads_major():
+    """The same logical rows laid out token-major (contiguous [L, Hkv, D] as on
+    the ferrox-cuda page, paged [pages, P, Hkv, D]) give bit-identical results
+    to the heads-major layouts, and gather back to the same rows."""
+    rng = np.random.default_rng(27)
+    for dtype in DTYPES:
+        L, hkv, group, d = 53, 3, 2, 64
+        q = rand_t(rng, (hkv * group, d), dtype)
+        rows_k, rows_v = rand_t(rng, (L, hkv, d), dtype), rand_t(rng, (L, hkv, d), dtype)
+        ref = O.decode_contig(dtype, W.bits(q), W.bits(contig_from_rows(rows_k, 60)),
+                              W.bits(contig_from_rows(rows_v, 60)), L, 0.125)
+        got = O.decode_contig(dtype, W.bits(q),
+                              W.bits(contig_from_rows(rows_k, 60, layout="nhd")),
+                              W.bits(contig_from_rows(rows_v, 60, layout="nhd")), L, 0.125,
+                              layout="nhd")
+        assert np.array_equal(ref[0], got[0]) and np.array_equal(ref[1], got[1]), dtype
+        lens = [L, 0, 16, 7]
+        k_rows = [rows_k] + [rand_t(rng, (n, hkv, d), dtype) for n in lens[1:]]
+        v_rows = [rows_v] + [rand_t(rng, (n, hkv, d), dtype) for n in lens[1:]]
+        qb = rand_t(rng, (len(lens), hkv * group, d), dtype)
+        seed = int(rng.integers(1 << 30))
+        out = {}
+        for layout in ("hnd", "nhd"):
+            p = _paged_problem(np.random.default_rng(seed), dtype, lens, hkv, group, d, 8,
+                               empty_last_page=(2,), k_rows=k_rows, v_rows=v_rows, q=qb,
+                               layout=layout)
+            out[layout] = _oracle_paged(p, 0.125)
+            got = O.gather_paged(dtype, W.bits(p["k_data"]), p["indices"], p["indptr"],
+                                 p["last_page_len"], layout=layout)
+            want = np.concatenate([W.bits(r) for r in k_rows if r.shape[0]])
+            assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), (dtype, layout)
+        assert np.array_equal(out["hnd"][0], out["nhd"][0]), dtype
+        assert np.array_equal(out["hnd"][1], out["nhd"][1]), dtype
 
 
 def pin_gather_inverse():

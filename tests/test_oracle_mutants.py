@@ -38,8 +38,17 @@ MUTANTS = [
     ("merge_lse_no_log", "double out_lse = M + log(sum);", "double out_lse = M + sum - 1.0;"),
     ("empty_seq_lse_zero", "*lse = -INFINITY;\n    return;\n  }\n  /* scores */",
      "*lse = 0.0;\n    return;\n  }\n  /* scores */"),
-    ("contig_row_stride", "((int64_t)g * max_kv_len + j) * head_dim",
-     "((int64_t)g * valid_kv_len + j) * head_dim"),
+    ("contig_row_stride", "contig_row_offset(layout, num_kv_heads, max_kv_len, head_dim, g, j)",
+     "contig_row_offset(layout, num_kv_heads, valid_kv_len, head_dim, g, j)"),
+    ("nhd_paged_as_heads_major",
+     "if (layout == OR_NHD) return ((page * page_size + r) * num_kv_heads + g) * head_dim;",
+     "if (layout == OR_NHD) return ((page * num_kv_heads + g) * page_size + r) * head_dim;"),
+    ("nhd_paged_drops_head",
+     "if (layout == OR_NHD) return ((page * page_size + r) * num_kv_heads + g) * head_dim;",
+     "if (layout == OR_NHD) return ((page * page_size + r) * num_kv_heads) * head_dim;"),
+    ("nhd_contig_as_heads_major",
+     "if (layout == OR_NHD) return (j * num_kv_heads + g) * head_dim;",
+     "if (layout == OR_NHD) return ((int64_t)g * max_kv_len + j) * head_dim;"),
     ("validate_skips_upper_bound", "indices[i] >= num_total_pages", "indices[i] > num_total_pages"),
 ]
 
