@@ -76,11 +76,12 @@ def committed_traffic(workload_name):
 
 def describe(p):
     if isinstance(p, W.ContigProblem):
-        return {"workload": p.name, "layout": "contiguous", "num_qo_heads": p.num_qo_heads,
+        return {"workload": p.name, "layout": "contiguous", "kv_order": p.layout,
+                "num_qo_heads": p.num_qo_heads,
                 "num_kv_heads": p.num_kv_heads, "head_dim": p.head_dim,
                 "max_kv_len": p.max_kv_len, "valid_kv_len": p.valid_kv_len}
     lens = np.asarray(p.kv_lens)
-    return {"workload": p.name, "layout": "paged", "batch": p.batch,
+    return {"workload": p.name, "layout": "paged", "kv_order": p.layout, "batch": p.batch,
             "num_qo_heads": p.num_qo_heads, "num_kv_heads": p.num_kv_heads,
             "head_dim": p.head_dim, "page_size": p.page_size,
             "num_total_pages": p.num_total_pages, "total_used_pages": p.total_used_pages,
@@ -97,11 +98,11 @@ def cpu_baseline(p, nbytes, min_seconds=2.0, max_runs=5):
         t0 = time.perf_counter()
         if isinstance(p, W.ContigProblem):
             oracle.decode_contig(p.dtype, W.bits(p.q), W.bits(p.k_cache), W.bits(p.v_cache),
-                                 p.valid_kv_len, p.scale, threads=threads)
+                                 p.valid_kv_len, p.scale, threads=threads, layout=p.layout)
         else:
             oracle.decode_paged(p.dtype, W.bits(p.q), W.bits(p.k_data), W.bits(p.v_data),
                                 p.indices.numpy(), p.indptr.numpy(), p.last_page_len.numpy(),
-                                p.scale, threads=threads)
+                                p.scale, threads=threads, layout=p.layout)
         times.append(time.perf_counter() - t0)
     dt = float(np.median(times))
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
@@ -166,6 +167,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c3", choices=sorted(W.FULL))
+    ap.add_argument("--layout", default="hnd", choices=["hnd", "nhd"],
+                    help="K/V storage: heads-major (default) or token-major")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe", action="store_true",
                     help="also measure the read probe and a device copy for context")
@@ -185,6 +188,8 @@ def main():
 
     t0 = time.perf_counter()
     p = W.FULL[args.workload]()
+    if args.layout == "nhd":
+        p = W.token_major(p)
     print(f"[bench] generated {p.name} in {time.perf_counter() - t0:.1f}s", file=sys.stderr,
           flush=True)
     nbytes = algorithmic_bytes(p)
@@ -197,7 +202,8 @@ def main():
                                  dev)
 
         def step():
-            fad.decode_contig(q, k, v, p.valid_kv_len, p.scale, o=o, lse=lse, workspace=ws)
+            fad.decode_contig(q, k, v, p.valid_kv_len, p.scale, o=o, lse=lse, workspace=ws,
+                              layout=p.layout)
     else:
         q, k, v = p.q.to(dev), p.k_data.to(dev), p.v_data.to(dev)
         ind, ptr, lpl = p.indices.to(dev), p.indptr.to(dev), p.last_page_len.to(dev)
@@ -207,7 +213,8 @@ def main():
                                  p.page_size, p.total_used_pages, dev)
 
         def step():
-            fad.decode_paged(q, k, v, ind, ptr, lpl, p.scale, o=o, lse=lse, workspace=ws)
+            fad.decode_paged(q, k, v, ind, ptr, lpl, p.scale, o=o, lse=lse, workspace=ws,
+                             layout=p.layout)
 
     for _ in range(args.warmup):
         step()

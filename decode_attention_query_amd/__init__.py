@@ -12,9 +12,10 @@ from ._binding import (CODE_TORCH_DTYPES, DTYPE_CODES, EXPORTED, FA_DTYPE_BF16, 
                        FA_DTYPE_F32, FA_ERR_INVALID_PROBLEM, FA_ERR_LAUNCH, FA_ERR_UNSUPPORTED,
                        FA_ERR_WORKSPACE_TOO_SMALL, FA_OK, LIB_PATH, STATUS_NAMES,
                        TORCH_DTYPE_CODES, FaError, fa_debug_gather_paged, fa_debug_plan,
-                       fa_debug_read_probe, fa_debug_schedule, fa_debug_timing_enable, fa_debug_timing_read, fa_decode_contig,
-                       fa_decode_paged, fa_decode_workspace_size, fa_status_string,
-                       load_library)
+                       fa_debug_read_probe, fa_debug_schedule, fa_debug_timing_enable,
+                       fa_debug_timing_read, fa_decode_contig, fa_decode_contig_nhd,
+                       fa_decode_paged, fa_decode_paged_nhd, fa_decode_workspace_size,
+                       fa_status_string, load_library)
 
 
 def _code(t):
@@ -34,11 +35,16 @@ def workspace_paged(batch, num_qo_heads, num_kv_heads, head_dim, page_size, tota
 
 
 def decode_paged(q, k_data, v_data, indices, indptr, last_page_len, sm_scale, o=None, lse=None,
-                 workspace=None, stream=None):
-    """q [B, Hq, D]; k_data/v_data [pages, Hkv, P, D]; int32 page table.
-    Returns (o [B, Hq, D] in q's dtype, lse [B, Hq] f32)."""
+                 workspace=None, stream=None, layout="hnd"):
+    """q [B, Hq, D]; k_data/v_data [pages, Hkv, P, D] (layout "nhd": [pages, P, Hkv, D]);
+    int32 page table.  Returns (o [B, Hq, D] in q's dtype, lse [B, Hq] f32)."""
     batch, hq, d = q.shape
-    pages, hkv, page_size, d2 = k_data.shape
+    if layout == "nhd":
+        pages, page_size, hkv, d2 = k_data.shape
+    elif layout == "hnd":
+        pages, hkv, page_size, d2 = k_data.shape
+    else:
+        raise ValueError(f"unknown layout {layout!r}")
     if d2 != d or tuple(v_data.shape) != tuple(k_data.shape):
         raise ValueError("q, k_data and v_data disagree on shape")
     if o is None:
@@ -48,18 +54,23 @@ def decode_paged(q, k_data, v_data, indices, indptr, last_page_len, sm_scale, o=
     used = indices.numel()
     if workspace is None:
         workspace = workspace_paged(batch, hq, hkv, d, page_size, used, q.device)
-    fa_decode_paged(_code(q), batch, hq, hkv, d, page_size, pages, used, sm_scale, q, k_data,
-                    v_data, indices if used else None, indptr, last_page_len, o, lse,
-                    workspace, stream)
+    fn = fa_decode_paged_nhd if layout == "nhd" else fa_decode_paged
+    fn(_code(q), batch, hq, hkv, d, page_size, pages, used, sm_scale, q, k_data, v_data,
+       indices if used else None, indptr, last_page_len, o, lse, workspace, stream)
     return o, lse
 
 
 def decode_contig(q, k_cache, v_cache, valid_kv_len, scale, o=None, lse=None, workspace=None,
-                  stream=None):
-    """q [Hq, D]; k_cache/v_cache [Hkv, max_kv_len, D].
+                  stream=None, layout="hnd"):
+    """q [Hq, D]; k_cache/v_cache [Hkv, max_kv_len, D] (layout "nhd": [max_kv_len, Hkv, D]).
     Returns (o [Hq, D] in q's dtype, lse [Hq] f32)."""
     hq, d = q.shape
-    hkv, max_kv_len, d2 = k_cache.shape
+    if layout == "nhd":
+        max_kv_len, hkv, d2 = k_cache.shape
+    elif layout == "hnd":
+        hkv, max_kv_len, d2 = k_cache.shape
+    else:
+        raise ValueError(f"unknown layout {layout!r}")
     if d2 != d or tuple(v_cache.shape) != tuple(k_cache.shape):
         raise ValueError("q, k_cache and v_cache disagree on shape")
     if o is None:
@@ -68,6 +79,7 @@ def decode_contig(q, k_cache, v_cache, valid_kv_len, scale, o=None, lse=None, wo
         lse = torch.empty((hq,), dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = workspace_paged(1, hq, hkv, d, max_kv_len, 1, q.device)
-    fa_decode_contig(_code(q), hq, hkv, d, max_kv_len, valid_kv_len, scale, q, k_cache,
-                     v_cache, o, lse, workspace, stream)
+    fn = fa_decode_contig_nhd if layout == "nhd" else fa_decode_contig
+    fn(_code(q), hq, hkv, d, max_kv_len, valid_kv_len, scale, q, k_cache, v_cache, o, lse,
+       workspace, stream)
     return o, lse

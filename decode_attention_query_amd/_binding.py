@@ -28,7 +28,8 @@ STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_INVALID_PROBLEM", 2: "FA_ERR_UNSUPPORTED"
 
 # every symbol the public headers declare
 EXPORTED = ("fa_decode_workspace_size", "fa_decode_contig", "fa_decode_paged",
-            "fa_status_string", "fa_debug_gather_paged", "fa_debug_timing_enable",
+            "fa_decode_contig_nhd", "fa_decode_paged_nhd", "fa_status_string",
+            "fa_debug_gather_paged", "fa_debug_gather_paged_nhd", "fa_debug_timing_enable",
             "fa_debug_timing_read", "fa_debug_plan", "fa_debug_schedule",
             "fa_debug_read_probe")
 
@@ -58,17 +59,20 @@ def load_library():
     lib = ctypes.CDLL(LIB_PATH)
     lib.fa_decode_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I]
     lib.fa_decode_workspace_size.restype = _SZ
-    lib.fa_decode_contig.argtypes = [_I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _SZ,
-                                     _P]
-    lib.fa_decode_contig.restype = _I
-    lib.fa_decode_paged.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P,
-                                    _P, _P, _P, _SZ, _P]
-    lib.fa_decode_paged.restype = _I
+    for name in ("fa_decode_contig", "fa_decode_contig_nhd"):
+        getattr(lib, name).argtypes = [_I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _P, _SZ,
+                                       _P]
+        getattr(lib, name).restype = _I
+    for name in ("fa_decode_paged", "fa_decode_paged_nhd"):
+        getattr(lib, name).argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P,
+                                       _P, _P, _P, _P, _SZ, _P]
+        getattr(lib, name).restype = _I
     lib.fa_status_string.argtypes = [_I]
     lib.fa_status_string.restype = ctypes.c_char_p
-    lib.fa_debug_gather_paged.argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I64,
-                                          _P, _SZ, _P]
-    lib.fa_debug_gather_paged.restype = _I
+    for name in ("fa_debug_gather_paged", "fa_debug_gather_paged_nhd"):
+        getattr(lib, name).argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I64,
+                                       _P, _SZ, _P]
+        getattr(lib, name).restype = _I
     lib.fa_debug_timing_enable.argtypes = [_I]
     lib.fa_debug_timing_enable.restype = _I
     lib.fa_debug_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double),
@@ -136,14 +140,14 @@ def fa_decode_workspace_size(batch, num_qo_heads, num_kv_heads, head_dim, page_s
                                                        head_dim, page_size, total_used_pages))
 
 
-def fa_decode_contig(dtype, num_qo_heads, num_kv_heads, head_dim, max_kv_len, valid_kv_len,
-                     scale, q, k_cache, v_cache, o, lse, workspace, stream=None):
+def _contig(fn, dtype, num_qo_heads, num_kv_heads, head_dim, max_kv_len, valid_kv_len,
+            scale, q, k_cache, v_cache, o, lse, workspace, stream):
     lib = load_library()
+    call = getattr(lib, fn)
     tdt = CODE_TORCH_DTYPES.get(dtype)
     if tdt is None:  # let the library report the unsupported dtype
-        _check("fa_decode_contig", lib.fa_decode_contig(
-            dtype, num_qo_heads, num_kv_heads, head_dim, max_kv_len, valid_kv_len, scale,
-            None, None, None, None, None, None, 0, None))
+        _check(fn, call(dtype, num_qo_heads, num_kv_heads, head_dim, max_kv_len, valid_kv_len,
+                        scale, None, None, None, None, None, None, 0, None))
     kv_numel = num_kv_heads * max_kv_len * head_dim
     args = (
         _dev_buf(q, "q", num_qo_heads * head_dim, tdt),
@@ -153,20 +157,33 @@ def fa_decode_contig(dtype, num_qo_heads, num_kv_heads, head_dim, max_kv_len, va
         _dev_buf(lse, "lse", num_qo_heads, torch.float32, allow_none=True),
     )
     ws_ptr, ws_bytes = _workspace(workspace, None)
-    _check("fa_decode_contig", lib.fa_decode_contig(
-        dtype, num_qo_heads, num_kv_heads, head_dim, max_kv_len, valid_kv_len, float(scale),
-        *args, ws_ptr, ws_bytes, _stream(stream)))
+    _check(fn, call(dtype, num_qo_heads, num_kv_heads, head_dim, max_kv_len, valid_kv_len,
+                    float(scale), *args, ws_ptr, ws_bytes, _stream(stream)))
 
 
-def fa_decode_paged(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
-                    num_total_pages, total_used_pages, sm_scale, q, k_data, v_data, indices,
-                    indptr, last_page_len, o, lse, workspace, stream=None):
+def fa_decode_contig(dtype, num_qo_heads, num_kv_heads, head_dim, max_kv_len, valid_kv_len,
+                     scale, q, k_cache, v_cache, o, lse, workspace, stream=None):
+    """k_cache, v_cache [Hkv, max_kv_len, D] (heads-major)."""
+    _contig("fa_decode_contig", dtype, num_qo_heads, num_kv_heads, head_dim, max_kv_len,
+            valid_kv_len, scale, q, k_cache, v_cache, o, lse, workspace, stream)
+
+
+def fa_decode_contig_nhd(dtype, num_qo_heads, num_kv_heads, head_dim, max_kv_len, valid_kv_len,
+                         scale, q, k_cache, v_cache, o, lse, workspace, stream=None):
+    """k_cache, v_cache [max_kv_len, Hkv, D] (token-major)."""
+    _contig("fa_decode_contig_nhd", dtype, num_qo_heads, num_kv_heads, head_dim, max_kv_len,
+            valid_kv_len, scale, q, k_cache, v_cache, o, lse, workspace, stream)
+
+
+def _paged(fn, dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_total_pages,
+           total_used_pages, sm_scale, q, k_data, v_data, indices, indptr, last_page_len, o,
+           lse, workspace, stream):
     lib = load_library()
+    call = getattr(lib, fn)
     tdt = CODE_TORCH_DTYPES.get(dtype)
     if tdt is None:
-        _check("fa_decode_paged", lib.fa_decode_paged(
-            dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_total_pages,
-            total_used_pages, sm_scale, *([None] * 9), 0, None))
+        _check(fn, call(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                        num_total_pages, total_used_pages, sm_scale, *([None] * 9), 0, None))
     pool = num_total_pages * num_kv_heads * page_size * head_dim
     args = (
         _dev_buf(q, "q", batch * num_qo_heads * head_dim, tdt),
@@ -180,15 +197,35 @@ def fa_decode_paged(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_siz
         _dev_buf(lse, "lse", batch * num_qo_heads, torch.float32),
     )
     ws_ptr, ws_bytes = _workspace(workspace, None)
-    _check("fa_decode_paged", lib.fa_decode_paged(
-        dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_total_pages,
-        total_used_pages, float(sm_scale), *args, ws_ptr, ws_bytes, _stream(stream)))
+    _check(fn, call(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                    num_total_pages, total_used_pages, float(sm_scale), *args, ws_ptr, ws_bytes,
+                    _stream(stream)))
+
+
+def fa_decode_paged(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                    num_total_pages, total_used_pages, sm_scale, q, k_data, v_data, indices,
+                    indptr, last_page_len, o, lse, workspace, stream=None):
+    """k_data, v_data [pages, Hkv, P, D] (heads-major)."""
+    _paged("fa_decode_paged", dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+           num_total_pages, total_used_pages, sm_scale, q, k_data, v_data, indices, indptr,
+           last_page_len, o, lse, workspace, stream)
+
+
+def fa_decode_paged_nhd(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                        num_total_pages, total_used_pages, sm_scale, q, k_data, v_data, indices,
+                        indptr, last_page_len, o, lse, workspace, stream=None):
+    """k_data, v_data [pages, P, Hkv, D] (token-major)."""
+    _paged("fa_decode_paged_nhd", dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+           num_total_pages, total_used_pages, sm_scale, q, k_data, v_data, indices, indptr,
+           last_page_len, o, lse, workspace, stream)
 
 
 def fa_debug_gather_paged(dtype, batch, num_kv_heads, head_dim, page_size, num_total_pages,
                           total_used_pages, data, indices, indptr, last_page_len, out,
-                          out_rows, workspace, stream=None):
+                          out_rows, workspace, stream=None, layout="hnd"):
+    """layout "nhd" calls fa_debug_gather_paged_nhd (data [pages, P, Hkv, D])."""
     lib = load_library()
+    fn = "fa_debug_gather_paged_nhd" if layout == "nhd" else "fa_debug_gather_paged"
     tdt = CODE_TORCH_DTYPES[dtype]
     args = (
         _dev_buf(data, "data", num_total_pages * num_kv_heads * page_size * head_dim, tdt),
@@ -199,7 +236,7 @@ def fa_debug_gather_paged(dtype, batch, num_kv_heads, head_dim, page_size, num_t
         _dev_buf(out, "out", out_rows * num_kv_heads * head_dim, tdt),
     )
     ws_ptr, ws_bytes = _workspace(workspace, None)
-    _check("fa_debug_gather_paged", lib.fa_debug_gather_paged(
+    _check(fn, getattr(lib, fn)(
         dtype, batch, num_kv_heads, head_dim, page_size, num_total_pages, total_used_pages,
         *args, int(out_rows), ws_ptr, ws_bytes, _stream(stream)))
 

@@ -65,6 +65,7 @@ struct DecodeParams {
   int chunk;          // KV rows per split unit (a multiple of 256)
   int units_bound;    // work indices launched; those past the real unit count exit at once
   int contig;         // 1: contiguous cache (a single page of max_kv_len rows)
+  int nhd;            // 1: token-major K/V ([.., P, Hkv, D]); 0: heads-major ([.., Hkv, P, D])
   int uniform_blocks; // 1: every 16-row block starting at a multiple of 16 lies in one page
   int contig_len;     // contiguous: valid_kv_len
   int contig_units;   // contiguous: ceil(valid_kv_len / chunk), at least 1
@@ -153,11 +154,22 @@ __device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 // valid score has been seen (keeps -inf - -inf out of the exponent).
 __device__ inline float safe_ref(float m) { return m == -INFINITY ? 0.0f : m; }
 
+// Element offset of row r of page `page`, KV head kvh.  Heads-major pages are
+// [Hkv, P, D] (baracuda-kernels 0.0.1-alpha.68, src/attention/batch_paged_decode.rs,
+// module doc "Layout"); token-major pages are [P, Hkv, D], row t of head g at
+// (t * Hkv + g) * D as in ferrox-cuda 0.15.2, src/attn.rs (gqa_decode kernel
+// source).  A contiguous cache is the single page 0 of P = max_kv_len rows.
+template <bool kNhd>
+__device__ inline int64_t kv_elem_offset(const DecodeParams &p, int64_t page, int kvh,
+                                         uint32_t r) {
+  if (kNhd) return ((page * p.page_size + r) * p.num_kv_heads + kvh) * (int64_t)p.head_dim;
+  return ((page * p.num_kv_heads + kvh) * (int64_t)p.page_size + r) * p.head_dim;
+}
+
 // Element offset of KV row t (of request b, KV head kvh), lane vector vi
-// excluded.  Paged: page = indices[page_base + t / P], row = t % P, layout
-// [pages, Hkv, P, D]; contiguous: the single page 0 of P = max_kv_len rows.
-// Page ids are clamped into the pool so that a table breaking its contract
-// cannot make a kernel read outside the K/V buffers.
+// excluded.  Paged: page = indices[page_base + t / P], row = t % P.  Page ids
+// are clamped into the pool so that a table breaking its contract cannot make
+// a kernel read outside the K/V buffers.
 __device__ inline int64_t kv_row_offset(const DecodeParams &p, int32_t page_base, int kvh,
                                         int t) {
   int64_t page = 0;
@@ -169,25 +181,7 @@ __device__ inline int64_t kv_row_offset(const DecodeParams &p, int32_t page_base
     id = min(max(id, 0), p.num_total_pages - 1);
     page = id;
   }
-  return ((page * p.num_kv_heads + kvh) * (int64_t)p.page_size + row) * p.head_dim;
-}
-
-// Element offset of the first row of the 16-row block starting at row tb
-// (wave-uniform), for blocks that lie in one page.  The page id is read with a
-// scalar load, so it does not queue behind the wave's outstanding K/V loads.
-__device__ inline int64_t block_row_offset(const DecodeParams &p, int32_t page_base, int kvh,
-                                           int tb) {
-  int64_t page = 0;
-  uint32_t row = (uint32_t)tb;
-  if (!p.contig) {
-    const uint32_t slot = fastdiv((uint32_t)tb, p.page_div);
-    row = (uint32_t)tb - slot * (uint32_t)p.page_size;
-    typedef const __attribute__((address_space(4))) int32_t cint32;
-    int32_t id = ((cint32 *)p.indices)[page_base + slot];
-    id = min(max(id, 0), p.num_total_pages - 1);
-    page = id;
-  }
-  return ((page * p.num_kv_heads + kvh) * (int64_t)p.page_size + row) * p.head_dim;
+  return p.nhd ? kv_elem_offset<true>(p, page, kvh, row) : kv_elem_offset<false>(p, page, kvh, row);
 }
 
 __device__ inline float wave_max(float v) {

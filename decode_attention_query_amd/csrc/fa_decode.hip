@@ -210,8 +210,11 @@ hipError_t launch_decode(const DecodeParams &p, const HostPlan &hp, hipStream_t 
 template <class E, int D>
 hipError_t launch_mfma(const DecodeParams &p, const HostPlan &hp, hipStream_t s) {
   dim3 grid(unsigned(hp.units_bound) * unsigned(hp.planes));
-  hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D>), grid, dim3(fa::MfmaGeom<E, D>::NW * 64), 0,
-                     s, p);
+  dim3 block(fa::MfmaGeom<E, D>::NW * 64);
+  if (p.nhd)
+    hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, true>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, false>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
@@ -280,11 +283,15 @@ size_t fa_decode_workspace_size(int batch, int num_qo_heads, int num_kv_heads, i
       .total;
 }
 
-fa_status_t fa_decode_contig(fa_dtype_t dtype, int num_qo_heads, int num_kv_heads,
-                             int head_dim, int max_kv_len, int valid_kv_len, float scale,
-                             const void *q, const void *k_cache, const void *v_cache, void *o,
-                             float *lse, void *workspace, size_t workspace_bytes,
-                             hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+fa_status_t decode_contig(int nhd, fa_dtype_t dtype, int num_qo_heads, int num_kv_heads,
+                          int head_dim, int max_kv_len, int valid_kv_len, float scale,
+                          const void *q, const void *k_cache, const void *v_cache, void *o,
+                          float *lse, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
   if (!dtype_ok(dtype)) return FA_ERR_UNSUPPORTED;
   if (!extents_ok(1, num_qo_heads, num_kv_heads, max_kv_len)) return FA_ERR_INVALID_PROBLEM;
   if (!head_dim_ok(head_dim)) return FA_ERR_UNSUPPORTED;
@@ -308,6 +315,7 @@ fa_status_t fa_decode_contig(fa_dtype_t dtype, int num_qo_heads, int num_kv_head
   p.o = o;
   p.lse = lse;
   p.contig = 1;
+  p.nhd = nhd;
   p.uniform_blocks = 1;
   p.contig_len = valid_kv_len;
   p.contig_units =
@@ -323,13 +331,13 @@ fa_status_t fa_decode_contig(fa_dtype_t dtype, int num_qo_heads, int num_kv_head
   return FA_OK;
 }
 
-fa_status_t fa_decode_paged(fa_dtype_t dtype, int batch, int num_qo_heads, int num_kv_heads,
-                            int head_dim, int page_size, int num_total_pages,
-                            int total_used_pages, float sm_scale, const void *q,
-                            const void *k_data, const void *v_data, const int32_t *indices,
-                            const int32_t *indptr, const int32_t *last_page_len, void *o,
-                            float *lse, void *workspace, size_t workspace_bytes,
-                            hipStream_t stream) {
+fa_status_t decode_paged(int nhd, fa_dtype_t dtype, int batch, int num_qo_heads,
+                         int num_kv_heads, int head_dim, int page_size, int num_total_pages,
+                         int total_used_pages, float sm_scale, const void *q,
+                         const void *k_data, const void *v_data, const int32_t *indices,
+                         const int32_t *indptr, const int32_t *last_page_len, void *o,
+                         float *lse, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
   if (!dtype_ok(dtype)) return FA_ERR_UNSUPPORTED;
   if (!extents_ok(batch, num_qo_heads, num_kv_heads, page_size) || num_total_pages <= 0)
     return FA_ERR_INVALID_PROBLEM;
@@ -359,6 +367,7 @@ fa_status_t fa_decode_paged(fa_dtype_t dtype, int batch, int num_qo_heads, int n
   p.indices = indices;
   p.indptr = indptr;
   p.last_page_len = last_page_len;
+  p.nhd = nhd;
   carve(p, hp, workspace);
   p.call_tag = next_call_tag();
 
@@ -368,6 +377,52 @@ fa_status_t fa_decode_paged(fa_dtype_t dtype, int batch, int num_qo_heads, int n
   ev.mark(2, stream);
   ev.finish(stream);
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status_t fa_decode_contig(fa_dtype_t dtype, int num_qo_heads, int num_kv_heads,
+                             int head_dim, int max_kv_len, int valid_kv_len, float scale,
+                             const void *q, const void *k_cache, const void *v_cache, void *o,
+                             float *lse, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  return decode_contig(0, dtype, num_qo_heads, num_kv_heads, head_dim, max_kv_len, valid_kv_len,
+                       scale, q, k_cache, v_cache, o, lse, workspace, workspace_bytes, stream);
+}
+
+fa_status_t fa_decode_contig_nhd(fa_dtype_t dtype, int num_qo_heads, int num_kv_heads,
+                                 int head_dim, int max_kv_len, int valid_kv_len, float scale,
+                                 const void *q, const void *k_cache, const void *v_cache,
+                                 void *o, float *lse, void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  return decode_contig(1, dtype, num_qo_heads, num_kv_heads, head_dim, max_kv_len, valid_kv_len,
+                       scale, q, k_cache, v_cache, o, lse, workspace, workspace_bytes, stream);
+}
+
+fa_status_t fa_decode_paged(fa_dtype_t dtype, int batch, int num_qo_heads, int num_kv_heads,
+                            int head_dim, int page_size, int num_total_pages,
+                            int total_used_pages, float sm_scale, const void *q,
+                            const void *k_data, const void *v_data, const int32_t *indices,
+                            const int32_t *indptr, const int32_t *last_page_len, void *o,
+                            float *lse, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  return decode_paged(0, dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                      num_total_pages, total_used_pages, sm_scale, q, k_data, v_data, indices,
+                      indptr, last_page_len, o, lse, workspace, workspace_bytes, stream);
+}
+
+fa_status_t fa_decode_paged_nhd(fa_dtype_t dtype, int batch, int num_qo_heads,
+                                int num_kv_heads, int head_dim, int page_size,
+                                int num_total_pages, int total_used_pages, float sm_scale,
+                                const void *q, const void *k_data, const void *v_data,
+                                const int32_t *indices, const int32_t *indptr,
+                                const int32_t *last_page_len, void *o, float *lse,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_paged(1, dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                      num_total_pages, total_used_pages, sm_scale, q, k_data, v_data, indices,
+                      indptr, last_page_len, o, lse, workspace, workspace_bytes, stream);
 }
 
 const char *fa_status_string(fa_status_t status) {
@@ -383,12 +438,15 @@ const char *fa_status_string(fa_status_t status) {
 
 // ------------------------------------------------------------------- hooks
 
-fa_status_t fa_debug_gather_paged(fa_dtype_t dtype, int batch, int num_kv_heads, int head_dim,
-                                  int page_size, int num_total_pages, int total_used_pages,
-                                  const void *data, const int32_t *indices,
-                                  const int32_t *indptr, const int32_t *last_page_len,
-                                  void *out, int64_t out_rows, void *workspace,
-                                  size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+fa_status_t gather_paged(int nhd, fa_dtype_t dtype, int batch, int num_kv_heads, int head_dim,
+                         int page_size, int num_total_pages, int total_used_pages,
+                         const void *data, const int32_t *indices, const int32_t *indptr,
+                         const int32_t *last_page_len, void *out, int64_t out_rows,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!dtype_ok(dtype)) return FA_ERR_UNSUPPORTED;
   if (!extents_ok(batch, num_kv_heads, num_kv_heads, page_size) || num_total_pages <= 0)
     return FA_ERR_INVALID_PROBLEM;
@@ -410,12 +468,40 @@ fa_status_t fa_debug_gather_paged(fa_dtype_t dtype, int batch, int num_kv_heads,
   p.indices = indices;
   p.indptr = indptr;
   p.last_page_len = last_page_len;
+  p.nhd = nhd;
   carve(p, hp, workspace);
   const int elem = dtype == FA_DTYPE_F32 ? 4 : 2;
   hipLaunchKernelGGL(fa::gather_kernel, dim3(hp.units_bound, num_kv_heads), dim3(256), 0,
                      stream, p, out, out_rows, elem);
   if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status_t fa_debug_gather_paged(fa_dtype_t dtype, int batch, int num_kv_heads, int head_dim,
+                                  int page_size, int num_total_pages, int total_used_pages,
+                                  const void *data, const int32_t *indices,
+                                  const int32_t *indptr, const int32_t *last_page_len,
+                                  void *out, int64_t out_rows, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  return gather_paged(0, dtype, batch, num_kv_heads, head_dim, page_size, num_total_pages,
+                      total_used_pages, data, indices, indptr, last_page_len, out, out_rows,
+                      workspace, workspace_bytes, stream);
+}
+
+fa_status_t fa_debug_gather_paged_nhd(fa_dtype_t dtype, int batch, int num_kv_heads,
+                                      int head_dim, int page_size, int num_total_pages,
+                                      int total_used_pages, const void *data,
+                                      const int32_t *indices, const int32_t *indptr,
+                                      const int32_t *last_page_len, void *out, int64_t out_rows,
+                                      void *workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+  return gather_paged(1, dtype, batch, num_kv_heads, head_dim, page_size, num_total_pages,
+                      total_used_pages, data, indices, indptr, last_page_len, out, out_rows,
+                      workspace, workspace_bytes, stream);
 }
 
 fa_status_t fa_debug_schedule(fa_dtype_t dtype, int batch, int num_qo_heads, int num_kv_heads,

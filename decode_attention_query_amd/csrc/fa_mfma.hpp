@@ -124,16 +124,11 @@ struct KVTile {
   uint4 v[NI];
 };
 
-// Issues the global loads of the tile whose first row is t0 (rows past t_end
-// are clamped to t_end - 1: in bounds, and masked out of the softmax later).
-// t0, t_end and page_base are wave-uniform.  When every 16-row block lies in
-// one page, the block's page is resolved once per wave with a scalar load;
-// otherwise (page sizes that are not multiples of 16) every lane resolves its
-// own rows.
 // Element offset of the first row of the 16-row block starting at row tb
 // (wave-uniform; the block lies in one page).  Page ids come from the unit's
 // slice of the page table, staged in LDS at the start of the workgroup
 // (s_pages[i] = page id of page slot slot0 + i).
+template <bool kNhd>
 __device__ inline int64_t staged_block_offset(const DecodeParams &p, const int32_t *s_pages,
                                               int slot0, int kvh, int tb) {
   int64_t page = 0;
@@ -143,14 +138,21 @@ __device__ inline int64_t staged_block_offset(const DecodeParams &p, const int32
     row = (uint32_t)tb - slot * (uint32_t)p.page_size;
     page = __builtin_amdgcn_readfirstlane(s_pages[slot - slot0]);
   }
-  return ((page * p.num_kv_heads + kvh) * (int64_t)p.page_size + row) * p.head_dim;
+  return kv_elem_offset<kNhd>(p, page, kvh, row);
 }
 
-template <class E, int D>
+// Issues the global loads of the tile whose first row is t0 (rows past t_end
+// are clamped to t_end - 1: in bounds, and masked out of the softmax later).
+// t0, t_end and page_base are wave-uniform.  When every 16-row block lies in
+// one page, the block's page comes from LDS once per block and rows follow at
+// the layout's row stride (D heads-major, Hkv * D token-major); otherwise
+// (page sizes that are not multiples of 16) every lane resolves its own rows.
+template <class E, int D, bool kNhd>
 __device__ inline void issue_tile(KVTile<MfmaGeom<E, D>::NI> &T, const DecodeParams &p,
                                   int32_t page_base, const int32_t *s_pages, int slot0, int kvh,
                                   int t0, int t_end, int lane) {
   using G = MfmaGeom<E, D>;
+  const int64_t rs = kNhd ? (int64_t)p.num_kv_heads * D : D;  // elements between rows
   const int r0 = lane / G::LPR;           // row within an instruction
   const int col = (lane % G::LPR) * 16;   // byte within the row
   const char *kb = static_cast<const char *>(p.k) + col;
@@ -160,7 +162,7 @@ __device__ inline void issue_tile(KVTile<MfmaGeom<E, D>::NI> &T, const DecodePar
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int tb = min(t0 + 16 * j, t_end - 1);
-      blk[j] = staged_block_offset(p, s_pages, slot0, kvh, tb) - (int64_t)tb * D;
+      blk[j] = staged_block_offset<kNhd>(p, s_pages, slot0, kvh, tb) - (int64_t)tb * rs;
     }
   }
 #pragma unroll
@@ -169,8 +171,8 @@ __device__ inline void issue_tile(KVTile<MfmaGeom<E, D>::NI> &T, const DecodePar
     const int t = min(t0 + r, t_end - 1);
     int64_t off;
     if (p.uniform_blocks) {
-      // rows of block j = r / 16 share its page: offset = block base + row * D
-      off = (blk[(G::RPI * i) / 16] + (int64_t)t * D) * 2;
+      // rows of block j = r / 16 share its page: offset = block base + row stride
+      off = (blk[(G::RPI * i) / 16] + (int64_t)t * rs) * 2;
     } else {
       off = kv_row_offset(p, page_base, kvh, t) * 2;
     }
@@ -179,7 +181,7 @@ __device__ inline void issue_tile(KVTile<MfmaGeom<E, D>::NI> &T, const DecodePar
   }
 }
 
-template <class E, int D>
+template <class E, int D, bool kNhd>
 __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1))) void decode_mfma_kernel(
     const DecodeParams p) {
   using G = MfmaGeom<E, D>;
@@ -335,15 +337,15 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   int t0 = t_begin + wave * TT;
   if (t0 < t_end) {
     KVTile<G::NI> A;
-    issue_tile<E, D>(A, p, page_base, s_pages, slot0, kvh, t0, t_end, lane);
+    issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, t0, t_end, lane);
     if constexpr (G::kPipelined) {
       KVTile<G::NI> B;
       while (true) {
-        issue_tile<E, D>(B, p, page_base, s_pages, slot0, kvh, t0 + stride, t_end, lane);
+        issue_tile<E, D, kNhd>(B, p, page_base, s_pages, slot0, kvh, t0 + stride, t_end, lane);
         compute(A, t0);
         t0 += stride;
         if (t0 >= t_end) break;
-        issue_tile<E, D>(A, p, page_base, s_pages, slot0, kvh, t0 + stride, t_end, lane);
+        issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, t0 + stride, t_end, lane);
         compute(B, t0);
         t0 += stride;
         if (t0 >= t_end) break;
@@ -353,7 +355,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
         compute(A, t0);
         t0 += stride;
         if (t0 >= t_end) break;
-        issue_tile<E, D>(A, p, page_base, s_pages, slot0, kvh, t0, t_end, lane);
+        issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, t0, t_end, lane);
       }
     }
   }

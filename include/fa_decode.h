@@ -166,6 +166,33 @@ fa_status_t fa_decode_paged(fa_dtype_t dtype, int batch, int num_qo_heads, int n
                             float *lse, void *workspace, size_t workspace_bytes,
                             hipStream_t stream);
 
+/* Token-major variants (ferrox-cuda 0.15.2, src/attn.rs: the gqa_decode kernel
+ * source and the k_cache / v_cache shape in its doc comment put row t of KV
+ * head g at (t * Hkv + g) * D).  Same arguments, checks, conventions and
+ * results as the entry points above; only the K/V layout differs:
+ *
+ *   fa_decode_contig_nhd:  k_cache, v_cache  [max_kv_len, Hkv, D]  T
+ *   fa_decode_paged_nhd:   k_data, v_data    [num_total_pages, page_size, Hkv, D]  T
+ *                          (all heads of one token adjacent inside a page; the
+ *                          pages print no paged token-major layout, this is the
+ *                          page-level form of the contiguous one)
+ *
+ * For the same logical rows the outputs are bit-identical to the heads-major
+ * entry points'. */
+fa_status_t fa_decode_contig_nhd(fa_dtype_t dtype, int num_qo_heads, int num_kv_heads,
+                                 int head_dim, int max_kv_len, int valid_kv_len, float scale,
+                                 const void *q, const void *k_cache, const void *v_cache,
+                                 void *o, float *lse, void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+fa_status_t fa_decode_paged_nhd(fa_dtype_t dtype, int batch, int num_qo_heads,
+                                int num_kv_heads, int head_dim, int page_size,
+                                int num_total_pages, int total_used_pages, float sm_scale,
+                                const void *q, const void *k_data, const void *v_data,
+                                const int32_t *indices, const int32_t *indptr,
+                                const int32_t *last_page_len, void *o, float *lse,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *fa_status_string(fa_status_t status);
 

@@ -65,6 +65,16 @@ fa_status_t fa_debug_schedule(fa_dtype_t dtype, int batch, int num_qo_heads, int
 fa_status_t fa_debug_read_probe(const void *buf, size_t bytes, uint32_t *sink,
                                 hipStream_t stream);
 
+/* fa_debug_gather_paged for a token-major store: data is
+ * [num_total_pages, page_size, Hkv, D]; out is laid out as above. */
+fa_status_t fa_debug_gather_paged_nhd(fa_dtype_t dtype, int batch, int num_kv_heads,
+                                      int head_dim, int page_size, int num_total_pages,
+                                      int total_used_pages, const void *data,
+                                      const int32_t *indices, const int32_t *indptr,
+                                      const int32_t *last_page_len, void *out, int64_t out_rows,
+                                      void *workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+
 /* Kernel timing.  While enabled, every decode call records a HIP event pair on
  * its stream around its main attention kernel (the one that streams K and V),
  * and another around the whole call.  fa_debug_timing_read waits for the

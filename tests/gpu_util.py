@@ -51,18 +51,19 @@ def run(p, d, o=None, lse=None, workspace=None):
     """The library's o and lse for problem p (device tensors d)."""
     if isinstance(p, W.PagedProblem):
         return fad.decode_paged(d["q"], d["k"], d["v"], d["indices"], d["indptr"], d["lpl"],
-                                p.scale, o=o, lse=lse, workspace=workspace)
+                                p.scale, o=o, lse=lse, workspace=workspace, layout=p.layout)
     return fad.decode_contig(d["q"], d["k"], d["v"], p.valid_kv_len, p.scale, o=o, lse=lse,
-                             workspace=workspace)
+                             workspace=workspace, layout=p.layout)
 
 
 def oracle_of(p, samples=None):
     if isinstance(p, W.PagedProblem):
         return oracle.decode_paged(p.dtype, W.bits(p.q), W.bits(p.k_data), W.bits(p.v_data),
                                    p.indices.numpy(), p.indptr.numpy(),
-                                   p.last_page_len.numpy(), p.scale, samples=samples)
+                                   p.last_page_len.numpy(), p.scale, samples=samples,
+                                   layout=p.layout)
     return oracle.decode_contig(p.dtype, W.bits(p.q), W.bits(p.k_cache), W.bits(p.v_cache),
-                                p.valid_kv_len, p.scale)
+                                p.valid_kv_len, p.scale, layout=p.layout)
 
 
 def compare(dtype, o_gpu, lse_gpu, o_ref, lse_ref, what="", strict=False):

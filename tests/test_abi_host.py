@@ -74,24 +74,24 @@ def test_plan_covers_units():
 
 
 def _paged(*, dtype=2, batch=2, hq=8, hkv=2, d=128, page=16, pages=10, used=4,
-           ptrs=None, ws=FAKE, ws_bytes=1 << 30):
+           ptrs=None, ws=FAKE, ws_bytes=1 << 30, fn="fa_decode_paged"):
     lib = fad.load_library()
     q = k = v = ind = ptr = lpl = o = lse = FAKE
     if ptrs:
         q, k, v, ind, ptr, lpl, o, lse = [ptrs.get(n, FAKE) for n in
                                           ("q", "k", "v", "ind", "ptr", "lpl", "o", "lse")]
-    return lib.fa_decode_paged(dtype, batch, hq, hkv, d, page, pages, used, 0.125, q, k, v, ind,
-                               ptr, lpl, o, lse, ws, ws_bytes, None)
+    return getattr(lib, fn)(dtype, batch, hq, hkv, d, page, pages, used, 0.125, q, k, v, ind,
+                            ptr, lpl, o, lse, ws, ws_bytes, None)
 
 
 def _contig(*, dtype=1, hq=8, hkv=2, d=64, max_len=256, valid=128, ptrs=None, ws=FAKE,
-            ws_bytes=1 << 30):
+            ws_bytes=1 << 30, fn="fa_decode_contig"):
     lib = fad.load_library()
     q = k = v = o = lse = FAKE
     if ptrs:
         q, k, v, o, lse = [ptrs.get(n, FAKE) for n in ("q", "k", "v", "o", "lse")]
-    return lib.fa_decode_contig(dtype, hq, hkv, d, max_len, valid, 0.125, q, k, v, o, lse, ws,
-                                ws_bytes, None)
+    return getattr(lib, fn)(dtype, hq, hkv, d, max_len, valid, 0.125, q, k, v, o, lse, ws,
+                            ws_bytes, None)
 
 
 INV, UNS, WS = fad.FA_ERR_INVALID_PROBLEM, fad.FA_ERR_UNSUPPORTED, fad.FA_ERR_WORKSPACE_TOO_SMALL
@@ -130,8 +130,9 @@ INV, UNS, WS = fad.FA_ERR_INVALID_PROBLEM, fad.FA_ERR_UNSUPPORTED, fad.FA_ERR_WO
     (dict(d=96, ptrs={"q": None}), UNS),
     (dict(ptrs={"q": None}, ws=None), INV),
 ])
-def test_paged_rejects(kw, status):
-    assert _paged(**kw) == status
+@pytest.mark.parametrize("fn", ["fa_decode_paged", "fa_decode_paged_nhd"])
+def test_paged_rejects(kw, status, fn):
+    assert _paged(**kw, fn=fn) == status
 
 
 def test_paged_workspace_exact_boundary():
@@ -155,18 +156,20 @@ def test_paged_workspace_exact_boundary():
     (dict(ws=None), WS),
     (dict(ws_bytes=0), WS),
 ])
-def test_contig_rejects(kw, status):
-    assert _contig(**kw) == status
+@pytest.mark.parametrize("fn", ["fa_decode_contig", "fa_decode_contig_nhd"])
+def test_contig_rejects(kw, status, fn):
+    assert _contig(**kw, fn=fn) == status
 
 
-def test_gather_rejects():
-    lib = fad.load_library()
+@pytest.mark.parametrize("fn", ["fa_debug_gather_paged", "fa_debug_gather_paged_nhd"])
+def test_gather_rejects(fn):
+    gather = getattr(fad.load_library(), fn)
     args = [2, 2, 2, 128, 16, 10, 4, FAKE, FAKE, FAKE, FAKE, FAKE]
-    assert lib.fa_debug_gather_paged(*args, -1, FAKE, 1 << 30, None) == INV
-    assert lib.fa_debug_gather_paged(*args, 10, None, 0, None) == WS
+    assert gather(*args, -1, FAKE, 1 << 30, None) == INV
+    assert gather(*args, 10, None, 0, None) == WS
     bad = list(args)
     bad[3] = 100
-    assert lib.fa_debug_gather_paged(*bad, 10, FAKE, 1 << 30, None) == UNS
+    assert gather(*bad, 10, FAKE, 1 << 30, None) == UNS
 
 
 def test_schedule_and_probe_reject():

@@ -48,8 +48,9 @@ class ContigProblem:
     valid_kv_len: int
     scale: float
     q: torch.Tensor          # [Hq, D]
-    k_cache: torch.Tensor    # [Hkv, max_kv_len, D]
-    v_cache: torch.Tensor    # [Hkv, max_kv_len, D]
+    k_cache: torch.Tensor    # [Hkv, max_kv_len, D]; [max_kv_len, Hkv, D] if token-major
+    v_cache: torch.Tensor    # same
+    layout: str = "hnd"      # "hnd" heads-major, "nhd" token-major
 
     @property
     def group(self):
@@ -68,12 +69,13 @@ class PagedProblem:
     num_total_pages: int
     scale: float
     q: torch.Tensor          # [B, Hq, D]
-    k_data: torch.Tensor     # [pages, Hkv, P, D]
-    v_data: torch.Tensor     # [pages, Hkv, P, D]
+    k_data: torch.Tensor     # [pages, Hkv, P, D]; [pages, P, Hkv, D] if token-major
+    v_data: torch.Tensor     # same
     indices: torch.Tensor    # [total_used_pages] int32
     indptr: torch.Tensor     # [B + 1] int32
     last_page_len: torch.Tensor  # [B] int32
     kv_lens: np.ndarray = field(default=None)  # lengths the recipe drew (int64)
+    layout: str = "hnd"      # "hnd" heads-major, "nhd" token-major
 
     @property
     def total_used_pages(self):
@@ -82,6 +84,21 @@ class PagedProblem:
     @property
     def group(self):
         return self.num_qo_heads // self.num_kv_heads
+
+
+def token_major(p):
+    """The same problem with K and V stored token-major: contiguous
+    [max_kv_len, Hkv, D], paged [pages, P, Hkv, D] (same values, same page
+    table)."""
+    import dataclasses
+    assert p.layout == "hnd"
+    if isinstance(p, ContigProblem):
+        return dataclasses.replace(p, name=p.name + "_nhd", layout="nhd",
+                                   k_cache=p.k_cache.permute(1, 0, 2).contiguous(),
+                                   v_cache=p.v_cache.permute(1, 0, 2).contiguous())
+    return dataclasses.replace(p, name=p.name + "_nhd", layout="nhd",
+                               k_data=p.k_data.permute(0, 2, 1, 3).contiguous(),
+                               v_data=p.v_data.permute(0, 2, 1, 3).contiguous())
 
 
 def bits(t: torch.Tensor) -> np.ndarray:
