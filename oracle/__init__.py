@@ -20,6 +20,8 @@ Functions and what they follow:
                     module doc "Layout" and "Query / output"); layout="nhd":
                     [pages, P, Hkv, D] (reading: the page-level token-major form)
   gather_paged   -- the page-table-resolved rows, raw bits (same page, "Layout")
+  append_paged   -- decode-time append of one new K/V row per request (same page,
+                    "Companion plans"; reading: the table already counts the row)
   seq_lens       -- L_b from the page table (reading: all pages but the last are full)
   validate_table -- the device-side page-table contract (same page, "Layout")
   attend_f64     -- one query row over explicit f64 rows (a split's partial)
@@ -71,6 +73,8 @@ class _Lib:
         lib.oracle_attend_f64.restype = None
         lib.oracle_merge.argtypes = [_I, _I, _P, _P, _P, _P]
         lib.oracle_merge.restype = None
+        lib.oracle_append_paged.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I]
+        lib.oracle_append_paged.restype = _I
         self.lib = lib
 
 
@@ -168,6 +172,22 @@ def gather_paged(dtype, data, indices, indptr, last_page_len, layout="hnd"):
                                     _ptr(out), LAYOUTS[layout])
     if r != 0:
         raise RuntimeError(f"oracle_gather_paged: {STATUS[r]}")
+    return out
+
+
+def append_paged(dtype, data, indices, indptr, last_page_len, new_rows, layout="hnd"):
+    """A copy of the paged store `data` with request b's new row new_rows[b]
+    ([batch, Hkv, D]) written at its last valid row L_b - 1 (none if L_b = 0)."""
+    out = np.array(_bits(data, dtype), copy=True)
+    new_rows = _bits(new_rows, dtype)
+    hkv, page_size, head_dim = _paged_dims(out.shape, layout)
+    indices, indptr, lpl = _i32(indices), _i32(indptr), _i32(last_page_len)
+    assert new_rows.shape == (lpl.size, hkv, head_dim)
+    r = _load().oracle_append_paged(DTYPES[dtype], int(lpl.size), hkv, head_dim, page_size,
+                                    _ptr(out), _ptr(indices), _ptr(indptr), _ptr(lpl),
+                                    _ptr(new_rows), LAYOUTS[layout])
+    if r != 0:
+        raise RuntimeError(f"oracle_append_paged: {STATUS[r]}")
     return out
 
 

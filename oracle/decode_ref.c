@@ -349,3 +349,34 @@ void oracle_merge(int head_dim, int n_parts, const double *o_parts, const double
   }
   *lse = out_lse;
 }
+
+/* ------------------------------------------------------------ KV append */
+
+/* Decode-time append of one new K (or V) row per request into a paged store
+ * (baracuda-kernels page, "Companion plans": a plan that writes the new K/V
+ * slices into the paged store at decode time; the page gives no signature).
+ * Reading: the page table passed in already counts the new token, so request
+ * b's new row is its last valid row, j = L_b - 1 (which lies in the
+ * second-to-last page when last_page_len[b] = 0); a request with L_b = 0
+ * receives nothing.  new_rows is [batch, Hkv, D]; data (layout as above) is
+ * updated in place, nothing else in it changes. */
+int oracle_append_paged(int dtype, int batch, int num_kv_heads, int head_dim, int page_size,
+                        void *data, const int32_t *indices, const int32_t *indptr,
+                        const int32_t *last_page_len, const void *new_rows, int layout) {
+  if (batch <= 0 || num_kv_heads <= 0 || head_dim <= 0 || page_size <= 0 ||
+      (layout != OR_HND && layout != OR_NHD))
+    return OR_BAD_ARG;
+  size_t es = elem_size(dtype);
+  for (int b = 0; b < batch; ++b) {
+    int64_t n = (int64_t)indptr[b + 1] - indptr[b];
+    int64_t L = n == 0 ? 0 : (n - 1) * page_size + last_page_len[b];
+    if (L == 0) continue;
+    for (int g = 0; g < num_kv_heads; ++g) {
+      int64_t dst = paged_row_offset(layout, num_kv_heads, page_size, head_dim, indices, indptr,
+                                     b, g, L - 1);
+      int64_t src = ((int64_t)b * num_kv_heads + g) * head_dim;
+      memcpy((char *)data + dst * es, (const char *)new_rows + src * es, head_dim * es);
+    }
+  }
+  return OR_OK;
+}

@@ -447,6 +447,37 @@ def pin_gather_inverse():
                                                               want.view(np.uint8))
 
 
+def pin_append_completes_the_scatter():
+    """Appending each request's last logical row into a store that holds all
+    but that row gives, bit for bit, the store holding every row (the test's
+    own scatter), in both layouts; empty requests and every other byte of the
+    pool are left alone."""
+    rng = np.random.default_rng(29)
+    for layout in ("hnd", "nhd"):
+        for dtype in DTYPES:
+            page_size, hkv, d = 4, 3, 8
+            lens = [1, 0, 4, 5, 9, 8]           # request 5 also gets an empty last page
+            rows = [rand_t(rng, (L, hkv, d), dtype) for L in lens]
+            seed = int(rng.integers(1 << 30))
+            full, ind, ptr, lpl = scatter_paged(rows, page_size, np.random.default_rng(seed), 3,
+                                                (5,), fill=7.0, layout=layout)
+            # the same table, but each request's last row still holds stale values
+            stale = [r.clone() for r in rows]
+            for r in stale:
+                if r.shape[0]:
+                    r[-1] = -3.0
+            before, ind2, _, _ = scatter_paged(stale, page_size, np.random.default_rng(seed), 3,
+                                               (5,), fill=7.0, layout=layout)
+            assert np.array_equal(ind, ind2)
+            new = torch.zeros((len(lens), hkv, d), dtype=rows[0].dtype)
+            for b, r in enumerate(rows):
+                new[b] = r[-1] if r.shape[0] else 99.0   # ignored for the empty request
+            got = O.append_paged(dtype, W.bits(before), ind, ptr, lpl, W.bits(new),
+                                 layout=layout)
+            assert np.array_equal(got.view(np.uint8), W.bits(full).view(np.uint8)), \
+                (layout, dtype)
+
+
 def pin_seq_lens():
     """The oracle's L_b equals the row count the test scattered."""
     rng = np.random.default_rng(26)

@@ -49,6 +49,11 @@ MUTANTS = [
     ("nhd_contig_as_heads_major",
      "if (layout == OR_NHD) return (j * num_kv_heads + g) * head_dim;",
      "if (layout == OR_NHD) return ((int64_t)g * max_kv_len + j) * head_dim;"),
+    ("append_past_last_row",
+     "indptr,\n                                     b, g, L - 1);",
+     "indptr,\n                                     b, g, L);"),
+    ("append_to_empty_request", "    if (L == 0) continue;\n    for (int g = 0; g < num_kv_heads",
+     "    if (L == 0) L = 1;\n    for (int g = 0; g < num_kv_heads"),
     ("validate_skips_upper_bound", "indices[i] >= num_total_pages", "indices[i] > num_total_pages"),
 ]
 
