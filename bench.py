@@ -161,6 +161,35 @@ def per_call_times(step, n, dev, flush):
     return out
 
 
+def time_append(p, d, dev, steps, warmup):
+    """The decode-time KV append of one new token per request, in place in the
+    device store d: µs per call and algorithmic GB/s (new rows read and
+    written, page-table words read)."""
+    es = W.ELEM_BYTES[p.dtype]
+    g = torch.Generator(device="cpu").manual_seed(5)
+    shape = (p.batch, p.num_kv_heads, p.head_dim)
+    k_new = torch.randn(shape, generator=g).to(W.TORCH_DTYPES[p.dtype]).to(dev)
+    v_new = torch.randn(shape, generator=g).to(W.TORCH_DTYPES[p.dtype]).to(dev)
+
+    def call():
+        fad.append_paged(k_new, v_new, d["k"], d["v"], d["ind"], d["ptr"], d["lpl"],
+                         layout=p.layout)
+
+    for _ in range(warmup):
+        call()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(steps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / steps
+    nbytes = 2 * 2 * p.batch * p.num_kv_heads * p.head_dim * es + 4 * (3 * p.batch + 1)
+    return {"us_per_call": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 2),
+            "algorithmic_bytes_per_call": nbytes}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,6 +198,8 @@ def main():
     ap.add_argument("--workload", default="c3", choices=sorted(W.FULL))
     ap.add_argument("--layout", default="hnd", choices=["hnd", "nhd"],
                     help="K/V storage: heads-major (default) or token-major")
+    ap.add_argument("--append", action="store_true",
+                    help="also time the decode-time KV append (paged workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe", action="store_true",
                     help="also measure the read probe and a device copy for context")
@@ -282,6 +313,9 @@ def main():
                      "kernel_us": round(kernel_ms * 1e3, 2),
                      "kernel": "decode attention with fused split merge (fa::decode_*_kernel)"},
     }
+    if args.append and not isinstance(p, W.ContigProblem):
+        line["append"] = time_append(p, {"k": k, "v": v, "ind": ind, "ptr": ptr, "lpl": lpl},
+                                     dev, args.steps, args.warmup)
     line["per_call"] = per_call
     if per_call_cold:
         line["per_call_flushed"] = per_call_cold

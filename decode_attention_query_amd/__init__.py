@@ -15,7 +15,7 @@ from ._binding import (CODE_TORCH_DTYPES, DTYPE_CODES, EXPORTED, FA_DTYPE_BF16, 
                        fa_debug_read_probe, fa_debug_schedule, fa_debug_timing_enable,
                        fa_debug_timing_read, fa_decode_contig, fa_decode_contig_nhd,
                        fa_decode_paged, fa_decode_paged_nhd, fa_decode_workspace_size,
-                       fa_status_string, load_library)
+                       fa_append_paged, fa_append_paged_nhd, fa_status_string, load_library)
 
 
 def _code(t):
@@ -83,3 +83,24 @@ def decode_contig(q, k_cache, v_cache, valid_kv_len, scale, o=None, lse=None, wo
     fn(_code(q), hq, hkv, d, max_kv_len, valid_kv_len, scale, q, k_cache, v_cache, o, lse,
        workspace, stream)
     return o, lse
+
+
+def append_paged(k_new, v_new, k_data, v_data, indices, indptr, last_page_len, stream=None,
+                 layout="hnd"):
+    """Writes request b's new K/V rows (k_new, v_new [B, Hkv, D]) at its last
+    valid row, in place in k_data / v_data ([pages, Hkv, P, D]; layout "nhd":
+    [pages, P, Hkv, D]).  The page table must already count the new token."""
+    batch, hkv, d = k_new.shape
+    if layout == "nhd":
+        pages, page_size, hkv2, d2 = k_data.shape
+    elif layout == "hnd":
+        pages, hkv2, page_size, d2 = k_data.shape
+    else:
+        raise ValueError(f"unknown layout {layout!r}")
+    if (hkv2, d2) != (hkv, d) or tuple(v_data.shape) != tuple(k_data.shape) or \
+            tuple(v_new.shape) != tuple(k_new.shape):
+        raise ValueError("k_new, v_new, k_data and v_data disagree on shape")
+    used = indices.numel()
+    fn = fa_append_paged_nhd if layout == "nhd" else fa_append_paged
+    fn(_code(k_new), batch, hkv, d, page_size, pages, used, k_new, v_new,
+       indices if used else None, indptr, last_page_len, k_data, v_data, stream)

@@ -28,7 +28,8 @@ STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_INVALID_PROBLEM", 2: "FA_ERR_UNSUPPORTED"
 
 # every symbol the public headers declare
 EXPORTED = ("fa_decode_workspace_size", "fa_decode_contig", "fa_decode_paged",
-            "fa_decode_contig_nhd", "fa_decode_paged_nhd", "fa_status_string",
+            "fa_decode_contig_nhd", "fa_decode_paged_nhd", "fa_append_paged",
+            "fa_append_paged_nhd", "fa_status_string",
             "fa_debug_gather_paged", "fa_debug_gather_paged_nhd", "fa_debug_timing_enable",
             "fa_debug_timing_read", "fa_debug_plan", "fa_debug_schedule",
             "fa_debug_read_probe")
@@ -69,6 +70,10 @@ def load_library():
         getattr(lib, name).restype = _I
     lib.fa_status_string.argtypes = [_I]
     lib.fa_status_string.restype = ctypes.c_char_p
+    for name in ("fa_append_paged", "fa_append_paged_nhd"):
+        getattr(lib, name).argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P,
+                                       _P]
+        getattr(lib, name).restype = _I
     for name in ("fa_debug_gather_paged", "fa_debug_gather_paged_nhd"):
         getattr(lib, name).argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I64,
                                        _P, _SZ, _P]
@@ -287,6 +292,49 @@ def fa_debug_read_probe(buf, sink, stream=None):
         raise ValueError("sink must be an int32 device tensor")
     _check("fa_debug_read_probe", lib.fa_debug_read_probe(
         buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), _stream(stream)))
+
+
+def _append(fn, dtype, batch, num_kv_heads, head_dim, page_size, num_total_pages,
+            total_used_pages, k_new, v_new, indices, indptr, last_page_len, k_data, v_data,
+            stream):
+    lib = load_library()
+    call = getattr(lib, fn)
+    tdt = CODE_TORCH_DTYPES.get(dtype)
+    if tdt is None:
+        _check(fn, call(dtype, batch, num_kv_heads, head_dim, page_size, num_total_pages,
+                        total_used_pages, *([None] * 7), None))
+    rows = batch * num_kv_heads * head_dim
+    pool = num_total_pages * num_kv_heads * page_size * head_dim
+    args = (
+        _dev_buf(k_new, "k_new", rows, tdt),
+        _dev_buf(v_new, "v_new", rows, tdt),
+        _dev_buf(indices, "indices", total_used_pages, torch.int32,
+                 allow_none=total_used_pages == 0),
+        _dev_buf(indptr, "indptr", batch + 1, torch.int32),
+        _dev_buf(last_page_len, "last_page_len", batch, torch.int32),
+        _dev_buf(k_data, "k_data", pool, tdt),
+        _dev_buf(v_data, "v_data", pool, tdt),
+    )
+    _check(fn, call(dtype, batch, num_kv_heads, head_dim, page_size, num_total_pages,
+                    total_used_pages, *args, _stream(stream)))
+
+
+def fa_append_paged(dtype, batch, num_kv_heads, head_dim, page_size, num_total_pages,
+                    total_used_pages, k_new, v_new, indices, indptr, last_page_len, k_data,
+                    v_data, stream=None):
+    """k_data, v_data [pages, Hkv, P, D] (heads-major), updated in place."""
+    _append("fa_append_paged", dtype, batch, num_kv_heads, head_dim, page_size,
+            num_total_pages, total_used_pages, k_new, v_new, indices, indptr, last_page_len,
+            k_data, v_data, stream)
+
+
+def fa_append_paged_nhd(dtype, batch, num_kv_heads, head_dim, page_size, num_total_pages,
+                        total_used_pages, k_new, v_new, indices, indptr, last_page_len, k_data,
+                        v_data, stream=None):
+    """k_data, v_data [pages, P, Hkv, D] (token-major), updated in place."""
+    _append("fa_append_paged_nhd", dtype, batch, num_kv_heads, head_dim, page_size,
+            num_total_pages, total_used_pages, k_new, v_new, indices, indptr, last_page_len,
+            k_data, v_data, stream)
 
 
 def fa_status_string(status):

@@ -379,9 +379,62 @@ fa_status_t decode_paged(int nhd, fa_dtype_t dtype, int batch, int num_qo_heads,
   return FA_OK;
 }
 
+fa_status_t append_paged(int nhd, fa_dtype_t dtype, int batch, int num_kv_heads, int head_dim,
+                         int page_size, int num_total_pages, int total_used_pages,
+                         const void *k_new, const void *v_new, const int32_t *indices,
+                         const int32_t *indptr, const int32_t *last_page_len, void *k_data,
+                         void *v_data, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return FA_ERR_UNSUPPORTED;
+  if (!extents_ok(batch, num_kv_heads, num_kv_heads, page_size) || num_total_pages <= 0)
+    return FA_ERR_INVALID_PROBLEM;
+  if (!head_dim_ok(head_dim)) return FA_ERR_UNSUPPORTED;
+  if (total_used_pages < 0) return FA_ERR_INVALID_PROBLEM;
+  if (!k_new || !v_new || !indptr || !last_page_len || !k_data || !v_data ||
+      (!indices && total_used_pages > 0))
+    return FA_ERR_INVALID_PROBLEM;
+  if (int64_t(total_used_pages) * page_size >= (int64_t(1) << 31)) return FA_ERR_UNSUPPORTED;
+  if (!pool_size_ok(num_total_pages, num_kv_heads, page_size, head_dim))
+    return FA_ERR_UNSUPPORTED;
+  if (int64_t(batch) * num_kv_heads >= (int64_t(1) << 31)) return FA_ERR_UNSUPPORTED;
+  const HostPlan hp = make_plan(dtype, batch, num_kv_heads, num_kv_heads, head_dim, page_size,
+                                total_used_pages, false);
+  DecodeParams p = base_params(batch, num_kv_heads, num_kv_heads, head_dim, page_size,
+                               num_total_pages, total_used_pages, 1.0f, hp);
+  p.indices = indices;
+  p.indptr = indptr;
+  p.last_page_len = last_page_len;
+  p.nhd = nhd;
+  const int elem = dtype == FA_DTYPE_F32 ? 4 : 2;
+  hipLaunchKernelGGL(fa::append_kernel, dim3(unsigned(batch) * unsigned(num_kv_heads)),
+                     dim3(64), 0, stream, p, static_cast<const char *>(k_new),
+                     static_cast<const char *>(v_new), static_cast<char *>(k_data),
+                     static_cast<char *>(v_data), elem);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
+
+fa_status_t fa_append_paged(fa_dtype_t dtype, int batch, int num_kv_heads, int head_dim,
+                            int page_size, int num_total_pages, int total_used_pages,
+                            const void *k_new, const void *v_new, const int32_t *indices,
+                            const int32_t *indptr, const int32_t *last_page_len, void *k_data,
+                            void *v_data, hipStream_t stream) {
+  return append_paged(0, dtype, batch, num_kv_heads, head_dim, page_size, num_total_pages,
+                      total_used_pages, k_new, v_new, indices, indptr, last_page_len, k_data,
+                      v_data, stream);
+}
+
+fa_status_t fa_append_paged_nhd(fa_dtype_t dtype, int batch, int num_kv_heads, int head_dim,
+                                int page_size, int num_total_pages, int total_used_pages,
+                                const void *k_new, const void *v_new, const int32_t *indices,
+                                const int32_t *indptr, const int32_t *last_page_len,
+                                void *k_data, void *v_data, hipStream_t stream) {
+  return append_paged(1, dtype, batch, num_kv_heads, head_dim, page_size, num_total_pages,
+                      total_used_pages, k_new, v_new, indices, indptr, last_page_len, k_data,
+                      v_data, stream);
+}
 
 fa_status_t fa_decode_contig(fa_dtype_t dtype, int num_qo_heads, int num_kv_heads,
                              int head_dim, int max_kv_len, int valid_kv_len, float scale,

@@ -542,6 +542,31 @@ __global__ __launch_bounds__(256) void schedule_kernel(const DecodeParams p, int
   o[7] = 0;
 }
 
+// -------------------------------------------------------------- KV append
+//
+// Decode-time append (baracuda-kernels 0.0.1-alpha.68, batch_paged_decode.rs,
+// module doc "Companion plans": the new K/V slices are written into the paged
+// store before decode).  The page table passed in already counts the new
+// token, so request b's new row is its last valid row L_b - 1; L_b = 0 writes
+// nothing.  One 64-lane workgroup per (request, KV head), 16 bytes per lane
+// (a row is 128 to 1024 bytes).  Page ids are clamped like every other read of
+// the table, so a broken table cannot send a write outside the K/V buffers.
+__global__ __launch_bounds__(64) void append_kernel(const DecodeParams p, const char *k_new,
+                                                    const char *v_new, char *k_data,
+                                                    char *v_data, int elem_bytes) {
+  const int b = blockIdx.x / p.num_kv_heads;
+  const int g = blockIdx.x - b * p.num_kv_heads;
+  const Request r = request_of(p, b);
+  if (r.L == 0) return;
+  const int row_bytes = p.head_dim * elem_bytes;
+  const int64_t dst = kv_row_offset(p, r.p0, g, r.L - 1) * elem_bytes;
+  const int64_t src = ((int64_t)b * p.num_kv_heads + g) * row_bytes;
+  for (int i = threadIdx.x * 16; i < row_bytes; i += 64 * 16) {
+    *reinterpret_cast<uint4 *>(k_data + dst + i) = *reinterpret_cast<const uint4 *>(k_new + src + i);
+    *reinterpret_cast<uint4 *>(v_data + dst + i) = *reinterpret_cast<const uint4 *>(v_new + src + i);
+  }
+}
+
 // ------------------------------------------------------------- read probe
 //
 // Measurement only: streams a buffer of whole 8 KiB blocks with the decode

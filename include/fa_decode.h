@@ -193,6 +193,50 @@ fa_status_t fa_decode_paged_nhd(fa_dtype_t dtype, int batch, int num_qo_heads,
                                 const int32_t *last_page_len, void *o, float *lse,
                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Decode-time KV append (baracuda-kernels page, module doc "Companion plans":
+ * the new K/V slices are written into the paged store before decode; the page
+ * names the plan but prints no signature).  Writes one new K row and one new V
+ * row per request:
+ *
+ *   k_new, v_new      [batch, Hkv, D]  T   the new token's K and V, per request
+ *   k_data, v_data    the paged store, [num_total_pages, Hkv, page_size, D]
+ *                     (fa_append_paged) or [num_total_pages, page_size, Hkv, D]
+ *                     (fa_append_paged_nhd); updated in place
+ *   indices, indptr, last_page_len   the page table AFTER the caller's
+ *                     allocator has made room for the new token: request b's
+ *                     row goes to its last valid row L_b - 1 (in the
+ *                     second-to-last page when last_page_len[b] = 0); a request
+ *                     with L_b = 0 receives nothing
+ *
+ * Nothing else in the store changes.  A table that gives two requests the same
+ * page, or breaks the contract of fa_decode_paged, gives unspecified contents
+ * but never a write outside k_data / v_data.  k_new and v_new must not overlap
+ * the store.  No workspace.  Asynchronous on stream, so a following decode
+ * call on the same stream sees the new rows.
+ *
+ * Checks, in order:
+ *   dtype not one of fa_dtype_t                                -> FA_ERR_UNSUPPORTED
+ *   batch, Hkv, page_size or num_total_pages <= 0              -> FA_ERR_INVALID_PROBLEM
+ *   head_dim not 64, 128 or 256                                -> FA_ERR_UNSUPPORTED
+ *   total_used_pages < 0                                       -> FA_ERR_INVALID_PROBLEM
+ *   k_new, v_new, indptr, last_page_len, k_data or v_data NULL,
+ *     or indices NULL with total_used_pages > 0                -> FA_ERR_INVALID_PROBLEM
+ *   total_used_pages * page_size >= 2^31                       -> FA_ERR_UNSUPPORTED
+ *   num_total_pages * Hkv * page_size * D >= 10^15 elements    -> FA_ERR_UNSUPPORTED
+ *   batch * Hkv >= 2^31                                        -> FA_ERR_UNSUPPORTED
+ *   a kernel launch fails                                      -> FA_ERR_LAUNCH */
+fa_status_t fa_append_paged(fa_dtype_t dtype, int batch, int num_kv_heads, int head_dim,
+                            int page_size, int num_total_pages, int total_used_pages,
+                            const void *k_new, const void *v_new, const int32_t *indices,
+                            const int32_t *indptr, const int32_t *last_page_len, void *k_data,
+                            void *v_data, hipStream_t stream);
+
+fa_status_t fa_append_paged_nhd(fa_dtype_t dtype, int batch, int num_kv_heads, int head_dim,
+                                int page_size, int num_total_pages, int total_used_pages,
+                                const void *k_new, const void *v_new, const int32_t *indices,
+                                const int32_t *indptr, const int32_t *last_page_len,
+                                void *k_data, void *v_data, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *fa_status_string(fa_status_t status);
 

@@ -172,6 +172,23 @@ def test_gather_rejects(fn):
     assert gather(*bad, 10, FAKE, 1 << 30, None) == UNS
 
 
+@pytest.mark.parametrize("fn", ["fa_append_paged", "fa_append_paged_nhd"])
+def test_append_rejects(fn):
+    append = getattr(fad.load_library(), fn)
+    ok = [2, 2, 2, 128, 16, 10, 4]
+    ptrs = [FAKE] * 7
+    assert append(7, *ok[1:], *ptrs, None) == UNS
+    assert append(2, 0, *ok[2:], *ptrs, None) == INV
+    assert append(2, 2, 2, 96, *ok[4:], *ptrs, None) == UNS
+    assert append(2, 2, 2, 128, 16, 0, 4, *ptrs, None) == INV
+    assert append(2, 2, 2, 128, 16, 10, -1, *ptrs, None) == INV
+    for i in range(7):
+        bad = list(ptrs)
+        bad[i] = None
+        assert append(*ok, *bad, None) == INV, i
+    assert append(2, 2, 2, 128, 1 << 20, 1 << 11, 1 << 11, *ptrs, None) == UNS
+
+
 def test_schedule_and_probe_reject():
     lib = fad.load_library()
     base = [2, 2, 8, 2, 128, 16, 4]
