@@ -253,46 +253,79 @@ __device__ inline float coherent_load(const float *ptr) {
 //   o = sum_s 2^(lse_s - M) o_s / W,  lse = (M + log2 W) * ln 2,
 // with s running over the request's units in order (one wave per head for M
 // and W, fixed butterfly order), so the result is reproducible bit for bit.
+//
+// Latency: the merge runs at the very end of one workgroup per (request, head
+// block), so it is kept to few dependent memory round trips.  A request of up
+// to 64 units reads each lse once (one per lane); the weights 2^(lse_s - M) of
+// up to `cap` units at a time are staged in LDS (s_w, the kernel's tile area,
+// free by now), so the output loop issues only its partial-output loads, 16
+// in flight per thread.
 template <class E>
 __device__ void merge_partials(const DecodeParams &p, int b, int u0, int n, int h0, int gt, int nw,
-                               float *s_stat /* LDS [32] */) {
+                               float *s_stat /* LDS [32] */, float *s_w, int w_cap) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
+  const int nthreads = nw * kWave;
   const int hq = p.num_qo_heads;
+  const float *lse_base = p.part_lse + (int64_t)u0 * hq + h0;
   for (int g = wave; g < gt; g += nw) {
-    float mx = -INFINITY;
-    for (int s = lane; s < n; s += kWave) mx = fmaxf(mx, coherent_load(p.part_lse + (int64_t)(u0 + s) * hq + h0 + g));
-    mx = wave_max(mx);
-    const float ref = safe_ref(mx);
-    float w = 0.0f;
-    for (int s = lane; s < n; s += kWave)
-      w += fast_exp2(coherent_load(p.part_lse + (int64_t)(u0 + s) * hq + h0 + g) - ref);
-    w = wave_sum(w);
+    float mx, w;
+    if (n <= kWave) {
+      const float v = lane < n ? coherent_load(lse_base + (int64_t)lane * hq + g) : -INFINITY;
+      mx = wave_max(v);
+      w = wave_sum(lane < n ? fast_exp2(v - safe_ref(mx)) : 0.0f);
+    } else {
+      mx = -INFINITY;
+      for (int s = lane; s < n; s += kWave) mx = fmaxf(mx, coherent_load(lse_base + (int64_t)s * hq + g));
+      mx = wave_max(mx);
+      const float ref = safe_ref(mx);
+      w = 0.0f;
+      for (int s = lane; s < n; s += kWave) w += fast_exp2(coherent_load(lse_base + (int64_t)s * hq + g) - ref);
+      w = wave_sum(w);
+    }
     if (lane == 0) {
       s_stat[g] = mx;
       s_stat[16 + g] = w;
     }
   }
-  __syncthreads();
   const int D = p.head_dim;
-  for (int idx = tid; idx < gt * D; idx += nw * kWave) {
-    const int g = idx / D;
-    const int d = idx % D;
+  const int cap = max(1, w_cap / gt);  // units whose weights fit s_w at once
+  // uniform trip counts: every thread reaches every barrier
+  for (int base = 0; base < gt * D; base += nthreads) {
+    const int idx = base + tid;
+    const bool live = idx < gt * D;
+    const int g = live ? idx / D : 0;
+    const int d = idx - g * D;
     const int h = h0 + g;
-    const float mx = s_stat[g];
-    const float W = s_stat[16 + g];
-    const float ref = safe_ref(mx);
     float a = 0.0f;
-#pragma unroll 8
-    for (int s = 0; s < n; ++s) {
-      const int64_t row = (int64_t)(u0 + s) * hq + h;
-      a = fmaf(fast_exp2(coherent_load(p.part_lse + row) - ref), coherent_load(p.part_o + row * D + d), a);
+    for (int s0 = 0; s0 < n; s0 += cap) {
+      const int cn = min(cap, n - s0);
+      if (base == 0 || n > cap) {  // stage the weights of units s0 .. s0 + cn
+        __syncthreads();           // s_stat written; earlier weights no longer read
+        for (int i = tid; i < cn * gt; i += nthreads) {
+          const int s = i / gt;
+          const int gg = i - s * gt;
+          s_w[i] = fast_exp2(coherent_load(lse_base + (int64_t)(s0 + s) * hq + gg) -
+                             safe_ref(s_stat[gg]));
+        }
+        __syncthreads();
+      }
+      if (live) {
+        const float *o_base = p.part_o + ((int64_t)(u0 + s0) * hq + h) * D + d;
+#pragma unroll 16
+        for (int s = 0; s < cn; ++s)
+          a = fmaf(s_w[s * gt + g], coherent_load(o_base + (int64_t)s * hq * D), a);
+      }
     }
-    const bool any = W > 0.0f;
-    const int64_t orow = (int64_t)b * hq + h;
-    static_cast<typename E::raw *>(p.o)[orow * D + d] = E::narrow(any ? a / W : 0.0f);
-    if (d == 0 && p.lse) p.lse[orow] = any ? (mx + fast_log2(W)) * kLn2 : -INFINITY;
+    if (live) {
+      const float mx = s_stat[g];
+      const float W = s_stat[16 + g];
+      const bool any = W > 0.0f;
+      const int64_t orow = (int64_t)b * hq + h;
+      static_cast<typename E::raw *>(p.o)[orow * D + d] = E::narrow(any ? a / W : 0.0f);
+      if (d == 0 && p.lse) p.lse[orow] = any ? (mx + fast_log2(W)) * kLn2 : -INFINITY;
+    }
   }
 }
 
@@ -307,39 +340,50 @@ __device__ void merge_partials(const DecodeParams &p, int b, int u0, int n, int 
 // write-back or invalidate (what a device-scope fence would emit, once per
 // workgroup) is needed, because no non-coherent data crosses workgroups.
 //
-// The counter holds (call tag << kCountBits) | units counted.  A compare-and-
-// swap counts the unit in: a counter whose tag is not this call's counts as
-// zero.  The loop ends: each failed swap means another unit of this request
-// was counted, and there are fewer than n_units of those.  The merging
-// workgroup leaves the counter at (tag, 0), so replaying the same launch (a
-// captured graph) also starts from zero.
+// The counter holds (call tag << kCountBits) | units counted.  A unit counts
+// in with one atomic add; the add also returns the tag, and a tag that is not
+// this call's marks a stale counter (left by an earlier call, or never
+// written).  Then the unit installs (this call's tag, 0) with compare-and-swap
+// -- unless another unit already did -- and adds again.  Adds made to the
+// stale value vanish with it, but every unit that made one saw the stale tag
+// and adds again after the install, so each unit is counted once.  The swap
+// loop ends: a failed swap means another unit added to the stale value (fewer
+// than n_units can) or installed the tag (which ends the loop).  Units of one
+// request that finish together thus cost one add each, not a queue of
+// swaps.  The merging workgroup leaves the counter at (tag, 0), so replaying
+// the same launch (a captured graph) also starts from zero.
+__device__ inline bool count_in_is_last(const DecodeParams &p, unsigned long long *counter,
+                                        int n_units) {
+  const unsigned long long tag = p.call_tag;
+  unsigned long long old = atomicAdd(counter, 1ull);
+  if ((old >> kCountBits) != tag) {
+    unsigned long long seen = __hip_atomic_load(counter, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    while ((seen >> kCountBits) != tag) {
+      const unsigned long long prev = atomicCAS(counter, seen, tag << kCountBits);
+      if (prev == seen) break;
+      seen = prev;
+    }
+    old = atomicAdd(counter, 1ull);
+  }
+  return (old & ((1ull << kCountBits) - 1)) + 1 == (unsigned long long)n_units;
+}
+
 template <class E>
 __device__ void finish_split(const DecodeParams &p, const UnitInfo &u, int plane, int h0, int gt, int nw,
-                             float *s_stat, int *s_last) {
+                             float *s_stat, int *s_last, float *s_w, int w_cap) {
   if (u.n_units <= 1) return;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   unsigned long long *counter = reinterpret_cast<unsigned long long *>(
       p.arrivals + (int64_t)u.b * p.num_qo_heads + plane);
-  const unsigned long long mine = (unsigned long long)p.call_tag << kCountBits;
-  if (threadIdx.x == 0) {
-    unsigned long long seen = __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    while (true) {
-      const unsigned long long want =
-          ((seen >> kCountBits) == p.call_tag ? seen : mine) + 1;
-      const unsigned long long prev = atomicCAS(counter, seen, want);
-      if (prev == seen) {
-        *s_last = want - mine == (unsigned long long)u.n_units;
-        break;
-      }
-      seen = prev;
-    }
-  }
+  if (threadIdx.x == 0) *s_last = count_in_is_last(p, counter, u.n_units);
   __syncthreads();
   if (!*s_last) return;
   if (threadIdx.x == 0)
-    __hip_atomic_store(counter, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  merge_partials<E>(p, u.b, u.u0, u.n_units, h0, gt, nw, s_stat);
+    __hip_atomic_store(counter, (unsigned long long)p.call_tag << kCountBits, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  merge_partials<E>(p, u.b, u.u0, u.n_units, h0, gt, nw, s_stat, s_w, w_cap);
 }
 
 // ------------------------------------------------------ vector-ALU decode
@@ -515,7 +559,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   }
   __shared__ float s_stat[32];
   __shared__ int s_last;
-  finish_split<E>(p, u, blockIdx.y, h0, GT, NW, s_stat, &s_last);
+  finish_split<E>(p, u, blockIdx.y, h0, GT, NW, s_stat, &s_last, &s_acc[0][0][0],
+                  NW * GT * D);
 }
 
 // ---------------------------------------------------------- schedule hook

@@ -393,7 +393,8 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
     }
     emit<E>(p, u, h0 + g, d, Mx, lsum, a);
   }
-  finish_split<E>(p, u, plane, h0, gt, NW, s_stat, &s_last);
+  finish_split<E>(p, u, plane, h0, gt, NW, s_stat, &s_last, reinterpret_cast<float *>(lds),
+                  G::LDS / 4);
 }
 
 }  // namespace fa

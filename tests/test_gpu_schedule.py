@@ -180,3 +180,20 @@ def test_read_probe_runs(dev):
     assert int(sink.item()) == 0
     with pytest.raises(fad.FaError):
         fad.fa_debug_read_probe(buf[:100], sink)
+
+
+@pytest.mark.parametrize("dtype,d,hq,length", [("f32", 64, 8, 100_000),
+                                               ("bf16", 64, 16, 200_000),
+                                               ("f16", 128, 4, 20_000)])
+def test_many_unit_merge(dev, dtype, d, hq, length):
+    """Requests split into hundreds of units: the merge reads the lse in several
+    lane rounds and stages its weights in LDS in several chunks."""
+    p = W.make_contig("long", dtype, hq, 1, d, length + 7, length, seed=length)
+    chunk, bound, _, _ = fad.fa_debug_plan(fad.DTYPE_CODES[dtype], 1, hq, 1, d, length + 7, 1)
+    announce(f"many-unit merge {dtype} D{d} Hq{hq} L{length}: chunk {chunk}, "
+             f"{-(-length // chunk)} units")
+    assert -(-length // chunk) > 64
+    o, lse = run(p, to_dev(p, dev))
+    torch.cuda.synchronize()
+    ro, rl = oracle_of(p)
+    compare(dtype, o, lse, ro, rl, p.name)
