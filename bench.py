@@ -190,6 +190,31 @@ def time_append(p, d, dev, steps, warmup):
             "algorithmic_bytes_per_call": nbytes}
 
 
+def graph_call_time(step, n_calls, reps):
+    """Mean µs per call when n_calls calls are captured in one HIP graph and
+    the graph is replayed reps times (what a serving loop that captures its
+    decode step sees)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n_calls):
+            step()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (reps * n_calls)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -198,6 +223,9 @@ def main():
     ap.add_argument("--workload", default="c3", choices=sorted(W.FULL))
     ap.add_argument("--layout", default="hnd", choices=["hnd", "nhd"],
                     help="K/V storage: heads-major (default) or token-major")
+    ap.add_argument("--graph-calls", type=int, default=0,
+                    help="also time N calls captured in one HIP graph (no host or launch "
+                         "overhead between calls)")
     ap.add_argument("--append", action="store_true",
                     help="also time the decode-time KV append (paged workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -316,6 +344,10 @@ def main():
     if args.append and not isinstance(p, W.ContigProblem):
         line["append"] = time_append(p, {"k": k, "v": v, "ind": ind, "ptr": ptr, "lpl": lpl},
                                      dev, args.steps, args.warmup)
+    if args.graph_calls > 0:
+        us = graph_call_time(step, args.graph_calls, max(1, args.steps // args.graph_calls) + 4)
+        line["graph_per_call"] = {"calls_per_graph": args.graph_calls, "us_per_call": round(us, 2),
+                                  "GBps": round(nbytes / (us * 1e-6) / 1e9, 2)}
     line["per_call"] = per_call
     if per_call_cold:
         line["per_call_flushed"] = per_call_cold
