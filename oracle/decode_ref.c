@@ -36,6 +36,15 @@
  * Element decoding is exact: f32 is widened, bf16 is the high half of an f32,
  * f16 is decoded from its sign / exponent / mantissa fields by hand.
  *
+ * Two variants of the scores that the baracuda-kernels page lists as not
+ * supported by its plan (module doc "Constraints"), with the readings taken:
+ *   window > 0:  a sliding window -- the query, the request's newest token at
+ *                position L_b - 1, sees only the last `window` rows,
+ *                j >= L_b - window (0: every row);
+ *   softcap > 0: logits soft-capping -- each scaled score x_j becomes
+ *                softcap * tanh(x_j / softcap), and lse sums exp of the capped
+ *                scores (0: off).
+ *
  * Two K/V layouts (argument `layout`):
  *   OR_HND (0), heads-major: contiguous [Hkv, max_kv_len, D] (ferrum-kernels
  *     page, decode_attention argument list), paged [pages, Hkv, P, D]
@@ -175,12 +184,17 @@ int oracle_gather_paged(int dtype, int batch, int num_kv_heads, int head_dim,
 
 /* ------------------------------------------------------------ attention */
 
+/* First row a query sees among L rows under a sliding window (0: no window). */
+static int64_t window_start(int64_t L, int window) {
+  return (window > 0 && L > window) ? L - window : 0;
+}
+
 /* One query row against L explicit K/V rows given by element offsets into k and
  * v.  q_off is the element offset of the query row.  Two-pass softmax in f64.
  * o gets head_dim values; *lse the natural-log log-sum-exp. */
-static void attend_rows(int dtype, int head_dim, double scale, const void *q, int64_t q_off,
-                        const void *k, const void *v, const int64_t *row_off, int64_t L,
-                        double *x, double *o, double *lse) {
+static void attend_rows(int dtype, int head_dim, double scale, double softcap, const void *q,
+                        int64_t q_off, const void *k, const void *v, const int64_t *row_off,
+                        int64_t L, double *x, double *o, double *lse) {
   for (int d = 0; d < head_dim; ++d) o[d] = 0.0;
   if (L == 0) {
     *lse = -INFINITY;
@@ -192,6 +206,7 @@ static void attend_rows(int dtype, int head_dim, double scale, const void *q, in
     for (int d = 0; d < head_dim; ++d)
       dot += load_elem(dtype, q, q_off + d) * load_elem(dtype, k, row_off[j] + d);
     x[j] = scale * dot;
+    if (softcap > 0.0) x[j] = softcap * tanh(x[j] / softcap);
   }
   /* pass 1: max */
   double M = x[0];
@@ -218,10 +233,10 @@ int oracle_decode_paged(int dtype, int batch, int num_qo_heads, int num_kv_heads
                         const void *k, const void *v, const int32_t *indices,
                         const int32_t *indptr, const int32_t *last_page_len, int n_sample,
                         const int32_t *sample_b, const int32_t *sample_h, double *o,
-                        double *lse, int threads, int layout) {
+                        double *lse, int threads, int layout, int window, double softcap) {
   if (batch <= 0 || num_qo_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       page_size <= 0 || num_qo_heads % num_kv_heads != 0 ||
-      (layout != OR_HND && layout != OR_NHD))
+      (layout != OR_HND && layout != OR_NHD) || window < 0 || !(softcap >= 0.0))
     return OR_BAD_ARG;
   int group = num_qo_heads / num_kv_heads;
   int64_t n_items = n_sample > 0 ? n_sample : (int64_t)batch * num_qo_heads;
@@ -241,11 +256,12 @@ int oracle_decode_paged(int dtype, int batch, int num_qo_heads, int num_kv_heads
     if (!row_off || !x) {
       status = OR_NO_MEMORY;
     } else {
-      for (int64_t j = 0; j < L; ++j)
-        row_off[j] = paged_row_offset(layout, num_kv_heads, page_size, head_dim, indices,
-                                      indptr, b, g, j);
+      int64_t j0 = window_start(L, window);
+      for (int64_t j = j0; j < L; ++j)
+        row_off[j - j0] = paged_row_offset(layout, num_kv_heads, page_size, head_dim, indices,
+                                           indptr, b, g, j);
       int64_t q_off = ((int64_t)b * num_qo_heads + h) * head_dim;
-      attend_rows(dtype, head_dim, scale, q, q_off, k, v, row_off, L, x,
+      attend_rows(dtype, head_dim, scale, softcap, q, q_off, k, v, row_off, L - j0, x,
                   o + it * head_dim, lse + it);
     }
     free(row_off);
@@ -261,10 +277,10 @@ int oracle_decode_paged(int dtype, int batch, int num_qo_heads, int num_kv_heads
 int oracle_decode_contig(int dtype, int num_qo_heads, int num_kv_heads, int head_dim,
                          int max_kv_len, int valid_kv_len, double scale, const void *q,
                          const void *k, const void *v, double *o, double *lse,
-                         int threads, int layout) {
+                         int threads, int layout, int window, double softcap) {
   if (num_qo_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_kv_len < 0 ||
       valid_kv_len < 0 || valid_kv_len > max_kv_len || num_qo_heads % num_kv_heads != 0 ||
-      (layout != OR_HND && layout != OR_NHD))
+      (layout != OR_HND && layout != OR_NHD) || window < 0 || !(softcap >= 0.0))
     return OR_BAD_ARG;
   int group = num_qo_heads / num_kv_heads;
   int status = OR_OK;
@@ -280,10 +296,11 @@ int oracle_decode_contig(int dtype, int num_qo_heads, int num_kv_heads, int head
     if (!row_off || !x) {
       status = OR_NO_MEMORY;
     } else {
-      for (int64_t j = 0; j < L; ++j)
-        row_off[j] = contig_row_offset(layout, num_kv_heads, max_kv_len, head_dim, g, j);
-      attend_rows(dtype, head_dim, scale, q, (int64_t)h * head_dim, k, v, row_off, L, x,
-                  o + (int64_t)h * head_dim, lse + h);
+      int64_t j0 = window_start(L, window);
+      for (int64_t j = j0; j < L; ++j)
+        row_off[j - j0] = contig_row_offset(layout, num_kv_heads, max_kv_len, head_dim, g, j);
+      attend_rows(dtype, head_dim, scale, softcap, q, (int64_t)h * head_dim, k, v, row_off,
+                  L - j0, x, o + (int64_t)h * head_dim, lse + h);
     }
     free(row_off);
     free(x);

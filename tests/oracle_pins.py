@@ -478,6 +478,109 @@ def pin_append_completes_the_scatter():
                 (layout, dtype)
 
 
+# ------------------------------------------------- sliding window, soft-cap
+
+def pin_window_is_truncation():
+    """A sliding window of W rows equals plain attention over each request's
+    last W rows, laid out by the test itself, bit for bit (paged and
+    contiguous); W = 0 and W >= L change nothing; W = 1 gives the newest row."""
+    rng = np.random.default_rng(32)
+    for dtype in DTYPES:
+        hkv, group, d, page_size = 2, 3, 16, 4
+        lens = [0, 1, 5, 13, 31]
+        k_rows = [rand_t(rng, (L, hkv, d), dtype) for L in lens]
+        v_rows = [rand_t(rng, (L, hkv, d), dtype) for L in lens]
+        q = rand_t(rng, (len(lens), hkv * group, d), dtype)
+        p = _paged_problem(rng, dtype, lens, hkv, group, d, page_size, k_rows=k_rows,
+                           v_rows=v_rows, q=q)
+        full = _oracle_paged(p, 0.3)
+        args = (dtype, W.bits(p["q"]), W.bits(p["k_data"]), W.bits(p["v_data"]), p["indices"],
+                p["indptr"], p["last_page_len"], 0.3)
+        for win in (0, 1, 4, 13, 40):
+            got = O.decode_paged(*args, window=win)
+            cut = [(r[max(0, r.shape[0] - win):] if win else r) for r in k_rows]
+            cutv = [(r[max(0, r.shape[0] - win):] if win else r) for r in v_rows]
+            pt = _paged_problem(rng, dtype, [r.shape[0] for r in cut], hkv, group, d, page_size,
+                                k_rows=cut, v_rows=cutv, q=q)
+            want = _oracle_paged(pt, 0.3)
+            assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1]), \
+                (dtype, win)
+            if win == 0 or win >= max(lens):
+                assert np.array_equal(got[0], full[0]) and np.array_equal(got[1], full[1])
+            if win == 1:
+                for b, L in enumerate(lens):
+                    if L:
+                        for h in range(hkv * group):
+                            assert np.array_equal(got[0][b, h], f64(v_rows[b][L - 1, h // group]))
+        # contiguous: the window of a cache equals the cache of the window
+        L, win = 29, 7
+        rk, rv = rand_t(rng, (L, hkv, d), dtype), rand_t(rng, (L, hkv, d), dtype)
+        qc = rand_t(rng, (hkv * group, d), dtype)
+        got = O.decode_contig(dtype, W.bits(qc), W.bits(contig_from_rows(rk, 40)),
+                              W.bits(contig_from_rows(rv, 40)), L, 0.3, window=win)
+        want = O.decode_contig(dtype, W.bits(qc), W.bits(contig_from_rows(rk[L - win:], 40)),
+                               W.bits(contig_from_rows(rv[L - win:], 40)), win, 0.3)
+        assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1]), dtype
+
+
+def _mp_attend_capped(qrow, krows, vrows, scale, cap):
+    """50-digit evaluation with capped scores cap * tanh(x / cap)."""
+    mpmath.mp.dps = 50
+    w = []
+    for j in range(len(krows)):
+        x = mpmath.mpf(scale) * mpmath.fsum(mpmath.mpf(a) * mpmath.mpf(b)
+                                            for a, b in zip(qrow, krows[j]))
+        w.append(mpmath.e ** (mpmath.mpf(cap) * mpmath.tanh(x / mpmath.mpf(cap))))
+    z = mpmath.fsum(w)
+    o = [mpmath.fsum(w[j] * mpmath.mpf(vrows[j][d]) for j in range(len(krows))) / z
+         for d in range(len(qrow))]
+    return o, mpmath.log(z)
+
+
+def pin_softcap_mpmath():
+    """Capped scores against a 50-digit evaluation, on tiny requests, for caps
+    that bind hard (0.5), moderately (3) and barely (50)."""
+    rng = np.random.default_rng(33)
+    for cap in (0.5, 3.0, 50.0):
+        for dtype in DTYPES:
+            hkv, group, d = 2, 2, 4
+            lens = [1, 3, 6]
+            p = _paged_problem(rng, dtype, lens, hkv, group, d, 2)
+            scale = 1.7
+            o, lse = O.decode_paged(dtype, W.bits(p["q"]), W.bits(p["k_data"]),
+                                    W.bits(p["v_data"]), p["indices"], p["indptr"],
+                                    p["last_page_len"], scale, softcap=cap)
+            qf = f64(p["q"])
+            for b in range(len(lens)):
+                kf, vf = f64(p["k_rows"][b]), f64(p["v_rows"][b])
+                for h in range(hkv * group):
+                    mo, ml = _mp_attend_capped(qf[b, h], kf[:, h // group], vf[:, h // group],
+                                               scale, cap)
+                    for dd in range(d):
+                        assert abs(o[b, h, dd] - float(mo[dd])) <= 1e-13 * max(1, abs(float(mo[dd])))
+                    assert abs(lse[b, h] - float(ml)) <= 1e-13 * max(1.0, abs(float(ml)))
+
+
+def pin_softcap_identical_k_rows():
+    """Identical K rows stay equally weighted under the cap: o is the mean of
+    V and lse = cap * tanh(x / cap) + ln L."""
+    rng = np.random.default_rng(34)
+    hkv, group, d, L, cap = 1, 2, 32, 9, 2.0
+    k_row = rand_t(rng, (1, hkv, d), "f32")
+    k_rows = [k_row.expand(L, hkv, d).contiguous()]
+    p = _paged_problem(rng, "f32", [L], hkv, group, d, 4, k_rows=k_rows)
+    o, lse = O.decode_paged("f32", W.bits(p["q"]), W.bits(p["k_data"]), W.bits(p["v_data"]),
+                            p["indices"], p["indptr"], p["last_page_len"], 0.5, softcap=cap)
+    vf = f64(p["v_rows"][0])
+    qf, kf = f64(p["q"]), f64(k_row)
+    for h in range(group):
+        np.testing.assert_allclose(o[0, h], vf[:, 0].mean(axis=0), rtol=1e-13, atol=1e-15)
+        x = 0.5 * float(mpmath.fsum(mpmath.mpf(a) * mpmath.mpf(b)
+                                    for a, b in zip(qf[0, h], kf[0, 0])))
+        want = cap * math.tanh(x / cap) + math.log(L)
+        assert abs(lse[0, h] - want) <= 1e-13 * max(1.0, abs(want))
+
+
 def pin_seq_lens():
     """The oracle's L_b equals the row count the test scattered."""
     rng = np.random.default_rng(26)

@@ -54,6 +54,14 @@ MUTANTS = [
      "indptr,\n                                     b, g, L);"),
     ("append_to_empty_request", "    if (L == 0) continue;\n    for (int g = 0; g < num_kv_heads",
      "    if (L == 0) L = 1;\n    for (int g = 0; g < num_kv_heads"),
+    ("window_one_row_short", "(window > 0 && L > window) ? L - window : 0",
+     "(window > 0 && L > window) ? L - window + 1 : 0"),
+    ("softcap_scale_outside",
+     "if (softcap > 0.0) x[j] = softcap * tanh(x[j] / softcap);",
+     "if (softcap > 0.0) x[j] = scale * softcap * tanh(dot / softcap);"),
+    ("softcap_drops_outer_factor",
+     "if (softcap > 0.0) x[j] = softcap * tanh(x[j] / softcap);",
+     "if (softcap > 0.0) x[j] = tanh(x[j] / softcap);"),
     ("validate_skips_upper_bound", "indices[i] >= num_total_pages", "indices[i] > num_total_pages"),
 ]
 
