@@ -33,13 +33,17 @@ METRIC = "achieved HBM GB/s (% of peak) + µs/call, batched paged bf16 GQA decod
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 
 
-def algorithmic_bytes(p):
-    """Valid K/V rows + q + o + lse + page table, each counted once."""
+def algorithmic_bytes(p, window=0):
+    """Valid K/V rows (the last `window` of each request under a sliding
+    window) + q + o + lse + page table, each counted once."""
     es = W.ELEM_BYTES[p.dtype]
     if isinstance(p, W.ContigProblem):
-        kv = p.valid_kv_len * p.num_kv_heads * p.head_dim * es * 2
+        rows = min(p.valid_kv_len, window) if window else p.valid_kv_len
+        kv = rows * p.num_kv_heads * p.head_dim * es * 2
         return kv + 2 * p.num_qo_heads * p.head_dim * es + 4 * p.num_qo_heads
     lens = np.asarray(p.kv_lens, dtype=np.int64)
+    if window:
+        lens = np.minimum(lens, window)
     kv = int(lens.sum()) * p.num_kv_heads * p.head_dim * es * 2
     qo = 2 * p.batch * p.num_qo_heads * p.head_dim * es
     lse = 4 * p.batch * p.num_qo_heads
@@ -88,7 +92,7 @@ def describe(p):
             "sum_kv_len": int(lens.sum()), "max_kv_len": int(lens.max())}
 
 
-def cpu_baseline(p, nbytes, min_seconds=2.0, max_runs=5):
+def cpu_baseline(p, nbytes, window=0, softcap=0.0, min_seconds=2.0, max_runs=5):
     """The float64 oracle over the whole workload on this host's cores: whole
     calls repeated until min_seconds have passed (at most max_runs), median."""
     import oracle
@@ -98,11 +102,13 @@ def cpu_baseline(p, nbytes, min_seconds=2.0, max_runs=5):
         t0 = time.perf_counter()
         if isinstance(p, W.ContigProblem):
             oracle.decode_contig(p.dtype, W.bits(p.q), W.bits(p.k_cache), W.bits(p.v_cache),
-                                 p.valid_kv_len, p.scale, threads=threads, layout=p.layout)
+                                 p.valid_kv_len, p.scale, threads=threads, layout=p.layout,
+                                 window=window, softcap=softcap)
         else:
             oracle.decode_paged(p.dtype, W.bits(p.q), W.bits(p.k_data), W.bits(p.v_data),
                                 p.indices.numpy(), p.indptr.numpy(), p.last_page_len.numpy(),
-                                p.scale, threads=threads, layout=p.layout)
+                                p.scale, threads=threads, layout=p.layout, window=window,
+                                softcap=softcap)
         times.append(time.perf_counter() - t0)
     dt = float(np.median(times))
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
@@ -228,6 +234,10 @@ def main():
                          "overhead between calls)")
     ap.add_argument("--append", action="store_true",
                     help="also time the decode-time KV append (paged workloads)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window: attend only each request's last W rows (0: all)")
+    ap.add_argument("--softcap", type=float, default=0.0,
+                    help="logits soft-cap c: scores -> c * tanh(x / c) (0: off)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe", action="store_true",
                     help="also measure the read probe and a device copy for context")
@@ -251,7 +261,7 @@ def main():
         p = W.token_major(p)
     print(f"[bench] generated {p.name} in {time.perf_counter() - t0:.1f}s", file=sys.stderr,
           flush=True)
-    nbytes = algorithmic_bytes(p)
+    nbytes = algorithmic_bytes(p, args.window)
 
     if isinstance(p, W.ContigProblem):
         q, k, v = p.q.to(dev), p.k_cache.to(dev), p.v_cache.to(dev)
@@ -262,7 +272,7 @@ def main():
 
         def step():
             fad.decode_contig(q, k, v, p.valid_kv_len, p.scale, o=o, lse=lse, workspace=ws,
-                              layout=p.layout)
+                              layout=p.layout, window=args.window, softcap=args.softcap)
     else:
         q, k, v = p.q.to(dev), p.k_data.to(dev), p.v_data.to(dev)
         ind, ptr, lpl = p.indices.to(dev), p.indptr.to(dev), p.last_page_len.to(dev)
@@ -273,7 +283,7 @@ def main():
 
         def step():
             fad.decode_paged(q, k, v, ind, ptr, lpl, p.scale, o=o, lse=lse, workspace=ws,
-                             layout=p.layout)
+                             layout=p.layout, window=args.window, softcap=args.softcap)
 
     for _ in range(args.warmup):
         step()
@@ -330,7 +340,8 @@ def main():
         "vs_baseline": None,
         "dtype": p.dtype,
         "data": "synthetic (seeded N(0,1) values, seeded page tables; no dataset)",
-        "config": {**describe(p), "algorithmic_bytes_per_call": int(nbytes),
+        "config": {**describe(p), "window": args.window, "softcap": args.softcap,
+                   "algorithmic_bytes_per_call": int(nbytes),
                    "chunk_rows": chunk, "heads_per_workgroup": gt,
                    "attention_kernel": "valu" if kind == 0 else "mfma"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
@@ -355,7 +366,7 @@ def main():
         line["hbm_probe"] = hbm_probe(dev)
     if not args.no_cpu_baseline:
         print("[bench] timing the float64 oracle on the host", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(p, nbytes)
+        line["cpu_baseline"] = cpu_baseline(p, nbytes, args.window, args.softcap)
     print(json.dumps(line), flush=True)
 
 

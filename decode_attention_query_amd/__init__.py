@@ -15,7 +15,8 @@ from ._binding import (CODE_TORCH_DTYPES, DTYPE_CODES, EXPORTED, FA_DTYPE_BF16, 
                        fa_debug_read_probe, fa_debug_schedule, fa_debug_timing_enable,
                        fa_debug_timing_read, fa_decode_contig, fa_decode_contig_nhd,
                        fa_decode_paged, fa_decode_paged_nhd, fa_decode_workspace_size,
-                       fa_append_paged, fa_append_paged_nhd, fa_status_string, load_library)
+                       fa_append_paged, fa_append_paged_nhd, fa_status_string, load_library,
+                       DecodeOptions, fa_decode_paged_opts, fa_decode_contig_opts)
 
 
 def _code(t):
@@ -35,7 +36,7 @@ def workspace_paged(batch, num_qo_heads, num_kv_heads, head_dim, page_size, tota
 
 
 def decode_paged(q, k_data, v_data, indices, indptr, last_page_len, sm_scale, o=None, lse=None,
-                 workspace=None, stream=None, layout="hnd"):
+                 workspace=None, stream=None, layout="hnd", window=0, softcap=0.0):
     """q [B, Hq, D]; k_data/v_data [pages, Hkv, P, D] (layout "nhd": [pages, P, Hkv, D]);
     int32 page table.  Returns (o [B, Hq, D] in q's dtype, lse [B, Hq] f32)."""
     batch, hq, d = q.shape
@@ -54,14 +55,18 @@ def decode_paged(q, k_data, v_data, indices, indptr, last_page_len, sm_scale, o=
     used = indices.numel()
     if workspace is None:
         workspace = workspace_paged(batch, hq, hkv, d, page_size, used, q.device)
-    fn = fa_decode_paged_nhd if layout == "nhd" else fa_decode_paged
-    fn(_code(q), batch, hq, hkv, d, page_size, pages, used, sm_scale, q, k_data, v_data,
-       indices if used else None, indptr, last_page_len, o, lse, workspace, stream)
+    args = (_code(q), batch, hq, hkv, d, page_size, pages, used, sm_scale, q, k_data, v_data,
+            indices if used else None, indptr, last_page_len, o, lse, workspace, stream)
+    if window or softcap:
+        fa_decode_paged_opts(DecodeOptions(int(layout == "nhd"), int(window), float(softcap)),
+                             *args)
+    else:
+        (fa_decode_paged_nhd if layout == "nhd" else fa_decode_paged)(*args)
     return o, lse
 
 
 def decode_contig(q, k_cache, v_cache, valid_kv_len, scale, o=None, lse=None, workspace=None,
-                  stream=None, layout="hnd"):
+                  stream=None, layout="hnd", window=0, softcap=0.0):
     """q [Hq, D]; k_cache/v_cache [Hkv, max_kv_len, D] (layout "nhd": [max_kv_len, Hkv, D]).
     Returns (o [Hq, D] in q's dtype, lse [Hq] f32)."""
     hq, d = q.shape
@@ -79,9 +84,13 @@ def decode_contig(q, k_cache, v_cache, valid_kv_len, scale, o=None, lse=None, wo
         lse = torch.empty((hq,), dtype=torch.float32, device=q.device)
     if workspace is None:
         workspace = workspace_paged(1, hq, hkv, d, max_kv_len, 1, q.device)
-    fn = fa_decode_contig_nhd if layout == "nhd" else fa_decode_contig
-    fn(_code(q), hq, hkv, d, max_kv_len, valid_kv_len, scale, q, k_cache, v_cache, o, lse,
-       workspace, stream)
+    args = (_code(q), hq, hkv, d, max_kv_len, valid_kv_len, scale, q, k_cache, v_cache, o, lse,
+            workspace, stream)
+    if window or softcap:
+        fa_decode_contig_opts(DecodeOptions(int(layout == "nhd"), int(window), float(softcap)),
+                              *args)
+    else:
+        (fa_decode_contig_nhd if layout == "nhd" else fa_decode_contig)(*args)
     return o, lse
 
 

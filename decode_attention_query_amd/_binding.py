@@ -29,10 +29,18 @@ STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_INVALID_PROBLEM", 2: "FA_ERR_UNSUPPORTED"
 # every symbol the public headers declare
 EXPORTED = ("fa_decode_workspace_size", "fa_decode_contig", "fa_decode_paged",
             "fa_decode_contig_nhd", "fa_decode_paged_nhd", "fa_append_paged",
-            "fa_append_paged_nhd", "fa_status_string",
+            "fa_append_paged_nhd", "fa_decode_paged_opts", "fa_decode_contig_opts",
+            "fa_status_string",
             "fa_debug_gather_paged", "fa_debug_gather_paged_nhd", "fa_debug_timing_enable",
             "fa_debug_timing_read", "fa_debug_plan", "fa_debug_schedule",
             "fa_debug_read_probe")
+
+
+class DecodeOptions(ctypes.Structure):
+    """fa_decode_options_t: K/V layout (0 heads-major, 1 token-major), sliding
+    window (rows, 0 = off) and logits soft-cap (0 = off)."""
+    _fields_ = [("kv_layout", ctypes.c_int), ("window", ctypes.c_int),
+                ("logits_soft_cap", ctypes.c_float)]
 
 
 class FaError(RuntimeError):
@@ -70,6 +78,10 @@ def load_library():
         getattr(lib, name).restype = _I
     lib.fa_status_string.argtypes = [_I]
     lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_decode_contig_opts.argtypes = [_P] + list(lib.fa_decode_contig.argtypes)
+    lib.fa_decode_contig_opts.restype = _I
+    lib.fa_decode_paged_opts.argtypes = [_P] + list(lib.fa_decode_paged.argtypes)
+    lib.fa_decode_paged_opts.restype = _I
     for name in ("fa_append_paged", "fa_append_paged_nhd"):
         getattr(lib, name).argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P,
                                        _P]
@@ -146,9 +158,12 @@ def fa_decode_workspace_size(batch, num_qo_heads, num_kv_heads, head_dim, page_s
 
 
 def _contig(fn, dtype, num_qo_heads, num_kv_heads, head_dim, max_kv_len, valid_kv_len,
-            scale, q, k_cache, v_cache, o, lse, workspace, stream):
+            scale, q, k_cache, v_cache, o, lse, workspace, stream, opts=None):
     lib = load_library()
     call = getattr(lib, fn)
+    if opts is not None:
+        raw = call
+        call = lambda *a: raw(ctypes.byref(opts), *a)  # noqa: E731
     tdt = CODE_TORCH_DTYPES.get(dtype)
     if tdt is None:  # let the library report the unsupported dtype
         _check(fn, call(dtype, num_qo_heads, num_kv_heads, head_dim, max_kv_len, valid_kv_len,
@@ -182,9 +197,12 @@ def fa_decode_contig_nhd(dtype, num_qo_heads, num_kv_heads, head_dim, max_kv_len
 
 def _paged(fn, dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size, num_total_pages,
            total_used_pages, sm_scale, q, k_data, v_data, indices, indptr, last_page_len, o,
-           lse, workspace, stream):
+           lse, workspace, stream, opts=None):
     lib = load_library()
     call = getattr(lib, fn)
+    if opts is not None:
+        raw = call
+        call = lambda *a: raw(ctypes.byref(opts), *a)  # noqa: E731
     tdt = CODE_TORCH_DTYPES.get(dtype)
     if tdt is None:
         _check(fn, call(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
@@ -214,6 +232,23 @@ def fa_decode_paged(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_siz
     _paged("fa_decode_paged", dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
            num_total_pages, total_used_pages, sm_scale, q, k_data, v_data, indices, indptr,
            last_page_len, o, lse, workspace, stream)
+
+
+def fa_decode_paged_opts(opts, dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                         num_total_pages, total_used_pages, sm_scale, q, k_data, v_data,
+                         indices, indptr, last_page_len, o, lse, workspace, stream=None):
+    """opts: DecodeOptions (layout, window, soft-cap)."""
+    _paged("fa_decode_paged_opts", dtype, batch, num_qo_heads, num_kv_heads, head_dim,
+           page_size, num_total_pages, total_used_pages, sm_scale, q, k_data, v_data, indices,
+           indptr, last_page_len, o, lse, workspace, stream, opts=opts)
+
+
+def fa_decode_contig_opts(opts, dtype, num_qo_heads, num_kv_heads, head_dim, max_kv_len,
+                          valid_kv_len, scale, q, k_cache, v_cache, o, lse, workspace,
+                          stream=None):
+    """opts: DecodeOptions (layout, window, soft-cap)."""
+    _contig("fa_decode_contig_opts", dtype, num_qo_heads, num_kv_heads, head_dim, max_kv_len,
+            valid_kv_len, scale, q, k_cache, v_cache, o, lse, workspace, stream, opts=opts)
 
 
 def fa_decode_paged_nhd(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,

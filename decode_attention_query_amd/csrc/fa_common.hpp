@@ -68,7 +68,13 @@ struct DecodeParams {
   int nhd;            // 1: token-major K/V ([.., P, Hkv, D]); 0: heads-major ([.., Hkv, P, D])
   int uniform_blocks; // 1: every 16-row block starting at a multiple of 16 lies in one page
   int contig_len;     // contiguous: valid_kv_len
-  int contig_units;   // contiguous: ceil(valid_kv_len / chunk), at least 1
+  int contig_units;   // contiguous: units over rows [contig_lo, valid_kv_len), at least 1
+  int contig_start;   // contiguous: first row the query attends (sliding window)
+  int contig_lo;      // contiguous: contig_start rounded down to a multiple of 16
+  // score variants
+  int window;         // > 0: the query attends only each request's last `window` rows
+  float softcap2;     // > 0: base-2 scores x -> softcap2 * tanh(x / softcap2) (cap * log2 e)
+  float softcap2_inv; // 1 / softcap2
   // workspace regions
   float *part_lse;        // [units_bound, Hq]     base-2 lse of each split's partial
   float *part_o;          // [units_bound, Hq, D]  normalised partial outputs

@@ -287,10 +287,39 @@ size_t fa_decode_workspace_size(int batch, int num_qo_heads, int num_kv_heads, i
 
 namespace {
 
-fa_status_t decode_contig(int nhd, fa_dtype_t dtype, int num_qo_heads, int num_kv_heads,
-                          int head_dim, int max_kv_len, int valid_kv_len, float scale,
-                          const void *q, const void *k_cache, const void *v_cache, void *o,
-                          float *lse, void *workspace, size_t workspace_bytes,
+// Layout and score variants of one call (fa_decode_options_t, validated).
+struct Variant {
+  int nhd = 0;
+  int window = 0;
+  float softcap = 0.0f;
+};
+
+// FA_OK, or why opts is rejected; fills v.
+fa_status_t read_options(const fa_decode_options_t *opts, Variant &v) {
+  if (!opts) return FA_OK;
+  if (opts->kv_layout != 0 && opts->kv_layout != 1) return FA_ERR_UNSUPPORTED;
+  if (opts->window < 0 || !(opts->logits_soft_cap >= 0.0f) ||
+      !std::isfinite(opts->logits_soft_cap))
+    return FA_ERR_INVALID_PROBLEM;
+  v.nhd = opts->kv_layout;
+  v.window = opts->window;
+  v.softcap = opts->logits_soft_cap;
+  return FA_OK;
+}
+
+void apply_variant(DecodeParams &p, const Variant &v) {
+  p.nhd = v.nhd;
+  p.window = v.window;
+  if (v.softcap > 0.0f) {
+    p.softcap2 = v.softcap * fa::kLog2e;  // capping commutes with the base-2 scale
+    p.softcap2_inv = 1.0f / p.softcap2;
+  }
+}
+
+fa_status_t decode_contig(const Variant &var, fa_dtype_t dtype, int num_qo_heads,
+                          int num_kv_heads, int head_dim, int max_kv_len, int valid_kv_len,
+                          float scale, const void *q, const void *k_cache, const void *v_cache,
+                          void *o, float *lse, void *workspace, size_t workspace_bytes,
                           hipStream_t stream) {
   if (!dtype_ok(dtype)) return FA_ERR_UNSUPPORTED;
   if (!extents_ok(1, num_qo_heads, num_kv_heads, max_kv_len)) return FA_ERR_INVALID_PROBLEM;
@@ -315,11 +344,14 @@ fa_status_t decode_contig(int nhd, fa_dtype_t dtype, int num_qo_heads, int num_k
   p.o = o;
   p.lse = lse;
   p.contig = 1;
-  p.nhd = nhd;
+  apply_variant(p, var);
   p.uniform_blocks = 1;
   p.contig_len = valid_kv_len;
-  p.contig_units =
-      valid_kv_len == 0 ? 1 : int((int64_t(valid_kv_len) + hp.chunk - 1) / hp.chunk);
+  p.contig_start =
+      (var.window > 0 && valid_kv_len > var.window) ? valid_kv_len - var.window : 0;
+  p.contig_lo = p.contig_start & ~15;
+  const int rows = valid_kv_len - p.contig_lo;
+  p.contig_units = rows == 0 ? 1 : int((int64_t(rows) + hp.chunk - 1) / hp.chunk);
   carve(p, hp, workspace);
   p.call_tag = next_call_tag();
 
@@ -331,7 +363,7 @@ fa_status_t decode_contig(int nhd, fa_dtype_t dtype, int num_qo_heads, int num_k
   return FA_OK;
 }
 
-fa_status_t decode_paged(int nhd, fa_dtype_t dtype, int batch, int num_qo_heads,
+fa_status_t decode_paged(const Variant &var, fa_dtype_t dtype, int batch, int num_qo_heads,
                          int num_kv_heads, int head_dim, int page_size, int num_total_pages,
                          int total_used_pages, float sm_scale, const void *q,
                          const void *k_data, const void *v_data, const int32_t *indices,
@@ -367,7 +399,7 @@ fa_status_t decode_paged(int nhd, fa_dtype_t dtype, int batch, int num_qo_heads,
   p.indices = indices;
   p.indptr = indptr;
   p.last_page_len = last_page_len;
-  p.nhd = nhd;
+  apply_variant(p, var);
   carve(p, hp, workspace);
   p.call_tag = next_call_tag();
 
@@ -441,7 +473,7 @@ fa_status_t fa_decode_contig(fa_dtype_t dtype, int num_qo_heads, int num_kv_head
                              const void *q, const void *k_cache, const void *v_cache, void *o,
                              float *lse, void *workspace, size_t workspace_bytes,
                              hipStream_t stream) {
-  return decode_contig(0, dtype, num_qo_heads, num_kv_heads, head_dim, max_kv_len, valid_kv_len,
+  return decode_contig(Variant{}, dtype, num_qo_heads, num_kv_heads, head_dim, max_kv_len, valid_kv_len,
                        scale, q, k_cache, v_cache, o, lse, workspace, workspace_bytes, stream);
 }
 
@@ -450,7 +482,7 @@ fa_status_t fa_decode_contig_nhd(fa_dtype_t dtype, int num_qo_heads, int num_kv_
                                  const void *q, const void *k_cache, const void *v_cache,
                                  void *o, float *lse, void *workspace, size_t workspace_bytes,
                                  hipStream_t stream) {
-  return decode_contig(1, dtype, num_qo_heads, num_kv_heads, head_dim, max_kv_len, valid_kv_len,
+  return decode_contig(Variant{1, 0, 0.0f}, dtype, num_qo_heads, num_kv_heads, head_dim, max_kv_len, valid_kv_len,
                        scale, q, k_cache, v_cache, o, lse, workspace, workspace_bytes, stream);
 }
 
@@ -461,7 +493,7 @@ fa_status_t fa_decode_paged(fa_dtype_t dtype, int batch, int num_qo_heads, int n
                             const int32_t *indptr, const int32_t *last_page_len, void *o,
                             float *lse, void *workspace, size_t workspace_bytes,
                             hipStream_t stream) {
-  return decode_paged(0, dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+  return decode_paged(Variant{}, dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
                       num_total_pages, total_used_pages, sm_scale, q, k_data, v_data, indices,
                       indptr, last_page_len, o, lse, workspace, workspace_bytes, stream);
 }
@@ -473,7 +505,35 @@ fa_status_t fa_decode_paged_nhd(fa_dtype_t dtype, int batch, int num_qo_heads,
                                 const int32_t *indices, const int32_t *indptr,
                                 const int32_t *last_page_len, void *o, float *lse,
                                 void *workspace, size_t workspace_bytes, hipStream_t stream) {
-  return decode_paged(1, dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+  return decode_paged(Variant{1, 0, 0.0f}, dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                      num_total_pages, total_used_pages, sm_scale, q, k_data, v_data, indices,
+                      indptr, last_page_len, o, lse, workspace, workspace_bytes, stream);
+}
+
+fa_status_t fa_decode_contig_opts(const fa_decode_options_t *opts, fa_dtype_t dtype,
+                                  int num_qo_heads, int num_kv_heads, int head_dim,
+                                  int max_kv_len, int valid_kv_len, float scale, const void *q,
+                                  const void *k_cache, const void *v_cache, void *o, float *lse,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  Variant var;
+  const fa_status_t st = read_options(opts, var);
+  if (st != FA_OK) return st;
+  return decode_contig(var, dtype, num_qo_heads, num_kv_heads, head_dim, max_kv_len,
+                       valid_kv_len, scale, q, k_cache, v_cache, o, lse, workspace,
+                       workspace_bytes, stream);
+}
+
+fa_status_t fa_decode_paged_opts(const fa_decode_options_t *opts, fa_dtype_t dtype, int batch,
+                                 int num_qo_heads, int num_kv_heads, int head_dim, int page_size,
+                                 int num_total_pages, int total_used_pages, float sm_scale,
+                                 const void *q, const void *k_data, const void *v_data,
+                                 const int32_t *indices, const int32_t *indptr,
+                                 const int32_t *last_page_len, void *o, float *lse,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  Variant var;
+  const fa_status_t st = read_options(opts, var);
+  if (st != FA_OK) return st;
+  return decode_paged(var, dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
                       num_total_pages, total_used_pages, sm_scale, q, k_data, v_data, indices,
                       indptr, last_page_len, o, lse, workspace, workspace_bytes, stream);
 }

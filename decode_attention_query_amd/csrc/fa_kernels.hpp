@@ -41,15 +41,19 @@ constexpr int kRegChunks = 4;  // 64-request chunks held in registers at once
 // A split unit: request, unit within the request, units of the request, L_b,
 // first partial-result slot of the request, page base, and (gather hook) the
 // request's first row in a concatenation of all requests' rows (sum L < 2^31).
+// With a sliding window the query attends rows [start, L); the units cover
+// rows [lo, L), lo = start rounded down to a multiple of 16 so that 16-row
+// blocks stay inside pages, and rows below start are masked.
 struct UnitInfo {
   int b, c, n_units, L;
   int u0;
   int32_t page_base;
   int row0;
+  int lo, start;
 };
 
 struct Request {
-  int L, full, part, p0;
+  int L, full, part, p0, lo, start;
 };
 
 // L_b and the unit counts of request b (zeros past the batch).  The page table
@@ -64,9 +68,12 @@ __device__ inline Request request_of(const DecodeParams &p, int b) {
   const int n = min(max(i1, r.p0), T) - r.p0;
   const int lpl = min(max(lpl_raw, 0), p.page_size);
   r.L = n == 0 ? 0 : (n - 1) * p.page_size + lpl;  // < 2^31: the host checks T * P
-  r.full = r.L / p.chunk;
-  r.part = (r.L % p.chunk != 0 || r.L == 0) ? 1 : 0;  // an empty request is one empty unit
-  if (b >= p.batch) r = Request{0, 0, 0, 0};
+  r.start = (p.window > 0 && r.L > p.window) ? r.L - p.window : 0;
+  r.lo = r.start & ~15;
+  const int rows = r.L - r.lo;  // rows the units cover
+  r.full = rows / p.chunk;
+  r.part = (rows % p.chunk != 0 || rows == 0) ? 1 : 0;  // an empty request is one empty unit
+  if (b >= p.batch) r = Request{0, 0, 0, 0, 0, 0};
   return r;
 }
 
@@ -74,7 +81,7 @@ __device__ inline Request request_of(const DecodeParams &p, int b) {
 // multiple of kClasses).
 __device__ inline int length_class(const DecodeParams &p, const Request &r) {
   if (!r.part) return -1;
-  return min((r.L - r.full * p.chunk) / (p.chunk / kClasses), kClasses - 1);
+  return min((r.L - r.lo - r.full * p.chunk) / (p.chunk / kClasses), kClasses - 1);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave: shifts within each row of
@@ -109,6 +116,8 @@ __device__ bool find_unit(const DecodeParams &p, int w, UnitInfo &u) {
     u.L = p.contig_len;
     u.page_base = 0;
     u.row0 = 0;
+    u.lo = p.contig_lo;
+    u.start = p.contig_start;
     return true;
   }
   const int lane = threadIdx.x & (kWave - 1);
@@ -129,6 +138,8 @@ __device__ bool find_unit(const DecodeParams &p, int w, UnitInfo &u) {
     u.u0 = u0;
     u.page_base = lane_value(r.p0, src);
     u.row0 = row0;
+    u.lo = lane_value(r.lo, src);
+    u.start = lane_value(r.start, src);
   };
 
   // pass 1: the full-length units, in request order
@@ -413,8 +424,9 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   if (!find_unit<false>(p, blockIdx.x, u)) return;
   const int kvh = blockIdx.y / p.n_gblocks;
   const int h0 = kvh * p.group + (blockIdx.y % p.n_gblocks) * GT;
-  const int t_begin = u.c * p.chunk;
+  const int t_begin = u.lo + u.c * p.chunk;
   const int t_end = min(u.L, t_begin + p.chunk);
+  const int t_lo = u.start;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -453,7 +465,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
 #pragma unroll
     for (int s = 0; s < U; ++s) {
       const int t = t0 + s * TPW + slot;
-      valid[s] = t < t_end;
+      valid[s] = t >= t_lo && t < t_end;
       const int64_t off = kv_row_offset(p, u.page_base, kvh, valid[s] ? t : t_end - 1);
       kr[s] = load16_stream(kb + off * E::kBytes);
       vr[s] = load16_stream(vb + off * E::kBytes);
@@ -486,6 +498,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
       float mt = -INFINITY;
 #pragma unroll
       for (int s = 0; s < U; ++s) {
+        if (p.softcap2 > 0.0f) sc[s][g] = p.softcap2 * tanhf(sc[s][g] * p.softcap2_inv);
         if (!valid[s]) sc[s][g] = -INFINITY;
         mt = fmaxf(mt, sc[s][g]);
       }
@@ -649,7 +662,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const DecodeParams p, void 
   UnitInfo u;
   if (!find_unit<true>(p, blockIdx.x, u)) return;
   const int kvh = blockIdx.y;
-  const int t_begin = u.c * p.chunk;
+  const int t_begin = u.lo + u.c * p.chunk;
   const int t_end = min(u.L, t_begin + p.chunk);
   const int vecs = p.head_dim * elem_bytes / 16;  // 16-byte vectors per row
   for (int idx = threadIdx.x; idx < (t_end - t_begin) * vecs; idx += blockDim.x) {

@@ -205,8 +205,9 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   const int kvh = plane / p.n_gblocks;
   const int h0 = kvh * p.group + (plane % p.n_gblocks) * gt;
   // workgroup-uniform values, kept in scalar registers
-  const int t_begin = __builtin_amdgcn_readfirstlane(u.c * p.chunk);
-  const int t_end = __builtin_amdgcn_readfirstlane(min(u.L, u.c * p.chunk + p.chunk));
+  const int t_begin = __builtin_amdgcn_readfirstlane(u.lo + u.c * p.chunk);
+  const int t_end = __builtin_amdgcn_readfirstlane(min(u.L, t_begin + p.chunk));
+  const int t_lo = __builtin_amdgcn_readfirstlane(u.start);  // rows below: outside the window
   const int32_t page_base = __builtin_amdgcn_readfirstlane(u.page_base);
 
   // The unit's page ids, once, into LDS: later lookups are LDS reads instead
@@ -292,7 +293,9 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = t0 + 16 * j + 4 * grp + i;
-        const float v = t < t_end ? s[j][i] * c : -INFINITY;
+        float v = s[j][i] * c;
+        if (p.softcap2 > 0.0f) v = p.softcap2 * tanhf(v * p.softcap2_inv);
+        if (t < t_lo || t >= t_end) v = -INFINITY;
         x[4 * j + i] = v;
         tmax = fmaxf(tmax, v);
       }

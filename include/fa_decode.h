@@ -193,6 +193,45 @@ fa_status_t fa_decode_paged_nhd(fa_dtype_t dtype, int batch, int num_qo_heads,
                                 const int32_t *last_page_len, void *o, float *lse,
                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Layout and score variants for fa_decode_paged_opts / fa_decode_contig_opts.
+ * The baracuda-kernels page lists a sliding window and logits soft-capping as
+ * not supported by its plan (module doc "Constraints") and defines neither;
+ * the readings here:
+ *   kv_layout        0: heads-major K/V (as fa_decode_paged / fa_decode_contig),
+ *                    1: token-major (as the _nhd entry points)
+ *   window           > 0: each request's query (its newest token, at row
+ *                    L_b - 1) attends only rows j >= L_b - window; 0: all rows
+ *   logits_soft_cap  > 0: every scaled score x becomes cap * tanh(x / cap)
+ *                    before the softmax, and lse sums exp of the capped scores;
+ *                    0: off
+ * A window keeps whole 16-row blocks of rows below it in the read set (they are
+ * masked, never weighted), so the bytes read grow by at most 15 rows per
+ * request. */
+typedef struct {
+  int kv_layout;
+  int window;
+  float logits_soft_cap;
+} fa_decode_options_t;
+
+/* fa_decode_paged / fa_decode_contig with options (opts may be NULL: all
+ * defaults, identical to the plain entry points).  Checked before the plain
+ * entry point's own checks:
+ *   opts->kv_layout not 0 or 1                                 -> FA_ERR_UNSUPPORTED
+ *   opts->window < 0, or logits_soft_cap negative or not finite -> FA_ERR_INVALID_PROBLEM */
+fa_status_t fa_decode_paged_opts(const fa_decode_options_t *opts, fa_dtype_t dtype, int batch,
+                                 int num_qo_heads, int num_kv_heads, int head_dim, int page_size,
+                                 int num_total_pages, int total_used_pages, float sm_scale,
+                                 const void *q, const void *k_data, const void *v_data,
+                                 const int32_t *indices, const int32_t *indptr,
+                                 const int32_t *last_page_len, void *o, float *lse,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+fa_status_t fa_decode_contig_opts(const fa_decode_options_t *opts, fa_dtype_t dtype,
+                                  int num_qo_heads, int num_kv_heads, int head_dim,
+                                  int max_kv_len, int valid_kv_len, float scale, const void *q,
+                                  const void *k_cache, const void *v_cache, void *o, float *lse,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Decode-time KV append (baracuda-kernels page, module doc "Companion plans":
  * the new K/V slices are written into the paged store before decode; the page
  * names the plan but prints no signature).  Writes one new K row and one new V
