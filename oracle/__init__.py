@@ -26,9 +26,10 @@ Functions and what they follow:
   validate_table -- the device-side page-table contract (same page, "Layout")
   attend_f64     -- one query row over explicit f64 rows (a split's partial)
   merge          -- combine partials over a partition of the rows via their lse
-Both decode functions take window= (sliding window, the last `window` rows)
-and softcap= (scores c * tanh(x / c)), the variants the baracuda-kernels page
-lists as unsupported by its plan (module doc "Constraints"); 0 turns each off.
+Both decode functions take window= (sliding window, the last `window` rows),
+softcap= (scores c * tanh(x / c)) and alibi= (per-head slopes of a linear
+distance penalty), the variants the baracuda-kernels page lists as unsupported
+by its plan (module doc "Constraints"); 0 / None turns each off.
 """
 import ctypes
 import os
@@ -67,10 +68,10 @@ class _Lib:
         lib.oracle_gather_paged.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I]
         lib.oracle_gather_paged.restype = _I
         lib.oracle_decode_paged.argtypes = [_I, _I, _I, _I, _I, _I, _D, _P, _P, _P, _P, _P,
-                                            _P, _I, _P, _P, _P, _P, _I, _I, _I, _D]
+                                            _P, _I, _P, _P, _P, _P, _I, _I, _I, _D, _P]
         lib.oracle_decode_paged.restype = _I
         lib.oracle_decode_contig.argtypes = [_I, _I, _I, _I, _I, _I, _D, _P, _P, _P, _P, _P,
-                                             _I, _I, _I, _D]
+                                             _I, _I, _I, _D, _P]
         lib.oracle_decode_contig.restype = _I
         lib.oracle_attend_f64.argtypes = [_I, _I64, _D, _P, _P, _P, _P, _P]
         lib.oracle_attend_f64.restype = None
@@ -125,6 +126,19 @@ def _i32(a):
 
 def _ptr(a):
     return a.ctypes.data_as(ctypes.c_void_p)
+
+
+_keep = []
+
+
+def _slopes(alibi, hq):
+    """Pointer to the ALiBi slopes as f64 [Hq], or NULL."""
+    if alibi is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(alibi, dtype=np.float64))
+    assert a.shape == (hq,)
+    _keep[:] = [a]  # alive for the duration of the call
+    return _ptr(a)
 
 
 def f16_to_f64(bits: int) -> float:
@@ -195,11 +209,12 @@ def append_paged(dtype, data, indices, indptr, last_page_len, new_rows, layout="
 
 
 def decode_paged(dtype, q, k_data, v_data, indices, indptr, last_page_len, scale,
-                 samples=None, threads=0, layout="hnd", window=0, softcap=0.0):
+                 samples=None, threads=0, layout="hnd", window=0, softcap=0.0, alibi=None):
     """q [B, Hq, D]; k_data/v_data [pages, Hkv, P, D] (layout="nhd":
     [pages, P, Hkv, D]).  Returns (o, lse) in f64: o [B, Hq, D], lse [B, Hq];
     with samples=[(b, h), ...] returns o [n, D], lse [n].  window > 0: only the
-    last `window` rows of each request; softcap > 0: scores capped with tanh."""
+    last `window` rows of each request; softcap > 0: scores capped with tanh;
+    alibi: per query head slopes [Hq] (None: off)."""
     q, k_data, v_data = _bits(q, dtype), _bits(k_data, dtype), _bits(v_data, dtype)
     batch, hq, head_dim = q.shape
     hkv, page_size, d2 = _paged_dims(k_data.shape, layout)
@@ -221,14 +236,14 @@ def decode_paged(dtype, q, k_data, v_data, indices, indptr, last_page_len, scale
                                     float(scale), _ptr(q), _ptr(k_data), _ptr(v_data),
                                     _ptr(indices), _ptr(indptr), _ptr(lpl), n_sample,
                                     _ptr(sb), _ptr(sh), _ptr(o), _ptr(lse), int(threads),
-                                    LAYOUTS[layout], int(window), float(softcap))
+                                    LAYOUTS[layout], int(window), float(softcap), _slopes(alibi, hq))
     if r != 0:
         raise RuntimeError(f"oracle_decode_paged: {STATUS[r]}")
     return o, lse
 
 
 def decode_contig(dtype, q, k_cache, v_cache, valid_kv_len, scale, threads=0, layout="hnd",
-                  window=0, softcap=0.0):
+                  window=0, softcap=0.0, alibi=None):
     """q [Hq, D]; k_cache/v_cache [Hkv, max_kv_len, D] (layout="nhd":
     [max_kv_len, Hkv, D]).  Returns (o [Hq, D], lse [Hq]) f64."""
     q, k_cache, v_cache = _bits(q, dtype), _bits(k_cache, dtype), _bits(v_cache, dtype)
@@ -245,7 +260,8 @@ def decode_contig(dtype, q, k_cache, v_cache, valid_kv_len, scale, threads=0, la
     r = _load().oracle_decode_contig(DTYPES[dtype], hq, hkv, head_dim, max_kv_len,
                                      int(valid_kv_len), float(scale), _ptr(q), _ptr(k_cache),
                                      _ptr(v_cache), _ptr(o), _ptr(lse), int(threads),
-                                     LAYOUTS[layout], int(window), float(softcap))
+                                     LAYOUTS[layout], int(window), float(softcap),
+                                     _slopes(alibi, hq))
     if r != 0:
         raise RuntimeError(f"oracle_decode_contig: {STATUS[r]}")
     return o, lse

@@ -43,7 +43,11 @@
  *                j >= L_b - window (0: every row);
  *   softcap > 0: logits soft-capping -- each scaled score x_j becomes
  *                softcap * tanh(x_j / softcap), and lse sums exp of the capped
- *                scores (0: off).
+ *                scores (0: off);
+ *   alibi:       per query head slopes m_h (NULL: off) -- the score of row j
+ *                gains m_h * (j - (L_b - 1)), a linear penalty on the distance
+ *                back from the query's own position, added to the scaled score
+ *                before any cap.
  *
  * Two K/V layouts (argument `layout`):
  *   OR_HND (0), heads-major: contiguous [Hkv, max_kv_len, D] (ferrum-kernels
@@ -190,11 +194,13 @@ static int64_t window_start(int64_t L, int window) {
 }
 
 /* One query row against L explicit K/V rows given by element offsets into k and
- * v.  q_off is the element offset of the query row.  Two-pass softmax in f64.
+ * v.  q_off is the element offset of the query row; row j's score gains
+ * slope * (dist0 + j).  Two-pass softmax in f64.
  * o gets head_dim values; *lse the natural-log log-sum-exp. */
-static void attend_rows(int dtype, int head_dim, double scale, double softcap, const void *q,
-                        int64_t q_off, const void *k, const void *v, const int64_t *row_off,
-                        int64_t L, double *x, double *o, double *lse) {
+static void attend_rows(int dtype, int head_dim, double scale, double softcap, double slope,
+                        int64_t dist0, const void *q, int64_t q_off, const void *k,
+                        const void *v, const int64_t *row_off, int64_t L, double *x, double *o,
+                        double *lse) {
   for (int d = 0; d < head_dim; ++d) o[d] = 0.0;
   if (L == 0) {
     *lse = -INFINITY;
@@ -205,7 +211,7 @@ static void attend_rows(int dtype, int head_dim, double scale, double softcap, c
     double dot = 0.0;
     for (int d = 0; d < head_dim; ++d)
       dot += load_elem(dtype, q, q_off + d) * load_elem(dtype, k, row_off[j] + d);
-    x[j] = scale * dot;
+    x[j] = scale * dot + slope * (double)(dist0 + j);
     if (softcap > 0.0) x[j] = softcap * tanh(x[j] / softcap);
   }
   /* pass 1: max */
@@ -233,7 +239,8 @@ int oracle_decode_paged(int dtype, int batch, int num_qo_heads, int num_kv_heads
                         const void *k, const void *v, const int32_t *indices,
                         const int32_t *indptr, const int32_t *last_page_len, int n_sample,
                         const int32_t *sample_b, const int32_t *sample_h, double *o,
-                        double *lse, int threads, int layout, int window, double softcap) {
+                        double *lse, int threads, int layout, int window, double softcap,
+                        const double *alibi) {
   if (batch <= 0 || num_qo_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       page_size <= 0 || num_qo_heads % num_kv_heads != 0 ||
       (layout != OR_HND && layout != OR_NHD) || window < 0 || !(softcap >= 0.0))
@@ -261,8 +268,8 @@ int oracle_decode_paged(int dtype, int batch, int num_qo_heads, int num_kv_heads
         row_off[j - j0] = paged_row_offset(layout, num_kv_heads, page_size, head_dim, indices,
                                            indptr, b, g, j);
       int64_t q_off = ((int64_t)b * num_qo_heads + h) * head_dim;
-      attend_rows(dtype, head_dim, scale, softcap, q, q_off, k, v, row_off, L - j0, x,
-                  o + it * head_dim, lse + it);
+      attend_rows(dtype, head_dim, scale, softcap, alibi ? alibi[h] : 0.0, j0 - (L - 1), q,
+                  q_off, k, v, row_off, L - j0, x, o + it * head_dim, lse + it);
     }
     free(row_off);
     free(x);
@@ -277,7 +284,8 @@ int oracle_decode_paged(int dtype, int batch, int num_qo_heads, int num_kv_heads
 int oracle_decode_contig(int dtype, int num_qo_heads, int num_kv_heads, int head_dim,
                          int max_kv_len, int valid_kv_len, double scale, const void *q,
                          const void *k, const void *v, double *o, double *lse,
-                         int threads, int layout, int window, double softcap) {
+                         int threads, int layout, int window, double softcap,
+                         const double *alibi) {
   if (num_qo_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_kv_len < 0 ||
       valid_kv_len < 0 || valid_kv_len > max_kv_len || num_qo_heads % num_kv_heads != 0 ||
       (layout != OR_HND && layout != OR_NHD) || window < 0 || !(softcap >= 0.0))
@@ -299,8 +307,9 @@ int oracle_decode_contig(int dtype, int num_qo_heads, int num_kv_heads, int head
       int64_t j0 = window_start(L, window);
       for (int64_t j = j0; j < L; ++j)
         row_off[j - j0] = contig_row_offset(layout, num_kv_heads, max_kv_len, head_dim, g, j);
-      attend_rows(dtype, head_dim, scale, softcap, q, (int64_t)h * head_dim, k, v, row_off,
-                  L - j0, x, o + (int64_t)h * head_dim, lse + h);
+      attend_rows(dtype, head_dim, scale, softcap, alibi ? alibi[h] : 0.0, j0 - (L - 1), q,
+                  (int64_t)h * head_dim, k, v, row_off, L - j0, x, o + (int64_t)h * head_dim,
+                  lse + h);
     }
     free(row_off);
     free(x);

@@ -581,6 +581,91 @@ def pin_softcap_identical_k_rows():
         assert abs(lse[0, h] - want) <= 1e-13 * max(1.0, abs(want))
 
 
+def _slopes(hq):
+    return [2.0 ** (-8.0 * (h + 1) / hq) for h in range(hq)]
+
+
+def pin_alibi_mpmath():
+    """ALiBi scores against a 50-digit evaluation of scale * q.k + m_h * (j - (L - 1))
+    (also under a cap, where the bias comes first)."""
+    rng = np.random.default_rng(35)
+    for cap in (0.0, 4.0):
+        for dtype in DTYPES:
+            hkv, group, d = 2, 2, 4
+            lens = [1, 4, 7]
+            p = _paged_problem(rng, dtype, lens, hkv, group, d, 3)
+            slopes = _slopes(hkv * group)
+            scale = 0.9
+            o, lse = O.decode_paged(dtype, W.bits(p["q"]), W.bits(p["k_data"]),
+                                    W.bits(p["v_data"]), p["indices"], p["indptr"],
+                                    p["last_page_len"], scale, softcap=cap, alibi=slopes)
+            mpmath.mp.dps = 50
+            qf = f64(p["q"])
+            for b, L in enumerate(lens):
+                kf, vf = f64(p["k_rows"][b]), f64(p["v_rows"][b])
+                for h in range(hkv * group):
+                    g = h // group
+                    xs = []
+                    for j in range(L):
+                        x = mpmath.mpf(scale) * mpmath.fsum(mpmath.mpf(a) * mpmath.mpf(c)
+                                                            for a, c in zip(qf[b, h], kf[j, g]))
+                        x += mpmath.mpf(slopes[h]) * (j - (L - 1))
+                        if cap:
+                            x = mpmath.mpf(cap) * mpmath.tanh(x / cap)
+                        xs.append(mpmath.e ** x)
+                    z = mpmath.fsum(xs)
+                    for dd in range(d):
+                        ref = float(mpmath.fsum(xs[j] * mpmath.mpf(vf[j, g, dd])
+                                                for j in range(L)) / z)
+                        assert abs(o[b, h, dd] - ref) <= 1e-13 * max(1.0, abs(ref))
+                    assert abs(lse[b, h] - float(mpmath.log(z))) <= 1e-13 * max(1.0, abs(float(mpmath.log(z))))
+
+
+def pin_alibi_geometric_weights():
+    """Identical K rows under ALiBi: row j weighs exp(m (j - L + 1)), a geometric
+    sequence, so o is the geometric mean-weighted V and lse = x + ln sum_k e^(-m k).
+    Zero slopes change nothing, bit for bit."""
+    rng = np.random.default_rng(36)
+    hkv, group, d, L = 1, 4, 16, 11
+    k_row = rand_t(rng, (1, hkv, d), "f32")
+    p = _paged_problem(rng, "f32", [L], hkv, group, d, 4,
+                       k_rows=[k_row.expand(L, hkv, d).contiguous()])
+    args = ("f32", W.bits(p["q"]), W.bits(p["k_data"]), W.bits(p["v_data"]), p["indices"],
+            p["indptr"], p["last_page_len"], 0.25)
+    plain = O.decode_paged(*args)
+    zero = O.decode_paged(*args, alibi=[0.0] * group)
+    assert np.array_equal(plain[0], zero[0]) and np.array_equal(plain[1], zero[1])
+    slopes = _slopes(group)
+    o, lse = O.decode_paged(*args, alibi=slopes)
+    vf = f64(p["v_rows"][0])[:, 0, :]
+    qf, kf = f64(p["q"])[0], f64(k_row)[0, 0]
+    for h in range(group):
+        w = np.exp(slopes[h] * (np.arange(L) - (L - 1)))
+        np.testing.assert_allclose(o[0, h], (w[:, None] * vf).sum(0) / w.sum(), rtol=1e-12,
+                                   atol=1e-14)
+        x = 0.25 * float(np.dot(qf[h], kf))
+        assert abs(lse[0, h] - (x + math.log(w.sum()))) <= 1e-12
+
+
+def pin_alibi_window_is_truncation():
+    """Distances count back from the query, so a window of W rows under ALiBi
+    equals the truncated request with the same slopes, bit for bit."""
+    rng = np.random.default_rng(37)
+    hkv, group, d, L, win = 2, 2, 8, 23, 9
+    rows_k, rows_v = rand_t(rng, (L, hkv, d), "bf16"), rand_t(rng, (L, hkv, d), "bf16")
+    q = rand_t(rng, (1, hkv * group, d), "bf16")
+    slopes = _slopes(hkv * group)
+    p = _paged_problem(rng, "bf16", [L], hkv, group, d, 4, k_rows=[rows_k], v_rows=[rows_v], q=q)
+    got = O.decode_paged("bf16", W.bits(p["q"]), W.bits(p["k_data"]), W.bits(p["v_data"]),
+                         p["indices"], p["indptr"], p["last_page_len"], 0.3, window=win,
+                         alibi=slopes)
+    pt = _paged_problem(rng, "bf16", [win], hkv, group, d, 4, k_rows=[rows_k[L - win:]],
+                        v_rows=[rows_v[L - win:]], q=q)
+    want = O.decode_paged("bf16", W.bits(pt["q"]), W.bits(pt["k_data"]), W.bits(pt["v_data"]),
+                          pt["indices"], pt["indptr"], pt["last_page_len"], 0.3, alibi=slopes)
+    assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+
+
 def pin_seq_lens():
     """The oracle's L_b equals the row count the test scattered."""
     rng = np.random.default_rng(26)

@@ -18,7 +18,7 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "decode_ref.c")
 
 # (name, text in decode_ref.c, replacement)
 MUTANTS = [
-    ("drop_scale", "x[j] = scale * dot;", "x[j] = dot;"),
+    ("drop_scale", "x[j] = scale * dot + slope", "x[j] = dot + slope"),
     ("head_map_modulo", "int g = h / group;", "int g = h % num_kv_heads;"),
     ("max_shift_sign", "double w = exp(x[j] - M);", "double w = exp(M - x[j]);"),
     ("lse_drops_max", "*lse = M + log(l);", "*lse = log(l);"),
@@ -62,6 +62,13 @@ MUTANTS = [
     ("softcap_drops_outer_factor",
      "if (softcap > 0.0) x[j] = softcap * tanh(x[j] / softcap);",
      "if (softcap > 0.0) x[j] = tanh(x[j] / softcap);"),
+    ("alibi_sign", "x[j] = scale * dot + slope * (double)(dist0 + j);",
+     "x[j] = scale * dot - slope * (double)(dist0 + j);"),
+    ("alibi_absolute_position", "alibi ? alibi[h] : 0.0, j0 - (L - 1)",
+     "alibi ? alibi[h] : 0.0, j0"),
+    ("alibi_after_cap",
+     "x[j] = scale * dot + slope * (double)(dist0 + j);\n    if (softcap > 0.0) x[j] = softcap * tanh(x[j] / softcap);",
+     "x[j] = scale * dot;\n    if (softcap > 0.0) x[j] = softcap * tanh(x[j] / softcap);\n    x[j] += slope * (double)(dist0 + j);"),
     ("validate_skips_upper_bound", "indices[i] >= num_total_pages", "indices[i] > num_total_pages"),
 ]
 
