@@ -38,9 +38,10 @@ EXPORTED = ("fa_decode_workspace_size", "fa_decode_contig", "fa_decode_paged",
 
 class DecodeOptions(ctypes.Structure):
     """fa_decode_options_t: K/V layout (0 heads-major, 1 token-major), sliding
-    window (rows, 0 = off) and logits soft-cap (0 = off)."""
+    window (rows, 0 = off), logits soft-cap (0 = off) and the device address of
+    f32 ALiBi slopes [Hq] (None = off)."""
     _fields_ = [("kv_layout", ctypes.c_int), ("window", ctypes.c_int),
-                ("logits_soft_cap", ctypes.c_float)]
+                ("logits_soft_cap", ctypes.c_float), ("alibi_slopes", ctypes.c_void_p)]
 
 
 class FaError(RuntimeError):

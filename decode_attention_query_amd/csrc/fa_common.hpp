@@ -75,6 +75,7 @@ struct DecodeParams {
   int window;         // > 0: the query attends only each request's last `window` rows
   float softcap2;     // > 0: base-2 scores x -> softcap2 * tanh(x / softcap2) (cap * log2 e)
   float softcap2_inv; // 1 / softcap2
+  const float *alibi; // [Hq] ALiBi slopes (natural-log units) or null
   // workspace regions
   float *part_lse;        // [units_bound, Hq]     base-2 lse of each split's partial
   float *part_o;          // [units_bound, Hq, D]  normalised partial outputs

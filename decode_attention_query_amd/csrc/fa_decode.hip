@@ -292,6 +292,7 @@ struct Variant {
   int nhd = 0;
   int window = 0;
   float softcap = 0.0f;
+  const float *alibi = nullptr;
 };
 
 // FA_OK, or why opts is rejected; fills v.
@@ -304,12 +305,14 @@ fa_status_t read_options(const fa_decode_options_t *opts, Variant &v) {
   v.nhd = opts->kv_layout;
   v.window = opts->window;
   v.softcap = opts->logits_soft_cap;
+  v.alibi = opts->alibi_slopes;
   return FA_OK;
 }
 
 void apply_variant(DecodeParams &p, const Variant &v) {
   p.nhd = v.nhd;
   p.window = v.window;
+  p.alibi = v.alibi;
   if (v.softcap > 0.0f) {
     p.softcap2 = v.softcap * fa::kLog2e;  // capping commutes with the base-2 scale
     p.softcap2_inv = 1.0f / p.softcap2;
@@ -482,7 +485,7 @@ fa_status_t fa_decode_contig_nhd(fa_dtype_t dtype, int num_qo_heads, int num_kv_
                                  const void *q, const void *k_cache, const void *v_cache,
                                  void *o, float *lse, void *workspace, size_t workspace_bytes,
                                  hipStream_t stream) {
-  return decode_contig(Variant{1, 0, 0.0f}, dtype, num_qo_heads, num_kv_heads, head_dim, max_kv_len, valid_kv_len,
+  return decode_contig(Variant{1, 0, 0.0f, nullptr}, dtype, num_qo_heads, num_kv_heads, head_dim, max_kv_len, valid_kv_len,
                        scale, q, k_cache, v_cache, o, lse, workspace, workspace_bytes, stream);
 }
 
@@ -505,7 +508,7 @@ fa_status_t fa_decode_paged_nhd(fa_dtype_t dtype, int batch, int num_qo_heads,
                                 const int32_t *indices, const int32_t *indptr,
                                 const int32_t *last_page_len, void *o, float *lse,
                                 void *workspace, size_t workspace_bytes, hipStream_t stream) {
-  return decode_paged(Variant{1, 0, 0.0f}, dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+  return decode_paged(Variant{1, 0, 0.0f, nullptr}, dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
                       num_total_pages, total_used_pages, sm_scale, q, k_data, v_data, indices,
                       indptr, last_page_len, o, lse, workspace, workspace_bytes, stream);
 }

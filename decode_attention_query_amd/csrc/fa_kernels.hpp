@@ -434,6 +434,12 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   const int slot = lane / LPT;
   const int vi = lane % LPT;
 
+  // ALiBi: score of row t gains slope * (t - (L - 1)), here in base-2 units
+  float slope2[GT];
+#pragma unroll
+  for (int g = 0; g < GT; ++g) slope2[g] = p.alibi ? p.alibi[h0 + g] * kLog2e : 0.0f;
+  const int last_row = u.L - 1;
+
   float qf[GT][VEC];
   {
     const char *qb = static_cast<const char *>(p.q) +
@@ -498,6 +504,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
       float mt = -INFINITY;
 #pragma unroll
       for (int s = 0; s < U; ++s) {
+        if (p.alibi) sc[s][g] += slope2[g] * (float)(t0 + s * TPW + slot - last_row);
         if (p.softcap2 > 0.0f) sc[s][g] = p.softcap2 * tanhf(sc[s][g] * p.softcap2_inv);
         if (!valid[s]) sc[s][g] = -INFINITY;
         mt = fmaxf(mt, sc[s][g]);

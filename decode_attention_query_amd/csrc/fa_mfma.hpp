@@ -208,6 +208,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   const int t_begin = __builtin_amdgcn_readfirstlane(u.lo + u.c * p.chunk);
   const int t_end = __builtin_amdgcn_readfirstlane(min(u.L, t_begin + p.chunk));
   const int t_lo = __builtin_amdgcn_readfirstlane(u.start);  // rows below: outside the window
+  const int last_row = __builtin_amdgcn_readfirstlane(u.L - 1);
   const int32_t page_base = __builtin_amdgcn_readfirstlane(u.page_base);
 
   // The unit's page ids, once, into LDS: later lookups are LDS reads instead
@@ -244,6 +245,9 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
       qb[kk] = __builtin_bit_cast(v8, r);
     }
   }
+
+  // ALiBi slope of head n (base-2 units): row t's score gains slope2 * (t - (L - 1))
+  const float slope2 = (p.alibi && n < gt) ? p.alibi[h0 + n] * kLog2e : 0.0f;
 
   f32x4 acc[MB];
 #pragma unroll
@@ -294,6 +298,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
       for (int i = 0; i < 4; ++i) {
         const int t = t0 + 16 * j + 4 * grp + i;
         float v = s[j][i] * c;
+        if (p.alibi) v += slope2 * (float)(t - last_row);
         if (p.softcap2 > 0.0f) v = p.softcap2 * tanhf(v * p.softcap2_inv);
         if (t < t_lo || t >= t_end) v = -INFINITY;
         x[4 * j + i] = v;

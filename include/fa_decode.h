@@ -204,6 +204,10 @@ fa_status_t fa_decode_paged_nhd(fa_dtype_t dtype, int batch, int num_qo_heads,
  *   logits_soft_cap  > 0: every scaled score x becomes cap * tanh(x / cap)
  *                    before the softmax, and lse sums exp of the capped scores;
  *                    0: off
+ *   alibi_slopes     device f32 [num_qo_heads] or NULL: query head h adds
+ *                    alibi_slopes[h] * (j - (L_b - 1)) to row j's scaled score
+ *                    (0 at the query's own row, more negative further back),
+ *                    before any cap; the pages list ALiBi as unsupported too
  * A window keeps whole 16-row blocks of rows below it in the read set (they are
  * masked, never weighted), so the bytes read grow by at most 15 rows per
  * request. */
@@ -211,6 +215,7 @@ typedef struct {
   int kv_layout;
   int window;
   float logits_soft_cap;
+  const float *alibi_slopes;
 } fa_decode_options_t;
 
 /* fa_decode_paged / fa_decode_contig with options (opts may be NULL: all

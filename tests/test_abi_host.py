@@ -192,18 +192,18 @@ def test_append_rejects(fn):
 def test_options_reject():
     lib = fad.load_library()
     base = [2, 2, 8, 2, 128, 16, 10, 4, 0.125] + [FAKE] * 8 + [FAKE, 1 << 30, None]
-    for opts, status in ((fad.DecodeOptions(2, 0, 0.0), UNS),
-                         (fad.DecodeOptions(-1, 0, 0.0), UNS),
-                         (fad.DecodeOptions(0, -1, 0.0), INV),
-                         (fad.DecodeOptions(0, 0, -1.0), INV),
-                         (fad.DecodeOptions(0, 0, float("inf")), INV),
-                         (fad.DecodeOptions(0, 0, float("nan")), INV)):
+    for opts, status in ((fad.DecodeOptions(2, 0, 0.0, None), UNS),
+                         (fad.DecodeOptions(-1, 0, 0.0, None), UNS),
+                         (fad.DecodeOptions(0, -1, 0.0, None), INV),
+                         (fad.DecodeOptions(0, 0, -1.0, None), INV),
+                         (fad.DecodeOptions(0, 0, float("inf"), None), INV),
+                         (fad.DecodeOptions(0, 0, float("nan"), None), INV)):
         assert lib.fa_decode_paged_opts(ctypes.byref(opts), *base) == status
         assert lib.fa_decode_contig_opts(ctypes.byref(opts), 1, 8, 2, 64, 256, 128, 0.125,
                                          FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
                                          None) == status
     # valid options, then the plain entry point's own checks
-    ok = fad.DecodeOptions(1, 64, 30.0)
+    ok = fad.DecodeOptions(1, 64, 30.0, None)
     assert lib.fa_decode_paged_opts(ctypes.byref(ok), 7, *base[1:]) == UNS
     assert lib.fa_decode_paged_opts(None, 2, 0, *base[2:]) == INV
 

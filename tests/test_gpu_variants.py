@@ -22,23 +22,32 @@ def dev():
     return device()
 
 
-def _oracle(p, window, softcap, samples=None):
+def _oracle(p, window, softcap, samples=None, alibi=None):
     if isinstance(p, W.PagedProblem):
         return oracle.decode_paged(p.dtype, W.bits(p.q), W.bits(p.k_data), W.bits(p.v_data),
                                    p.indices.numpy(), p.indptr.numpy(), p.last_page_len.numpy(),
                                    p.scale, samples=samples, layout=p.layout, window=window,
-                                   softcap=softcap)
+                                   softcap=softcap, alibi=alibi)
     return oracle.decode_contig(p.dtype, W.bits(p.q), W.bits(p.k_cache), W.bits(p.v_cache),
                                 p.valid_kv_len, p.scale, layout=p.layout, window=window,
-                                softcap=softcap)
+                                softcap=softcap, alibi=alibi)
 
 
-def _run(p, d, window, softcap):
+def _run(p, d, window, softcap, alibi=None):
+    dev_alibi = None
+    if alibi is not None:
+        dev_alibi = torch.tensor(alibi, dtype=torch.float32, device=d["q"].device)
     if isinstance(p, W.PagedProblem):
         return fad.decode_paged(d["q"], d["k"], d["v"], d["indices"], d["indptr"], d["lpl"],
-                                p.scale, layout=p.layout, window=window, softcap=softcap)
+                                p.scale, layout=p.layout, window=window, softcap=softcap,
+                                alibi=dev_alibi)
     return fad.decode_contig(d["q"], d["k"], d["v"], p.valid_kv_len, p.scale, layout=p.layout,
-                             window=window, softcap=softcap)
+                             window=window, softcap=softcap, alibi=dev_alibi)
+
+
+def alibi_slopes(hq, max_bias=8.0):
+    """The usual geometric ALiBi slopes 2^(-max_bias (h + 1) / Hq), rounded to f32."""
+    return [float(np.float32(2.0 ** (-max_bias * (h + 1) / hq))) for h in range(hq)]
 
 
 CASES = [
@@ -49,15 +58,18 @@ CASES = [
     ("f16", 256, 1, 8, 32, [1023, 1025, 64]),
     ("bf16", 128, 1, 16, 1, [40, 3]),
 ]
-VARIANTS = [(1, 0.0), (5, 0.0), (16, 0.0), (17, 0.0), (257, 0.0), (0, 1.0), (0, 30.0),
-            (100, 5.0)]
+VARIANTS = [(1, 0.0, False), (5, 0.0, False), (16, 0.0, False), (17, 0.0, False),
+            (257, 0.0, False), (0, 1.0, False), (0, 30.0, False), (100, 5.0, False),
+            (0, 0.0, True), (33, 0.0, True), (0, 20.0, True)]
 
 
-@pytest.mark.parametrize("variant", VARIANTS, ids=lambda v: f"w{v[0]}-cap{v[1]:g}")
+@pytest.mark.parametrize("variant", VARIANTS,
+                         ids=lambda v: f"w{v[0]}-cap{v[1]:g}" + ("-alibi" if v[2] else ""))
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}-D{c[1]}-G{c[3]}-P{c[4]}")
 def test_paged_variants(dev, case, variant):
     dtype, d, hkv, group, page_size, lens = case
-    window, cap = variant
+    window, cap, with_alibi = variant
+    slopes = alibi_slopes(hkv * group) if with_alibi else None
     rng = np.random.default_rng(zlib.crc32(str(case).encode()))
     k_rows = [rand_t(rng, (L, hkv, d), dtype) for L in lens]
     v_rows = [rand_t(rng, (L, hkv, d), dtype) for L in lens]
@@ -73,20 +85,23 @@ def test_paged_variants(dev, case, variant):
                        indptr=torch.from_numpy(ptr), last_page_len=torch.from_numpy(lpl))
     for layout in ("hnd", "nhd"):
         pp = p if layout == "hnd" else W.token_major(p)
-        o, lse = _run(pp, to_dev(pp, dev), window, cap)
+        o, lse = _run(pp, to_dev(pp, dev), window, cap, slopes)
         torch.cuda.synchronize()
-        ro, rl = _oracle(pp, window, cap)
+        ro, rl = _oracle(pp, window, cap, alibi=slopes)
         compare(dtype, o, lse, ro, rl, f"{case} {variant} {layout}")
 
 
-@pytest.mark.parametrize("variant", [(1, 0.0), (100, 0.0), (4000, 0.0), (0, 20.0), (64, 10.0)],
-                         ids=lambda v: f"w{v[0]}-cap{v[1]:g}")
+@pytest.mark.parametrize("variant", [(1, 0.0, False), (100, 0.0, False), (4000, 0.0, False),
+                                     (0, 20.0, False), (64, 10.0, False), (0, 0.0, True),
+                                     (300, 5.0, True)],
+                         ids=lambda v: f"w{v[0]}-cap{v[1]:g}" + ("-alibi" if v[2] else ""))
 def test_contig_variants(dev, variant):
-    window, cap = variant
+    window, cap, with_alibi = variant
+    slopes = alibi_slopes(16) if with_alibi else None
     p = W.make_contig("variant", "f16", 16, 4, 128, 5000, 4999, seed=77, q_std=4.0)
-    o, lse = _run(p, to_dev(p, dev), window, cap)
+    o, lse = _run(p, to_dev(p, dev), window, cap, slopes)
     torch.cuda.synchronize()
-    ro, rl = _oracle(p, window, cap)
+    ro, rl = _oracle(p, window, cap, alibi=slopes)
     compare("f16", o, lse, ro, rl, f"contig {variant}")
 
 
