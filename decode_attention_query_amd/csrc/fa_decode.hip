@@ -211,10 +211,18 @@ template <class E, int D>
 hipError_t launch_mfma(const DecodeParams &p, const HostPlan &hp, hipStream_t s) {
   dim3 grid(unsigned(hp.units_bound) * unsigned(hp.planes));
   dim3 block(fa::MfmaGeom<E, D>::NW * 64);
-  if (p.nhd)
-    hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, true>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, false>), grid, block, 0, s, p);
+  const bool mods = p.window > 0 || p.softcap2 > 0.0f || p.alibi != nullptr;
+  if (p.nhd) {
+    if (mods)
+      hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, true, true>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, true, false>), grid, block, 0, s, p);
+  } else {
+    if (mods)
+      hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, false, true>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, false, false>), grid, block, 0, s, p);
+  }
   return hipGetLastError();
 }
 

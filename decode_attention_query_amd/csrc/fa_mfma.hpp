@@ -181,7 +181,9 @@ __device__ inline void issue_tile(KVTile<MfmaGeom<E, D>::NI> &T, const DecodePar
   }
 }
 
-template <class E, int D, bool kNhd>
+// kMods: a sliding window, soft-cap or ALiBi is in use (the plain instance
+// carries none of their per-score work).
+template <class E, int D, bool kNhd, bool kMods>
 __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1))) void decode_mfma_kernel(
     const DecodeParams p) {
   using G = MfmaGeom<E, D>;
@@ -247,7 +249,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   }
 
   // ALiBi slope of head n (base-2 units): row t's score gains slope2 * (t - (L - 1))
-  const float slope2 = (p.alibi && n < gt) ? p.alibi[h0 + n] * kLog2e : 0.0f;
+  const float slope2 = (kMods && p.alibi && n < gt) ? p.alibi[h0 + n] * kLog2e : 0.0f;
 
   f32x4 acc[MB];
 #pragma unroll
@@ -298,9 +300,12 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
       for (int i = 0; i < 4; ++i) {
         const int t = t0 + 16 * j + 4 * grp + i;
         float v = s[j][i] * c;
-        if (p.alibi) v += slope2 * (float)(t - last_row);
-        if (p.softcap2 > 0.0f) v = p.softcap2 * tanhf(v * p.softcap2_inv);
-        if (t < t_lo || t >= t_end) v = -INFINITY;
+        if constexpr (kMods) {
+          if (p.alibi) v += slope2 * (float)(t - last_row);
+          if (p.softcap2 > 0.0f) v = p.softcap2 * tanhf(v * p.softcap2_inv);
+          if (t < t_lo) v = -INFINITY;
+        }
+        if (t >= t_end) v = -INFINITY;
         x[4 * j + i] = v;
         tmax = fmaxf(tmax, v);
       }
