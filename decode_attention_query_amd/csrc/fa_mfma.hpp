@@ -214,7 +214,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   const int32_t page_base = __builtin_amdgcn_readfirstlane(u.page_base);
 
   // The unit's page ids, once, into LDS: later lookups are LDS reads instead
-  // of scalar loads that each tile would wait for.  The host keeps a unit
+  // of memory loads that each tile would wait for.  The host keeps a unit
   // within kPageTable page slots.
   __shared__ int32_t s_pages[kPageTable];
   int slot0 = 0;
