@@ -52,14 +52,19 @@ def algorithmic_bytes(p, window=0):
 
 
 def kernel_source_sha():
-    """Hash of the HIP sources: a traffic figure holds only for the kernel it was taken on."""
+    """Hash of the HIP sources with comments and whitespace removed: a traffic
+    figure holds only for the code it was taken on."""
     import glob
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "decode_attention_query_amd", "csrc", "*"))):
         if f.endswith((".hpp", ".hip")):
+            text = open(f).read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
             h.update(os.path.basename(f).encode())
-            h.update(open(f, "rb").read())
+            h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
