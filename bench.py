@@ -243,6 +243,10 @@ def main():
                     help="sliding window: attend only each request's last W rows (0: all)")
     ap.add_argument("--softcap", type=float, default=0.0,
                     help="logits soft-cap c: scores -> c * tanh(x / c) (0: off)")
+    ap.add_argument("--rotate", type=int, default=1,
+                    help="cycle the calls over this many distinct device copies of the K/V "
+                         "store (paged), as successive layers of a model would, so no call "
+                         "finds the previous call's rows in the 256 MB last-level cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe", action="store_true",
                     help="also measure the read probe and a device copy for context")
@@ -285,9 +289,13 @@ def main():
         lse = torch.empty((p.batch, p.num_qo_heads), dtype=torch.float32, device=dev)
         ws = fad.workspace_paged(p.batch, p.num_qo_heads, p.num_kv_heads, p.head_dim,
                                  p.page_size, p.total_used_pages, dev)
+        stores = [(k, v)] + [(k.clone(), v.clone()) for _ in range(args.rotate - 1)]
+        turn = [0]
 
         def step():
-            fad.decode_paged(q, k, v, ind, ptr, lpl, p.scale, o=o, lse=lse, workspace=ws,
+            ks, vs = stores[turn[0] % len(stores)]
+            turn[0] += 1
+            fad.decode_paged(q, ks, vs, ind, ptr, lpl, p.scale, o=o, lse=lse, workspace=ws,
                              layout=p.layout, window=args.window, softcap=args.softcap)
 
     for _ in range(args.warmup):
@@ -346,6 +354,7 @@ def main():
         "dtype": p.dtype,
         "data": "synthetic (seeded N(0,1) values, seeded page tables; no dataset)",
         "config": {**describe(p), "window": args.window, "softcap": args.softcap,
+                   "kv_copies_rotated": args.rotate,
                    "algorithmic_bytes_per_call": int(nbytes),
                    "chunk_rows": chunk, "heads_per_workgroup": gt,
                    "attention_kernel": "valu" if kind == 0 else "mfma"},
