@@ -276,24 +276,6 @@ DecodeParams base_params(int batch, int hq, int hkv, int d, int page_size, int p
   return p;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t fa_decode_workspace_size(int batch, int num_qo_heads, int num_kv_heads, int head_dim,
-                                int page_size, int total_used_pages) {
-  if (!extents_ok(batch, num_qo_heads, num_kv_heads, page_size) || !head_dim_ok(head_dim) ||
-      total_used_pages < 0)
-    return 0;
-  if (int64_t(total_used_pages) * page_size >= (int64_t(1) << 31)) return 0;
-  return make_plan(FA_DTYPE_BF16, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
-                   total_used_pages, false)
-      .total;
-}
-
-}  // extern "C"
-
-namespace {
 
 // Layout and score variants of one call (fa_decode_options_t, validated).
 struct Variant {
@@ -455,9 +437,55 @@ fa_status_t append_paged(int nhd, fa_dtype_t dtype, int batch, int num_kv_heads,
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+fa_status_t gather_paged(int nhd, fa_dtype_t dtype, int batch, int num_kv_heads, int head_dim,
+                         int page_size, int num_total_pages, int total_used_pages,
+                         const void *data, const int32_t *indices, const int32_t *indptr,
+                         const int32_t *last_page_len, void *out, int64_t out_rows,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return FA_ERR_UNSUPPORTED;
+  if (!extents_ok(batch, num_kv_heads, num_kv_heads, page_size) || num_total_pages <= 0)
+    return FA_ERR_INVALID_PROBLEM;
+  if (!head_dim_ok(head_dim)) return FA_ERR_UNSUPPORTED;
+  if (total_used_pages < 0 || out_rows < 0) return FA_ERR_INVALID_PROBLEM;
+  if (!data || !indptr || !last_page_len || !out || (!indices && total_used_pages > 0))
+    return FA_ERR_INVALID_PROBLEM;
+  if (int64_t(total_used_pages) * page_size >= (int64_t(1) << 31)) return FA_ERR_UNSUPPORTED;
+  if (!pool_size_ok(num_total_pages, num_kv_heads, page_size, head_dim))
+    return FA_ERR_UNSUPPORTED;
+  const size_t need = fa_decode_workspace_size(batch, num_kv_heads, num_kv_heads, head_dim,
+                                               page_size, total_used_pages);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
+  const HostPlan hp = make_plan(dtype, batch, num_kv_heads, num_kv_heads, head_dim, page_size,
+                                total_used_pages, false);
+  DecodeParams p = base_params(batch, num_kv_heads, num_kv_heads, head_dim, page_size,
+                               num_total_pages, total_used_pages, 1.0f, hp);
+  p.k = data;
+  p.indices = indices;
+  p.indptr = indptr;
+  p.last_page_len = last_page_len;
+  p.nhd = nhd;
+  carve(p, hp, workspace);
+  const int elem = dtype == FA_DTYPE_F32 ? 4 : 2;
+  hipLaunchKernelGGL(fa::gather_kernel, dim3(hp.units_bound, num_kv_heads), dim3(256), 0,
+                     stream, p, out, out_rows, elem);
+  if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t fa_decode_workspace_size(int batch, int num_qo_heads, int num_kv_heads, int head_dim,
+                                int page_size, int total_used_pages) {
+  if (!extents_ok(batch, num_qo_heads, num_kv_heads, page_size) || !head_dim_ok(head_dim) ||
+      total_used_pages < 0)
+    return 0;
+  if (int64_t(total_used_pages) * page_size >= (int64_t(1) << 31)) return 0;
+  return make_plan(FA_DTYPE_BF16, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                   total_used_pages, false)
+      .total;
+}
 
 fa_status_t fa_append_paged(fa_dtype_t dtype, int batch, int num_kv_heads, int head_dim,
                             int page_size, int num_total_pages, int total_used_pages,
@@ -561,49 +589,6 @@ const char *fa_status_string(fa_status_t status) {
 }
 
 // ------------------------------------------------------------------- hooks
-
-}  // extern "C"
-
-namespace {
-
-fa_status_t gather_paged(int nhd, fa_dtype_t dtype, int batch, int num_kv_heads, int head_dim,
-                         int page_size, int num_total_pages, int total_used_pages,
-                         const void *data, const int32_t *indices, const int32_t *indptr,
-                         const int32_t *last_page_len, void *out, int64_t out_rows,
-                         void *workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (!dtype_ok(dtype)) return FA_ERR_UNSUPPORTED;
-  if (!extents_ok(batch, num_kv_heads, num_kv_heads, page_size) || num_total_pages <= 0)
-    return FA_ERR_INVALID_PROBLEM;
-  if (!head_dim_ok(head_dim)) return FA_ERR_UNSUPPORTED;
-  if (total_used_pages < 0 || out_rows < 0) return FA_ERR_INVALID_PROBLEM;
-  if (!data || !indptr || !last_page_len || !out || (!indices && total_used_pages > 0))
-    return FA_ERR_INVALID_PROBLEM;
-  if (int64_t(total_used_pages) * page_size >= (int64_t(1) << 31)) return FA_ERR_UNSUPPORTED;
-  if (!pool_size_ok(num_total_pages, num_kv_heads, page_size, head_dim))
-    return FA_ERR_UNSUPPORTED;
-  const size_t need = fa_decode_workspace_size(batch, num_kv_heads, num_kv_heads, head_dim,
-                                               page_size, total_used_pages);
-  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
-  const HostPlan hp = make_plan(dtype, batch, num_kv_heads, num_kv_heads, head_dim, page_size,
-                                total_used_pages, false);
-  DecodeParams p = base_params(batch, num_kv_heads, num_kv_heads, head_dim, page_size,
-                               num_total_pages, total_used_pages, 1.0f, hp);
-  p.k = data;
-  p.indices = indices;
-  p.indptr = indptr;
-  p.last_page_len = last_page_len;
-  p.nhd = nhd;
-  carve(p, hp, workspace);
-  const int elem = dtype == FA_DTYPE_F32 ? 4 : 2;
-  hipLaunchKernelGGL(fa::gather_kernel, dim3(hp.units_bound, num_kv_heads), dim3(256), 0,
-                     stream, p, out, out_rows, elem);
-  if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
-  return FA_OK;
-}
-
-}  // namespace
-
-extern "C" {
 
 fa_status_t fa_debug_gather_paged(fa_dtype_t dtype, int batch, int num_kv_heads, int head_dim,
                                   int page_size, int num_total_pages, int total_used_pages,
