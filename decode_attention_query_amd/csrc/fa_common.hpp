@@ -146,6 +146,9 @@ struct F16 {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 // 16-byte load with the streaming (non-temporal) hint: K/V rows are read once.
 __device__ inline uint4 load16_stream(const void *ptr) {
   const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4 *>(ptr));

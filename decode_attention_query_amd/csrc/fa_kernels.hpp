@@ -256,6 +256,23 @@ __device__ inline void emit(const DecodeParams &p, const UnitInfo &u, int h, int
 __device__ inline float coherent_load(const float *ptr) {
   return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// The same for 16 bytes: a buffer load with the sc1 cache-policy bit, which
+// is what an agent-scope atomic load sets, so the data comes from memory and
+// not from a line this XCD's L2 may still hold from an earlier call.  The
+// resource covers 2 GiB from `base` (raw buffer, 32-bit data format, the
+// gfx9 descriptor word); voff + soff stays far below that.
+constexpr int kCachePolicySc1 = 16;
+
+__device__ inline __amdgpu_buffer_rsrc_t coherent_rsrc(const float *base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, 0x7fffffff,
+                                           0x00020000);
+}
+
+__device__ inline f32x4 coherent_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(
+      f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCachePolicySc1));
+}
 //
 // Combines request b's split partials (o_s normalised over its rows, lse_s in
 // base 2) for query heads h0 .. h0 + gt - 1; every thread of the nw-wave
@@ -266,12 +283,27 @@ __device__ inline float coherent_load(const float *ptr) {
 // and W, fixed butterfly order), so the result is reproducible bit for bit.
 //
 // Latency: the merge runs at the very end of one workgroup per (request, head
-// block), so it is kept to few dependent memory round trips.  A request of up
-// to 64 units reads each lse once (one per lane); the weights 2^(lse_s - M) of
-// up to `cap` units at a time are staged in LDS (s_w, the kernel's tile area,
-// free by now), so the output loop issues only its partial-output loads, 16
-// in flight per thread.
+// block), so it is kept to few dependent memory round trips and little code
+// (it runs once per workgroup, from a cold instruction cache).  With up to 64
+// units, each wave loads the lse of four of its heads at a time (one unit per
+// lane) and writes the weights 2^(lse_s - M) straight to LDS (s_w, the
+// kernel's tile area, free by now); with more, the lse is read per head and
+// the weights of up to `cap` units at a time are staged.  The partial outputs
+// are then read 16 bytes per load, one 4-feature column per thread, kDepth
+// units in flight (kDepth is what the kernel's register budget leaves room
+// for) and the last units four at a time.
 template <class E>
+__device__ inline void store4(typename E::raw *out, const f32x4 &v) {
+  if constexpr (E::kBytes == 4) {
+    *reinterpret_cast<f32x4 *>(out) = v;
+  } else {
+    const uint32_t lo = (uint32_t)E::narrow(v[0]) | ((uint32_t)E::narrow(v[1]) << 16);
+    const uint32_t hi = (uint32_t)E::narrow(v[2]) | ((uint32_t)E::narrow(v[3]) << 16);
+    *reinterpret_cast<uint2 *>(out) = make_uint2(lo, hi);
+  }
+}
+
+template <class E, int kDepth>
 __device__ void merge_partials(const DecodeParams &p, int b, int u0, int n, int h0, int gt, int nw,
                                float *s_stat /* LDS [32] */, float *s_w, int w_cap) {
   const int tid = threadIdx.x;
@@ -279,41 +311,64 @@ __device__ void merge_partials(const DecodeParams &p, int b, int u0, int n, int 
   const int wave = tid / kWave;
   const int nthreads = nw * kWave;
   const int hq = p.num_qo_heads;
+  const int D = p.head_dim;
   const float *lse_base = p.part_lse + (int64_t)u0 * hq + h0;
-  for (int g = wave; g < gt; g += nw) {
-    float mx, w;
-    if (n <= kWave) {
-      const float v = lane < n ? coherent_load(lse_base + (int64_t)lane * hq + g) : -INFINITY;
-      mx = wave_max(v);
-      w = wave_sum(lane < n ? fast_exp2(v - safe_ref(mx)) : 0.0f);
-    } else {
-      mx = -INFINITY;
-      for (int s = lane; s < n; s += kWave) mx = fmaxf(mx, coherent_load(lse_base + (int64_t)s * hq + g));
+  const int cap = max(1, w_cap / gt);  // units whose weights fit s_w at once
+  const bool resident = n <= kWave && n <= cap;
+  if (resident) {
+    const float *lrow = lse_base + (int64_t)min(lane, n - 1) * hq;
+    for (int g0 = wave; g0 < gt; g0 += 4 * nw) {
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = coherent_load(lrow + min(g0 + j * nw, gt - 1));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int g = g0 + j * nw;
+        if (g < gt) {
+          const float x = lane < n ? v[j] : -INFINITY;
+          const float mx = wave_max(x);
+          const float e = lane < n ? fast_exp2(x - safe_ref(mx)) : 0.0f;
+          const float w = wave_sum(e);
+          if (lane < n) s_w[lane * gt + g] = e;
+          if (lane == 0) {
+            s_stat[g] = mx;
+            s_stat[16 + g] = w;
+          }
+        }
+      }
+    }
+    __syncthreads();
+  } else {
+    for (int g = wave; g < gt; g += nw) {
+      float mx = -INFINITY;
+      for (int s = lane; s < n; s += kWave)
+        mx = fmaxf(mx, coherent_load(lse_base + (int64_t)s * hq + g));
       mx = wave_max(mx);
       const float ref = safe_ref(mx);
-      w = 0.0f;
-      for (int s = lane; s < n; s += kWave) w += fast_exp2(coherent_load(lse_base + (int64_t)s * hq + g) - ref);
+      float w = 0.0f;
+      for (int s = lane; s < n; s += kWave)
+        w += fast_exp2(coherent_load(lse_base + (int64_t)s * hq + g) - ref);
       w = wave_sum(w);
-    }
-    if (lane == 0) {
-      s_stat[g] = mx;
-      s_stat[16 + g] = w;
+      if (lane == 0) {
+        s_stat[g] = mx;
+        s_stat[16 + g] = w;
+      }
     }
   }
-  const int D = p.head_dim;
-  const int cap = max(1, w_cap / gt);  // units whose weights fit s_w at once
+  const int q4 = D / 4;  // 4-feature columns per head
+  const int cols = gt * q4;
+  const uint32_t ustride = (uint32_t)hq * (uint32_t)D * 4u;  // bytes between units
   // uniform trip counts: every thread reaches every barrier
-  for (int base = 0; base < gt * D; base += nthreads) {
-    const int idx = base + tid;
-    const bool live = idx < gt * D;
-    const int g = live ? idx / D : 0;
-    const int d = idx - g * D;
-    const int h = h0 + g;
-    float a = 0.0f;
+  for (int c0 = 0; c0 < cols; c0 += nthreads) {
+    const int c = min(c0 + tid, cols - 1);
+    const int g = c / q4;
+    const uint32_t voff = (uint32_t)(g * D + 4 * (c - g * q4)) * 4u;
+    const bool wave_live = c0 + wave * kWave < cols;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int s0 = 0; s0 < n; s0 += cap) {
       const int cn = min(cap, n - s0);
-      if (base == 0 || n > cap) {  // stage the weights of units s0 .. s0 + cn
-        __syncthreads();           // s_stat written; earlier weights no longer read
+      if (!resident && (c0 == 0 || n > cap)) {  // stage the weights of units s0 .. s0 + cn
+        __syncthreads();                        // s_stat written; earlier weights no longer read
         for (int i = tid; i < cn * gt; i += nthreads) {
           const int s = i / gt;
           const int gg = i - s * gt;
@@ -322,19 +377,43 @@ __device__ void merge_partials(const DecodeParams &p, int b, int u0, int n, int 
         }
         __syncthreads();
       }
-      if (live) {
-        const float *o_base = p.part_o + ((int64_t)(u0 + s0) * hq + h) * D + d;
-#pragma unroll 16
-        for (int s = 0; s < cn; ++s)
-          a = fmaf(s_w[s * gt + g], coherent_load(o_base + (int64_t)s * hq * D), a);
+      if (!wave_live) continue;
+      const float *o_base = p.part_o + ((int64_t)(u0 + s0) * hq + h0) * D;
+      int sb = 0;
+      for (; sb + kDepth <= cn; sb += kDepth) {
+        const __amdgpu_buffer_rsrc_t r = coherent_rsrc(o_base + (int64_t)sb * hq * D);
+        f32x4 x[kDepth];
+#pragma unroll
+        for (int k = 0; k < kDepth; ++k) x[k] = coherent_load4(r, voff, k * ustride);
+#pragma unroll
+        for (int k = 0; k < kDepth; ++k) {
+          const float w = s_w[(sb + k) * gt + g];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, x[k][e], acc[e]);
+        }
+      }
+      for (; sb < cn; sb += 4) {  // the last 1 .. kDepth - 1 units
+        const int rem = cn - sb;
+        const __amdgpu_buffer_rsrc_t r = coherent_rsrc(o_base + (int64_t)sb * hq * D);
+        f32x4 x[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) x[k] = coherent_load4(r, voff, min(k, rem - 1) * ustride);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float w = s_w[(sb + min(k, rem - 1)) * gt + g];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] = k < rem ? fmaf(w, x[k][e], acc[e]) : acc[e];
+        }
       }
     }
-    if (live) {
+    if (c0 + tid < cols) {
       const float mx = s_stat[g];
       const float W = s_stat[16 + g];
       const bool any = W > 0.0f;
-      const int64_t orow = (int64_t)b * hq + h;
-      static_cast<typename E::raw *>(p.o)[orow * D + d] = E::narrow(any ? a / W : 0.0f);
+      const int64_t orow = (int64_t)b * hq + h0 + g;
+      const int d = 4 * (c - g * q4);
+      const f32x4 o4 = any ? acc / W : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      store4<E>(static_cast<typename E::raw *>(p.o) + orow * D + d, o4);
       if (d == 0 && p.lse) p.lse[orow] = any ? (mx + fast_log2(W)) * kLn2 : -INFINITY;
     }
   }
@@ -380,7 +459,7 @@ __device__ inline bool count_in_is_last(const DecodeParams &p, unsigned long lon
   return (old & ((1ull << kCountBits) - 1)) + 1 == (unsigned long long)n_units;
 }
 
-template <class E>
+template <class E, int kDepth>
 __device__ void finish_split(const DecodeParams &p, const UnitInfo &u, int plane, int h0, int gt, int nw,
                              float *s_stat, int *s_last, float *s_w, int w_cap) {
   if (u.n_units <= 1) return;
@@ -394,7 +473,7 @@ __device__ void finish_split(const DecodeParams &p, const UnitInfo &u, int plane
   if (threadIdx.x == 0)
     __hip_atomic_store(counter, (unsigned long long)p.call_tag << kCountBits, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
-  merge_partials<E>(p, u.b, u.u0, u.n_units, h0, gt, nw, s_stat, s_w, w_cap);
+  merge_partials<E, kDepth>(p, u.b, u.u0, u.n_units, h0, gt, nw, s_stat, s_w, w_cap);
 }
 
 // ------------------------------------------------------ vector-ALU decode
@@ -579,7 +658,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   }
   __shared__ float s_stat[32];
   __shared__ int s_last;
-  finish_split<E>(p, u, blockIdx.y, h0, GT, NW, s_stat, &s_last, &s_acc[0][0][0],
+  finish_split<E, 8>(p, u, blockIdx.y, h0, GT, NW, s_stat, &s_last, &s_acc[0][0][0],
                   NW * GT * D);
 }
 

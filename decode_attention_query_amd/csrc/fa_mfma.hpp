@@ -34,9 +34,6 @@
 
 namespace fa {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
 template <class E>
 struct Mfma;
 
@@ -406,7 +403,8 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
     }
     emit<E>(p, u, h0 + g, d, Mx, lsum, a);
   }
-  finish_split<E>(p, u, plane, h0, gt, NW, s_stat, &s_last, reinterpret_cast<float *>(lds),
+  // merge depth: the main loop already needs more registers than 16 at D >= 128
+  finish_split<E, (D >= 128 ? 16 : 8)>(p, u, plane, h0, gt, NW, s_stat, &s_last, reinterpret_cast<float *>(lds),
                   G::LDS / 4);
 }
 
