@@ -79,7 +79,8 @@ struct DecodeParams {
   // workspace regions
   float *part_lse;        // [units_bound, Hq]     base-2 lse of each split's partial
   float *part_o;          // [units_bound, Hq, D]  normalised partial outputs
-  uint64_t *arrivals;     // [B, Hq]  per (request, head block): call tag << kCountBits | units done
+  uint64_t *arrivals;     // [B, Hq, kArrivalStride]  per (request, head block), first word:
+                          // call tag << kCountBits | units done
   uint64_t call_tag;      // this call's tag (< 2^40), different for every call
 };
 
@@ -87,6 +88,12 @@ struct DecodeParams {
 // counter left by an earlier call (or never written) reads as zero and the
 // workspace needs no clearing between calls.
 constexpr int kCountBits = 24;  // a request has fewer than 2^24 split units
+
+// 64-bit words from one arrival counter to the next: 128 bytes, one cache line
+// each.  Atomics on one line are serialised where they are performed, and the
+// units of one request finish close together, so counters that shared a line
+// queued behind each other (a 16-unit request on 8 head blocks: 128 atomics).
+constexpr int kArrivalStride = 16;
 
 // ---------------------------------------------------------------- elements
 //

@@ -94,8 +94,9 @@ HostPlan make_plan(fa_dtype_t dt, int batch, int hq, int hkv, int d, int page_si
   size_t off = 0;
   hp.part_lse = off;    off = align_up(off + sizeof(float) * size_t(hp.units_bound) * hq);
   hp.part_o = off;      off = align_up(off + sizeof(float) * size_t(hp.units_bound) * hq * d);
-  // one counter per (request, head block); Hq per request bounds the blocks
-  hp.arrivals = off;    off = align_up(off + sizeof(uint64_t) * size_t(batch) * hq);
+  // one counter line per (request, head block); Hq per request bounds the blocks
+  hp.arrivals = off;
+  off = align_up(off + sizeof(uint64_t) * fa::kArrivalStride * size_t(batch) * hq);
   hp.total = off;
   return hp;
 }

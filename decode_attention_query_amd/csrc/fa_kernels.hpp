@@ -466,7 +466,7 @@ __device__ void finish_split(const DecodeParams &p, const UnitInfo &u, int plane
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   unsigned long long *counter = reinterpret_cast<unsigned long long *>(
-      p.arrivals + (int64_t)u.b * p.num_qo_heads + plane);
+      p.arrivals + ((int64_t)u.b * p.num_qo_heads + plane) * kArrivalStride);
   if (threadIdx.x == 0) *s_last = count_in_is_last(p, counter, u.n_units);
   __syncthreads();
   if (!*s_last) return;

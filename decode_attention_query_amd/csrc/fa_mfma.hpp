@@ -403,9 +403,10 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
     }
     emit<E>(p, u, h0 + g, d, Mx, lsum, a);
   }
-  // merge depth: the main loop already needs more registers than 16 at D >= 128
-  finish_split<E, (D >= 128 ? 16 : 8)>(p, u, plane, h0, gt, NW, s_stat, &s_last, reinterpret_cast<float *>(lds),
-                  G::LDS / 4);
+  // merge depth 16 where the main loop's register peak already covers it
+  // (D >= 128); 8 at D = 64, where 16 would cost occupancy
+  finish_split<E, (D >= 128 ? 16 : 8)>(p, u, plane, h0, gt, NW, s_stat, &s_last,
+                                        reinterpret_cast<float *>(lds), G::LDS / 4);
 }
 
 }  // namespace fa
