@@ -80,14 +80,17 @@ struct DecodeParams {
   float *part_lse;        // [units_bound, Hq]     base-2 lse of each split's partial
   float *part_o;          // [units_bound, Hq, D]  normalised partial outputs
   uint64_t *arrivals;     // [B, Hq, kArrivalStride]  per (request, head block), first word:
-                          // call tag << kCountBits | units done
-  uint64_t call_tag;      // this call's tag (< 2^40), different for every call
+                          // kArrivalMark << kCountBits | units done
 };
 
-// Arrival counters carry the tag of the call that last counted in them, so a
-// counter left by an earlier call (or never written) reads as zero and the
-// workspace needs no clearing between calls.
+// An arrival counter at rest holds kArrivalMark << kCountBits (count 0): the
+// merging workgroup leaves it so.  A counter without the mark -- a workspace
+// never used, or last used for something else -- is stale and is set to rest
+// by the first unit that meets it, so the workspace needs no clearing.  The
+// mark's upper 32 bits are a NaN with a payload no arithmetic produces, so
+// left-over partial results (finite floats) never look like a counter.
 constexpr int kCountBits = 24;  // a request has fewer than 2^24 split units
+constexpr unsigned long long kArrivalMark = 0x7FF3A5C35Aull;  // 40 bits
 
 // 64-bit words from one arrival counter to the next: 128 bytes, one cache line
 // each.  Atomics on one line are serialised where they are performed, and the

@@ -4,12 +4,9 @@
 
 #include <algorithm>
 #include <array>
-#include <atomic>
-#include <chrono>
 #include <cmath>
 #include <cstdint>
 #include <mutex>
-#include <random>
 #include <vector>
 
 #include "../../include/fa_decode.h"
@@ -111,24 +108,6 @@ void carve(DecodeParams &p, const HostPlan &hp, void *ws) {
   p.part_lse = reinterpret_cast<float *>(w + hp.part_lse);
   p.part_o = reinterpret_cast<float *>(w + hp.part_o);
   p.arrivals = reinterpret_cast<uint64_t *>(w + hp.arrivals);
-}
-
-// Call tags: distinct for every call of the process, in [2^39, 2^40), starting
-// at a random point so that a counter word left in memory by anything else
-// is unlikely to carry a live tag.
-uint64_t first_call_tag() {
-  uint64_t r = uint64_t(std::chrono::steady_clock::now().time_since_epoch().count());
-  try {
-    std::random_device rd;
-    r ^= (uint64_t(rd()) << 32) ^ rd();
-  } catch (...) {
-  }
-  return (uint64_t(1) << 39) | (r & ((uint64_t(1) << 38) - 1));
-}
-
-uint64_t next_call_tag() {
-  static std::atomic<uint64_t> next{first_call_tag()};
-  return next.fetch_add(1, std::memory_order_relaxed) & ((uint64_t(1) << 40) - 1);
 }
 
 // ------------------------------------------------------------------ timing
@@ -347,7 +326,6 @@ fa_status_t decode_contig(const Variant &var, fa_dtype_t dtype, int num_qo_heads
   const int rows = valid_kv_len - p.contig_lo;
   p.contig_units = rows == 0 ? 1 : int((int64_t(rows) + hp.chunk - 1) / hp.chunk);
   carve(p, hp, workspace);
-  p.call_tag = next_call_tag();
 
   CallEvents ev(stream);
   ev.mark(1, stream);
@@ -395,7 +373,6 @@ fa_status_t decode_paged(const Variant &var, fa_dtype_t dtype, int batch, int nu
   p.last_page_len = last_page_len;
   apply_variant(p, var);
   carve(p, hp, workspace);
-  p.call_tag = next_call_tag();
 
   CallEvents ev(stream);
   ev.mark(1, stream);

@@ -430,21 +430,19 @@ __device__ void merge_partials(const DecodeParams &p, int b, int u0, int n, int 
 // write-back or invalidate (what a device-scope fence would emit, once per
 // workgroup) is needed, because no non-coherent data crosses workgroups.
 //
-// The counter holds (call tag << kCountBits) | units counted.  A unit counts
-// in with one atomic add; the add also returns the tag, and a tag that is not
-// this call's marks a stale counter (left by an earlier call, or never
-// written).  Then the unit installs (this call's tag, 0) with compare-and-swap
-// -- unless another unit already did -- and adds again.  Adds made to the
-// stale value vanish with it, but every unit that made one saw the stale tag
-// and adds again after the install, so each unit is counted once.  The swap
-// loop ends: a failed swap means another unit added to the stale value (fewer
-// than n_units can) or installed the tag (which ends the loop).  Units of one
-// request that finish together thus cost one add each, not a queue of
-// swaps.  The merging workgroup leaves the counter at (tag, 0), so replaying
-// the same launch (a captured graph) also starts from zero.
-__device__ inline bool count_in_is_last(const DecodeParams &p, unsigned long long *counter,
-                                        int n_units) {
-  const unsigned long long tag = p.call_tag;
+// The counter holds (kArrivalMark << kCountBits) | units counted.  A unit
+// counts in with one atomic add, which also returns the mark; a counter
+// without it is stale (never used, or left by other data).  Then the unit
+// sets it to rest, (mark, 0), with compare-and-swap -- unless another unit
+// already did -- and adds again.  Adds made to the stale value vanish with it,
+// but every unit that made one saw the stale value and adds again after the
+// swap, so each unit is counted once.  The swap loop ends: a failed swap means
+// another unit added to the stale value (fewer than n_units can) or set the
+// mark (which ends the loop).  The merging workgroup puts the counter back to
+// rest, so the next call, or a replay of a captured graph, counts in with a
+// single add per unit; only a counter's first use pays for the swap.
+__device__ inline bool count_in_is_last(unsigned long long *counter, int n_units) {
+  const unsigned long long tag = kArrivalMark;
   unsigned long long old = atomicAdd(counter, 1ull);
   if ((old >> kCountBits) != tag) {
     unsigned long long seen = __hip_atomic_load(counter, __ATOMIC_RELAXED,
@@ -467,11 +465,11 @@ __device__ void finish_split(const DecodeParams &p, const UnitInfo &u, int plane
   __syncthreads();
   unsigned long long *counter = reinterpret_cast<unsigned long long *>(
       p.arrivals + ((int64_t)u.b * p.num_qo_heads + plane) * kArrivalStride);
-  if (threadIdx.x == 0) *s_last = count_in_is_last(p, counter, u.n_units);
+  if (threadIdx.x == 0) *s_last = count_in_is_last(counter, u.n_units);
   __syncthreads();
   if (!*s_last) return;
   if (threadIdx.x == 0)
-    __hip_atomic_store(counter, (unsigned long long)p.call_tag << kCountBits, __ATOMIC_RELAXED,
+    __hip_atomic_store(counter, kArrivalMark << kCountBits, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   merge_partials<E, kDepth>(p, u.b, u.u0, u.n_units, h0, gt, nw, s_stat, s_w, w_cap);
 }

@@ -79,9 +79,12 @@ typedef enum {
  *   contiguous calls:  fa_decode_workspace_size(1, Hq, Hkv, D, max_kv_len, 1)
  * Returns 0 when the arguments are not a valid problem (the entry point then
  * reports why); otherwise a positive size.  The workspace holds the split
- * partial results and one arrival counter per (request, head block); each
- * counter is tagged with the call that last used it, so the workspace needs no
- * initialisation and may hold anything between calls. */
+ * partial results and one arrival counter per (request, head block).  A
+ * counter at rest carries a fixed mark and a count of zero, and each call
+ * leaves its counters at rest; a counter without the mark is reset by the
+ * first unit that meets it.  So the workspace needs no initialisation and may
+ * hold anything between calls (a first use costs each counter one extra
+ * compare-and-swap). */
 size_t fa_decode_workspace_size(int batch, int num_qo_heads, int num_kv_heads, int head_dim,
                                 int page_size, int total_used_pages);
 

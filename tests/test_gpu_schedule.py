@@ -138,9 +138,32 @@ def test_garbage_workspace(dev):
     compare(p.dtype, ref_o, ref_l, ro, rl, p.name)
 
 
+def test_workspace_shared_across_shapes(dev):
+    """One workspace buffer serving calls of different shapes in turn: each
+    call finds counters that the other shape left as partial results or at
+    rest at other offsets, and still matches a call on a fresh workspace."""
+    pa = _split_problem(seed=81)
+    pb = W.make_paged("split-mix-b", "f16", 5, 8, 2, 64, 16, 82,
+                      lens=np.array([20000, 3, 0, 7777, 16384]), pool_slack=0.1)
+    da, db = to_dev(pa, dev), to_dev(pb, dev)
+    refs = [run(pa, da), run(pb, db)]
+    torch.cuda.synchronize()
+    sizes = [fad.workspace_paged(q.batch, q.num_qo_heads, q.num_kv_heads, q.head_dim,
+                                 q.page_size, q.total_used_pages, dev).numel() for q in (pa, pb)]
+    ws = torch.empty(max(sizes), dtype=torch.uint8, device=dev)
+    for step, (q, d, ref) in enumerate([(pa, da, refs[0]), (pb, db, refs[1]), (pa, da, refs[0]),
+                                        (pb, db, refs[1]), (pb, db, refs[1])]):
+        o, l = run(q, d, workspace=ws[:sizes[0 if q is pa else 1]])
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref[0]) and torch.equal(l, ref[1]), f"step {step} ({q.name})"
+    for q, ref in ((pa, refs[0]), (pb, refs[1])):
+        ro, rl = oracle_of(q)
+        compare(q.dtype, ref[0], ref[1], ro, rl, q.name)
+
+
 def test_graph_replay(dev):
-    """A captured call replays correctly again and again (the merge counters
-    return to zero for the same call tag), with eager work in between."""
+    """A captured call replays correctly again and again (each merge leaves its
+    arrival counter at rest), with eager work in between."""
     p = _split_problem(seed=78)
     d = to_dev(p, dev)
     ws = fad.workspace_paged(p.batch, p.num_qo_heads, p.num_kv_heads, p.head_dim,
