@@ -6,6 +6,7 @@
 #include <array>
 #include <cmath>
 #include <cstdint>
+#include <initializer_list>
 #include <mutex>
 #include <vector>
 
@@ -228,6 +229,22 @@ bool dtype_ok(fa_dtype_t dt) {
   return dt == FA_DTYPE_F32 || dt == FA_DTYPE_F16 || dt == FA_DTYPE_BF16;
 }
 
+// The kernels move q, K, V, o and workspace data 16 bytes per access and
+// int32 / f32 arrays 4 bytes per access; row strides (D * element size >= 128
+// bytes) keep every row at the alignment of its base.  NULL counts as aligned.
+bool aligned(const void *ptr, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0;
+}
+
+bool all_aligned(std::initializer_list<const void *> wide,
+                 std::initializer_list<const void *> narrow) {
+  for (const void *ptr : wide)
+    if (!aligned(ptr, 16)) return false;
+  for (const void *ptr : narrow)
+    if (!aligned(ptr, 4)) return false;
+  return true;
+}
+
 // Elements of a [pages, Hkv, P, D] pool must stay far inside int64 offsets.
 bool pool_size_ok(int pages, int hkv, int page_size, int d) {
   const double n = double(pages) * hkv * page_size * d;
@@ -270,7 +287,7 @@ fa_status_t read_options(const fa_decode_options_t *opts, Variant &v) {
   if (!opts) return FA_OK;
   if (opts->kv_layout != 0 && opts->kv_layout != 1) return FA_ERR_UNSUPPORTED;
   if (opts->window < 0 || !(opts->logits_soft_cap >= 0.0f) ||
-      !std::isfinite(opts->logits_soft_cap))
+      !std::isfinite(opts->logits_soft_cap) || !aligned(opts->alibi_slopes, 4))
     return FA_ERR_INVALID_PROBLEM;
   v.nhd = opts->kv_layout;
   v.window = opts->window;
@@ -299,6 +316,7 @@ fa_status_t decode_contig(const Variant &var, fa_dtype_t dtype, int num_qo_heads
   if (!head_dim_ok(head_dim)) return FA_ERR_UNSUPPORTED;
   if (!grid_ok(num_qo_heads, num_kv_heads)) return FA_ERR_UNSUPPORTED;
   if (!q || !k_cache || !v_cache || !o) return FA_ERR_INVALID_PROBLEM;
+  if (!all_aligned({q, k_cache, v_cache, o, workspace}, {lse})) return FA_ERR_INVALID_PROBLEM;
   if (valid_kv_len < 0 || valid_kv_len > max_kv_len) return FA_ERR_INVALID_PROBLEM;
   if (!pool_size_ok(1, num_kv_heads, max_kv_len, head_dim)) return FA_ERR_UNSUPPORTED;
   const size_t need =
@@ -351,6 +369,8 @@ fa_status_t decode_paged(const Variant &var, fa_dtype_t dtype, int batch, int nu
   if (!q || !k_data || !v_data || !indptr || !last_page_len || !o || !lse ||
       (!indices && total_used_pages > 0))
     return FA_ERR_INVALID_PROBLEM;
+  if (!all_aligned({q, k_data, v_data, o, workspace}, {indices, indptr, last_page_len, lse}))
+    return FA_ERR_INVALID_PROBLEM;
   if (int64_t(total_used_pages) * page_size >= (int64_t(1) << 31)) return FA_ERR_UNSUPPORTED;
   if (!pool_size_ok(num_total_pages, num_kv_heads, page_size, head_dim))
     return FA_ERR_UNSUPPORTED;
@@ -395,6 +415,8 @@ fa_status_t append_paged(int nhd, fa_dtype_t dtype, int batch, int num_kv_heads,
   if (!k_new || !v_new || !indptr || !last_page_len || !k_data || !v_data ||
       (!indices && total_used_pages > 0))
     return FA_ERR_INVALID_PROBLEM;
+  if (!all_aligned({k_new, v_new, k_data, v_data}, {indices, indptr, last_page_len}))
+    return FA_ERR_INVALID_PROBLEM;
   if (int64_t(total_used_pages) * page_size >= (int64_t(1) << 31)) return FA_ERR_UNSUPPORTED;
   if (!pool_size_ok(num_total_pages, num_kv_heads, page_size, head_dim))
     return FA_ERR_UNSUPPORTED;
@@ -426,6 +448,8 @@ fa_status_t gather_paged(int nhd, fa_dtype_t dtype, int batch, int num_kv_heads,
   if (!head_dim_ok(head_dim)) return FA_ERR_UNSUPPORTED;
   if (total_used_pages < 0 || out_rows < 0) return FA_ERR_INVALID_PROBLEM;
   if (!data || !indptr || !last_page_len || !out || (!indices && total_used_pages > 0))
+    return FA_ERR_INVALID_PROBLEM;
+  if (!all_aligned({data, out, workspace}, {indices, indptr, last_page_len}))
     return FA_ERR_INVALID_PROBLEM;
   if (int64_t(total_used_pages) * page_size >= (int64_t(1) << 31)) return FA_ERR_UNSUPPORTED;
   if (!pool_size_ok(num_total_pages, num_kv_heads, page_size, head_dim))
@@ -600,6 +624,7 @@ fa_status_t fa_debug_schedule(fa_dtype_t dtype, int batch, int num_qo_heads, int
   if (!head_dim_ok(head_dim)) return FA_ERR_UNSUPPORTED;
   if (total_used_pages < 0) return FA_ERR_INVALID_PROBLEM;
   if (!indptr || !last_page_len || !out) return FA_ERR_INVALID_PROBLEM;
+  if (!all_aligned({}, {indptr, last_page_len, out})) return FA_ERR_INVALID_PROBLEM;
   if (int64_t(total_used_pages) * page_size >= (int64_t(1) << 31)) return FA_ERR_UNSUPPORTED;
   const HostPlan hp = make_plan(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
                                 total_used_pages, false);
@@ -614,7 +639,7 @@ fa_status_t fa_debug_schedule(fa_dtype_t dtype, int batch, int num_qo_heads, int
 
 fa_status_t fa_debug_read_probe(const void *buf, size_t bytes, uint32_t *sink,
                                 hipStream_t stream) {
-  if (!buf || !sink || bytes == 0 || bytes % fa::kProbeBlock != 0)
+  if (!buf || !sink || bytes == 0 || bytes % fa::kProbeBlock != 0 || !all_aligned({buf}, {sink}))
     return FA_ERR_INVALID_PROBLEM;
   const int64_t n_blocks = int64_t(bytes / fa::kProbeBlock);
   hipLaunchKernelGGL(fa::read_probe_kernel, dim3(8192), dim3(256), 0, stream,

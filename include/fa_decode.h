@@ -106,6 +106,8 @@ size_t fa_decode_workspace_size(int batch, int num_qo_heads, int num_kv_heads, i
  *   head_dim not 64, 128 or 256                              -> FA_ERR_UNSUPPORTED
  *   num_qo_heads > 65535                                     -> FA_ERR_UNSUPPORTED
  *   q, k_cache, v_cache or o NULL                            -> FA_ERR_INVALID_PROBLEM
+ *   q, k_cache, v_cache, o or workspace not 16-byte aligned,
+ *     or lse not 4-byte aligned                              -> FA_ERR_INVALID_PROBLEM
  *   valid_kv_len < 0 or > max_kv_len                         -> FA_ERR_INVALID_PROBLEM
  *   Hkv * max_kv_len * D >= 10^15 elements                   -> FA_ERR_UNSUPPORTED
  *   workspace NULL or workspace_bytes short                  -> FA_ERR_WORKSPACE_TOO_SMALL
@@ -154,6 +156,8 @@ fa_status_t fa_decode_contig(fa_dtype_t dtype, int num_qo_heads, int num_kv_head
  *   num_qo_heads > 65535                                      -> FA_ERR_UNSUPPORTED
  *   q, k_data, v_data, indptr, last_page_len, o or lse NULL,
  *     or indices NULL with total_used_pages > 0               -> FA_ERR_INVALID_PROBLEM
+ *   q, k_data, v_data, o or workspace not 16-byte aligned, or
+ *     indices, indptr, last_page_len or lse not 4-byte aligned -> FA_ERR_INVALID_PROBLEM
  *   total_used_pages * page_size >= 2^31 (row index range)    -> FA_ERR_UNSUPPORTED
  *   num_total_pages * Hkv * page_size * D >= 10^15 elements   -> FA_ERR_UNSUPPORTED
  *   (batch + total_used_pages * page_size / chunk) * Hq / G >= 2^31, where
@@ -225,7 +229,8 @@ typedef struct {
  * defaults, identical to the plain entry points).  Checked before the plain
  * entry point's own checks:
  *   opts->kv_layout not 0 or 1                                 -> FA_ERR_UNSUPPORTED
- *   opts->window < 0, or logits_soft_cap negative or not finite -> FA_ERR_INVALID_PROBLEM */
+ *   opts->window < 0, or logits_soft_cap negative or not finite,
+ *     or alibi_slopes not 4-byte aligned                         -> FA_ERR_INVALID_PROBLEM */
 fa_status_t fa_decode_paged_opts(const fa_decode_options_t *opts, fa_dtype_t dtype, int batch,
                                  int num_qo_heads, int num_kv_heads, int head_dim, int page_size,
                                  int num_total_pages, int total_used_pages, float sm_scale,
@@ -268,6 +273,8 @@ fa_status_t fa_decode_contig_opts(const fa_decode_options_t *opts, fa_dtype_t dt
  *   total_used_pages < 0                                       -> FA_ERR_INVALID_PROBLEM
  *   k_new, v_new, indptr, last_page_len, k_data or v_data NULL,
  *     or indices NULL with total_used_pages > 0                -> FA_ERR_INVALID_PROBLEM
+ *   k_new, v_new, k_data or v_data not 16-byte aligned, or
+ *     indices, indptr or last_page_len not 4-byte aligned      -> FA_ERR_INVALID_PROBLEM
  *   total_used_pages * page_size >= 2^31                       -> FA_ERR_UNSUPPORTED
  *   num_total_pages * Hkv * page_size * D >= 10^15 elements    -> FA_ERR_UNSUPPORTED
  *   batch * Hkv >= 2^31                                        -> FA_ERR_UNSUPPORTED

@@ -27,7 +27,9 @@ extern "C" {
  *   workspace      >= fa_decode_workspace_size(batch, Hkv, Hkv, D, page_size,
  *                                              total_used_pages)
  * Checks are those of fa_decode_paged that apply (dtype, extents, head_dim,
- * NULL pointers, row range, workspace), plus out_rows < 0 -> FA_ERR_INVALID_PROBLEM.
+ * NULL pointers, alignment -- data, out and workspace 16 bytes, the int32
+ * arrays 4 --, row range, workspace), plus out_rows < 0 ->
+ * FA_ERR_INVALID_PROBLEM.
  * Asynchronous on stream, like the decode calls. */
 fa_status_t fa_debug_gather_paged(fa_dtype_t dtype, int batch, int num_kv_heads, int head_dim,
                                   int page_size, int num_total_pages, int total_used_pages,
@@ -46,7 +48,8 @@ fa_status_t fa_debug_gather_paged(fa_dtype_t dtype, int batch, int num_kv_heads,
  *   indptr, last_page_len   as for fa_decode_paged (same contract)
  *   out                     device int32 [out_entries], at least 8 * units_bound
  * Checks: dtype, extents, head_dim and total_used_pages as fa_decode_paged;
- * indptr, last_page_len or out NULL -> FA_ERR_INVALID_PROBLEM; rows beyond
+ * indptr, last_page_len or out NULL or not 4-byte aligned ->
+ * FA_ERR_INVALID_PROBLEM; rows beyond
  * the index range -> FA_ERR_UNSUPPORTED; out_entries short ->
  * FA_ERR_WORKSPACE_TOO_SMALL; a failed launch -> FA_ERR_LAUNCH.
  * Asynchronous on stream. */
@@ -60,8 +63,9 @@ fa_status_t fa_debug_schedule(fa_dtype_t dtype, int batch, int num_qo_heads, int
  * contiguous per wave instruction, non-temporal), so a benchmark can compare
  * the attention kernel with what that shape reaches on the device.  sink is a
  * device uint32 that is left unchanged unless the folded data happen to equal
- * one fixed 32-bit constant.  NULL pointers or a bad size ->
- * FA_ERR_INVALID_PROBLEM; a failed launch -> FA_ERR_LAUNCH.  Asynchronous. */
+ * one fixed 32-bit constant.  NULL pointers, buf not 16-byte or sink not
+ * 4-byte aligned, or a bad size -> FA_ERR_INVALID_PROBLEM; a failed launch ->
+ * FA_ERR_LAUNCH.  Asynchronous. */
 fa_status_t fa_debug_read_probe(const void *buf, size_t bytes, uint32_t *sink,
                                 hipStream_t stream);
 

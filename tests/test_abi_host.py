@@ -16,6 +16,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 INCLUDE = os.path.join(ROOT, "include")
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below is rejected first
+MIS2 = ctypes.c_void_p(0x1002)  # misaligned for every array the library reads or writes
+MIS8 = ctypes.c_void_p(0x1008)  # 8-byte aligned: enough for int32 / f32, not for 16-byte moves
 
 
 def _declared_functions():
@@ -117,6 +119,16 @@ INV, UNS, WS = fad.FA_ERR_INVALID_PROBLEM, fad.FA_ERR_UNSUPPORTED, fad.FA_ERR_WO
     (dict(ptrs={"lpl": None}), INV),
     (dict(ptrs={"o": None}), INV),
     (dict(ptrs={"lse": None}), INV),
+    (dict(ptrs={"q": MIS2}), INV),                     # 16-byte arrays off by 2 or 8
+    (dict(ptrs={"k": MIS8}), INV),
+    (dict(ptrs={"v": MIS2}), INV),
+    (dict(ptrs={"o": MIS8}), INV),
+    (dict(ws=MIS8), INV),
+    (dict(ptrs={"ind": MIS2}), INV),                   # 4-byte arrays off by 2
+    (dict(ptrs={"ptr": MIS2}), INV),
+    (dict(ptrs={"lpl": MIS2}), INV),
+    (dict(ptrs={"lse": MIS2}), INV),
+    (dict(ptrs={"q": MIS2}, page=1 << 20, used=1 << 11, pages=1 << 11), INV),  # before range
     (dict(page=1 << 20, used=1 << 11, pages=1 << 11), UNS),
     (dict(hq=70000, hkv=70000), UNS),                  # more query heads than a launch takes
     (dict(pages=1 << 30, hkv=64, hq=64, page=1 << 9), UNS),  # pool beyond 10^15 elements
@@ -151,6 +163,12 @@ def test_paged_workspace_exact_boundary():
     (dict(ptrs={"k": None}), INV),
     (dict(ptrs={"v": None}), INV),
     (dict(ptrs={"o": None}), INV),
+    (dict(ptrs={"q": MIS8}), INV),
+    (dict(ptrs={"k": MIS2}), INV),
+    (dict(ptrs={"v": MIS8}), INV),
+    (dict(ptrs={"o": MIS2}), INV),
+    (dict(ptrs={"lse": MIS2}), INV),
+    (dict(ws=MIS8), INV),
     (dict(valid=-1), INV),
     (dict(valid=257), INV),
     (dict(ws=None), WS),
@@ -170,6 +188,11 @@ def test_gather_rejects(fn):
     bad = list(args)
     bad[3] = 100
     assert gather(*bad, 10, FAKE, 1 << 30, None) == UNS
+    for i, mis in ((7, MIS8), (8, MIS2), (9, MIS2), (10, MIS2), (11, MIS8)):
+        bad = list(args)
+        bad[i] = mis
+        assert gather(*bad, 10, FAKE, 1 << 30, None) == INV, i
+    assert gather(*args, 10, MIS8, 1 << 30, None) == INV
 
 
 @pytest.mark.parametrize("fn", ["fa_append_paged", "fa_append_paged_nhd"])
@@ -187,6 +210,11 @@ def test_append_rejects(fn):
         bad[i] = None
         assert append(*ok, *bad, None) == INV, i
     assert append(2, 2, 2, 128, 1 << 20, 1 << 11, 1 << 11, *ptrs, None) == UNS
+    # k_new, v_new 16-byte; indices, indptr, last_page_len 4-byte; k_data, v_data 16-byte
+    for i, mis in enumerate((MIS8, MIS8, MIS2, MIS2, MIS2, MIS8, MIS8)):
+        bad = list(ptrs)
+        bad[i] = mis
+        assert append(*ok, *bad, None) == INV, i
 
 
 def test_options_reject():
@@ -197,7 +225,8 @@ def test_options_reject():
                          (fad.DecodeOptions(0, -1, 0.0, None), INV),
                          (fad.DecodeOptions(0, 0, -1.0, None), INV),
                          (fad.DecodeOptions(0, 0, float("inf"), None), INV),
-                         (fad.DecodeOptions(0, 0, float("nan"), None), INV)):
+                         (fad.DecodeOptions(0, 0, float("nan"), None), INV),
+                         (fad.DecodeOptions(0, 0, 0.0, MIS2.value), INV)):
         assert lib.fa_decode_paged_opts(ctypes.byref(opts), *base) == status
         assert lib.fa_decode_contig_opts(ctypes.byref(opts), 1, 8, 2, 64, 256, 128, 0.125,
                                          FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
@@ -219,6 +248,10 @@ def test_schedule_and_probe_reject():
     assert lib.fa_debug_read_probe(FAKE, 8192, None, None) == INV
     assert lib.fa_debug_read_probe(FAKE, 0, FAKE, None) == INV
     assert lib.fa_debug_read_probe(FAKE, 8192 + 16, FAKE, None) == INV
+    assert lib.fa_debug_read_probe(MIS8, 8192, FAKE, None) == INV
+    assert lib.fa_debug_read_probe(FAKE, 8192, MIS2, None) == INV
+    assert lib.fa_debug_schedule(*base, MIS2, FAKE, FAKE, 1 << 20, None) == INV
+    assert lib.fa_debug_schedule(*base, FAKE, FAKE, MIS2, 1 << 20, None) == INV
 
 
 def test_binding_rejects_host_tensors():
