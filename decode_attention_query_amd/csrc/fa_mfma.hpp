@@ -108,7 +108,12 @@ struct MfmaGeom {
   static constexpr int ROWV = D * 2 + 32;
   static constexpr int WAVE_LDS = TT * (ROWK + ROWV);
   static constexpr int LDS_KV = NW * WAVE_LDS;
-  static constexpr int LDS_ACC = NW * 16 * D * 4;  // merge area (reuses the K/V area)
+  // Wave-merge area (reuses the K/V area): per wave 16 head rows of D floats,
+  // padded by 16 bytes so that the 16 lanes writing one feature block of 16
+  // different heads hit distinct banks (an unpadded 2^k-byte row puts them
+  // all in one).
+  static constexpr int ACC_ROW = D + 4;
+  static constexpr int LDS_ACC = NW * 16 * ACC_ROW * 4;
   static constexpr int LDS = LDS_KV > LDS_ACC ? LDS_KV : LDS_ACC;
   static constexpr bool kPipelined = D <= 128;   // prefetch one tile ahead
 };
@@ -374,13 +379,13 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
   __syncthreads();  // every wave is done with its V area; reuse it for the merge
-  float *s_acc = reinterpret_cast<float *>(lds);  // [NW][16][D]
+  float *s_acc = reinterpret_cast<float *>(lds);  // [NW][16][ACC_ROW]
   if (n < gt) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        s_acc[(wave * 16 + n) * D + 16 * mb + 4 * grp + i] = acc[mb][i];
+        s_acc[(wave * 16 + n) * G::ACC_ROW + 16 * mb + 4 * grp + i] = acc[mb][i];
     if (grp == 0) {
       s_m[wave][n] = m_run;
       s_l[wave][n] = l_run;
@@ -399,7 +404,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
     for (int w = 0; w < NW; ++w) {
       const float sw = fast_exp2(s_m[w][g] - ref);
       lsum += s_l[w][g] * sw;
-      a += s_acc[(w * 16 + g) * D + d] * sw;
+      a += s_acc[(w * 16 + g) * G::ACC_ROW + d] * sw;
     }
     emit<E>(p, u, h0 + g, d, Mx, lsum, a);
   }
