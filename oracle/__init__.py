@@ -68,10 +68,10 @@ class _Lib:
         lib.oracle_gather_paged.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I]
         lib.oracle_gather_paged.restype = _I
         lib.oracle_decode_paged.argtypes = [_I, _I, _I, _I, _I, _I, _D, _P, _P, _P, _P, _P,
-                                            _P, _I, _P, _P, _P, _P, _I, _I, _I, _D, _P]
+                                            _P, _I, _P, _P, _P, _P, _I, _I, _I, _D, _P, _P]
         lib.oracle_decode_paged.restype = _I
         lib.oracle_decode_contig.argtypes = [_I, _I, _I, _I, _I, _I, _D, _P, _P, _P, _P, _P,
-                                             _I, _I, _I, _D, _P]
+                                             _I, _I, _I, _D, _P, _P]
         lib.oracle_decode_contig.restype = _I
         lib.oracle_attend_f64.argtypes = [_I, _I64, _D, _P, _P, _P, _P, _P]
         lib.oracle_attend_f64.restype = None
@@ -129,6 +129,7 @@ def _ptr(a):
 
 
 _keep = []
+_keep_mask = []
 
 
 def _slopes(alibi, hq):
@@ -139,6 +140,17 @@ def _slopes(alibi, hq):
     assert a.shape == (hq,)
     _keep[:] = [a]  # alive for the duration of the call
     return _ptr(a)
+
+
+def _mask(mask, total_rows):
+    """Pointer to a packed custom mask (uint8, bit i at byte i // 8, bit i % 8,
+    at least total_rows bits), or NULL."""
+    if mask is None:
+        return None
+    m = np.ascontiguousarray(np.asarray(mask, dtype=np.uint8).reshape(-1))
+    assert m.size * 8 >= total_rows, "custom mask shorter than the rows it covers"
+    _keep_mask[:] = [m]  # alive for the duration of the call
+    return _ptr(m)
 
 
 def f16_to_f64(bits: int) -> float:
@@ -209,12 +221,14 @@ def append_paged(dtype, data, indices, indptr, last_page_len, new_rows, layout="
 
 
 def decode_paged(dtype, q, k_data, v_data, indices, indptr, last_page_len, scale,
-                 samples=None, threads=0, layout="hnd", window=0, softcap=0.0, alibi=None):
+                 samples=None, threads=0, layout="hnd", window=0, softcap=0.0, alibi=None,
+                 mask=None):
     """q [B, Hq, D]; k_data/v_data [pages, Hkv, P, D] (layout="nhd":
     [pages, P, Hkv, D]).  Returns (o, lse) in f64: o [B, Hq, D], lse [B, Hq];
     with samples=[(b, h), ...] returns o [n, D], lse [n].  window > 0: only the
     last `window` rows of each request; softcap > 0: scores capped with tanh;
-    alibi: per query head slopes [Hq] (None: off)."""
+    alibi: per query head slopes [Hq] (None: off); mask: packed custom mask,
+    one bit per row of every request, requests back to back (None: off)."""
     q, k_data, v_data = _bits(q, dtype), _bits(k_data, dtype), _bits(v_data, dtype)
     batch, hq, head_dim = q.shape
     hkv, page_size, d2 = _paged_dims(k_data.shape, layout)
@@ -236,16 +250,18 @@ def decode_paged(dtype, q, k_data, v_data, indices, indptr, last_page_len, scale
                                     float(scale), _ptr(q), _ptr(k_data), _ptr(v_data),
                                     _ptr(indices), _ptr(indptr), _ptr(lpl), n_sample,
                                     _ptr(sb), _ptr(sh), _ptr(o), _ptr(lse), int(threads),
-                                    LAYOUTS[layout], int(window), float(softcap), _slopes(alibi, hq))
+                                    LAYOUTS[layout], int(window), float(softcap), _slopes(alibi, hq),
+                                    _mask(mask, int(seq_lens(page_size, indptr, lpl).sum())))
     if r != 0:
         raise RuntimeError(f"oracle_decode_paged: {STATUS[r]}")
     return o, lse
 
 
 def decode_contig(dtype, q, k_cache, v_cache, valid_kv_len, scale, threads=0, layout="hnd",
-                  window=0, softcap=0.0, alibi=None):
+                  window=0, softcap=0.0, alibi=None, mask=None):
     """q [Hq, D]; k_cache/v_cache [Hkv, max_kv_len, D] (layout="nhd":
-    [max_kv_len, Hkv, D]).  Returns (o [Hq, D], lse [Hq]) f64."""
+    [max_kv_len, Hkv, D]).  Returns (o [Hq, D], lse [Hq]) f64.  mask: packed
+    custom mask, bit j for row j (None: off)."""
     q, k_cache, v_cache = _bits(q, dtype), _bits(k_cache, dtype), _bits(v_cache, dtype)
     hq, head_dim = q.shape
     if layout == "nhd":
@@ -261,7 +277,7 @@ def decode_contig(dtype, q, k_cache, v_cache, valid_kv_len, scale, threads=0, la
                                      int(valid_kv_len), float(scale), _ptr(q), _ptr(k_cache),
                                      _ptr(v_cache), _ptr(o), _ptr(lse), int(threads),
                                      LAYOUTS[layout], int(window), float(softcap),
-                                     _slopes(alibi, hq))
+                                     _slopes(alibi, hq), _mask(mask, int(valid_kv_len)))
     if r != 0:
         raise RuntimeError(f"oracle_decode_contig: {STATUS[r]}")
     return o, lse

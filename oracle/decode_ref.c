@@ -47,7 +47,18 @@
  *   alibi:       per query head slopes m_h (NULL: off) -- the score of row j
  *                gains m_h * (j - (L_b - 1)), a linear penalty on the distance
  *                back from the query's own position, added to the scaled score
- *                before any cap.
+ *                before any cap;
+ *   mask:        a custom mask (NULL: off), one bit per K/V row of every
+ *                request, requests back to back in request order: row j of
+ *                request b is bit R_b + j with R_b = L_0 + .. + L_{b-1} (for
+ *                a contiguous cache, bit j), bit i at byte i / 8, bit i % 8.
+ *                A set bit keeps the row, a clear bit removes it from the
+ *                softmax as if it were not there (positions, and so ALiBi
+ *                distances, of the kept rows do not change).  Rows must pass
+ *                both the window and the mask; a query with no row left gets
+ *                o = 0 and lse = -inf.  The baracuda-kernels page lists custom
+ *                masks as not supported without defining one; this reading
+ *                is the plainest for a single query row per request.
  *
  * Two K/V layouts (argument `layout`):
  *   OR_HND (0), heads-major: contiguous [Hkv, max_kv_len, D] (ferrum-kernels
@@ -193,12 +204,17 @@ static int64_t window_start(int64_t L, int window) {
   return (window > 0 && L > window) ? L - window : 0;
 }
 
+/* Whether row bit `bit` of a custom mask keeps its row (NULL mask: every row). */
+static int mask_keeps(const uint8_t *mask, int64_t bit) {
+  return mask == NULL || ((mask[bit >> 3] >> (bit & 7)) & 1);
+}
+
 /* One query row against L explicit K/V rows given by element offsets into k and
  * v.  q_off is the element offset of the query row; row j's score gains
- * slope * (dist0 + j).  Two-pass softmax in f64.
- * o gets head_dim values; *lse the natural-log log-sum-exp. */
+ * slope * dist[j] (its distance from the query's position).  Two-pass softmax
+ * in f64.  o gets head_dim values; *lse the natural-log log-sum-exp. */
 static void attend_rows(int dtype, int head_dim, double scale, double softcap, double slope,
-                        int64_t dist0, const void *q, int64_t q_off, const void *k,
+                        const int64_t *dist, const void *q, int64_t q_off, const void *k,
                         const void *v, const int64_t *row_off, int64_t L, double *x, double *o,
                         double *lse) {
   for (int d = 0; d < head_dim; ++d) o[d] = 0.0;
@@ -211,7 +227,7 @@ static void attend_rows(int dtype, int head_dim, double scale, double softcap, d
     double dot = 0.0;
     for (int d = 0; d < head_dim; ++d)
       dot += load_elem(dtype, q, q_off + d) * load_elem(dtype, k, row_off[j] + d);
-    x[j] = scale * dot + slope * (double)(dist0 + j);
+    x[j] = scale * dot + slope * (double)dist[j];
     if (softcap > 0.0) x[j] = softcap * tanh(x[j] / softcap);
   }
   /* pass 1: max */
@@ -240,13 +256,21 @@ int oracle_decode_paged(int dtype, int batch, int num_qo_heads, int num_kv_heads
                         const int32_t *indptr, const int32_t *last_page_len, int n_sample,
                         const int32_t *sample_b, const int32_t *sample_h, double *o,
                         double *lse, int threads, int layout, int window, double softcap,
-                        const double *alibi) {
+                        const double *alibi, const uint8_t *mask) {
   if (batch <= 0 || num_qo_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       page_size <= 0 || num_qo_heads % num_kv_heads != 0 ||
       (layout != OR_HND && layout != OR_NHD) || window < 0 || !(softcap >= 0.0))
     return OR_BAD_ARG;
   int group = num_qo_heads / num_kv_heads;
   int64_t n_items = n_sample > 0 ? n_sample : (int64_t)batch * num_qo_heads;
+  /* rows_before[b] = L_0 + .. + L_{b-1}: where request b's mask bits start */
+  int64_t *rows_before = (int64_t *)malloc(sizeof(int64_t) * (size_t)(batch + 1));
+  if (!rows_before) return OR_NO_MEMORY;
+  rows_before[0] = 0;
+  for (int b = 0; b < batch; ++b) {
+    int64_t n = (int64_t)indptr[b + 1] - indptr[b];
+    rows_before[b + 1] = rows_before[b] + (n == 0 ? 0 : (n - 1) * page_size + last_page_len[b]);
+  }
   int status = OR_OK;
 #ifdef _OPENMP
   if (threads <= 0) threads = omp_get_max_threads();
@@ -258,22 +282,29 @@ int oracle_decode_paged(int dtype, int batch, int num_qo_heads, int num_kv_heads
     int g = h / group;
     int64_t n = (int64_t)indptr[b + 1] - indptr[b];
     int64_t L = n == 0 ? 0 : (n - 1) * page_size + last_page_len[b];
-    int64_t *row_off = (int64_t *)malloc(sizeof(int64_t) * (size_t)(L > 0 ? L : 1));
-    double *x = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
-    if (!row_off || !x) {
+    size_t cap = (size_t)(L > 0 ? L : 1);
+    int64_t *row_off = (int64_t *)malloc(sizeof(int64_t) * cap);
+    int64_t *dist = (int64_t *)malloc(sizeof(int64_t) * cap);
+    double *x = (double *)malloc(sizeof(double) * cap);
+    if (!row_off || !dist || !x) {
       status = OR_NO_MEMORY;
     } else {
-      int64_t j0 = window_start(L, window);
-      for (int64_t j = j0; j < L; ++j)
-        row_off[j - j0] = paged_row_offset(layout, num_kv_heads, page_size, head_dim, indices,
-                                           indptr, b, g, j);
+      int64_t kept = 0;
+      for (int64_t j = window_start(L, window); j < L; ++j) {
+        if (!mask_keeps(mask, rows_before[b] + j)) continue;
+        row_off[kept] = paged_row_offset(layout, num_kv_heads, page_size, head_dim, indices,
+                                         indptr, b, g, j);
+        dist[kept++] = j - (L - 1);
+      }
       int64_t q_off = ((int64_t)b * num_qo_heads + h) * head_dim;
-      attend_rows(dtype, head_dim, scale, softcap, alibi ? alibi[h] : 0.0, j0 - (L - 1), q,
-                  q_off, k, v, row_off, L - j0, x, o + it * head_dim, lse + it);
+      attend_rows(dtype, head_dim, scale, softcap, alibi ? alibi[h] : 0.0, dist, q, q_off, k,
+                  v, row_off, kept, x, o + it * head_dim, lse + it);
     }
     free(row_off);
+    free(dist);
     free(x);
   }
+  free(rows_before);
   return status;
 }
 
@@ -285,7 +316,7 @@ int oracle_decode_contig(int dtype, int num_qo_heads, int num_kv_heads, int head
                          int max_kv_len, int valid_kv_len, double scale, const void *q,
                          const void *k, const void *v, double *o, double *lse,
                          int threads, int layout, int window, double softcap,
-                         const double *alibi) {
+                         const double *alibi, const uint8_t *mask) {
   if (num_qo_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_kv_len < 0 ||
       valid_kv_len < 0 || valid_kv_len > max_kv_len || num_qo_heads % num_kv_heads != 0 ||
       (layout != OR_HND && layout != OR_NHD) || window < 0 || !(softcap >= 0.0))
@@ -299,19 +330,25 @@ int oracle_decode_contig(int dtype, int num_qo_heads, int num_kv_heads, int head
   for (int h = 0; h < num_qo_heads; ++h) {
     int g = h / group;
     int64_t L = valid_kv_len;
-    int64_t *row_off = (int64_t *)malloc(sizeof(int64_t) * (size_t)(L > 0 ? L : 1));
-    double *x = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
-    if (!row_off || !x) {
+    size_t cap = (size_t)(L > 0 ? L : 1);
+    int64_t *row_off = (int64_t *)malloc(sizeof(int64_t) * cap);
+    int64_t *dist = (int64_t *)malloc(sizeof(int64_t) * cap);
+    double *x = (double *)malloc(sizeof(double) * cap);
+    if (!row_off || !dist || !x) {
       status = OR_NO_MEMORY;
     } else {
-      int64_t j0 = window_start(L, window);
-      for (int64_t j = j0; j < L; ++j)
-        row_off[j - j0] = contig_row_offset(layout, num_kv_heads, max_kv_len, head_dim, g, j);
-      attend_rows(dtype, head_dim, scale, softcap, alibi ? alibi[h] : 0.0, j0 - (L - 1), q,
-                  (int64_t)h * head_dim, k, v, row_off, L - j0, x, o + (int64_t)h * head_dim,
+      int64_t kept = 0;
+      for (int64_t j = window_start(L, window); j < L; ++j) {
+        if (!mask_keeps(mask, j)) continue;
+        row_off[kept] = contig_row_offset(layout, num_kv_heads, max_kv_len, head_dim, g, j);
+        dist[kept++] = j - (L - 1);
+      }
+      attend_rows(dtype, head_dim, scale, softcap, alibi ? alibi[h] : 0.0, dist, q,
+                  (int64_t)h * head_dim, k, v, row_off, kept, x, o + (int64_t)h * head_dim,
                   lse + h);
     }
     free(row_off);
+    free(dist);
     free(x);
   }
   return status;

@@ -666,6 +666,96 @@ def pin_alibi_window_is_truncation():
     assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
 
 
+def _masked_rows(rows, keep):
+    return rows[torch.from_numpy(np.asarray(keep, dtype=bool))]
+
+
+def pin_mask_is_compaction():
+    """A custom mask equals plain attention over the kept rows, laid out by the
+    test itself, bit for bit: random and all-ones masks, requests whose rows
+    are all dropped (o = 0, lse = -inf), and a window on top (a row must pass
+    both).  Several requests, so each request's bits must start at its own
+    offset; paged and contiguous."""
+    rng = np.random.default_rng(38)
+    for dtype in DTYPES:
+        hkv, group, d, page_size = 2, 2, 8, 4
+        lens = [6, 0, 13, 1, 22, 9]
+        k_rows = [rand_t(rng, (L, hkv, d), dtype) for L in lens]
+        v_rows = [rand_t(rng, (L, hkv, d), dtype) for L in lens]
+        q = rand_t(rng, (len(lens), hkv * group, d), dtype)
+        p = _paged_problem(rng, dtype, lens, hkv, group, d, page_size, k_rows=k_rows,
+                           v_rows=v_rows, q=q)
+        args = (dtype, W.bits(p["q"]), W.bits(p["k_data"]), W.bits(p["v_data"]), p["indices"],
+                p["indptr"], p["last_page_len"], 0.4)
+        starts = np.concatenate([[0], np.cumsum(lens)])
+        plain = O.decode_paged(*args)
+        for trial, win in ((0, 0), (1, 0), (2, 0), (3, 5)):
+            keep = W.random_mask(100 + trial, lens, keep=0.5) if trial else np.ones(sum(lens), bool)
+            if trial == 2:
+                keep[starts[4]:starts[5]] = False  # a request with every row dropped
+            got = O.decode_paged(*args, window=win, mask=W.pack_mask(keep))
+            per = []
+            for b, L in enumerate(lens):
+                kb = keep[starts[b]:starts[b + 1]].copy()
+                if win:
+                    kb[:max(0, L - win)] = False
+                per.append(kb)
+            pt = _paged_problem(rng, dtype, [int(m.sum()) for m in per], hkv, group, d, page_size,
+                                k_rows=[_masked_rows(r, m) for r, m in zip(k_rows, per)],
+                                v_rows=[_masked_rows(r, m) for r, m in zip(v_rows, per)], q=q)
+            want = _oracle_paged(pt, 0.4)
+            assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1]), \
+                (dtype, trial)
+            if trial == 0:
+                assert np.array_equal(got[0], plain[0]) and np.array_equal(got[1], plain[1])
+            if trial == 2:
+                assert np.all(got[0][4] == 0.0) and np.all(np.isneginf(got[1][4]))
+        # contiguous: bit j for row j
+        L = 27
+        rk, rv = rand_t(rng, (L, hkv, d), dtype), rand_t(rng, (L, hkv, d), dtype)
+        qc = rand_t(rng, (hkv * group, d), dtype)
+        keep = W.random_mask(7, [L], keep=0.4, blocks=True)
+        got = O.decode_contig(dtype, W.bits(qc), W.bits(contig_from_rows(rk, 32)),
+                              W.bits(contig_from_rows(rv, 32)), L, 0.4, mask=W.pack_mask(keep))
+        n = int(keep.sum())
+        want = O.decode_contig(dtype, W.bits(qc), W.bits(contig_from_rows(_masked_rows(rk, keep), 32)),
+                               W.bits(contig_from_rows(_masked_rows(rv, keep), 32)), n, 0.4)
+        assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1]), dtype
+
+
+def pin_mask_alibi_mpmath():
+    """Under a mask, ALiBi still measures each kept row's distance from the
+    query at its original position: a 50-digit evaluation over the kept rows
+    with m_h * (j - (L - 1))."""
+    rng = np.random.default_rng(39)
+    hkv, group, d = 1, 2, 4
+    lens = [9, 5]
+    p = _paged_problem(rng, "f32", lens, hkv, group, d, 3)
+    keep = W.random_mask(11, lens, keep=0.6)
+    slopes = [0.5, 0.125]
+    o, lse = O.decode_paged("f32", W.bits(p["q"]), W.bits(p["k_data"]), W.bits(p["v_data"]),
+                            p["indices"], p["indptr"], p["last_page_len"], 0.7, alibi=slopes,
+                            mask=W.pack_mask(keep))
+    mpmath.mp.dps = 50
+    qf = f64(p["q"])
+    start = 0
+    for b, L in enumerate(lens):
+        kf, vf = f64(p["k_rows"][b]), f64(p["v_rows"][b])
+        rows = [j for j in range(L) if keep[start + j]]
+        start += L
+        for h in range(group):
+            xs = {}
+            for j in rows:
+                x = mpmath.mpf(0.7) * mpmath.fsum(mpmath.mpf(a) * mpmath.mpf(c)
+                                                  for a, c in zip(qf[b, h], kf[j, 0]))
+                xs[j] = mpmath.e ** (x + mpmath.mpf(slopes[h]) * (j - (L - 1)))
+            z = mpmath.fsum(xs.values())
+            for dd in range(d):
+                ref = float(mpmath.fsum(xs[j] * mpmath.mpf(vf[j, 0, dd]) for j in rows) / z)
+                assert abs(o[b, h, dd] - ref) <= 1e-13 * max(1.0, abs(ref))
+            assert abs(lse[b, h] - float(mpmath.log(z))) <= 1e-13
+
+
 def pin_seq_lens():
     """The oracle's L_b equals the row count the test scattered."""
     rng = np.random.default_rng(26)

@@ -62,13 +62,20 @@ MUTANTS = [
     ("softcap_drops_outer_factor",
      "if (softcap > 0.0) x[j] = softcap * tanh(x[j] / softcap);",
      "if (softcap > 0.0) x[j] = tanh(x[j] / softcap);"),
-    ("alibi_sign", "x[j] = scale * dot + slope * (double)(dist0 + j);",
-     "x[j] = scale * dot - slope * (double)(dist0 + j);"),
-    ("alibi_absolute_position", "alibi ? alibi[h] : 0.0, j0 - (L - 1)",
-     "alibi ? alibi[h] : 0.0, j0"),
+    ("alibi_sign", "x[j] = scale * dot + slope * (double)dist[j];",
+     "x[j] = scale * dot - slope * (double)dist[j];"),
+    ("alibi_absolute_position", "dist[kept++] = j - (L - 1);", "dist[kept++] = j;"),
     ("alibi_after_cap",
-     "x[j] = scale * dot + slope * (double)(dist0 + j);\n    if (softcap > 0.0) x[j] = softcap * tanh(x[j] / softcap);",
-     "x[j] = scale * dot;\n    if (softcap > 0.0) x[j] = softcap * tanh(x[j] / softcap);\n    x[j] += slope * (double)(dist0 + j);"),
+     "x[j] = scale * dot + slope * (double)dist[j];\n    if (softcap > 0.0) x[j] = softcap * tanh(x[j] / softcap);",
+     "x[j] = scale * dot;\n    if (softcap > 0.0) x[j] = softcap * tanh(x[j] / softcap);\n    x[j] += slope * (double)dist[j];"),
+    ("mask_ignored", "return mask == NULL || ((mask[bit >> 3] >> (bit & 7)) & 1);", "return 1;"),
+    ("mask_inverted", "return mask == NULL || ((mask[bit >> 3] >> (bit & 7)) & 1);",
+     "return mask == NULL || !((mask[bit >> 3] >> (bit & 7)) & 1);"),
+    ("mask_bit_order_msb_first", "((mask[bit >> 3] >> (bit & 7)) & 1)",
+     "((mask[bit >> 3] >> (7 - (bit & 7))) & 1)"),
+    ("mask_ignores_request_offset", "mask_keeps(mask, rows_before[b] + j)", "mask_keeps(mask, j)"),
+    ("mask_renumbers_positions", "dist[kept++] = j - (L - 1);",
+     "dist[kept] = kept - (L - 1);\n        kept++;"),
     ("validate_skips_upper_bound", "indices[i] >= num_total_pages", "indices[i] > num_total_pages"),
 ]
 

@@ -101,6 +101,30 @@ def token_major(p):
                                v_data=p.v_data.permute(0, 2, 1, 3).contiguous())
 
 
+def pack_mask(keep) -> np.ndarray:
+    """A custom mask in the packed form the library and the oracle read: the
+    flattened booleans (row i of the concatenated per-request rows) at byte
+    i // 8, bit i % 8; a set bit keeps the row."""
+    return np.packbits(np.asarray(keep, dtype=bool).reshape(-1), bitorder="little")
+
+
+def random_mask(seed, lens, keep=0.5, blocks=False) -> np.ndarray:
+    """Seeded keep-booleans for requests of the given lengths, concatenated in
+    request order: independent rows kept with probability `keep`, or
+    (blocks=True) runs of 1-40 rows kept or dropped together."""
+    rng = np.random.default_rng(seed)
+    total = int(np.sum(lens))
+    if not blocks:
+        return rng.random(total) < keep
+    out = np.empty(total, dtype=bool)
+    i = 0
+    while i < total:
+        n = int(rng.integers(1, 41))
+        out[i:i + n] = rng.random() < keep
+        i += n
+    return out
+
+
 def bits(t: torch.Tensor) -> np.ndarray:
     """Raw element storage of a CPU tensor as numpy (float32, or uint16 patterns)."""
     t = t.contiguous()
