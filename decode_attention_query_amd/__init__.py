@@ -26,14 +26,21 @@ def _code(t):
         raise TypeError(f"unsupported element type {t.dtype}") from None
 
 
-def _options(layout, window, softcap, alibi, hq):
+def _options(layout, window, softcap, alibi, mask, hq):
     slopes = None
     if alibi is not None:
         if not (isinstance(alibi, torch.Tensor) and alibi.device.type == "cuda" and
                 alibi.dtype == torch.float32 and alibi.is_contiguous() and alibi.numel() == hq):
             raise ValueError(f"alibi must be a contiguous f32 device tensor of {hq} slopes")
         slopes = alibi.data_ptr()
-    return DecodeOptions(int(layout == "nhd"), int(window), float(softcap), slopes)
+    mask_ptr, mask_bytes = None, 0
+    if mask is not None:
+        if not (isinstance(mask, torch.Tensor) and mask.device.type == "cuda" and
+                mask.dtype == torch.uint8 and mask.is_contiguous() and mask.numel() > 0):
+            raise ValueError("mask must be a non-empty contiguous uint8 device tensor of packed bits")
+        mask_ptr, mask_bytes = mask.data_ptr(), mask.numel()
+    return DecodeOptions(int(layout == "nhd"), int(window), float(softcap), slopes, mask_ptr,
+                         mask_bytes)
 
 
 def workspace_paged(batch, num_qo_heads, num_kv_heads, head_dim, page_size, total_used_pages,
@@ -46,9 +53,11 @@ def workspace_paged(batch, num_qo_heads, num_kv_heads, head_dim, page_size, tota
 
 
 def decode_paged(q, k_data, v_data, indices, indptr, last_page_len, sm_scale, o=None, lse=None,
-                 workspace=None, stream=None, layout="hnd", window=0, softcap=0.0, alibi=None):
+                 workspace=None, stream=None, layout="hnd", window=0, softcap=0.0, alibi=None,
+                 mask=None):
     """q [B, Hq, D]; k_data/v_data [pages, Hkv, P, D] (layout "nhd": [pages, P, Hkv, D]);
-    int32 page table; alibi: f32 device tensor [Hq] of slopes.
+    int32 page table; alibi: f32 device tensor [Hq] of slopes; mask: uint8 device
+    tensor of packed keep-bits, one per row of every request, requests back to back.
     Returns (o [B, Hq, D] in q's dtype, lse [B, Hq] f32)."""
     batch, hq, d = q.shape
     if layout == "nhd":
@@ -68,16 +77,17 @@ def decode_paged(q, k_data, v_data, indices, indptr, last_page_len, sm_scale, o=
         workspace = workspace_paged(batch, hq, hkv, d, page_size, used, q.device)
     args = (_code(q), batch, hq, hkv, d, page_size, pages, used, sm_scale, q, k_data, v_data,
             indices if used else None, indptr, last_page_len, o, lse, workspace, stream)
-    if window or softcap or alibi is not None:
-        fa_decode_paged_opts(_options(layout, window, softcap, alibi, hq), *args)
+    if window or softcap or alibi is not None or mask is not None:
+        fa_decode_paged_opts(_options(layout, window, softcap, alibi, mask, hq), *args)
     else:
         (fa_decode_paged_nhd if layout == "nhd" else fa_decode_paged)(*args)
     return o, lse
 
 
 def decode_contig(q, k_cache, v_cache, valid_kv_len, scale, o=None, lse=None, workspace=None,
-                  stream=None, layout="hnd", window=0, softcap=0.0, alibi=None):
-    """q [Hq, D]; k_cache/v_cache [Hkv, max_kv_len, D] (layout "nhd": [max_kv_len, Hkv, D]).
+                  stream=None, layout="hnd", window=0, softcap=0.0, alibi=None, mask=None):
+    """q [Hq, D]; k_cache/v_cache [Hkv, max_kv_len, D] (layout "nhd": [max_kv_len, Hkv, D]);
+    mask: uint8 device tensor of packed keep-bits, bit j for row j.
     Returns (o [Hq, D] in q's dtype, lse [Hq] f32)."""
     hq, d = q.shape
     if layout == "nhd":
@@ -96,8 +106,8 @@ def decode_contig(q, k_cache, v_cache, valid_kv_len, scale, o=None, lse=None, wo
         workspace = workspace_paged(1, hq, hkv, d, max_kv_len, 1, q.device)
     args = (_code(q), hq, hkv, d, max_kv_len, valid_kv_len, scale, q, k_cache, v_cache, o, lse,
             workspace, stream)
-    if window or softcap or alibi is not None:
-        fa_decode_contig_opts(_options(layout, window, softcap, alibi, hq), *args)
+    if window or softcap or alibi is not None or mask is not None:
+        fa_decode_contig_opts(_options(layout, window, softcap, alibi, mask, hq), *args)
     else:
         (fa_decode_contig_nhd if layout == "nhd" else fa_decode_contig)(*args)
     return o, lse

@@ -38,10 +38,12 @@ EXPORTED = ("fa_decode_workspace_size", "fa_decode_contig", "fa_decode_paged",
 
 class DecodeOptions(ctypes.Structure):
     """fa_decode_options_t: K/V layout (0 heads-major, 1 token-major), sliding
-    window (rows, 0 = off), logits soft-cap (0 = off) and the device address of
-    f32 ALiBi slopes [Hq] (None = off)."""
+    window (rows, 0 = off), logits soft-cap (0 = off), the device address of
+    f32 ALiBi slopes [Hq] (None = off) and of a packed custom mask with its
+    size in bytes (None = off)."""
     _fields_ = [("kv_layout", ctypes.c_int), ("window", ctypes.c_int),
-                ("logits_soft_cap", ctypes.c_float), ("alibi_slopes", ctypes.c_void_p)]
+                ("logits_soft_cap", ctypes.c_float), ("alibi_slopes", ctypes.c_void_p),
+                ("custom_mask", ctypes.c_void_p), ("custom_mask_bytes", ctypes.c_size_t)]
 
 
 class FaError(RuntimeError):

@@ -76,6 +76,8 @@ struct DecodeParams {
   float softcap2;     // > 0: base-2 scores x -> softcap2 * tanh(x / softcap2) (cap * log2 e)
   float softcap2_inv; // 1 / softcap2
   const float *alibi; // [Hq] ALiBi slopes (natural-log units) or null
+  const uint8_t *mask; // custom mask, one bit per row of every request (keep = 1), or null
+  uint32_t mask_bytes; // its size; bits past it read as 0
   // workspace regions
   float *part_lse;        // [units_bound, Hq]     base-2 lse of each split's partial
   float *part_o;          // [units_bound, Hq, D]  normalised partial outputs

@@ -192,7 +192,7 @@ template <class E, int D>
 hipError_t launch_mfma(const DecodeParams &p, const HostPlan &hp, hipStream_t s) {
   dim3 grid(unsigned(hp.units_bound) * unsigned(hp.planes));
   dim3 block(fa::MfmaGeom<E, D>::NW * 64);
-  const bool mods = p.window > 0 || p.softcap2 > 0.0f || p.alibi != nullptr;
+  const bool mods = p.window > 0 || p.softcap2 > 0.0f || p.alibi != nullptr || p.mask != nullptr;
   if (p.nhd) {
     if (mods)
       hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, true, true>), grid, block, 0, s, p);
@@ -280,6 +280,8 @@ struct Variant {
   int window = 0;
   float softcap = 0.0f;
   const float *alibi = nullptr;
+  const uint8_t *mask = nullptr;
+  uint32_t mask_bytes = 0;
 };
 
 // FA_OK, or why opts is rejected; fills v.
@@ -287,12 +289,16 @@ fa_status_t read_options(const fa_decode_options_t *opts, Variant &v) {
   if (!opts) return FA_OK;
   if (opts->kv_layout != 0 && opts->kv_layout != 1) return FA_ERR_UNSUPPORTED;
   if (opts->window < 0 || !(opts->logits_soft_cap >= 0.0f) ||
-      !std::isfinite(opts->logits_soft_cap) || !aligned(opts->alibi_slopes, 4))
+      !std::isfinite(opts->logits_soft_cap) || !aligned(opts->alibi_slopes, 4) ||
+      (opts->custom_mask && opts->custom_mask_bytes == 0))
     return FA_ERR_INVALID_PROBLEM;
   v.nhd = opts->kv_layout;
   v.window = opts->window;
   v.softcap = opts->logits_soft_cap;
   v.alibi = opts->alibi_slopes;
+  v.mask = opts->custom_mask;
+  // rows are int-indexed, so no bit past 2^31 is ever asked for
+  v.mask_bytes = uint32_t(std::min<size_t>(opts->custom_mask_bytes, size_t(1) << 28));
   return FA_OK;
 }
 
@@ -300,6 +306,8 @@ void apply_variant(DecodeParams &p, const Variant &v) {
   p.nhd = v.nhd;
   p.window = v.window;
   p.alibi = v.alibi;
+  p.mask = v.mask;
+  p.mask_bytes = v.mask_bytes;
   if (v.softcap > 0.0f) {
     p.softcap2 = v.softcap * fa::kLog2e;  // capping commutes with the base-2 scale
     p.softcap2_inv = 1.0f / p.softcap2;

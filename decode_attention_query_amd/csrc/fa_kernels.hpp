@@ -227,6 +227,16 @@ __device__ bool find_unit(const DecodeParams &p, int w, UnitInfo &u) {
   return false;  // not reached: the class counts hold the rank
 }
 
+// Custom mask: whether row t of the unit's request is kept -- bit row0 + t of
+// the packed mask, at byte (row0 + t) / 8, bit (row0 + t) % 8, where row0 is
+// the rows of all earlier requests (0 for a contiguous cache).  A bit past the
+// caller's mask size reads as 0 and is never loaded.
+__device__ inline bool mask_keeps(const DecodeParams &p, int row0, int t) {
+  const uint32_t bit = (uint32_t)(row0 + t);
+  const uint32_t byte = min(bit >> 3, p.mask_bytes - 1);
+  return (bit >> 3) < p.mask_bytes && ((p.mask[byte] >> (bit & 7)) & 1);
+}
+
 // Writes the combined result of one (request, query head, feature) of a unit:
 // the final o / lse if the request has a single unit, else the partial.
 template <class E>
@@ -498,7 +508,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
   __shared__ float s_l[NW][GT];
 
   UnitInfo u;
-  if (!find_unit<false>(p, blockIdx.x, u)) return;
+  if (!find_unit<true>(p, blockIdx.x, u)) return;  // row0 for a custom mask
   const int kvh = blockIdx.y / p.n_gblocks;
   const int h0 = kvh * p.group + (blockIdx.y % p.n_gblocks) * GT;
   const int t_begin = u.lo + u.c * p.chunk;
@@ -549,6 +559,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) 
     for (int s = 0; s < U; ++s) {
       const int t = t0 + s * TPW + slot;
       valid[s] = t >= t_lo && t < t_end;
+      if (p.mask && valid[s]) valid[s] = mask_keeps(p, u.row0, t);
       const int64_t off = kv_row_offset(p, u.page_base, kvh, valid[s] ? t : t_end - 1);
       kr[s] = load16_stream(kb + off * E::kBytes);
       vr[s] = load16_stream(vb + off * E::kBytes);

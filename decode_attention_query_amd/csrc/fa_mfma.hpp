@@ -204,7 +204,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   const int unit = blockIdx.x / p.planes;
   const int plane = blockIdx.x - unit * p.planes;
   UnitInfo u;
-  if (!find_unit<false>(p, unit, u)) return;
+  if (!find_unit<kMods>(p, unit, u)) return;  // row0 (for a custom mask) in the kMods instance
   const int gt = p.heads_per_unit;  // valid columns of the 16-wide head block
   const int kvh = plane / p.n_gblocks;
   const int h0 = kvh * p.group + (plane % p.n_gblocks) * gt;
@@ -270,7 +270,26 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   // where this lane's loaded 16 bytes go: row RPI * i + lane / LPR
   const int st_row = lane / G::LPR, st_col = (lane % G::LPR) * 16;
 
-  auto compute = [&](const KVTile<G::NI> &T, int t0) {
+  // Custom mask bits of the lane's 8 rows of the tile at t0: bit 4j + i for row
+  // t0 + 16j + 4grp + i (rows past the request read its last row's bit and are
+  // cut by t_end anyway).  Loaded with the tile, so the latency overlaps.
+  auto mask_bits = [&](int t0) -> uint32_t {
+    uint32_t bits = 0;
+    if constexpr (kMods) {
+      if (p.mask) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = min(t0 + 16 * j + 4 * grp + i, u.L - 1);
+            bits |= (uint32_t)mask_keeps(p, u.row0, t) << (4 * j + i);
+          }
+      }
+    }
+    return bits;
+  };
+
+  auto compute = [&](const KVTile<G::NI> &T, int t0, uint32_t mbits) {
     // K and V tiles to LDS
 #pragma unroll
     for (int i = 0; i < G::NI; ++i) {
@@ -306,6 +325,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
           if (p.alibi) v += slope2 * (float)(t - last_row);
           if (p.softcap2 > 0.0f) v = p.softcap2 * tanhf(v * p.softcap2_inv);
           if (t < t_lo) v = -INFINITY;
+          if (p.mask && !((mbits >> (4 * j + i)) & 1u)) v = -INFINITY;
         }
         if (t >= t_end) v = -INFINITY;
         x[4 * j + i] = v;
@@ -353,24 +373,29 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   if (t0 < t_end) {
     KVTile<G::NI> A;
     issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, t0, t_end, lane);
+    uint32_t mA = mask_bits(t0);
     if constexpr (G::kPipelined) {
       KVTile<G::NI> B;
+      uint32_t mB;
       while (true) {
         issue_tile<E, D, kNhd>(B, p, page_base, s_pages, slot0, kvh, t0 + stride, t_end, lane);
-        compute(A, t0);
+        mB = mask_bits(t0 + stride);
+        compute(A, t0, mA);
         t0 += stride;
         if (t0 >= t_end) break;
         issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, t0 + stride, t_end, lane);
-        compute(B, t0);
+        mA = mask_bits(t0 + stride);
+        compute(B, t0, mB);
         t0 += stride;
         if (t0 >= t_end) break;
       }
     } else {
       while (true) {
-        compute(A, t0);
+        compute(A, t0, mA);
         t0 += stride;
         if (t0 >= t_end) break;
         issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, t0, t_end, lane);
+        mA = mask_bits(t0);
       }
     }
   }

@@ -215,6 +215,22 @@ fa_status_t fa_decode_paged_nhd(fa_dtype_t dtype, int batch, int num_qo_heads,
  *                    alibi_slopes[h] * (j - (L_b - 1)) to row j's scaled score
  *                    (0 at the query's own row, more negative further back),
  *                    before any cap; the pages list ALiBi as unsupported too
+ *   custom_mask      device uint8 bit array or NULL: one bit per K/V row of
+ *                    every request, requests back to back in request order, so
+ *                    row j of request b is bit R_b + j with R_b = L_0 + .. +
+ *                    L_{b-1} (a contiguous cache: bit j), bit i at byte i / 8,
+ *                    bit i % 8.  A set bit keeps the row; a clear bit removes
+ *                    it from the softmax (kept rows keep their positions, so
+ *                    ALiBi distances do not change).  A row must pass both the
+ *                    window and the mask; a request left with no row gets o = 0
+ *                    and lse = -inf.  The pages list custom masks as
+ *                    unsupported and define none; this is the plainest reading
+ *                    for one query row per request.  Masked rows are still read.
+ *   custom_mask_bytes  size of custom_mask in bytes (ignored when it is NULL):
+ *                    ceil(sum L_b / 8) covers every row (ceil(valid_kv_len / 8)
+ *                    for a contiguous cache).  Bits at or past 8 *
+ *                    custom_mask_bytes read as 0 (row dropped), so a short
+ *                    mask never makes the library read past it.
  * A window keeps whole 16-row blocks of rows below it in the read set (they are
  * masked, never weighted), so the bytes read grow by at most 15 rows per
  * request. */
@@ -223,6 +239,8 @@ typedef struct {
   int window;
   float logits_soft_cap;
   const float *alibi_slopes;
+  const uint8_t *custom_mask;
+  size_t custom_mask_bytes;
 } fa_decode_options_t;
 
 /* fa_decode_paged / fa_decode_contig with options (opts may be NULL: all
@@ -230,7 +248,8 @@ typedef struct {
  * entry point's own checks:
  *   opts->kv_layout not 0 or 1                                 -> FA_ERR_UNSUPPORTED
  *   opts->window < 0, or logits_soft_cap negative or not finite,
- *     or alibi_slopes not 4-byte aligned                         -> FA_ERR_INVALID_PROBLEM */
+ *     or alibi_slopes not 4-byte aligned, or custom_mask set with
+ *     custom_mask_bytes 0                                        -> FA_ERR_INVALID_PROBLEM */
 fa_status_t fa_decode_paged_opts(const fa_decode_options_t *opts, fa_dtype_t dtype, int batch,
                                  int num_qo_heads, int num_kv_heads, int head_dim, int page_size,
                                  int num_total_pages, int total_used_pages, float sm_scale,

@@ -226,7 +226,8 @@ def test_options_reject():
                          (fad.DecodeOptions(0, 0, -1.0, None), INV),
                          (fad.DecodeOptions(0, 0, float("inf"), None), INV),
                          (fad.DecodeOptions(0, 0, float("nan"), None), INV),
-                         (fad.DecodeOptions(0, 0, 0.0, MIS2.value), INV)):
+                         (fad.DecodeOptions(0, 0, 0.0, MIS2.value), INV),
+                         (fad.DecodeOptions(0, 0, 0.0, None, FAKE.value, 0), INV)):
         assert lib.fa_decode_paged_opts(ctypes.byref(opts), *base) == status
         assert lib.fa_decode_contig_opts(ctypes.byref(opts), 1, 8, 2, 64, 256, 128, 0.125,
                                          FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,

@@ -1,6 +1,7 @@
-"""Sliding window and logits soft-cap on the GPU (fa_decode_paged_opts,
-fa_decode_contig_opts) against the oracle's window= / softcap= paths, element
-by element with the same tolerances as the plain entry points."""
+"""Sliding window, logits soft-cap, ALiBi and the custom mask on the GPU
+(fa_decode_paged_opts, fa_decode_contig_opts) against the oracle's window= /
+softcap= / alibi= / mask= paths, element by element with the same tolerances
+as the plain entry points."""
 import math
 import zlib
 
@@ -22,27 +23,29 @@ def dev():
     return device()
 
 
-def _oracle(p, window, softcap, samples=None, alibi=None):
+def _oracle(p, window, softcap, samples=None, alibi=None, mask=None):
     if isinstance(p, W.PagedProblem):
         return oracle.decode_paged(p.dtype, W.bits(p.q), W.bits(p.k_data), W.bits(p.v_data),
                                    p.indices.numpy(), p.indptr.numpy(), p.last_page_len.numpy(),
                                    p.scale, samples=samples, layout=p.layout, window=window,
-                                   softcap=softcap, alibi=alibi)
+                                   softcap=softcap, alibi=alibi, mask=mask)
     return oracle.decode_contig(p.dtype, W.bits(p.q), W.bits(p.k_cache), W.bits(p.v_cache),
                                 p.valid_kv_len, p.scale, layout=p.layout, window=window,
-                                softcap=softcap, alibi=alibi)
+                                softcap=softcap, alibi=alibi, mask=mask)
 
 
-def _run(p, d, window, softcap, alibi=None):
-    dev_alibi = None
+def _run(p, d, window, softcap, alibi=None, mask=None):
+    dev_alibi = dev_mask = None
     if alibi is not None:
         dev_alibi = torch.tensor(alibi, dtype=torch.float32, device=d["q"].device)
+    if mask is not None:
+        dev_mask = torch.from_numpy(np.ascontiguousarray(mask)).to(d["q"].device)
     if isinstance(p, W.PagedProblem):
         return fad.decode_paged(d["q"], d["k"], d["v"], d["indices"], d["indptr"], d["lpl"],
                                 p.scale, layout=p.layout, window=window, softcap=softcap,
-                                alibi=dev_alibi)
+                                alibi=dev_alibi, mask=dev_mask)
     return fad.decode_contig(d["q"], d["k"], d["v"], p.valid_kv_len, p.scale, layout=p.layout,
-                             window=window, softcap=softcap, alibi=dev_alibi)
+                             window=window, softcap=softcap, alibi=dev_alibi, mask=dev_mask)
 
 
 def alibi_slopes(hq, max_bias=8.0):
@@ -124,3 +127,102 @@ def test_variants_full_c3(dev):
     torch.cuda.synchronize()
     assert torch.allclose(o1.float(), o0.float(), atol=4e-3, rtol=0)
     assert torch.allclose(l1, l0, atol=1e-4, rtol=0)
+
+
+# ------------------------------------------------------------ custom mask
+
+MASKS = [  # keep probability, blocks of rows, window, cap, alibi
+    (0.5, False, 0, 0.0, False),
+    (0.9, False, 0, 0.0, False),
+    (0.05, False, 0, 0.0, False),
+    (0.5, True, 0, 0.0, False),
+    (0.7, False, 40, 0.0, True),
+    (0.5, True, 0, 10.0, True),
+]
+
+
+@pytest.mark.parametrize("mvar", MASKS, ids=lambda m: f"keep{m[0]}" + ("-blocks" if m[1] else "")
+                         + (f"-w{m[2]}" if m[2] else "") + (f"-cap{m[3]:g}" if m[3] else "")
+                         + ("-alibi" if m[4] else ""))
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}-D{c[1]}-G{c[3]}-P{c[4]}")
+def test_paged_mask(dev, case, mvar):
+    """Random and block masks over requests of ragged lengths (empty, one row,
+    page edges, split requests), one request with every row dropped, alone
+    and with a window, a cap and ALiBi; both K/V layouts."""
+    dtype, d, hkv, group, page_size, lens = case
+    keep_p, blocks, window, cap, with_alibi = mvar
+    slopes = alibi_slopes(hkv * group) if with_alibi else None
+    rng = np.random.default_rng(zlib.crc32(str(case).encode()) + 1)
+    k_rows = [rand_t(rng, (L, hkv, d), dtype) for L in lens]
+    v_rows = [rand_t(rng, (L, hkv, d), dtype) for L in lens]
+    kd, ind, ptr, lpl = scatter_paged(k_rows, page_size, np.random.default_rng(4), 3, (),
+                                      fill=1.0e4)
+    vd, _, _, _ = scatter_paged(v_rows, page_size, np.random.default_rng(4), 3, (), fill=1.0e4)
+    q = rand_t(rng, (len(lens), hkv * group, d), dtype, std=2.0)
+    p = W.PagedProblem(name="mask", dtype=dtype, batch=len(lens), num_qo_heads=hkv * group,
+                       num_kv_heads=hkv, head_dim=d, page_size=page_size,
+                       num_total_pages=kd.shape[0], scale=float(np.float32(1 / math.sqrt(d))),
+                       q=q, k_data=kd, v_data=vd, indices=torch.from_numpy(ind),
+                       indptr=torch.from_numpy(ptr), last_page_len=torch.from_numpy(lpl))
+    keep = W.random_mask(zlib.crc32(str(mvar).encode()), lens, keep=keep_p, blocks=blocks)
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    mid = len(lens) // 2
+    keep[starts[mid]:starts[mid + 1]] = False  # a request left with no row
+    packed = W.pack_mask(keep)
+    for layout in ("hnd", "nhd"):
+        pp = p if layout == "hnd" else W.token_major(p)
+        o, lse = _run(pp, to_dev(pp, dev), window, cap, slopes, mask=packed)
+        torch.cuda.synchronize()
+        ro, rl = _oracle(pp, window, cap, alibi=slopes, mask=packed)
+        compare(dtype, o, lse, ro, rl, f"{case} {mvar} {layout}")
+
+
+def test_mask_all_ones_and_short(dev):
+    """An all-ones mask gives the plain call's output bit for bit; a mask
+    shorter than the rows drops the rows past its end (and reads nothing past
+    it), which equals an explicit mask with those bits cleared."""
+    p = W.make_paged("mask-short", "bf16", 6, 16, 4, 128, 16, 91,
+                     lens=np.array([700, 3000, 1, 0, 2500, 40]), pool_slack=0.1)
+    lens = oracle.seq_lens(p.page_size, p.indptr.numpy(), p.last_page_len.numpy())
+    total = int(lens.sum())
+    d = to_dev(p, dev)
+    plain = _run(p, d, 0, 0.0)
+    ones = _run(p, d, 0, 0.0, mask=W.pack_mask(np.ones(total, bool)))
+    torch.cuda.synchronize()
+    assert torch.equal(plain[0], ones[0]) and torch.equal(plain[1], ones[1])
+    keep = W.random_mask(5, lens, keep=0.6)
+    full = W.pack_mask(keep)
+    cut = full[: full.size // 2]  # the second half of the rows read as dropped
+    keep_cut = keep.copy()
+    keep_cut[cut.size * 8:] = False
+    got = _run(p, d, 0, 0.0, mask=cut)
+    want = _run(p, d, 0, 0.0, mask=W.pack_mask(keep_cut))
+    torch.cuda.synchronize()
+    assert torch.equal(got[0], want[0]) and torch.equal(got[1], want[1])
+    ro, rl = _oracle(p, 0, 0.0, mask=W.pack_mask(keep_cut))
+    compare(p.dtype, got[0], got[1], ro, rl, "short mask")
+
+
+@pytest.mark.parametrize("keep_p,blocks", [(0.5, False), (0.3, True)])
+def test_contig_mask(dev, keep_p, blocks):
+    p = W.make_contig("mask", "f16", 16, 4, 128, 5000, 4999, seed=78, q_std=2.0)
+    keep = W.random_mask(12, [p.valid_kv_len], keep=keep_p, blocks=blocks)
+    o, lse = _run(p, to_dev(p, dev), 0, 0.0, mask=W.pack_mask(keep))
+    torch.cuda.synchronize()
+    ro, rl = _oracle(p, 0, 0.0, mask=W.pack_mask(keep))
+    compare("f16", o, lse, ro, rl, f"contig mask {keep_p} {blocks}")
+
+
+def test_mask_full_c3(dev):
+    """The full C3 workload under a random half mask, sampled against the oracle."""
+    p = W.FULL["c3"]()
+    announce("mask full c3")
+    lens = oracle.seq_lens(p.page_size, p.indptr.numpy(), p.last_page_len.numpy())
+    packed = W.pack_mask(W.random_mask(13, lens, keep=0.5))
+    o, lse = _run(p, to_dev(p, dev), 0, 0.0, mask=packed)
+    torch.cuda.synchronize()
+    pairs = sample_pairs(p, 64, np.random.default_rng(9))
+    ro, rl = _oracle(p, 0, 0.0, samples=pairs, mask=packed)
+    idx = (torch.from_numpy(pairs[:, 0].astype(np.int64)),
+           torch.from_numpy(pairs[:, 1].astype(np.int64)))
+    compare(p.dtype, o.cpu()[idx], lse.cpu()[idx], ro, rl, "c3 mask", strict=True)
