@@ -33,17 +33,31 @@ METRIC = "achieved HBM GB/s (% of peak) + µs/call, batched paged bf16 GQA decod
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 
 
-def algorithmic_bytes(p, window=0):
-    """Valid K/V rows (the last `window` of each request under a sliding
-    window) + q + o + lse + page table, each counted once."""
+def kept_rows(lens, window=0, keep=None):
+    """K/V rows that take part, per request: the last `window` rows under a
+    sliding window, and of those the ones a custom mask keeps."""
+    lens = np.asarray(lens, dtype=np.int64)
+    if keep is None:
+        return np.minimum(lens, window) if window else lens
+    out = np.zeros_like(lens)
+    start = 0
+    for b, L in enumerate(lens):
+        lo = max(0, L - window) if window else 0
+        out[b] = int(np.count_nonzero(keep[start + lo:start + L]))
+        start += L
+    return out
+
+
+def algorithmic_bytes(p, window=0, keep=None):
+    """K/V rows that take part (valid rows; under a sliding window the last
+    `window` of each request; under a custom mask the kept ones) + q + o + lse
+    + page table, each counted once."""
     es = W.ELEM_BYTES[p.dtype]
     if isinstance(p, W.ContigProblem):
-        rows = min(p.valid_kv_len, window) if window else p.valid_kv_len
+        rows = int(kept_rows([p.valid_kv_len], window, keep)[0])
         kv = rows * p.num_kv_heads * p.head_dim * es * 2
         return kv + 2 * p.num_qo_heads * p.head_dim * es + 4 * p.num_qo_heads
-    lens = np.asarray(p.kv_lens, dtype=np.int64)
-    if window:
-        lens = np.minimum(lens, window)
+    lens = kept_rows(p.kv_lens, window, keep)
     kv = int(lens.sum()) * p.num_kv_heads * p.head_dim * es * 2
     qo = 2 * p.batch * p.num_qo_heads * p.head_dim * es
     lse = 4 * p.batch * p.num_qo_heads
@@ -97,7 +111,7 @@ def describe(p):
             "sum_kv_len": int(lens.sum()), "max_kv_len": int(lens.max())}
 
 
-def cpu_baseline(p, nbytes, window=0, softcap=0.0, min_seconds=2.0, max_runs=5):
+def cpu_baseline(p, nbytes, window=0, softcap=0.0, mask=None, min_seconds=2.0, max_runs=5):
     """The float64 oracle over the whole workload on this host's cores: whole
     calls repeated until min_seconds have passed (at most max_runs), median."""
     import oracle
@@ -108,12 +122,12 @@ def cpu_baseline(p, nbytes, window=0, softcap=0.0, min_seconds=2.0, max_runs=5):
         if isinstance(p, W.ContigProblem):
             oracle.decode_contig(p.dtype, W.bits(p.q), W.bits(p.k_cache), W.bits(p.v_cache),
                                  p.valid_kv_len, p.scale, threads=threads, layout=p.layout,
-                                 window=window, softcap=softcap)
+                                 window=window, softcap=softcap, mask=mask)
         else:
             oracle.decode_paged(p.dtype, W.bits(p.q), W.bits(p.k_data), W.bits(p.v_data),
                                 p.indices.numpy(), p.indptr.numpy(), p.last_page_len.numpy(),
                                 p.scale, threads=threads, layout=p.layout, window=window,
-                                softcap=softcap)
+                                softcap=softcap, mask=mask)
         times.append(time.perf_counter() - t0)
     dt = float(np.median(times))
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
@@ -243,6 +257,9 @@ def main():
                     help="sliding window: attend only each request's last W rows (0: all)")
     ap.add_argument("--softcap", type=float, default=0.0,
                     help="logits soft-cap c: scores -> c * tanh(x / c) (0: off)")
+    ap.add_argument("--mask-keep", type=float, default=0.0,
+                    help="custom mask: keep each K/V row with this probability (seeded; "
+                         "0: no mask); bytes count the kept rows only")
     ap.add_argument("--rotate", type=int, default=1,
                     help="cycle the calls over this many distinct device copies of the K/V "
                          "store (paged), as successive layers of a model would, so no call "
@@ -270,7 +287,13 @@ def main():
         p = W.token_major(p)
     print(f"[bench] generated {p.name} in {time.perf_counter() - t0:.1f}s", file=sys.stderr,
           flush=True)
-    nbytes = algorithmic_bytes(p, args.window)
+    keep = mask = dev_mask = None
+    if args.mask_keep > 0.0:
+        lens = [p.valid_kv_len] if isinstance(p, W.ContigProblem) else p.kv_lens
+        keep = W.random_mask(4242, lens, keep=args.mask_keep)
+        mask = W.pack_mask(keep)
+        dev_mask = torch.from_numpy(mask).to(dev)
+    nbytes = algorithmic_bytes(p, args.window, keep)
 
     if isinstance(p, W.ContigProblem):
         q, k, v = p.q.to(dev), p.k_cache.to(dev), p.v_cache.to(dev)
@@ -281,7 +304,8 @@ def main():
 
         def step():
             fad.decode_contig(q, k, v, p.valid_kv_len, p.scale, o=o, lse=lse, workspace=ws,
-                              layout=p.layout, window=args.window, softcap=args.softcap)
+                              layout=p.layout, window=args.window, softcap=args.softcap,
+                              mask=dev_mask)
     else:
         q, k, v = p.q.to(dev), p.k_data.to(dev), p.v_data.to(dev)
         ind, ptr, lpl = p.indices.to(dev), p.indptr.to(dev), p.last_page_len.to(dev)
@@ -296,7 +320,8 @@ def main():
             ks, vs = stores[turn[0] % len(stores)]
             turn[0] += 1
             fad.decode_paged(q, ks, vs, ind, ptr, lpl, p.scale, o=o, lse=lse, workspace=ws,
-                             layout=p.layout, window=args.window, softcap=args.softcap)
+                             layout=p.layout, window=args.window, softcap=args.softcap,
+                             mask=dev_mask)
 
     for _ in range(args.warmup):
         step()
@@ -337,7 +362,9 @@ def main():
           f"{kernel_ms * 1e3:.1f} us (call with event markers {call_ms / max(calls, 1) * 1e3:.1f} "
           f"us), {value:.0f} GB/s call, {achieved:.0f} GB/s kernel", file=sys.stderr, flush=True)
 
-    traffic = committed_traffic(p.name)
+    # the committed counter figures were taken on plain calls (no window, cap or mask)
+    plain = not (args.window or args.softcap or mask is not None)
+    traffic = committed_traffic(p.name) if plain else None
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -354,6 +381,7 @@ def main():
         "dtype": p.dtype,
         "data": "synthetic (seeded N(0,1) values, seeded page tables; no dataset)",
         "config": {**describe(p), "window": args.window, "softcap": args.softcap,
+                   "mask_keep": args.mask_keep,
                    "kv_copies_rotated": args.rotate,
                    "algorithmic_bytes_per_call": int(nbytes),
                    "chunk_rows": chunk, "heads_per_workgroup": gt,
@@ -380,7 +408,7 @@ def main():
         line["hbm_probe"] = hbm_probe(dev)
     if not args.no_cpu_baseline:
         print("[bench] timing the float64 oracle on the host", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(p, nbytes, args.window, args.softcap)
+        line["cpu_baseline"] = cpu_baseline(p, nbytes, args.window, args.softcap, mask)
     print(json.dumps(line), flush=True)
 
 

@@ -270,26 +270,32 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   // where this lane's loaded 16 bytes go: row RPI * i + lane / LPR
   const int st_row = lane / G::LPR, st_col = (lane % G::LPR) * 16;
 
-  // Custom mask bits of the lane's 8 rows of the tile at t0: bit 4j + i for row
-  // t0 + 16j + 4grp + i (rows past the request read its last row's bit and are
-  // cut by t_end anyway).  Loaded with the tile, so the latency overlaps.
-  auto mask_bits = [&](int t0) -> uint32_t {
-    uint32_t bits = 0;
+  // Custom mask of the tile at t0: its 32 bits start at bit B = row0 + t0 and
+  // span bytes B/8 .. B/8 + 4.  mask_load issues one load instruction for
+  // them with the tile's K/V loads (lanes 0-4, a byte each; bytes past the
+  // mask's end read as 0); mask_bits, at compute time, assembles the wave's
+  // bytes and returns the lane's rows: bit 4j + i for row t0 + 16j + 4grp + i.
+  // Rows past the request (a prefetched tile, the tail of the last one) see
+  // other bits and are cut by t_end.
+  auto mask_load = [&](int t0) -> uint32_t {
+    uint32_t v = 0;
     if constexpr (kMods) {
       if (p.mask) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = min(t0 + 16 * j + 4 * grp + i, u.L - 1);
-            bits |= (uint32_t)mask_keeps(p, u.row0, t) << (4 * j + i);
-          }
+        const uint32_t byte = ((uint32_t)(u.row0 + t0) >> 3) + (uint32_t)lane;
+        if (lane < 5 && byte < p.mask_bytes) v = p.mask[byte];
       }
     }
-    return bits;
+    return v;
+  };
+  auto mask_bits = [&](int t0, uint32_t v) -> uint32_t {
+    uint64_t w = 0;
+#pragma unroll
+    for (int k = 0; k < 5; ++k) w |= (uint64_t)__builtin_amdgcn_readlane(v, k) << (8 * k);
+    const uint32_t tile = (uint32_t)(w >> ((uint32_t)(u.row0 + t0) & 7));  // bit r: row t0 + r
+    return ((tile >> (4 * grp)) & 0xFu) | (((tile >> (16 + 4 * grp)) & 0xFu) << 4);
   };
 
-  auto compute = [&](const KVTile<G::NI> &T, int t0, uint32_t mbits) {
+  auto compute = [&](const KVTile<G::NI> &T, int t0, uint32_t mraw) {
     // K and V tiles to LDS
 #pragma unroll
     for (int i = 0; i < G::NI; ++i) {
@@ -300,6 +306,9 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    uint32_t mbits = 0;
+    if constexpr (kMods)
+      if (p.mask) mbits = mask_bits(t0, mraw);
     // scores; A = K rows 16j + n, features 32kk + 8grp .. + 8
     f32x4 s[2];
 #pragma unroll
@@ -373,18 +382,18 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   if (t0 < t_end) {
     KVTile<G::NI> A;
     issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, t0, t_end, lane);
-    uint32_t mA = mask_bits(t0);
+    uint32_t mA = mask_load(t0);
     if constexpr (G::kPipelined) {
       KVTile<G::NI> B;
       uint32_t mB;
       while (true) {
         issue_tile<E, D, kNhd>(B, p, page_base, s_pages, slot0, kvh, t0 + stride, t_end, lane);
-        mB = mask_bits(t0 + stride);
+        mB = mask_load(t0 + stride);
         compute(A, t0, mA);
         t0 += stride;
         if (t0 >= t_end) break;
         issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, t0 + stride, t_end, lane);
-        mA = mask_bits(t0 + stride);
+        mA = mask_load(t0 + stride);
         compute(B, t0, mB);
         t0 += stride;
         if (t0 >= t_end) break;
@@ -395,7 +404,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
         t0 += stride;
         if (t0 >= t_end) break;
         issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, t0, t_end, lane);
-        mA = mask_bits(t0);
+        mA = mask_load(t0);
       }
     }
   }
