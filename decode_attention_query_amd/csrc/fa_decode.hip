@@ -38,8 +38,10 @@ int heads_per_unit(int group, int max_heads) {
   return 1;
 }
 
-// 0: vector-ALU kernel (f32); 1: matrix-core kernel (f16, bf16)
-int kernel_kind(fa_dtype_t dt) { return dt == FA_DTYPE_F32 ? 0 : 1; }
+// 0: vector-ALU kernel (f32 at D = 256, whose 16-row f32 tiles would not fit
+// the matrix-core kernel's registers next to its accumulators); 1: matrix-core
+// kernel (f16 and bf16; f32 at D <= 128 with k = 4 products)
+int kernel_kind(fa_dtype_t dt, int d) { return dt == FA_DTYPE_F32 && d > 128 ? 0 : 1; }
 
 struct HostPlan {
   int group = 0, gt = 0, n_gblocks = 0, planes = 0;
@@ -62,7 +64,7 @@ bool grid_ok(int hq, int hkv) { return hq / hkv > 0 && hkv * (hq / hkv) <= 65535
 HostPlan make_plan(fa_dtype_t dt, int batch, int hq, int hkv, int d, int page_size,
                    int total_used_pages, bool contig) {
   HostPlan hp;
-  hp.kind = kernel_kind(dt);
+  hp.kind = kernel_kind(dt, d);
   hp.group = hq / hkv;
   hp.gt = heads_per_unit(hp.group, hp.kind == 0 ? 8 : 16);
   hp.n_gblocks = hp.group / hp.gt;
@@ -179,14 +181,6 @@ hipError_t launch_valu_gt(const DecodeParams &p, const HostPlan &hp, hipStream_t
   }
 }
 
-template <class E>
-hipError_t launch_decode(const DecodeParams &p, const HostPlan &hp, hipStream_t s) {
-  switch (p.head_dim) {
-    case 64: return launch_valu_gt<E, 64>(p, hp, s);
-    case 128: return launch_valu_gt<E, 128>(p, hp, s);
-    default: return launch_valu_gt<E, 256>(p, hp, s);
-  }
-}
 
 template <class E, int D>
 hipError_t launch_mfma(const DecodeParams &p, const HostPlan &hp, hipStream_t s) {
@@ -216,10 +210,19 @@ hipError_t launch_decode_mfma(const DecodeParams &p, const HostPlan &hp, hipStre
   }
 }
 
+// f32: matrix cores at D <= 128, the vector-ALU kernel at D = 256
+hipError_t launch_decode_f32(const DecodeParams &p, const HostPlan &hp, hipStream_t s) {
+  switch (p.head_dim) {
+    case 64: return launch_mfma<fa::F32, 64>(p, hp, s);
+    case 128: return launch_mfma<fa::F32, 128>(p, hp, s);
+    default: return launch_valu_gt<fa::F32, 256>(p, hp, s);
+  }
+}
+
 hipError_t dispatch_decode(fa_dtype_t dt, const DecodeParams &p, const HostPlan &hp,
                            hipStream_t s) {
   switch (dt) {
-    case FA_DTYPE_F32: return launch_decode<fa::F32>(p, hp, s);
+    case FA_DTYPE_F32: return launch_decode_f32(p, hp, s);
     case FA_DTYPE_F16: return launch_decode_mfma<fa::F16>(p, hp, s);
     default: return launch_decode_mfma<fa::BF16>(p, hp, s);
   }

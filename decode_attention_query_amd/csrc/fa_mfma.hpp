@@ -57,6 +57,18 @@ struct Mfma<F16> {
   }
 };
 
+// f32 K/V: v_mfma_f32_16x16x4_f32, one element per lane and operand (A: lane
+// l holds A[l % 16][l / 16]; B: B[l / 16][l % 16]; the 16x16 result in the
+// same lane layout as the 16-bit products).  v8 is unused on this path.
+template <>
+struct Mfma<F32> {
+  typedef float v8 __attribute__((ext_vector_type(8)));
+  static constexpr bool kSplitP = false;
+  __device__ static inline f32x4 mma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
 // 8 probabilities -> MFMA operand(s), round-to-nearest-even; with kSplitP the
 // residual p - hi is rounded into lo, so hi + lo carries ~16 significant bits.
 template <class E>
@@ -90,22 +102,29 @@ constexpr int mfma_waves(int d) { return d <= 128 ? 4 : 2; }
 
 template <class E, int D>
 struct MfmaGeom {
+  static constexpr bool kF32 = E::kBytes == 4;
   static constexpr int NW = mfma_waves(D);
-  static constexpr int TT = 32;          // rows per wave tile
-  static constexpr int KK = D / 32;      // score k-steps per 16-row block
+  // rows per wave tile: 32 (two 16-row MFMA blocks) for 16-bit K/V; 16 for
+  // f32, whose rows are twice as wide (the same 16 KiB per tile at D = 128)
+  static constexpr int TT = kF32 ? 16 : 32;
+  static constexpr int JB = TT / 16;     // 16-row blocks per tile
+  static constexpr int KK = D / 32;      // 16-bit score k-steps (k = 32) per 16-row block
+  static constexpr int QC = D / 16;      // f32: 4-feature chunks of a lane's quarter of D
   static constexpr int MB = D / 16;      // 16-feature blocks of O^T
   // Global loads: each instruction reads whole rows, 1 KiB contiguous per
   // wave (LPR lanes per row, RPI rows per instruction, NI instructions per
   // 32-row tile of K, and as many of V).  An instruction shaped like the MFMA
   // operand instead (16 rows x 64 bytes) streams ~13% slower from HBM.
-  static constexpr int LPR = D * 2 / 16;
+  static constexpr int LPR = D * E::kBytes / 16;
   static constexpr int RPI = 64 / LPR;
   static constexpr int NI = TT / RPI;
   // LDS row strides.  K is read back 16 bytes per lane from 16 rows at once:
-  // a 16-byte pad puts those rows in distinct banks.  V is read with
-  // transposed 8-byte reads spanning 8 rows: a 32-byte pad does the same.
-  static constexpr int ROWK = D * 2 + 16;
-  static constexpr int ROWV = D * 2 + 32;
+  // a 16-byte pad puts those rows in distinct banks.  16-bit V is read with
+  // transposed 8-byte reads spanning 8 rows: a 32-byte pad does the same; f32
+  // V is read 4 bytes per lane, 16 features of 4 rows at once: a 64-byte pad
+  // puts the 4 rows in distinct banks.
+  static constexpr int ROWK = D * E::kBytes + 16;
+  static constexpr int ROWV = kF32 ? D * 4 + 64 : D * 2 + 32;
   static constexpr int WAVE_LDS = TT * (ROWK + ROWV);
   static constexpr int LDS_KV = NW * WAVE_LDS;
   // Wave-merge area (reuses the K/V area): per wave 16 head rows of D floats,
@@ -118,7 +137,7 @@ struct MfmaGeom {
   static constexpr bool kPipelined = D <= 128;   // prefetch one tile ahead
 };
 
-// K and V of one 32-row tile as loaded: instruction i, lane l holds row
+// K and V of one tile as loaded: instruction i, lane l holds row
 // RPI * i + l / LPR, bytes 16 (l % LPR) .. + 16.
 template <int NI>
 struct KVTile {
@@ -159,10 +178,10 @@ __device__ inline void issue_tile(KVTile<MfmaGeom<E, D>::NI> &T, const DecodePar
   const int col = (lane % G::LPR) * 16;   // byte within the row
   const char *kb = static_cast<const char *>(p.k) + col;
   const char *vb = static_cast<const char *>(p.v) + col;
-  int64_t blk[2];
+  int64_t blk[G::JB];
   if (p.uniform_blocks) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < G::JB; ++j) {
       const int tb = min(t0 + 16 * j, t_end - 1);
       blk[j] = staged_block_offset<kNhd>(p, s_pages, slot0, kvh, tb) - (int64_t)tb * rs;
     }
@@ -174,9 +193,9 @@ __device__ inline void issue_tile(KVTile<MfmaGeom<E, D>::NI> &T, const DecodePar
     int64_t off;
     if (p.uniform_blocks) {
       // rows of block j = r / 16 share its page: offset = block base + row stride
-      off = (blk[(G::RPI * i) / 16] + (int64_t)t * rs) * 2;
+      off = (blk[(G::RPI * i) / 16] + (int64_t)t * rs) * E::kBytes;
     } else {
-      off = kv_row_offset(p, page_base, kvh, t) * 2;
+      off = kv_row_offset(p, page_base, kvh, t) * E::kBytes;
     }
     T.k[i] = load16_stream(kb + off);
     T.v[i] = load16_stream(vb + off);
@@ -191,7 +210,8 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   using G = MfmaGeom<E, D>;
   using M = Mfma<E>;
   using v8 = typename M::v8;
-  constexpr int KK = G::KK, MB = G::MB, NW = G::NW, TT = G::TT;
+  constexpr int KK = G::KK, MB = G::MB, NW = G::NW, TT = G::TT, JB = G::JB, QC = G::QC;
+  constexpr bool kF32 = G::kF32;
 
   __shared__ __attribute__((aligned(16))) char lds[G::LDS];
   __shared__ float s_m[NW][16];
@@ -236,17 +256,30 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   const int n = lane & 15;
   const int grp = lane >> 4;
 
-  // B operand of the score MFMA: Q^T, head n, features 32kk + 8grp .. +8.
-  v8 qb[KK];
+  // B operand of the score MFMA: Q^T, head n.  16-bit: features 32kk + 8grp
+  // .. + 8 (qb).  f32: lane group grp takes features grp D/4 .. + D/4 as its
+  // share of every product, four per 16-byte chunk (qf); any split of the
+  // contraction works as long as the A operand (K) uses the same one.
+  v8 qb[kF32 ? 1 : KK];
+  f32x4 qf[kF32 ? QC : 1];
   {
     const bool live = n < gt;
     const char *qrow = static_cast<const char *>(p.q) +
-                       (((int64_t)u.b * p.num_qo_heads + h0 + (live ? n : 0)) * D + 8 * grp) * 2;
+                       ((int64_t)u.b * p.num_qo_heads + h0 + (live ? n : 0)) * D * E::kBytes;
+    if constexpr (kF32) {
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      uint4 r = *reinterpret_cast<const uint4 *>(qrow + kk * 64);
-      if (!live) r = make_uint4(0, 0, 0, 0);
-      qb[kk] = __builtin_bit_cast(v8, r);
+      for (int q4 = 0; q4 < QC; ++q4) {
+        uint4 r = *reinterpret_cast<const uint4 *>(qrow + (grp * (D / 4) + 4 * q4) * 4);
+        if (!live) r = make_uint4(0, 0, 0, 0);
+        qf[q4] = __builtin_bit_cast(f32x4, r);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        uint4 r = *reinterpret_cast<const uint4 *>(qrow + (8 * grp) * 2 + kk * 64);
+        if (!live) r = make_uint4(0, 0, 0, 0);
+        qb[kk] = __builtin_bit_cast(v8, r);
+      }
     }
   }
 
@@ -264,9 +297,11 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   const float c = p.scale_log2;
   typedef short s16x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  // this lane's address in each transposed read: row 4 grp + (n / 4) of the
-  // 16-row half, features 4 (n % 4) .. + 3 of the 16-feature block
-  const char *vt = wv + (4 * grp + (n >> 2)) * G::ROWV + (4 * (n & 3)) * 2;
+  // 16-bit V: this lane's address in each transposed read: row 4 grp + (n / 4)
+  // of the 16-row half, features 4 (n % 4) .. + 3 of the 16-feature block.
+  // f32 V: row 4 grp (+ i) and feature n (+ 16 mb), read directly.
+  const char *vt = kF32 ? wv + (4 * grp) * G::ROWV + n * 4
+                        : wv + (4 * grp + (n >> 2)) * G::ROWV + (4 * (n & 3)) * 2;
   // where this lane's loaded 16 bytes go: row RPI * i + lane / LPR
   const int st_row = lane / G::LPR, st_col = (lane % G::LPR) * 16;
 
@@ -274,7 +309,8 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   // span bytes B/8 .. B/8 + 4.  mask_load issues one load instruction for
   // them with the tile's K/V loads (lanes 0-4, a byte each; bytes past the
   // mask's end read as 0); mask_bits, at compute time, assembles the wave's
-  // bytes and returns the lane's rows: bit 4j + i for row t0 + 16j + 4grp + i.
+  // bytes and returns the lane's rows: bit 4j + i for row t0 + 16j + 4grp + i
+  // (j < JB).
   // Rows past the request (a prefetched tile, the tail of the last one) see
   // other bits and are cut by t_end.
   auto mask_load = [&](int t0) -> uint32_t {
@@ -292,7 +328,8 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
 #pragma unroll
     for (int k = 0; k < 5; ++k) w |= (uint64_t)__builtin_amdgcn_readlane(v, k) << (8 * k);
     const uint32_t tile = (uint32_t)(w >> ((uint32_t)(u.row0 + t0) & 7));  // bit r: row t0 + r
-    return ((tile >> (4 * grp)) & 0xFu) | (((tile >> (16 + 4 * grp)) & 0xFu) << 4);
+    const uint32_t lo = (tile >> (4 * grp)) & 0xFu;
+    return JB == 2 ? lo | (((tile >> (16 + 4 * grp)) & 0xFu) << 4) : lo;
   };
 
   auto compute = [&](const KVTile<G::NI> &T, int t0, uint32_t mraw) {
@@ -309,23 +346,34 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
     uint32_t mbits = 0;
     if constexpr (kMods)
       if (p.mask) mbits = mask_bits(t0, mraw);
-    // scores; A = K rows 16j + n, features 32kk + 8grp .. + 8
-    f32x4 s[2];
+    // scores; A = K row 16j + n: features 32kk + 8grp .. + 8 (16-bit), or the
+    // lane group's quarter of D, one feature per product (f32)
+    f32x4 s[JB];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < JB; ++j) {
       s[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (kF32) {
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const uint4 ka =
-            *reinterpret_cast<const uint4 *>(wk + (16 * j + n) * G::ROWK + (32 * kk + 8 * grp) * 2);
-        s[j] = M::mma(__builtin_bit_cast(v8, ka), qb[kk], s[j]);
+        for (int q4 = 0; q4 < QC; ++q4) {
+          const f32x4 ka = *reinterpret_cast<const f32x4 *>(
+              wk + (16 * j + n) * G::ROWK + (grp * (D / 4) + 4 * q4) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[j] = Mfma<F32>::mma4(ka[e], qf[q4][e], s[j]);
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const uint4 ka = *reinterpret_cast<const uint4 *>(wk + (16 * j + n) * G::ROWK +
+                                                            (32 * kk + 8 * grp) * 2);
+          s[j] = M::mma(__builtin_bit_cast(v8, ka), qb[kk], s[j]);
+        }
       }
     }
     // online softmax for head n over the tile's rows 16j + 4grp + i
-    float x[8];
+    float x[4 * JB];
     float tmax = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < JB; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = t0 + 16 * j + 4 * grp + i;
@@ -345,10 +393,10 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
     const float m_new = fmaxf(m_run, tmax);
     const float ref = safe_ref(m_new);
     const float alpha = fast_exp2(m_run - ref);
-    float pr[8];
+    float pr[4 * JB];
     float psum = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < 4 * JB; ++e) {
       pr[e] = fast_exp2(x[e] - ref);
       psum += pr[e];
     }
@@ -356,20 +404,33 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
     m_run = m_new;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[mb] *= alpha;
-    v8 ph, pl;
-    pack_probs<E>(pr, ph, pl);
+    if constexpr (kF32) {
+      // O^T += V^T P^T over the 16 rows, 4 at a time: in product i, lane group
+      // grp contributes row 4grp + i, so B is the lane's own probability pr[i]
+      // and A is V[row 4grp + i][feature 16mb + n]
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      // A = V^T: rows 16h + 4grp + r (r < 4) of feature 16mb + n, for h = 0, 1
-      const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4 *)(vt + 32 * mb));
-      const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4 *)(vt + 16 * G::ROWV + 32 * mb));
-      typedef short s16x8 __attribute__((ext_vector_type(8)));
-      const s16x8 a16 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-      const v8 a = __builtin_bit_cast(v8, a16);
-      acc[mb] = M::mma(a, ph, acc[mb]);
-      if constexpr (M::kSplitP) acc[mb] = M::mma(a, pl, acc[mb]);
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = *reinterpret_cast<const float *>(vt + i * G::ROWV + 64 * mb);
+          acc[mb] = Mfma<F32>::mma4(a, pr[i], acc[mb]);
+        }
+    } else {
+      v8 ph, pl;
+      pack_probs<E>(pr, ph, pl);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        // A = V^T: rows 16h + 4grp + r (r < 4) of feature 16mb + n, for h = 0, 1
+        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4 *)(vt + 32 * mb));
+        const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4 *)(vt + 16 * G::ROWV + 32 * mb));
+        typedef short s16x8 __attribute__((ext_vector_type(8)));
+        const s16x8 a16 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        const v8 a = __builtin_bit_cast(v8, a16);
+        acc[mb] = M::mma(a, ph, acc[mb]);
+        if constexpr (M::kSplitP) acc[mb] = M::mma(a, pl, acc[mb]);
+      }
     }
     // the reads above complete before the next tile overwrites the area
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
