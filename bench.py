@@ -246,6 +246,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c3", choices=sorted(W.FULL))
+    ap.add_argument("--dtype", default=None, choices=["f32", "f16", "bf16"],
+                    help="store the workload's shapes in this element type instead of its own")
     ap.add_argument("--layout", default="hnd", choices=["hnd", "nhd"],
                     help="K/V storage: heads-major (default) or token-major")
     ap.add_argument("--graph-calls", type=int, default=0,
@@ -282,7 +284,7 @@ def main():
     dev = torch.device("cuda:0")
 
     t0 = time.perf_counter()
-    p = W.FULL[args.workload]()
+    p = W.FULL[args.workload](dtype=args.dtype)
     if args.layout == "nhd":
         p = W.token_major(p)
     print(f"[bench] generated {p.name} in {time.perf_counter() - t0:.1f}s", file=sys.stderr,

@@ -78,6 +78,29 @@ def test_full_config_parity(dev, name):
         assert np.all(np.isfinite(lse_all[lens > 0]))
     announce(f"  max|do|={eo:.2e} max|dlse|={el:.2e}")
     del d, o, lse
+
+
+@pytest.mark.parametrize("name,dtype", [("c3", "f32"), ("c2", "f32"), ("c3", "f16")])
+def test_full_shapes_other_dtype(dev, name, dtype):
+    """Full-size shapes stored in another element type (f32 runs the matrix-core
+    kernel with k = 4 products at these head dims), sampled against the
+    oracle at that type's tolerance."""
+    p = W.FULL[name](dtype=dtype)
+    announce(f"full {name} as {dtype}: {p.name}")
+    d = to_dev(p, dev)
+    o, lse = run(p, d)
+    torch.cuda.synchronize()
+    if isinstance(p, W.ContigProblem):
+        ro, rl = oracle_of(p)
+        compare(p.dtype, o, lse, ro, rl, p.name, strict=True)
+    else:
+        pairs = sample_pairs(p, 64, np.random.default_rng(6))
+        ro, rl = oracle_of(p, samples=pairs)
+        idx = torch.from_numpy(pairs[:, 0].astype(np.int64)), \
+            torch.from_numpy(pairs[:, 1].astype(np.int64))
+        compare(p.dtype, o.cpu()[idx[0], idx[1]], lse.cpu()[idx[0], idx[1]], ro, rl, p.name,
+                strict=True)
+    del d, o, lse
     torch.cuda.empty_cache()
 
 

@@ -286,30 +286,42 @@ def _c5_tables(lens, page_size):
     return n_pages, lpl
 
 
-def c1(seed=1001):
-    return make_contig("c1_contig_f32", "f32", 8, 2, 64, 256, 128, seed)
+# The five configurations.  dtype, if given, stores the same shapes and
+# draws in another element type (the name gains a suffix); None keeps the
+# configuration's own.
+def _named(name, own, dtype):
+    return (name, own) if dtype in (None, own) else (f"{name}_as_{dtype}", dtype)
 
 
-def c2(seed=1002):
-    return make_contig("c2_contig_f16", "f16", 32, 8, 128, 8192, 4096, seed, kv_std=0.5)
+def c1(seed=1001, dtype=None):
+    name, dt = _named("c1_contig_f32", "f32", dtype)
+    return make_contig(name, dt, 8, 2, 64, 256, 128, seed)
 
 
-def c3(seed=1003):
-    return make_paged("c3_paged_bf16", "bf16", 64, 32, 8, 128, 16, seed,
+def c2(seed=1002, dtype=None):
+    name, dt = _named("c2_contig_f16", "f16", dtype)
+    return make_contig(name, dt, 32, 8, 128, 8192, 4096, seed, kv_std=0.5)
+
+
+def c3(seed=1003, dtype=None):
+    name, dt = _named("c3_paged_bf16", "bf16", dtype)
+    return make_paged(name, dt, 64, 32, 8, 128, 16, seed,
                       lens_fn=lambda r: r.integers(512, 8192, size=64, endpoint=True),
                       pool_pages=40000)
 
 
-def c4(seed=1004):
-    return make_paged("c4_paged_bf16_g8", "bf16", 32, 64, 8, 128, 32, seed,
+def c4(seed=1004, dtype=None):
+    name, dt = _named("c4_paged_bf16_g8", "bf16", dtype)
+    return make_paged(name, dt, 32, 64, 8, 128, 32, seed,
                       lens=np.full(32, 32768), pool_pages=32768)
 
 
-def c5(seed=1005):
+def c5(seed=1005, dtype=None):
+    name, dt = _named("c5_paged_f16_skew", "f16", dtype)
     ss = np.random.SeedSequence(seed)
     lens = _c5_lens(np.random.default_rng(ss.spawn(1)[0]), 128, 7.0, 1.5, 131072)
     n_pages, lpl = _c5_tables(lens, 16)
-    return make_paged("c5_paged_f16_skew", "f16", 128, 16, 4, 256, 16, seed,
+    return make_paged(name, dt, 128, 16, 4, 256, 16, seed,
                       n_pages=n_pages, last_page_len=lpl, pool_slack=0.25)
 
 
