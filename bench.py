@@ -387,7 +387,7 @@ def main():
                    "kv_copies_rotated": args.rotate,
                    "algorithmic_bytes_per_call": int(nbytes),
                    "chunk_rows": chunk, "heads_per_workgroup": gt,
-                   "attention_kernel": "valu" if kind == 0 else "mfma"},
+                   "attention_kernel": "mfma" if kind == 1 else f"kind {kind}"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic["traffic_bytes"] if traffic else None,

@@ -30,18 +30,16 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Query heads per workgroup: the largest power of two dividing the group that
-// the kernel's head block holds (8 for the vector-ALU kernel, 16 for the
-// matrix-core kernel's 16-wide MFMA column block).
+// the kernel's head block holds (16, the MFMA column block).
 int heads_per_unit(int group, int max_heads) {
   for (int gt = max_heads; gt > 1; gt /= 2)
     if (group % gt == 0) return gt;
   return 1;
 }
 
-// 0: vector-ALU kernel (f32 at D = 256, whose 16-row f32 tiles would not fit
-// the matrix-core kernel's registers next to its accumulators); 1: matrix-core
-// kernel (f16 and bf16; f32 at D <= 128 with k = 4 products)
-int kernel_kind(fa_dtype_t dt, int d) { return dt == FA_DTYPE_F32 && d > 128 ? 0 : 1; }
+// The attention kernel of a call: 1, the matrix-core kernel, for every element
+// type and head dim (the value fa_debug_plan reports).
+constexpr int kKernelMfma = 1;
 
 struct HostPlan {
   int group = 0, gt = 0, n_gblocks = 0, planes = 0;
@@ -64,9 +62,9 @@ bool grid_ok(int hq, int hkv) { return hq / hkv > 0 && hkv * (hq / hkv) <= 65535
 HostPlan make_plan(fa_dtype_t dt, int batch, int hq, int hkv, int d, int page_size,
                    int total_used_pages, bool contig) {
   HostPlan hp;
-  hp.kind = kernel_kind(dt, d);
+  hp.kind = kKernelMfma;
   hp.group = hq / hkv;
-  hp.gt = heads_per_unit(hp.group, hp.kind == 0 ? 8 : 16);
+  hp.gt = heads_per_unit(hp.group, 16);
   hp.n_gblocks = hp.group / hp.gt;
   hp.planes = hkv * hp.n_gblocks;
   // The split size depends on the KV heads only (not on the kernel's head
@@ -164,24 +162,6 @@ struct CallEvents {
 
 // --------------------------------------------------------------- dispatch
 
-template <class E, int D, int GT>
-hipError_t launch_valu(const DecodeParams &p, const HostPlan &hp, hipStream_t s) {
-  dim3 grid(hp.units_bound, hp.planes);
-  hipLaunchKernelGGL((fa::decode_valu_kernel<E, D, GT>), grid, dim3(256), 0, s, p);
-  return hipGetLastError();
-}
-
-template <class E, int D>
-hipError_t launch_valu_gt(const DecodeParams &p, const HostPlan &hp, hipStream_t s) {
-  switch (hp.gt) {
-    case 8: return launch_valu<E, D, 8>(p, hp, s);
-    case 4: return launch_valu<E, D, 4>(p, hp, s);
-    case 2: return launch_valu<E, D, 2>(p, hp, s);
-    default: return launch_valu<E, D, 1>(p, hp, s);
-  }
-}
-
-
 template <class E, int D>
 hipError_t launch_mfma(const DecodeParams &p, const HostPlan &hp, hipStream_t s) {
   dim3 grid(unsigned(hp.units_bound) * unsigned(hp.planes));
@@ -210,19 +190,10 @@ hipError_t launch_decode_mfma(const DecodeParams &p, const HostPlan &hp, hipStre
   }
 }
 
-// f32: matrix cores at D <= 128, the vector-ALU kernel at D = 256
-hipError_t launch_decode_f32(const DecodeParams &p, const HostPlan &hp, hipStream_t s) {
-  switch (p.head_dim) {
-    case 64: return launch_mfma<fa::F32, 64>(p, hp, s);
-    case 128: return launch_mfma<fa::F32, 128>(p, hp, s);
-    default: return launch_valu_gt<fa::F32, 256>(p, hp, s);
-  }
-}
-
 hipError_t dispatch_decode(fa_dtype_t dt, const DecodeParams &p, const HostPlan &hp,
                            hipStream_t s) {
   switch (dt) {
-    case FA_DTYPE_F32: return launch_decode_f32(p, hp, s);
+    case FA_DTYPE_F32: return launch_decode_mfma<fa::F32>(p, hp, s);
     case FA_DTYPE_F16: return launch_decode_mfma<fa::F16>(p, hp, s);
     default: return launch_decode_mfma<fa::BF16>(p, hp, s);
   }

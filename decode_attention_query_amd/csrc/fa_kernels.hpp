@@ -1,5 +1,5 @@
-// fa_kernels.hpp -- split-unit schedule, vector-ALU decode, LSE merge and the
-// gather hook.
+// fa_kernels.hpp -- split-unit schedule, LSE merge, and the append, gather,
+// schedule and read-probe kernels.
 //
 // Work decomposition (all kernels): a *split unit* is one request's KV rows
 // [c * chunk, min(L_b, (c + 1) * chunk)).  A decode workgroup handles one split
@@ -482,193 +482,6 @@ __device__ void finish_split(const DecodeParams &p, const UnitInfo &u, int plane
     __hip_atomic_store(counter, kArrivalMark << kCountBits, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   merge_partials<E, kDepth>(p, u.b, u.u0, u.n_units, h0, gt, nw, s_stat, s_w, w_cap);
-}
-
-// ------------------------------------------------------ vector-ALU decode
-//
-// 4 waves.  A wave reads TPW = 64 / LPT KV rows per step, LPT lanes per row,
-// 16 bytes per lane (one global_load_dwordx4), U steps per tile.  Each lane
-// keeps, for its row slot, an online-softmax state per query head: running
-// max m (base 2), normaliser l and its D / LPT accumulator features
-// (ferrox-cuda 0.15.2, src/attn.rs, kernel gqa_decode: the running-max
-// rescale of the normaliser and the accumulator; here once per tile instead
-// of once per row).  Slots and waves are merged at the end.
-template <class E, int D, int GT>
-__global__ __launch_bounds__(256) void decode_valu_kernel(const DecodeParams p) {
-  constexpr int VEC = 16 / E::kBytes;  // elements per 16-byte lane load
-  constexpr int LPT = D / VEC;         // lanes per KV row
-  constexpr int TPW = kWave / LPT;     // KV rows per wave step
-  constexpr int NW = 4;
-  constexpr int U = GT >= 8 ? 2 : 4;   // steps per tile
-  constexpr int TILE = NW * TPW * U;   // rows per workgroup iteration
-  static_assert(LPT >= 1 && LPT <= kWave && TPW * LPT == kWave, "row split");
-
-  __shared__ float s_acc[NW][GT][D];
-  __shared__ float s_m[NW][GT];
-  __shared__ float s_l[NW][GT];
-
-  UnitInfo u;
-  if (!find_unit<true>(p, blockIdx.x, u)) return;  // row0 for a custom mask
-  const int kvh = blockIdx.y / p.n_gblocks;
-  const int h0 = kvh * p.group + (blockIdx.y % p.n_gblocks) * GT;
-  const int t_begin = u.lo + u.c * p.chunk;
-  const int t_end = min(u.L, t_begin + p.chunk);
-  const int t_lo = u.start;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int slot = lane / LPT;
-  const int vi = lane % LPT;
-
-  // ALiBi: score of row t gains slope * (t - (L - 1)), here in base-2 units
-  float slope2[GT];
-#pragma unroll
-  for (int g = 0; g < GT; ++g) slope2[g] = p.alibi ? p.alibi[h0 + g] * kLog2e : 0.0f;
-  const int last_row = u.L - 1;
-
-  float qf[GT][VEC];
-  {
-    const char *qb = static_cast<const char *>(p.q) +
-                     (((int64_t)u.b * p.num_qo_heads + h0) * D + vi * VEC) * E::kBytes;
-#pragma unroll
-    for (int g = 0; g < GT; ++g) {
-      const uint4 r = *reinterpret_cast<const uint4 *>(qb + (int64_t)g * D * E::kBytes);
-      E::widen(r, qf[g]);
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) qf[g][i] *= p.scale_log2;
-    }
-  }
-
-  float m[GT], l[GT], acc[GT][VEC];
-#pragma unroll
-  for (int g = 0; g < GT; ++g) {
-    m[g] = -INFINITY;
-    l[g] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) acc[g][i] = 0.0f;
-  }
-
-  const char *kb = static_cast<const char *>(p.k) + (int64_t)vi * VEC * E::kBytes;
-  const char *vb = static_cast<const char *>(p.v) + (int64_t)vi * VEC * E::kBytes;
-
-  for (int t0 = t_begin + wave * TPW * U; t0 < t_end; t0 += TILE) {
-    uint4 kr[U], vr[U];
-    bool valid[U];
-#pragma unroll
-    for (int s = 0; s < U; ++s) {
-      const int t = t0 + s * TPW + slot;
-      valid[s] = t >= t_lo && t < t_end;
-      if (p.mask && valid[s]) valid[s] = mask_keeps(p, u.row0, t);
-      const int64_t off = kv_row_offset(p, u.page_base, kvh, valid[s] ? t : t_end - 1);
-      kr[s] = load16_stream(kb + off * E::kBytes);
-      vr[s] = load16_stream(vb + off * E::kBytes);
-    }
-    float sc[U][GT];
-#pragma unroll
-    for (int s = 0; s < U; ++s) {
-      float kf[VEC];
-      E::widen(kr[s], kf);
-#pragma unroll
-      for (int g = 0; g < GT; ++g) {
-        float dot = 0.0f;
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) dot = fmaf(qf[g][i], kf[i], dot);
-        sc[s][g] = dot;
-      }
-    }
-#pragma unroll
-    for (int off = 1; off < LPT; off <<= 1) {
-#pragma unroll
-      for (int s = 0; s < U; ++s)
-#pragma unroll
-        for (int g = 0; g < GT; ++g) sc[s][g] += __shfl_xor(sc[s][g], off);
-    }
-    float vf[U][VEC];
-#pragma unroll
-    for (int s = 0; s < U; ++s) E::widen(vr[s], vf[s]);
-#pragma unroll
-    for (int g = 0; g < GT; ++g) {
-      float mt = -INFINITY;
-#pragma unroll
-      for (int s = 0; s < U; ++s) {
-        if (p.alibi) sc[s][g] += slope2[g] * (float)(t0 + s * TPW + slot - last_row);
-        if (p.softcap2 > 0.0f) sc[s][g] = p.softcap2 * tanhf(sc[s][g] * p.softcap2_inv);
-        if (!valid[s]) sc[s][g] = -INFINITY;
-        mt = fmaxf(mt, sc[s][g]);
-      }
-      const float mn = fmaxf(m[g], mt);
-      const float ref = safe_ref(mn);
-      const float alpha = fast_exp2(m[g] - ref);
-      float pw[U];
-      float psum = 0.0f;
-#pragma unroll
-      for (int s = 0; s < U; ++s) {
-        pw[s] = fast_exp2(sc[s][g] - ref);
-        psum += pw[s];
-      }
-      l[g] = l[g] * alpha + psum;
-      m[g] = mn;
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) {
-        float a = acc[g][i] * alpha;
-#pragma unroll
-        for (int s = 0; s < U; ++s) a = fmaf(pw[s], vf[s][i], a);
-        acc[g][i] = a;
-      }
-    }
-  }
-
-  // merge the row slots of the wave (lanes LPT, 2 LPT, ... apart)
-#pragma unroll
-  for (int off = LPT; off < kWave; off <<= 1) {
-#pragma unroll
-    for (int g = 0; g < GT; ++g) {
-      const float mo = __shfl_xor(m[g], off);
-      const float lo = __shfl_xor(l[g], off);
-      const float mn = fmaxf(m[g], mo);
-      const float ref = safe_ref(mn);
-      const float a = fast_exp2(m[g] - ref);
-      const float bw = fast_exp2(mo - ref);
-      l[g] = l[g] * a + lo * bw;
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) acc[g][i] = acc[g][i] * a + __shfl_xor(acc[g][i], off) * bw;
-      m[g] = mn;
-    }
-  }
-  if (slot == 0) {
-#pragma unroll
-    for (int g = 0; g < GT; ++g) {
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) s_acc[wave][g][vi * VEC + i] = acc[g][i];
-      if (vi == 0) {
-        s_m[wave][g] = m[g];
-        s_l[wave][g] = l[g];
-      }
-    }
-  }
-  __syncthreads();
-  // merge the waves; one thread per (query head, feature)
-  for (int idx = tid; idx < GT * D; idx += NW * kWave) {
-    const int g = idx / D;
-    const int d = idx % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][g]);
-    const float ref = safe_ref(M);
-    float lsum = 0.0f, a = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float sw = fast_exp2(s_m[w][g] - ref);
-      lsum += s_l[w][g] * sw;
-      a += s_acc[w][g][d] * sw;
-    }
-    emit<E>(p, u, h0 + g, d, M, lsum, a);
-  }
-  __shared__ float s_stat[32];
-  __shared__ int s_last;
-  finish_split<E, 8>(p, u, blockIdx.y, h0, GT, NW, s_stat, &s_last, &s_acc[0][0][0],
-                  NW * GT * D);
 }
 
 // ---------------------------------------------------------- schedule hook

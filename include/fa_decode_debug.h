@@ -90,9 +90,10 @@ fa_status_t fa_debug_timing_read(double *main_kernel_ms, double *whole_call_ms, 
 
 /* The launch plan a decode call with these arguments would use (host-side
  * arithmetic only): KV rows per split unit, the bound on split units, query
- * heads per workgroup, and which attention kernel runs (0 = vector ALU,
- * 1 = matrix-core).  Returns FA_ERR_INVALID_PROBLEM for arguments the entry
- * points would reject on extents. */
+ * heads per workgroup, and which attention kernel runs (always 1, the
+ * matrix-core kernel, for every element type).  Returns
+ * FA_ERR_INVALID_PROBLEM for arguments the entry points would reject on
+ * extents. */
 fa_status_t fa_debug_plan(fa_dtype_t dtype, int batch, int num_qo_heads, int num_kv_heads,
                           int head_dim, int page_size, int total_used_pages, int *chunk_rows,
                           int *units_bound, int *heads_per_unit, int *kernel_kind);
