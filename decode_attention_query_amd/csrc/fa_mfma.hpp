@@ -1,15 +1,17 @@
-// fa_mfma.hpp -- matrix-core (MFMA) decode kernel for f16 / bf16 K/V on gfx950.
+// fa_mfma.hpp -- the matrix-core (MFMA) decode kernel for f32 / f16 / bf16 K/V
+// on gfx950.
 //
 // One workgroup = one split unit of one KV head and a block of up to 16 query
 // heads of its group (the whole group when G <= 16), so K and V are read from
 // HBM once for all those heads.  Four waves (two at D = 256); each wave
-// streams its own 32-row tiles of the unit and keeps its own online-softmax
-// state; the waves are merged through LDS at the end.
+// streams its own tiles of the unit (32 rows for 16-bit K/V, 16 for f32),
+// loads whole rows from HBM, stages K and V in its LDS area, and keeps its own
+// online-softmax state; the waves are merged through LDS at the end.
 //
-// Per 32-row tile, with n = lane % 16 and grp = lane / 16:
+// Per 32-row 16-bit tile, with n = lane % 16 and grp = lane / 16:
 //   scores   S^T[t][g] = sum_d K[t][d] Q[g][d]        v_mfma_f32_16x16x32 (bf16|f16)
-//            A = K rows (lane: row n of a 16-row block, 8 features at 32kk + 8grp,
-//            straight from a 16-byte global load), B = Q^T (lane: head n).
+//            A = K rows read back from LDS (lane: row n of a 16-row block, 8
+//            features at 32kk + 8grp), B = Q^T (lane: head n, in registers).
 //            Result: lane holds S for head g = n and rows 4grp + i (i < 4) of
 //            each of the two 16-row blocks.
 //   softmax  per head (column): the tile max over the 32 rows (in-lane max of
@@ -27,6 +29,12 @@
 // row(k = 8 grp + i) = 16 (i / 4) + 4 grp + (i % 4), which is where the score
 // MFMA left each lane's probabilities; any k order works as long as A and B
 // agree, which they do by construction.
+//
+// f32 tiles (16 rows) use v_mfma_f32_16x16x4_f32, one element per lane and
+// operand: the scores split D into four quarters, lane group grp taking
+// features grp D/4 .. + D/4 in successive products; P.V takes four rows per
+// product, lane group grp contributing row 4grp + i, so B is the lane's own
+// probability and A one f32 of V read from LDS.
 #pragma once
 
 #include "fa_common.hpp"
