@@ -23,7 +23,7 @@ using fa::DecodeParams;
 // Split sizing: aim for about this many decode workgroups per call, so the
 // 256 CUs each get several and the tail is short.
 constexpr int64_t kTargetWorkgroups = 1024;
-constexpr int64_t kChunkQuantum = 256;  // KV rows; a multiple of every kernel's tile
+constexpr int64_t kChunkQuantum = 128;  // KV rows; a multiple of every tile (32 rows)
 constexpr int64_t kMaxChunk = int64_t(1) << 30;
 constexpr size_t kAlign = 256;
 

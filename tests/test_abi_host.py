@@ -68,7 +68,7 @@ def test_plan_covers_units():
                                           (0, 1, 8, 2, 64, 256, 1),
                                           (2, 3, 12, 4, 64, 3, 7)]:
         chunk, bound, gt, kind = fad.fa_debug_plan(dtype, b, hq, hkv, d, p, used)
-        assert chunk > 0 and chunk % 256 == 0
+        assert chunk > 0 and chunk % 128 == 0
         assert (hq // hkv) % gt == 0 and gt in (1, 2, 4, 8, 16)
         # worst case: every row in one request, or spread so each request wastes a unit
         rows = used * p
