@@ -121,7 +121,7 @@ struct MfmaGeom {
   static constexpr int MB = D / 16;      // 16-feature blocks of O^T
   // Global loads: each instruction reads whole rows, 1 KiB contiguous per
   // wave (LPR lanes per row, RPI rows per instruction, NI instructions per
-  // 32-row tile of K, and as many of V).  An instruction shaped like the MFMA
+  // tile of K, and as many of V).  An instruction shaped like the MFMA
   // operand instead (16 rows x 64 bytes) streams ~13% slower from HBM.
   static constexpr int LPR = D * E::kBytes / 16;
   static constexpr int RPI = 64 / LPR;
