@@ -120,6 +120,11 @@ EDGE = [
     ("bf16", 64, 4, 4, 16, [0, 0, 0], ()),
     ("f32", 128, 3, 5, 8, [64, 129, 2], ()),
     ("f16", 256, 2, 8, 64, [4096, 64, 65], ()),
+    # groups wider than one 16-head block: a KV head's query heads span workgroups
+    ("bf16", 128, 1, 32, 16, [700, 1, 3000], ()),
+    ("f16", 64, 2, 24, 16, [0, 100, 2500], ()),
+    ("f32", 128, 1, 64, 32, [513, 40], ()),
+    ("f16", 256, 1, 17, 16, [300, 2], ()),
 ]
 
 
@@ -155,6 +160,8 @@ CONTIG_EDGE = [
     ("bf16", 128, 4, 2, 5000, 4999),
     ("f16", 64, 1, 1, 64, 63),
     ("f32", 128, 2, 3, 700, 513),
+    ("bf16", 128, 1, 32, 4096, 4000),
+    ("f32", 64, 1, 20, 300, 299),
 ]
 
 
