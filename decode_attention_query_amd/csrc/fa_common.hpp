@@ -83,6 +83,8 @@ struct DecodeParams {
   float *part_o;          // [units_bound, Hq, D]  normalised partial outputs
   uint64_t *arrivals;     // [B, Hq, kArrivalStride]  per (request, head block), first word:
                           // kArrivalMark << kCountBits | units done
+  uint64_t *tickets;      // one counter line, same format: work indices handed out
+  int ticket_from;        // workgroups from this launch index on draw their work index
 };
 
 // An arrival counter at rest holds kArrivalMark << kCountBits (count 0): the

@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <array>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <initializer_list>
@@ -45,7 +46,7 @@ struct HostPlan {
   int group = 0, gt = 0, n_gblocks = 0, planes = 0;
   int chunk = 0, units_bound = 0, kind = 0;
   // workspace byte offsets
-  size_t part_lse = 0, part_o = 0, arrivals = 0, total = 0;
+  size_t part_lse = 0, part_o = 0, arrivals = 0, tickets = 0, total = 0;
 };
 
 bool extents_ok(int batch, int hq, int hkv, int page_size) {
@@ -95,6 +96,9 @@ HostPlan make_plan(fa_dtype_t dt, int batch, int hq, int hkv, int d, int page_si
   // one counter line per (request, head block); Hq per request bounds the blocks
   hp.arrivals = off;
   off = align_up(off + sizeof(uint64_t) * fa::kArrivalStride * size_t(batch) * hq);
+  // and one line for the counter that hands out work items past the first round
+  hp.tickets = off;
+  off = align_up(off + sizeof(uint64_t) * fa::kArrivalStride);
   hp.total = off;
   return hp;
 }
@@ -109,6 +113,7 @@ void carve(DecodeParams &p, const HostPlan &hp, void *ws) {
   p.part_lse = reinterpret_cast<float *>(w + hp.part_lse);
   p.part_o = reinterpret_cast<float *>(w + hp.part_o);
   p.arrivals = reinterpret_cast<uint64_t *>(w + hp.arrivals);
+  p.tickets = reinterpret_cast<uint64_t *>(w + hp.tickets);
 }
 
 // ------------------------------------------------------------------ timing
@@ -162,10 +167,31 @@ struct CallEvents {
 
 // --------------------------------------------------------------- dispatch
 
+// Workgroups of the first resident round (two per compute unit) take their
+// work item from their launch index; the rest of a launch of n draw theirs
+// from a counter.  The compute-unit count is read once per device.
+int first_round(int64_t n) {
+  static std::atomic<int> cus_of[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return int(n);
+  int cus = cus_of[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      return int(n);
+    cus_of[dev].store(cus, std::memory_order_relaxed);
+  }
+  const int64_t r = 2 * int64_t(cus);
+  if (n <= r || n - r >= (int64_t(1) << fa::kCountBits)) return int(n);
+  return int(r);
+}
+
 template <class E, int D>
-hipError_t launch_mfma(const DecodeParams &p, const HostPlan &hp, hipStream_t s) {
+hipError_t launch_mfma(const DecodeParams &params, const HostPlan &hp, hipStream_t s) {
   dim3 grid(unsigned(hp.units_bound) * unsigned(hp.planes));
   dim3 block(fa::MfmaGeom<E, D>::NW * 64);
+  DecodeParams p = params;
+  p.ticket_from = first_round(int64_t(hp.units_bound) * hp.planes);
   const bool mods = p.window > 0 || p.softcap2 > 0.0f || p.alibi != nullptr || p.mask != nullptr;
   if (p.nhd) {
     if (mods)

@@ -451,7 +451,7 @@ __device__ void merge_partials(const DecodeParams &p, int b, int u0, int n, int 
 // mark (which ends the loop).  The merging workgroup puts the counter back to
 // rest, so the next call, or a replay of a captured graph, counts in with a
 // single add per unit; only a counter's first use pays for the swap.
-__device__ inline bool count_in_is_last(unsigned long long *counter, int n_units) {
+__device__ inline int count_in(unsigned long long *counter) {
   const unsigned long long tag = kArrivalMark;
   unsigned long long old = atomicAdd(counter, 1ull);
   if ((old >> kCountBits) != tag) {
@@ -464,7 +464,25 @@ __device__ inline bool count_in_is_last(unsigned long long *counter, int n_units
     }
     old = atomicAdd(counter, 1ull);
   }
-  return (old & ((1ull << kCountBits) - 1)) + 1 == (unsigned long long)n_units;
+  return int(old & ((1ull << kCountBits) - 1));
+}
+
+__device__ inline bool count_in_is_last(unsigned long long *counter, int n_units) {
+  return count_in(counter) + 1 == n_units;
+}
+
+// Work index of a workgroup that starts after the first resident round: the
+// next of n tickets, in the order workgroups reach the counter, so compute
+// units (and dies) that finish early take more of the remaining, shorter
+// units instead of each running a fixed share of the launch.  The counter
+// works like an arrival counter; the workgroup that draws the last ticket is
+// the last to touch it and puts it back to rest for the next call.
+__device__ inline int draw_ticket(unsigned long long *counter, int n) {
+  const int t = count_in(counter);
+  if (t == n - 1)
+    __hip_atomic_store(counter, kArrivalMark << kCountBits, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  return t;
 }
 
 template <class E, int kDepth>

@@ -226,11 +226,21 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   __shared__ float s_l[NW][16];
   __shared__ float s_stat[32];
   __shared__ int s_last;
+  __shared__ int s_work;
 
   // work item = unit * planes + head block: a unit's head blocks are adjacent,
-  // so the launch runs the (longest-first) unit order
-  const int unit = blockIdx.x / p.planes;
-  const int plane = blockIdx.x - unit * p.planes;
+  // and work items run in (longest-first) unit order.  The first resident
+  // round takes its item from its launch index; later workgroups draw theirs.
+  int w = blockIdx.x;
+  if (w >= p.ticket_from) {
+    if (threadIdx.x == 0)
+      s_work = p.ticket_from + draw_ticket(reinterpret_cast<unsigned long long *>(p.tickets),
+                                           (int)gridDim.x - p.ticket_from);
+    __syncthreads();
+    w = __builtin_amdgcn_readfirstlane(s_work);
+  }
+  const int unit = w / p.planes;
+  const int plane = w - unit * p.planes;
   UnitInfo u;
   if (!find_unit<kMods>(p, unit, u)) return;  // row0 (for a custom mask) in the kMods instance
   const int gt = p.heads_per_unit;  // valid columns of the 16-wide head block

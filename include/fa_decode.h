@@ -79,10 +79,11 @@ typedef enum {
  *   contiguous calls:  fa_decode_workspace_size(1, Hq, Hkv, D, max_kv_len, 1)
  * Returns 0 when the arguments are not a valid problem (the entry point then
  * reports why); otherwise a positive size.  The workspace holds the split
- * partial results and one arrival counter per (request, head block).  A
- * counter at rest carries a fixed mark and a count of zero, and each call
- * leaves its counters at rest; a counter without the mark is reset by the
- * first unit that meets it.  So the workspace needs no initialisation and may
+ * partial results, one arrival counter per (request, head block) and one
+ * counter that hands out work items to the workgroups of a launch that start
+ * after its first resident round.  A counter at rest carries a fixed mark and
+ * a count of zero, and each call leaves its counters at rest; a counter
+ * without the mark is reset by the first workgroup that meets it.  So the workspace needs no initialisation and may
  * hold anything between calls (a first use costs each counter one extra
  * compare-and-swap). */
 size_t fa_decode_workspace_size(int batch, int num_qo_heads, int num_kv_heads, int head_dim,

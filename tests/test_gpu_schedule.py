@@ -119,9 +119,19 @@ def _split_problem(dtype="bf16", seed=77):
                         pool_slack=0.1)
 
 
+def _launch_size(p):
+    _, bound, gt, _ = fad.fa_debug_plan(fad.DTYPE_CODES[p.dtype], p.batch, p.num_qo_heads,
+                                        p.num_kv_heads, p.head_dim, p.page_size,
+                                        p.total_used_pages)
+    return bound * p.num_kv_heads * ((p.num_qo_heads // p.num_kv_heads) // gt)
+
+
 def test_garbage_workspace(dev):
-    """The workspace needs no clearing: random bytes in it change nothing."""
+    """The workspace needs no clearing: random bytes in it change nothing,
+    neither in the arrival counters nor in the counter that hands out work
+    items past the first resident round (two workgroups per compute unit)."""
     p = _split_problem()
+    assert _launch_size(p) > 2 * torch.cuda.get_device_properties(dev).multi_processor_count
     d = to_dev(p, dev)
     ref_o, ref_l = run(p, d)
     ws = fad.workspace_paged(p.batch, p.num_qo_heads, p.num_kv_heads, p.head_dim,
