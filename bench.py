@@ -215,6 +215,42 @@ def time_append(p, d, dev, steps, warmup):
             "algorithmic_bytes_per_call": nbytes}
 
 
+def time_merge(p, dev, parts, steps, warmup):
+    """The standalone merge of `parts` split partials per output row of the
+    workload (rows = B * Hq, f32 partials, o in the workload's element type):
+    µs per call back to back and captured 16 calls to a graph, and GB/s over
+    its algorithmic bytes (partials and their lse read once, o and lse
+    written)."""
+    es = W.ELEM_BYTES[p.dtype]
+    batch = 1 if isinstance(p, W.ContigProblem) else p.batch
+    rows, d = batch * p.num_qo_heads, p.head_dim
+    g = torch.Generator(device="cpu").manual_seed(9)
+    o_parts = torch.randn((parts, rows, d), generator=g).to(dev)
+    lse_parts = (torch.randn((parts, rows), generator=g) * 3.0).to(dev)
+    o = torch.empty((rows, d), dtype=W.TORCH_DTYPES[p.dtype], device=dev)
+    lse = torch.empty((rows,), dtype=torch.float32, device=dev)
+
+    def call():
+        fad.fa_merge_states(fad.DTYPE_CODES[p.dtype], rows, parts, d, o_parts, lse_parts, o, lse)
+
+    for _ in range(warmup):
+        call()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(steps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / steps
+    us_graph = graph_call_time(call, 16, max(1, steps // 16) + 4)
+    nbytes = parts * rows * (d + 1) * 4 + rows * (d * es + 4)
+    return {"parts": parts, "rows": rows, "us_per_call": round(us, 2),
+            "graph_us_per_call": round(us_graph, 2),
+            "GBps_graph": round(nbytes / (us_graph * 1e-6) / 1e9, 2),
+            "algorithmic_bytes_per_call": nbytes}
+
+
 def graph_call_time(step, n_calls, reps):
     """Mean µs per call when n_calls calls are captured in one HIP graph and
     the graph is replayed reps times (what a serving loop that captures its
@@ -255,6 +291,9 @@ def main():
                          "overhead between calls)")
     ap.add_argument("--append", action="store_true",
                     help="also time the decode-time KV append (paged workloads)")
+    ap.add_argument("--merge-parts", type=int, default=0,
+                    help="also time the standalone merge of this many split partials per "
+                         "output row of the workload (0: off)")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window: attend only each request's last W rows (0: all)")
     ap.add_argument("--softcap", type=float, default=0.0,
@@ -399,6 +438,8 @@ def main():
     if args.append and not isinstance(p, W.ContigProblem):
         line["append"] = time_append(p, {"k": k, "v": v, "ind": ind, "ptr": ptr, "lpl": lpl},
                                      dev, args.steps, args.warmup)
+    if args.merge_parts > 0:
+        line["merge"] = time_merge(p, dev, args.merge_parts, args.steps, args.warmup)
     if args.graph_calls > 0:
         us = graph_call_time(step, args.graph_calls, max(1, args.steps // args.graph_calls) + 4)
         line["graph_per_call"] = {"calls_per_graph": args.graph_calls, "us_per_call": round(us, 2),

@@ -3,8 +3,9 @@
 The computation runs in libfadecode.so (hand-written HIP kernels for gfx950);
 this package is its binding.  The C entry points are available under their
 own names (fa_decode_contig, fa_decode_paged, fa_decode_workspace_size, and
-the fa_debug_* hooks); decode_contig and decode_paged below are conveniences
-that read the dimensions off the tensors and allocate outputs and workspace.
+the fa_debug_* hooks); decode_contig, decode_paged, merge_states and
+append_paged below are conveniences that read the dimensions off the tensors
+and allocate outputs and workspace.
 """
 import torch
 
@@ -15,7 +16,8 @@ from ._binding import (CODE_TORCH_DTYPES, DTYPE_CODES, EXPORTED, FA_DTYPE_BF16, 
                        fa_debug_read_probe, fa_debug_schedule, fa_debug_timing_enable,
                        fa_debug_timing_read, fa_decode_contig, fa_decode_contig_nhd,
                        fa_decode_paged, fa_decode_paged_nhd, fa_decode_workspace_size,
-                       fa_append_paged, fa_append_paged_nhd, fa_status_string, load_library,
+                       fa_append_paged, fa_append_paged_nhd, fa_merge_states, fa_status_string,
+                       load_library,
                        DecodeOptions, fa_decode_paged_opts, fa_decode_contig_opts)
 
 
@@ -132,3 +134,20 @@ def append_paged(k_new, v_new, k_data, v_data, indices, indptr, last_page_len, s
     fn = fa_append_paged_nhd if layout == "nhd" else fa_append_paged
     fn(_code(k_new), batch, hkv, d, page_size, pages, used, k_new, v_new,
        indices if used else None, indptr, last_page_len, k_data, v_data, stream)
+
+
+def merge_states(o_parts, lse_parts, out_dtype=torch.float32, o=None, lse=None, stream=None):
+    """Combines split partials: o_parts [S, ..., D] f32 and lse_parts [S, ...] f32
+    (natural log; -inf marks an empty part) -> o [..., D] in out_dtype and
+    lse [...] f32, the result over the union of the parts' rows."""
+    if o_parts.dim() < 2 or tuple(lse_parts.shape) != tuple(o_parts.shape[:-1]):
+        raise ValueError("o_parts must be [S, ..., D] and lse_parts [S, ...]")
+    s, d = o_parts.shape[0], o_parts.shape[-1]
+    rows = lse_parts[0].numel()
+    if o is None:
+        o = torch.empty(tuple(o_parts.shape[1:]), dtype=out_dtype, device=o_parts.device)
+    if lse is None:
+        lse = torch.empty(tuple(lse_parts.shape[1:]), dtype=torch.float32,
+                          device=o_parts.device)
+    fa_merge_states(_code(o), rows, s, d, o_parts, lse_parts, o, lse, stream)
+    return o, lse

@@ -30,7 +30,7 @@ STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_INVALID_PROBLEM", 2: "FA_ERR_UNSUPPORTED"
 EXPORTED = ("fa_decode_workspace_size", "fa_decode_contig", "fa_decode_paged",
             "fa_decode_contig_nhd", "fa_decode_paged_nhd", "fa_append_paged",
             "fa_append_paged_nhd", "fa_decode_paged_opts", "fa_decode_contig_opts",
-            "fa_status_string",
+            "fa_merge_states", "fa_status_string",
             "fa_debug_gather_paged", "fa_debug_gather_paged_nhd", "fa_debug_timing_enable",
             "fa_debug_timing_read", "fa_debug_plan", "fa_debug_schedule",
             "fa_debug_read_probe")
@@ -93,6 +93,8 @@ def load_library():
         getattr(lib, name).argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I64,
                                        _P, _SZ, _P]
         getattr(lib, name).restype = _I
+    lib.fa_merge_states.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P]
+    lib.fa_merge_states.restype = _I
     lib.fa_debug_timing_enable.argtypes = [_I]
     lib.fa_debug_timing_enable.restype = _I
     lib.fa_debug_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double),
@@ -373,6 +375,28 @@ def fa_append_paged_nhd(dtype, batch, num_kv_heads, head_dim, page_size, num_tot
     _append("fa_append_paged_nhd", dtype, batch, num_kv_heads, head_dim, page_size,
             num_total_pages, total_used_pages, k_new, v_new, indices, indptr, last_page_len,
             k_data, v_data, stream)
+
+
+def fa_merge_states(dtype, num_rows, num_parts, head_dim, o_parts, lse_parts, o, lse=None,
+                    stream=None):
+    """o_parts [num_parts, num_rows, D] f32, lse_parts [num_parts, num_rows] f32 ->
+    o [num_rows, D] in dtype, lse [num_rows] f32 (None: not written)."""
+    lib = load_library()
+    tdt = CODE_TORCH_DTYPES.get(dtype)
+    if tdt is None or num_rows <= 0 or num_parts <= 0:
+        # the library reports the problem with the arguments (or, for no rows,
+        # accepts the call without looking at the buffers)
+        _check("fa_merge_states", lib.fa_merge_states(dtype, num_rows, num_parts, head_dim,
+                                                      None, None, None, None, _stream(stream)))
+        return
+    args = (
+        _dev_buf(o_parts, "o_parts", num_parts * num_rows * head_dim, torch.float32),
+        _dev_buf(lse_parts, "lse_parts", num_parts * num_rows, torch.float32),
+        _dev_buf(o, "o", num_rows * head_dim, tdt),
+        _dev_buf(lse, "lse", num_rows, torch.float32, allow_none=True),
+    )
+    _check("fa_merge_states", lib.fa_merge_states(dtype, num_rows, num_parts, head_dim, *args,
+                                                  _stream(stream)))
 
 
 def fa_status_string(status):

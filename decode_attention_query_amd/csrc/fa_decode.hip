@@ -482,6 +482,44 @@ fa_status_t gather_paged(int nhd, fa_dtype_t dtype, int batch, int num_kv_heads,
   return FA_OK;
 }
 
+template <class E>
+hipError_t launch_merge_states(const float *o_parts, const float *lse_parts, void *o,
+                               float *lse, int rows, int n_parts, int d, hipStream_t s) {
+  const int64_t threads = int64_t(rows) * (d / 4);
+  hipLaunchKernelGGL(fa::merge_states_kernel<E>, dim3(unsigned((threads + 255) / 256)),
+                     dim3(256), 0, s, o_parts, lse_parts,
+                     static_cast<typename E::raw *>(o), lse, rows, n_parts, d);
+  return hipGetLastError();
+}
+
+fa_status_t merge_states(fa_dtype_t dtype, int num_rows, int num_parts, int head_dim,
+                         const float *o_parts, const float *lse_parts, void *o, float *lse,
+                         hipStream_t stream) {
+  if (!dtype_ok(dtype)) return FA_ERR_UNSUPPORTED;
+  if (num_rows < 0 || num_parts <= 0) return FA_ERR_INVALID_PROBLEM;
+  if (!head_dim_ok(head_dim)) return FA_ERR_UNSUPPORTED;
+  if (num_rows == 0) return FA_OK;
+  if (!o_parts || !lse_parts || !o) return FA_ERR_INVALID_PROBLEM;
+  if (!all_aligned({o_parts, o}, {lse_parts, lse})) return FA_ERR_INVALID_PROBLEM;
+  if (double(num_parts) * num_rows * head_dim >= 1.0e15) return FA_ERR_UNSUPPORTED;
+  hipError_t e;
+  switch (dtype) {
+    case FA_DTYPE_F32:
+      e = launch_merge_states<fa::F32>(o_parts, lse_parts, o, lse, num_rows, num_parts,
+                                       head_dim, stream);
+      break;
+    case FA_DTYPE_F16:
+      e = launch_merge_states<fa::F16>(o_parts, lse_parts, o, lse, num_rows, num_parts,
+                                       head_dim, stream);
+      break;
+    default:
+      e = launch_merge_states<fa::BF16>(o_parts, lse_parts, o, lse, num_rows, num_parts,
+                                        head_dim, stream);
+      break;
+  }
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -585,6 +623,12 @@ fa_status_t fa_decode_paged_opts(const fa_decode_options_t *opts, fa_dtype_t dty
   return decode_paged(var, dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
                       num_total_pages, total_used_pages, sm_scale, q, k_data, v_data, indices,
                       indptr, last_page_len, o, lse, workspace, workspace_bytes, stream);
+}
+
+fa_status_t fa_merge_states(fa_dtype_t dtype, int num_rows, int num_parts, int head_dim,
+                            const float *o_parts, const float *lse_parts, void *o, float *lse,
+                            hipStream_t stream) {
+  return merge_states(dtype, num_rows, num_parts, head_dim, o_parts, lse_parts, o, lse, stream);
 }
 
 const char *fa_status_string(fa_status_t status) {

@@ -502,6 +502,71 @@ __device__ void finish_split(const DecodeParams &p, const UnitInfo &u, int plane
   merge_partials<E, kDepth>(p, u.b, u.u0, u.n_units, h0, gt, nw, s_stat, s_w, w_cap);
 }
 
+// ------------------------------------------------------- standalone merge
+//
+// The combine step of split-KV decode as a kernel of its own, for partial
+// results made outside one decode call: the shares of one request's rows
+// decoded on different devices (context-parallel decode, after the partials
+// have been gathered), or a caller's own split.  For each output row, S
+// partials, each o_s normalised over its rows and lse_s its natural-log
+// log-sum-exp:
+//   M = max_s lse_s,  W = sum_s exp(lse_s - M),
+//   o = sum_s exp(lse_s - M) o_s / W,  lse = M + ln W,
+// with s running 0 .. S-1 in order in every thread, so the result is
+// reproducible bit for bit.  A partial with lse_s = -inf covers no rows: its
+// weight is 0 and its o_s (whatever it holds) does not reach the result.  A
+// row whose partials are all empty gets o = 0 and lse = -inf.
+//
+// Layout: o_parts [S, rows, D] f32, lse_parts [S, rows] f32, o [rows, D] T,
+// lse [rows] f32.  One thread per 4-feature column of a row (D / 4 threads per
+// row, a row's threads adjacent), so every partial byte is read once, 16 bytes
+// per load; the S lse values of a row are read by all its threads from the
+// same addresses (one request per wave and address).  kDepth partials are
+// loaded before any is used, so that many loads are in flight per thread.
+template <class E>
+__global__ __launch_bounds__(256) void merge_states_kernel(const float *o_parts,
+                                                           const float *lse_parts,
+                                                           typename E::raw *o, float *lse,
+                                                           int rows, int n_parts, int d) {
+  constexpr int kDepth = 8;
+  const int q4 = d / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = idx / q4;
+  if (row >= rows) return;
+  const int col = 4 * (int)(idx - row * q4);
+  const int64_t lstride = rows;                    // between the lse of two partials
+  const int64_t ostride = (int64_t)rows * d;       // between two partial outputs
+  const float *lrow = lse_parts + row;
+  const float *orow = o_parts + row * d + col;
+  float mx = -INFINITY;
+  for (int s = 0; s < n_parts; ++s) mx = fmaxf(mx, lrow[s * lstride]);
+  const float ref = safe_ref(mx);
+  float W = 0.0f;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s0 = 0; s0 < n_parts; s0 += kDepth) {
+    f32x4 x[kDepth];
+    float w[kDepth];
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) {
+      const int s = min(s0 + k, n_parts - 1);
+      x[k] = *reinterpret_cast<const f32x4 *>(orow + s * ostride);
+      w[k] = s0 + k < n_parts ? fast_exp2((lrow[s * lstride] - ref) * kLog2e) : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) {
+      W += w[k];
+      if (w[k] > 0.0f) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = fmaf(w[k], x[k][e], acc[e]);
+      }
+    }
+  }
+  const bool any = W > 0.0f;
+  const f32x4 o4 = any ? acc / W : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  store4<E>(o + row * d + col, o4);
+  if (col == 0 && lse) lse[row] = any ? mx + fast_log2(W) * kLn2 : -INFINITY;
+}
+
 // ---------------------------------------------------------- schedule hook
 //
 // Test-only: the unit each work index runs, from find_unit, 8 int32 per index:

@@ -311,6 +311,46 @@ fa_status_t fa_append_paged_nhd(fa_dtype_t dtype, int batch, int num_kv_heads, i
                                 const int32_t *indptr, const int32_t *last_page_len,
                                 void *k_data, void *v_data, hipStream_t stream);
 
+/* Merge of split partial results: the combine step of split-KV decode as a
+ * call of its own, for partials made outside one decode call -- the shares of
+ * a request's K/V rows decoded on different devices and gathered onto one, or
+ * a caller's own split of the rows.  It follows from the per-row log-sum-exp
+ * the decode calls return (baracuda-kernels page, module doc "Query /
+ * output"): with the rows of a query split into S disjoint parts, part s
+ * giving o_s (normalised over its rows) and lse_s,
+ *
+ *     lse = ln sum_s exp(lse_s),   o = sum_s exp(lse_s - lse) * o_s,
+ *
+ * which is exactly the result over all the rows.  fa_decode_paged and
+ * fa_decode_contig make the same combination inside one call when they split
+ * a long request.
+ *
+ *   o_parts    [num_parts, num_rows, head_dim] f32   partial outputs, each
+ *              normalised over its part (f32: the element type of partials)
+ *   lse_parts  [num_parts, num_rows]           f32   natural-log LSE of each
+ *              part; -inf marks an empty part, whose o_parts row may hold
+ *              anything (it does not reach the result)
+ *   o          [num_rows, head_dim]            T     output, rounded once to T
+ *   lse        [num_rows]                      f32   output; may be NULL
+ * A row is any flattening of the caller's (request, query head) pairs.  A row
+ * whose parts are all empty gets o = 0 and lse = -inf.  The parts of a row
+ * are combined in index order, so results are bit-identical from run to run.
+ * Inputs must not overlap the outputs.  No workspace.  Asynchronous on stream.
+ *
+ * Checks, in order:
+ *   dtype not one of fa_dtype_t                               -> FA_ERR_UNSUPPORTED
+ *   num_rows < 0 or num_parts <= 0                            -> FA_ERR_INVALID_PROBLEM
+ *   head_dim not 64, 128 or 256                               -> FA_ERR_UNSUPPORTED
+ *   num_rows == 0                                             -> FA_OK, nothing enqueued
+ *   o_parts, lse_parts or o NULL                              -> FA_ERR_INVALID_PROBLEM
+ *   o_parts or o not 16-byte aligned, or lse_parts or lse
+ *     not 4-byte aligned                                      -> FA_ERR_INVALID_PROBLEM
+ *   num_parts * num_rows * head_dim >= 10^15                  -> FA_ERR_UNSUPPORTED
+ *   a kernel launch fails                                     -> FA_ERR_LAUNCH */
+fa_status_t fa_merge_states(fa_dtype_t dtype, int num_rows, int num_parts, int head_dim,
+                            const float *o_parts, const float *lse_parts, void *o, float *lse,
+                            hipStream_t stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *fa_status_string(fa_status_t status);
 

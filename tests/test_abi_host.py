@@ -268,3 +268,28 @@ def test_timing_hooks_without_calls():
     main_ms, call_ms, n = fad.fa_debug_timing_read()
     fad.fa_debug_timing_enable(0)
     assert (main_ms, call_ms, n) == (0.0, 0.0, 0)
+
+
+def test_merge_rejects():
+    merge = fad.load_library().fa_merge_states
+    ptrs = [FAKE] * 4
+    assert merge(3, 16, 2, 128, *ptrs, None) == UNS
+    assert merge(0, -1, 2, 128, *ptrs, None) == INV
+    assert merge(0, 16, 0, 128, *ptrs, None) == INV
+    assert merge(0, 16, 2, 96, *ptrs, None) == UNS
+    # no rows: accepted before the buffers are looked at, nothing enqueued
+    assert merge(0, 0, 2, 128, None, None, None, None, None) == fad.FA_OK
+    for i in range(3):
+        bad = list(ptrs)
+        bad[i] = None
+        assert merge(0, 16, 2, 128, *bad, None) == INV, i
+    # o_parts and o 16-byte, lse_parts and lse 4-byte
+    for i, mis in enumerate((MIS8, MIS2, MIS8, MIS2)):
+        bad = list(ptrs)
+        bad[i] = mis
+        assert merge(0, 16, 2, 128, *bad, None) == INV, i
+    assert merge(0, 1 << 30, 1 << 14, 256, *ptrs, None) == UNS
+    # order: dtype, then extents, then head_dim, then pointers
+    assert merge(9, -1, 0, 96, None, None, None, None, None) == UNS
+    assert merge(1, -1, 2, 96, None, None, None, None, None) == INV
+    assert merge(1, 16, 2, 96, None, None, None, None, None) == UNS
