@@ -284,6 +284,9 @@ def main():
     ap.add_argument("--workload", default="c3", choices=sorted(W.FULL))
     ap.add_argument("--dtype", default=None, choices=["f32", "f16", "bf16"],
                     help="store the workload's shapes in this element type instead of its own")
+    ap.add_argument("--qo-heads", type=int, default=None,
+                    help="paged workloads: this many query heads over the same KV heads and "
+                         "K/V (another GQA group size)")
     ap.add_argument("--layout", default="hnd", choices=["hnd", "nhd"],
                     help="K/V storage: heads-major (default) or token-major")
     ap.add_argument("--graph-calls", type=int, default=0,
@@ -323,7 +326,12 @@ def main():
     dev = torch.device("cuda:0")
 
     t0 = time.perf_counter()
-    p = W.FULL[args.workload](dtype=args.dtype)
+    if args.qo_heads is not None:
+        if args.workload not in ("c3", "c4", "c5"):
+            sys.exit("--qo-heads applies to the paged workloads c3, c4 and c5")
+        p = W.FULL[args.workload](dtype=args.dtype, qo_heads=args.qo_heads)
+    else:
+        p = W.FULL[args.workload](dtype=args.dtype)
     if args.layout == "nhd":
         p = W.token_major(p)
     print(f"[bench] generated {p.name} in {time.perf_counter() - t0:.1f}s", file=sys.stderr,

@@ -339,3 +339,23 @@ def test_binding_checks_shapes(dev):
                             p.head_dim, p.page_size, p.num_total_pages, p.total_used_pages,
                             p.scale, d["q"], d["k"], d["v"], d["indices"], d["indptr"], d["lpl"],
                             o, lse, ws[:16])
+
+
+@pytest.mark.parametrize("name,qo_heads", [("c3", 8), ("c3", 16), ("c3", 128), ("c5", 4)])
+def test_full_shapes_other_group(dev, name, qo_heads):
+    """Full-size K/V and page tables with another number of query heads per KV
+    head (G = 1, 2 and 16 on C3's store, G = 1 on C5's), as bench.py
+    --qo-heads times them: sampled pairs against the oracle."""
+    p = W.FULL[name](qo_heads=qo_heads)
+    announce(f"full {name} with {qo_heads} query heads: {p.name}")
+    d = to_dev(p, dev)
+    o, lse = run(p, d)
+    torch.cuda.synchronize()
+    pairs = sample_pairs(p, 64, np.random.default_rng(7))
+    ro, rl = oracle_of(p, samples=pairs)
+    idx = torch.from_numpy(pairs[:, 0].astype(np.int64)), \
+        torch.from_numpy(pairs[:, 1].astype(np.int64))
+    compare(p.dtype, o.cpu()[idx[0], idx[1]], lse.cpu()[idx[0], idx[1]], ro, rl, p.name,
+            strict=True)
+    del d, o, lse
+    torch.cuda.empty_cache()

@@ -303,25 +303,34 @@ def c2(seed=1002, dtype=None):
     return make_contig(name, dt, 32, 8, 128, 8192, 4096, seed, kv_std=0.5)
 
 
-def c3(seed=1003, dtype=None):
+def _heads(name, own, qo_heads):
+    """qo_heads, if given, replaces the number of query heads (the KV heads and
+    every draw of K, V and the page table stay; q is drawn at the new shape)."""
+    return (name, own) if qo_heads in (None, own) else (f"{name}_hq{qo_heads}", qo_heads)
+
+
+def c3(seed=1003, dtype=None, qo_heads=None):
     name, dt = _named("c3_paged_bf16", "bf16", dtype)
-    return make_paged(name, dt, 64, 32, 8, 128, 16, seed,
+    name, hq = _heads(name, 32, qo_heads)
+    return make_paged(name, dt, 64, hq, 8, 128, 16, seed,
                       lens_fn=lambda r: r.integers(512, 8192, size=64, endpoint=True),
                       pool_pages=40000)
 
 
-def c4(seed=1004, dtype=None):
+def c4(seed=1004, dtype=None, qo_heads=None):
     name, dt = _named("c4_paged_bf16_g8", "bf16", dtype)
-    return make_paged(name, dt, 32, 64, 8, 128, 32, seed,
+    name, hq = _heads(name, 64, qo_heads)
+    return make_paged(name, dt, 32, hq, 8, 128, 32, seed,
                       lens=np.full(32, 32768), pool_pages=32768)
 
 
-def c5(seed=1005, dtype=None):
+def c5(seed=1005, dtype=None, qo_heads=None):
     name, dt = _named("c5_paged_f16_skew", "f16", dtype)
+    name, hq = _heads(name, 16, qo_heads)
     ss = np.random.SeedSequence(seed)
     lens = _c5_lens(np.random.default_rng(ss.spawn(1)[0]), 128, 7.0, 1.5, 131072)
     n_pages, lpl = _c5_tables(lens, 16)
-    return make_paged(name, dt, 128, 16, 4, 256, 16, seed,
+    return make_paged(name, dt, 128, hq, 4, 256, 16, seed,
                       n_pages=n_pages, last_page_len=lpl, pool_slack=0.25)
 
 
