@@ -102,6 +102,10 @@ constexpr unsigned long long kArrivalMark = 0x7FF3A5C35Aull;  // 40 bits
 // queued behind each other (a 16-unit request on 8 head blocks: 128 atomics).
 constexpr int kArrivalStride = 16;
 
+// Query heads a decode workgroup serves at most (two 16-column head blocks):
+// the split merge keeps a maximum and a normaliser per head in LDS.
+constexpr int kStatHeads = 32;
+
 // ---------------------------------------------------------------- elements
 //
 // Each element type knows how to widen a 16-byte vector to f32 and how to

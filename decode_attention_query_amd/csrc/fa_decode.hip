@@ -43,7 +43,7 @@ int heads_per_unit(int group, int max_heads) {
 constexpr int kKernelMfma = 1;
 
 struct HostPlan {
-  int group = 0, gt = 0, n_gblocks = 0, planes = 0;
+  int group = 0, gt = 0, nb = 1, n_gblocks = 0, planes = 0;
   int chunk = 0, units_bound = 0, kind = 0;
   // workspace byte offsets
   size_t part_lse = 0, part_o = 0, arrivals = 0, tickets = 0, total = 0;
@@ -59,14 +59,18 @@ bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
 bool grid_ok(int hq, int hkv) { return hq / hkv > 0 && hkv * (hq / hkv) <= 65535; }
 
 // The plan for a call; `page_size` is max_kv_len and total_used_pages 1 for a
-// contiguous cache.  Pure host arithmetic.
+// contiguous cache.  Pure host arithmetic.  `shared_ok`: the call may use the
+// two-block workgroups (plain calls: no window, cap, ALiBi or mask).
 HostPlan make_plan(fa_dtype_t dt, int batch, int hq, int hkv, int d, int page_size,
-                   int total_used_pages, bool contig) {
+                   int total_used_pages, bool contig, bool shared_ok = true) {
   HostPlan hp;
   hp.kind = kKernelMfma;
   hp.group = hq / hkv;
   hp.gt = heads_per_unit(hp.group, 16);
-  hp.n_gblocks = hp.group / hp.gt;
+  // a group of an even number of head blocks: two blocks per workgroup, so
+  // K/V are read once per 2 * gt query heads
+  hp.nb = shared_ok && (hp.group / hp.gt) % 2 == 0 ? 2 : 1;
+  hp.n_gblocks = hp.group / (hp.gt * hp.nb);
   hp.planes = hkv * hp.n_gblocks;
   // The split size depends on the KV heads only (not on the kernel's head
   // blocking), so the workspace size is the same for every element type.
@@ -193,16 +197,21 @@ hipError_t launch_mfma(const DecodeParams &params, const HostPlan &hp, hipStream
   DecodeParams p = params;
   p.ticket_from = first_round(int64_t(hp.units_bound) * hp.planes);
   const bool mods = p.window > 0 || p.softcap2 > 0.0f || p.alibi != nullptr || p.mask != nullptr;
+  if (mods && hp.nb != 1) return hipErrorInvalidValue;  // the plan assumed a plain call
   if (p.nhd) {
     if (mods)
-      hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, true, true>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, true, true, 1>), grid, block, 0, s, p);
+    else if (hp.nb == 2)
+      hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, true, false, 2>), grid, block, 0, s, p);
     else
-      hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, true, false>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, true, false, 1>), grid, block, 0, s, p);
   } else {
     if (mods)
-      hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, false, true>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, false, true, 1>), grid, block, 0, s, p);
+    else if (hp.nb == 2)
+      hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, false, false, 2>), grid, block, 0, s, p);
     else
-      hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, false, false>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, false, false, 1>), grid, block, 0, s, p);
   }
   return hipGetLastError();
 }
@@ -302,6 +311,12 @@ fa_status_t read_options(const fa_decode_options_t *opts, Variant &v) {
   return FA_OK;
 }
 
+// A window, cap, ALiBi or mask is in use: the kernel instance with their
+// per-score work (and one head block per workgroup) runs.
+bool has_variant(const Variant &v) {
+  return v.window > 0 || v.softcap > 0.0f || v.alibi != nullptr || v.mask != nullptr;
+}
+
 void apply_variant(DecodeParams &p, const Variant &v) {
   p.nhd = v.nhd;
   p.window = v.window;
@@ -334,7 +349,7 @@ fa_status_t decode_contig(const Variant &var, fa_dtype_t dtype, int num_qo_heads
   // Sized like the workspace query (a single page of max_kv_len rows) so the
   // split units fit what the caller allocated.
   const HostPlan hp = make_plan(dtype, 1, num_qo_heads, num_kv_heads, head_dim, max_kv_len, 1,
-                                /*contig=*/true);
+                                /*contig=*/true, !has_variant(var));
   DecodeParams p = base_params(1, num_qo_heads, num_kv_heads, head_dim, max_kv_len, 1, 1,
                                scale, hp);
   p.q = q;
@@ -383,7 +398,7 @@ fa_status_t decode_paged(const Variant &var, fa_dtype_t dtype, int batch, int nu
   if (!pool_size_ok(num_total_pages, num_kv_heads, page_size, head_dim))
     return FA_ERR_UNSUPPORTED;
   const HostPlan hp = make_plan(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
-                                total_used_pages, false);
+                                total_used_pages, false, !has_variant(var));
   if (!launch_ok(hp)) return FA_ERR_UNSUPPORTED;
   const size_t need = fa_decode_workspace_size(batch, num_qo_heads, num_kv_heads, head_dim,
                                                page_size, total_used_pages);
@@ -740,7 +755,7 @@ fa_status_t fa_debug_plan(fa_dtype_t dtype, int batch, int num_qo_heads, int num
                                 total_used_pages, false);
   if (chunk_rows) *chunk_rows = hp.chunk;
   if (units_bound) *units_bound = hp.units_bound;
-  if (heads_per_unit_out) *heads_per_unit_out = hp.gt;
+  if (heads_per_unit_out) *heads_per_unit_out = hp.gt * hp.nb;
   if (kernel_kind) *kernel_kind = hp.kind;
   return FA_OK;
 }

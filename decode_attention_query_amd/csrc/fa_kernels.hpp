@@ -315,7 +315,8 @@ __device__ inline void store4(typename E::raw *out, const f32x4 &v) {
 
 template <class E, int kDepth>
 __device__ void merge_partials(const DecodeParams &p, int b, int u0, int n, int h0, int gt, int nw,
-                               float *s_stat /* LDS [32] */, float *s_w, int w_cap) {
+                               float *s_stat /* LDS [2 kStatHeads] */, float *s_w,
+                               int w_cap) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -342,7 +343,7 @@ __device__ void merge_partials(const DecodeParams &p, int b, int u0, int n, int 
           if (lane < n) s_w[lane * gt + g] = e;
           if (lane == 0) {
             s_stat[g] = mx;
-            s_stat[16 + g] = w;
+            s_stat[kStatHeads + g] = w;
           }
         }
       }
@@ -361,7 +362,7 @@ __device__ void merge_partials(const DecodeParams &p, int b, int u0, int n, int 
       w = wave_sum(w);
       if (lane == 0) {
         s_stat[g] = mx;
-        s_stat[16 + g] = w;
+        s_stat[kStatHeads + g] = w;
       }
     }
   }
@@ -418,7 +419,7 @@ __device__ void merge_partials(const DecodeParams &p, int b, int u0, int n, int 
     }
     if (c0 + tid < cols) {
       const float mx = s_stat[g];
-      const float W = s_stat[16 + g];
+      const float W = s_stat[kStatHeads + g];
       const bool any = W > 0.0f;
       const int64_t orow = (int64_t)b * hq + h0 + g;
       const int d = 4 * (c - g * q4);

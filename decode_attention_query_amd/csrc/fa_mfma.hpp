@@ -6,7 +6,10 @@
 // HBM once for all those heads.  Four waves (two at D = 256); each wave
 // streams its own tiles of the unit (32 rows for 16-bit K/V, 16 for f32),
 // loads whole rows from HBM, stages K and V in its LDS area, and keeps its own
-// online-softmax state; the waves are merged through LDS at the end.
+// online-softmax state; the waves are merged through LDS at the end.  A group
+// of an even number of 16-head blocks (plain calls) takes two blocks per
+// workgroup: the waves share each step's tiles through LDS, half of them
+// computing for each block (NB = 2 below).
 //
 // Per 32-row 16-bit tile, with n = lane % 16 and grp = lane / 16:
 //   scores   S^T[t][g] = sum_d K[t][d] Q[g][d]        v_mfma_f32_16x16x32 (bf16|f16)
@@ -212,7 +215,16 @@ __device__ inline void issue_tile(KVTile<MfmaGeom<E, D>::NI> &T, const DecodePar
 
 // kMods: a sliding window, soft-cap or ALiBi is in use (the plain instance
 // carries none of their per-score work).
-template <class E, int D, bool kNhd, bool kMods>
+//
+// NB: 16-column head blocks per workgroup.  NB = 1: every wave serves the
+// workgroup's one block and streams its own tiles.  NB = 2 (plain calls whose
+// query group splits into an even number of blocks, e.g. G = 32): the waves
+// still load one tile each per step into their LDS areas, and after a
+// workgroup barrier the first NW / 2 waves compute every tile of the step for
+// block 0 and the others for block 1, each wave for its own 16 heads -- so
+// K and V leave HBM once for 32 query heads, with the per-wave registers of
+// the one-block kernel.
+template <class E, int D, bool kNhd, bool kMods, int NB>
 __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1))) void decode_mfma_kernel(
     const DecodeParams p) {
   using G = MfmaGeom<E, D>;
@@ -220,11 +232,13 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   using v8 = typename M::v8;
   constexpr int KK = G::KK, MB = G::MB, NW = G::NW, TT = G::TT, JB = G::JB, QC = G::QC;
   constexpr bool kF32 = G::kF32;
+  static_assert(NB == 1 || (NB == 2 && NW % 2 == 0 && !kMods), "head blocks per workgroup");
+  constexpr int WPB = NW / NB;  // waves per head block
 
   __shared__ __attribute__((aligned(16))) char lds[G::LDS];
   __shared__ float s_m[NW][16];
   __shared__ float s_l[NW][16];
-  __shared__ float s_stat[32];
+  __shared__ float s_stat[2 * kStatHeads];
   __shared__ int s_last;
   __shared__ int s_work;
 
@@ -243,9 +257,9 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   const int plane = w - unit * p.planes;
   UnitInfo u;
   if (!find_unit<kMods>(p, unit, u)) return;  // row0 (for a custom mask) in the kMods instance
-  const int gt = p.heads_per_unit;  // valid columns of the 16-wide head block
+  const int gt = p.heads_per_unit;  // valid columns of each 16-wide head block
   const int kvh = plane / p.n_gblocks;
-  const int h0 = kvh * p.group + (plane % p.n_gblocks) * gt;
+  const int h0 = kvh * p.group + (plane % p.n_gblocks) * gt * NB;  // the workgroup's first head
   // workgroup-uniform values, kept in scalar registers
   const int t_begin = __builtin_amdgcn_readfirstlane(u.lo + u.c * p.chunk);
   const int t_end = __builtin_amdgcn_readfirstlane(min(u.L, t_begin + p.chunk));
@@ -273,6 +287,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15;
   const int grp = lane >> 4;
+  const int hb = h0 + (wave / WPB) * gt;  // first head of this wave's block
 
   // B operand of the score MFMA: Q^T, head n.  16-bit: features 32kk + 8grp
   // .. + 8 (qb).  f32: lane group grp takes features grp D/4 .. + D/4 as its
@@ -283,7 +298,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   {
     const bool live = n < gt;
     const char *qrow = static_cast<const char *>(p.q) +
-                       ((int64_t)u.b * p.num_qo_heads + h0 + (live ? n : 0)) * D * E::kBytes;
+                       ((int64_t)u.b * p.num_qo_heads + hb + (live ? n : 0)) * D * E::kBytes;
     if constexpr (kF32) {
 #pragma unroll
       for (int q4 = 0; q4 < QC; ++q4) {
@@ -302,7 +317,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   }
 
   // ALiBi slope of head n (base-2 units): row t's score gains slope2 * (t - (L - 1))
-  const float slope2 = (kMods && p.alibi && n < gt) ? p.alibi[h0 + n] * kLog2e : 0.0f;
+  const float slope2 = (kMods && p.alibi && n < gt) ? p.alibi[hb + n] * kLog2e : 0.0f;
 
   f32x4 acc[MB];
 #pragma unroll
@@ -318,8 +333,8 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   // 16-bit V: this lane's address in each transposed read: row 4 grp + (n / 4)
   // of the 16-row half, features 4 (n % 4) .. + 3 of the 16-feature block.
   // f32 V: row 4 grp (+ i) and feature n (+ 16 mb), read directly.
-  const char *vt = kF32 ? wv + (4 * grp) * G::ROWV + n * 4
-                        : wv + (4 * grp + (n >> 2)) * G::ROWV + (4 * (n & 3)) * 2;
+  const int vt_off = kF32 ? (4 * grp) * G::ROWV + n * 4
+                          : (4 * grp + (n >> 2)) * G::ROWV + (4 * (n & 3)) * 2;
   // where this lane's loaded 16 bytes go: row RPI * i + lane / LPR
   const int st_row = lane / G::LPR, st_col = (lane % G::LPR) * 16;
 
@@ -350,17 +365,20 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
     return JB == 2 ? lo | (((tile >> (16 + 4 * grp)) & 0xFu) << 4) : lo;
   };
 
-  auto compute = [&](const KVTile<G::NI> &T, int t0, uint32_t mraw) {
-    // K and V tiles to LDS
+  // K and V tiles as loaded -> this wave's LDS area
+  auto store_tile = [&](const KVTile<G::NI> &T) {
 #pragma unroll
     for (int i = 0; i < G::NI; ++i) {
       const int r = G::RPI * i + st_row;
       *reinterpret_cast<uint4 *>(wk + r * G::ROWK + st_col) = T.k[i];
       *reinterpret_cast<uint4 *>(wv + r * G::ROWV + st_col) = T.v[i];
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // One tile (rows t0 .. t0 + TT) for this wave's heads, from the LDS area at
+  // ck (K rows, then V rows).
+  auto compute_tile = [&](const char *ck, int t0, uint32_t mraw) {
+    const char *vt = ck + TT * G::ROWK + vt_off;
     uint32_t mbits = 0;
     if constexpr (kMods)
       if (p.mask) mbits = mask_bits(t0, mraw);
@@ -374,14 +392,14 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
 #pragma unroll
         for (int q4 = 0; q4 < QC; ++q4) {
           const f32x4 ka = *reinterpret_cast<const f32x4 *>(
-              wk + (16 * j + n) * G::ROWK + (grp * (D / 4) + 4 * q4) * 4);
+              ck + (16 * j + n) * G::ROWK + (grp * (D / 4) + 4 * q4) * 4);
 #pragma unroll
           for (int e = 0; e < 4; ++e) s[j] = Mfma<F32>::mma4(ka[e], qf[q4][e], s[j]);
         }
       } else {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          const uint4 ka = *reinterpret_cast<const uint4 *>(wk + (16 * j + n) * G::ROWK +
+          const uint4 ka = *reinterpret_cast<const uint4 *>(ck + (16 * j + n) * G::ROWK +
                                                             (32 * kk + 8 * grp) * 2);
           s[j] = M::mma(__builtin_bit_cast(v8, ka), qb[kk], s[j]);
         }
@@ -450,6 +468,15 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
         if constexpr (M::kSplitP) acc[mb] = M::mma(a, pl, acc[mb]);
       }
     }
+  };
+
+  // One-block workgroups: each wave stores its tile and computes it alone.
+  auto compute = [&](const KVTile<G::NI> &T, int t0, uint32_t mraw) {
+    store_tile(T);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    compute_tile(wk, t0, mraw);
     // the reads above complete before the next tile overwrites the area
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -458,6 +485,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
 
   const int stride = NW * TT;
   int t0 = t_begin + wave * TT;
+  if constexpr (NB == 1) {
   if (t0 < t_end) {
     KVTile<G::NI> A;
     issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, t0, t_end, lane);
@@ -487,6 +515,50 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
       }
     }
   }
+  } else {
+    // Shared tiles: step s covers rows t_begin + s * stride ..; wave w loads
+    // the step's tile w into its LDS area and computes tiles cw .. cw + NB - 1
+    // for its block's heads.  Every wave runs every step (the barriers are the
+    // workgroup's), loading clamped rows where its tile lies past the unit.
+    const int steps = t_begin < t_end ? (t_end - t_begin + stride - 1) / stride : 0;
+    const int cw = (wave % WPB) * NB;
+    auto shared_step = [&](const KVTile<G::NI> &T, int s) {
+      store_tile(T);
+      __syncthreads();
+      const int ts = t_begin + s * stride;
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int tc = ts + (cw + i) * TT;
+        if (tc < t_end) compute_tile(lds + (cw + i) * G::WAVE_LDS, tc, 0u);
+      }
+      __syncthreads();  // the step's tiles are read by every wave before they are replaced
+    };
+    if (steps > 0) {
+      KVTile<G::NI> A;
+      issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, t0, t_end, lane);
+      if constexpr (G::kPipelined) {
+        KVTile<G::NI> B;
+        for (int s = 0; s < steps; s += 2) {
+          if (s + 1 < steps)
+            issue_tile<E, D, kNhd>(B, p, page_base, s_pages, slot0, kvh, t0 + (s + 1) * stride,
+                                   t_end, lane);
+          shared_step(A, s);
+          if (s + 1 >= steps) break;
+          if (s + 2 < steps)
+            issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, t0 + (s + 2) * stride,
+                                   t_end, lane);
+          shared_step(B, s + 1);
+        }
+      } else {
+        for (int s = 0; s < steps; ++s) {
+          shared_step(A, s);
+          if (s + 1 < steps)
+            issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, t0 + (s + 1) * stride,
+                                   t_end, lane);
+        }
+      }
+    }
+  }
 
   // ---- merge the four lane groups' normalisers, then the waves
   l_run += __shfl_xor(l_run, 16);
@@ -505,25 +577,30 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < gt * D; idx += NW * 64) {
-    const int g = idx / D;
+  // workgroup head hh = block k's head g (k = hh / gt): merged over the WPB
+  // waves of block k
+  for (int idx = tid; idx < NB * gt * D; idx += NW * 64) {
+    const int hh = idx / D;
     const int d = idx % D;
+    const int k = NB == 1 ? 0 : hh / gt;
+    const int g = hh - k * gt;
     float Mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) Mx = fmaxf(Mx, s_m[w][g]);
+    for (int w = 0; w < WPB; ++w) Mx = fmaxf(Mx, s_m[k * WPB + w][g]);
     const float ref = safe_ref(Mx);
     float lsum = 0.0f, a = 0.0f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float sw = fast_exp2(s_m[w][g] - ref);
-      lsum += s_l[w][g] * sw;
-      a += s_acc[(w * 16 + g) * G::ACC_ROW + d] * sw;
+    for (int w = 0; w < WPB; ++w) {
+      const int ww = k * WPB + w;
+      const float sw = fast_exp2(s_m[ww][g] - ref);
+      lsum += s_l[ww][g] * sw;
+      a += s_acc[(ww * 16 + g) * G::ACC_ROW + d] * sw;
     }
-    emit<E>(p, u, h0 + g, d, Mx, lsum, a);
+    emit<E>(p, u, h0 + hh, d, Mx, lsum, a);
   }
   // merge depth 16 where the main loop's register peak already covers it
   // (D >= 128); 8 at D = 64, where 16 would cost occupancy
-  finish_split<E, (D >= 128 ? 16 : 8)>(p, u, plane, h0, gt, NW, s_stat, &s_last,
+  finish_split<E, (D >= 128 ? 16 : 8)>(p, u, plane, h0, NB * gt, NW, s_stat, &s_last,
                                         reinterpret_cast<float *>(lds), G::LDS / 4);
 }
 

@@ -69,7 +69,7 @@ def test_plan_covers_units():
                                           (2, 3, 12, 4, 64, 3, 7)]:
         chunk, bound, gt, kind = fad.fa_debug_plan(dtype, b, hq, hkv, d, p, used)
         assert chunk > 0 and chunk % 128 == 0
-        assert (hq // hkv) % gt == 0 and gt in (1, 2, 4, 8, 16)
+        assert (hq // hkv) % gt == 0 and gt in (1, 2, 4, 8, 16, 32)
         # worst case: every row in one request, or spread so each request wastes a unit
         rows = used * p
         assert bound >= -(-rows // chunk) + (b - 1)
@@ -132,8 +132,9 @@ INV, UNS, WS = fad.FA_ERR_INVALID_PROBLEM, fad.FA_ERR_UNSUPPORTED, fad.FA_ERR_WO
     (dict(page=1 << 20, used=1 << 11, pages=1 << 11), UNS),
     (dict(hq=70000, hkv=70000), UNS),                  # more query heads than a launch takes
     (dict(pages=1 << 30, hkv=64, hq=64, page=1 << 9), UNS),  # pool beyond 10^15 elements
-    (dict(batch=1 << 20, hq=32768, hkv=1), UNS),       # 2^31 workgroups or more
-    (dict(batch=1 << 20, hq=32768, hkv=1, ws=None), UNS),  # ... checked before the workspace
+    # 2^31 workgroups or more (32,768 heads of one KV head: 1,024 two-block workgroups per unit)
+    (dict(batch=1 << 21, hq=32768, hkv=1), UNS),
+    (dict(batch=1 << 21, hq=32768, hkv=1, ws=None), UNS),  # ... checked before the workspace
     (dict(ws=None), WS),
     (dict(ws_bytes=16), WS),
     # order: the dtype is checked before the extents, the extents before head_dim

@@ -125,6 +125,14 @@ EDGE = [
     ("f16", 64, 2, 24, 16, [0, 100, 2500], ()),
     ("f32", 128, 1, 64, 32, [513, 40], ()),
     ("f16", 256, 1, 17, 16, [300, 2], ()),
+    # an even number of 16-head blocks: two blocks per workgroup share each
+    # K/V tile (G = 32: one workgroup per KV head and unit; G = 64: two)
+    ("f16", 256, 2, 32, 16, [0, 1, 31, 33, 2049], ()),
+    ("bf16", 64, 3, 32, 8, [7, 96, 1500], ()),
+    ("f32", 64, 1, 32, 16, [100, 16, 1], ()),
+    ("f32", 256, 1, 32, 5, [77, 3000], ()),
+    ("bf16", 128, 2, 64, 16, [5000, 16, 0], (1,)),
+    ("f16", 128, 1, 96, 32, [31, 640], ()),
 ]
 
 
@@ -162,6 +170,8 @@ CONTIG_EDGE = [
     ("f32", 128, 2, 3, 700, 513),
     ("bf16", 128, 1, 32, 4096, 4000),
     ("f32", 64, 1, 20, 300, 299),
+    ("f16", 256, 2, 64, 2000, 1999),
+    ("f32", 64, 1, 32, 100, 0),
 ]
 
 
