@@ -212,16 +212,75 @@ __device__ inline int64_t kv_row_offset(const DecodeParams &p, int32_t page_base
   return p.nhd ? kv_elem_offset<true>(p, page, kvh, row) : kv_elem_offset<false>(p, page, kvh, row);
 }
 
+// Max and sum over the four 16-lane rows of a wave (lanes l, l ^ 16, l ^ 32,
+// l ^ 48), in registers: v_permlane16_swap with both operands = v returns,
+// at lane l, the values of lanes l & ~16 and l | 16 (rows 0-1 and 2-3
+// paired), and v_permlane32_swap those of l & 31 and l | 32; combining each
+// pair gives every lane the same bits.  No LDS traffic, unlike a lane shuffle.
+//
+// Both results of a swap pass through `opaque` (an empty asm statement on a
+// register) before use: when the two results feed one operation, this
+// compiler otherwise reads the first result for both operands.
+__device__ inline uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+__device__ inline void swap_rows16(float v, float &a, float &b) {
+  const uint32_t x = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  a = __builtin_bit_cast(float, opaque(r[0]));
+  b = __builtin_bit_cast(float, opaque(r[1]));
+}
+
+__device__ inline void swap_halves32(float v, float &a, float &b) {
+  const uint32_t x = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  a = __builtin_bit_cast(float, opaque(r[0]));
+  b = __builtin_bit_cast(float, opaque(r[1]));
+}
+
+__device__ inline float rows4_max(float v) {
+  float a, b;
+  swap_rows16(v, a, b);
+  swap_halves32(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
+}
+
+__device__ inline float rows4_sum(float v) {
+  float a, b;
+  swap_rows16(v, a, b);
+  swap_halves32(a + b, a, b);
+  return a + b;
+}
+
+// Value of a partner lane within each 16-lane row (DPP): quad_perm [1,0,3,2]
+// and [2,3,0,1] pair lanes l ^ 1 and l ^ 2; row_half_mirror (lane i of each
+// 8-lane half -> 7 - i) pairs the two quads of a half, row_mirror (i -> 15 -
+// i) the two halves of a row.  After each combining step all lanes of the
+// group hold the same bits, so the pairings reduce like an xor butterfly.
+template <int kCtrl>
+__device__ inline float dpp_partner(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, true));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+// Max and sum over all 64 lanes (every lane active), in registers.
 __device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
+  v = fmaxf(v, dpp_partner<kDppXor1>(v));
+  v = fmaxf(v, dpp_partner<kDppXor2>(v));
+  v = fmaxf(v, dpp_partner<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_partner<kDppMirror>(v));
+  return rows4_max(v);
 }
 
 __device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  v += dpp_partner<kDppXor1>(v);
+  v += dpp_partner<kDppXor2>(v);
+  v += dpp_partner<kDppHalfMirror>(v);
+  v += dpp_partner<kDppMirror>(v);
+  return rows4_sum(v);
 }
 
 }  // namespace fa

@@ -424,8 +424,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
         x[4 * j + i] = v;
         tmax = fmaxf(tmax, v);
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = rows4_max(tmax);
     const float m_new = fmaxf(m_run, tmax);
     const float ref = safe_ref(m_new);
     const float alpha = fast_exp2(m_run - ref);
@@ -561,8 +560,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   }
 
   // ---- merge the four lane groups' normalisers, then the waves
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = rows4_sum(l_run);
   __syncthreads();  // every wave is done with its V area; reuse it for the merge
   float *s_acc = reinterpret_cast<float *>(lds);  // [NW][16][ACC_ROW]
   if (n < gt) {
