@@ -267,21 +267,6 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   const int last_row = __builtin_amdgcn_readfirstlane(u.L - 1);
   const int32_t page_base = __builtin_amdgcn_readfirstlane(u.page_base);
 
-  // The unit's page ids, once, into LDS: later lookups are LDS reads instead
-  // of memory loads that each tile would wait for.  The host keeps a unit
-  // within kPageTable page slots.
-  __shared__ int32_t s_pages[kPageTable];
-  int slot0 = 0;
-  if (p.uniform_blocks && !p.contig && t_begin < t_end) {
-    slot0 = (int)fastdiv((uint32_t)t_begin, p.page_div);
-    const int count = (int)fastdiv((uint32_t)(t_end - 1), p.page_div) - slot0 + 1;
-    for (int i = threadIdx.x; i < count; i += NW * 64) {
-      const int32_t id = p.indices[page_base + slot0 + i];
-      s_pages[i] = min(max(id, 0), p.num_total_pages - 1);
-    }
-    __syncthreads();
-  }
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -289,10 +274,12 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   const int grp = lane >> 4;
   const int hb = h0 + (wave / WPB) * gt;  // first head of this wave's block
 
-  // B operand of the score MFMA: Q^T, head n.  16-bit: features 32kk + 8grp
-  // .. + 8 (qb).  f32: lane group grp takes features grp D/4 .. + D/4 as its
-  // share of every product, four per 16-byte chunk (qf); any split of the
-  // contraction works as long as the A operand (K) uses the same one.
+  // B operand of the score MFMA: Q^T, head n, loaded before the page ids are
+  // staged so that the two memory round trips overlap.  16-bit: features
+  // 32kk + 8grp .. + 8 (qb).  f32: lane group grp takes features grp D/4 ..
+  // + D/4 as its share of every product, four per 16-byte chunk (qf); any
+  // split of the contraction works as long as the A operand (K) uses the
+  // same one.
   v8 qb[kF32 ? 1 : KK];
   f32x4 qf[kF32 ? QC : 1];
   {
@@ -314,6 +301,21 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
         qb[kk] = __builtin_bit_cast(v8, r);
       }
     }
+  }
+
+  // The unit's page ids, once, into LDS: later lookups are LDS reads instead
+  // of memory loads that each tile would wait for.  The host keeps a unit
+  // within kPageTable page slots.
+  __shared__ int32_t s_pages[kPageTable];
+  int slot0 = 0;
+  if (p.uniform_blocks && !p.contig && t_begin < t_end) {
+    slot0 = (int)fastdiv((uint32_t)t_begin, p.page_div);
+    const int count = (int)fastdiv((uint32_t)(t_end - 1), p.page_div) - slot0 + 1;
+    for (int i = threadIdx.x; i < count; i += NW * 64) {
+      const int32_t id = p.indices[page_base + slot0 + i];
+      s_pages[i] = min(max(id, 0), p.num_total_pages - 1);
+    }
+    __syncthreads();
   }
 
   // ALiBi slope of head n (base-2 units): row t's score gains slope2 * (t - (L - 1))
