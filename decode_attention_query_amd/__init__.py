@@ -143,7 +143,9 @@ def merge_states(o_parts, lse_parts, out_dtype=torch.float32, o=None, lse=None, 
     if o_parts.dim() < 2 or tuple(lse_parts.shape) != tuple(o_parts.shape[:-1]):
         raise ValueError("o_parts must be [S, ..., D] and lse_parts [S, ...]")
     s, d = o_parts.shape[0], o_parts.shape[-1]
-    rows = lse_parts[0].numel()
+    rows = 1
+    for n in lse_parts.shape[1:]:
+        rows *= int(n)
     if o is None:
         o = torch.empty(tuple(o_parts.shape[1:]), dtype=out_dtype, device=o_parts.device)
     if lse is None:

@@ -294,3 +294,12 @@ def test_merge_rejects():
     assert merge(9, -1, 0, 96, None, None, None, None, None) == UNS
     assert merge(1, -1, 2, 96, None, None, None, None, None) == INV
     assert merge(1, 16, 2, 96, None, None, None, None, None) == UNS
+
+
+def test_merge_binding_reports_no_parts():
+    """Zero parts reach the library, which reports an invalid problem (no
+    buffer is looked at, so host tensors of the right shape suffice)."""
+    import torch
+    with pytest.raises(fad.FaError) as e:
+        fad.merge_states(torch.zeros((0, 4, 64)), torch.zeros((0, 4)), stream=0)
+    assert e.value.status == fad.FA_ERR_INVALID_PROBLEM
