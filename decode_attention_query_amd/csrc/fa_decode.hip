@@ -59,17 +59,16 @@ bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
 bool grid_ok(int hq, int hkv) { return hq / hkv > 0 && hkv * (hq / hkv) <= 65535; }
 
 // The plan for a call; `page_size` is max_kv_len and total_used_pages 1 for a
-// contiguous cache.  Pure host arithmetic.  `shared_ok`: the call may use the
-// two-block workgroups (plain calls: no window, cap, ALiBi or mask).
+// contiguous cache.  Pure host arithmetic.
 HostPlan make_plan(fa_dtype_t dt, int batch, int hq, int hkv, int d, int page_size,
-                   int total_used_pages, bool contig, bool shared_ok = true) {
+                   int total_used_pages, bool contig) {
   HostPlan hp;
   hp.kind = kKernelMfma;
   hp.group = hq / hkv;
   hp.gt = heads_per_unit(hp.group, 16);
   // a group of an even number of head blocks: two blocks per workgroup, so
   // K/V are read once per 2 * gt query heads
-  hp.nb = shared_ok && (hp.group / hp.gt) % 2 == 0 ? 2 : 1;
+  hp.nb = (hp.group / hp.gt) % 2 == 0 ? 2 : 1;
   hp.n_gblocks = hp.group / (hp.gt * hp.nb);
   hp.planes = hkv * hp.n_gblocks;
   // The split size depends on the KV heads only (not on the kernel's head
@@ -190,6 +189,23 @@ int first_round(int64_t n) {
   return int(r);
 }
 
+template <class E, int D, int NB>
+hipError_t launch_mfma_nb(const DecodeParams &p, bool mods, dim3 grid, dim3 block,
+                          hipStream_t s) {
+  if (p.nhd) {
+    if (mods)
+      hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, true, true, NB>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, true, false, NB>), grid, block, 0, s, p);
+  } else {
+    if (mods)
+      hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, false, true, NB>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, false, false, NB>), grid, block, 0, s, p);
+  }
+  return hipGetLastError();
+}
+
 template <class E, int D>
 hipError_t launch_mfma(const DecodeParams &params, const HostPlan &hp, hipStream_t s) {
   dim3 grid(unsigned(hp.units_bound) * unsigned(hp.planes));
@@ -197,23 +213,9 @@ hipError_t launch_mfma(const DecodeParams &params, const HostPlan &hp, hipStream
   DecodeParams p = params;
   p.ticket_from = first_round(int64_t(hp.units_bound) * hp.planes);
   const bool mods = p.window > 0 || p.softcap2 > 0.0f || p.alibi != nullptr || p.mask != nullptr;
-  if (mods && hp.nb != 1) return hipErrorInvalidValue;  // the plan assumed a plain call
-  if (p.nhd) {
-    if (mods)
-      hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, true, true, 1>), grid, block, 0, s, p);
-    else if (hp.nb == 2)
-      hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, true, false, 2>), grid, block, 0, s, p);
-    else
-      hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, true, false, 1>), grid, block, 0, s, p);
-  } else {
-    if (mods)
-      hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, false, true, 1>), grid, block, 0, s, p);
-    else if (hp.nb == 2)
-      hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, false, false, 2>), grid, block, 0, s, p);
-    else
-      hipLaunchKernelGGL((fa::decode_mfma_kernel<E, D, false, false, 1>), grid, block, 0, s, p);
-  }
-  return hipGetLastError();
+  if (hp.nb == 2)
+    return launch_mfma_nb<E, D, 2>(p, mods, grid, block, s);
+  return launch_mfma_nb<E, D, 1>(p, mods, grid, block, s);
 }
 
 template <class E>
@@ -311,12 +313,6 @@ fa_status_t read_options(const fa_decode_options_t *opts, Variant &v) {
   return FA_OK;
 }
 
-// A window, cap, ALiBi or mask is in use: the kernel instance with their
-// per-score work (and one head block per workgroup) runs.
-bool has_variant(const Variant &v) {
-  return v.window > 0 || v.softcap > 0.0f || v.alibi != nullptr || v.mask != nullptr;
-}
-
 void apply_variant(DecodeParams &p, const Variant &v) {
   p.nhd = v.nhd;
   p.window = v.window;
@@ -349,7 +345,7 @@ fa_status_t decode_contig(const Variant &var, fa_dtype_t dtype, int num_qo_heads
   // Sized like the workspace query (a single page of max_kv_len rows) so the
   // split units fit what the caller allocated.
   const HostPlan hp = make_plan(dtype, 1, num_qo_heads, num_kv_heads, head_dim, max_kv_len, 1,
-                                /*contig=*/true, !has_variant(var));
+                                /*contig=*/true);
   DecodeParams p = base_params(1, num_qo_heads, num_kv_heads, head_dim, max_kv_len, 1, 1,
                                scale, hp);
   p.q = q;
@@ -398,7 +394,7 @@ fa_status_t decode_paged(const Variant &var, fa_dtype_t dtype, int batch, int nu
   if (!pool_size_ok(num_total_pages, num_kv_heads, page_size, head_dim))
     return FA_ERR_UNSUPPORTED;
   const HostPlan hp = make_plan(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
-                                total_used_pages, false, !has_variant(var));
+                                total_used_pages, false);
   if (!launch_ok(hp)) return FA_ERR_UNSUPPORTED;
   const size_t need = fa_decode_workspace_size(batch, num_qo_heads, num_kv_heads, head_dim,
                                                page_size, total_used_pages);

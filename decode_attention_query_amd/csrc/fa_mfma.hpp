@@ -7,8 +7,7 @@
 // streams its own tiles of the unit (32 rows for 16-bit K/V, 16 for f32),
 // loads whole rows from HBM, stages K and V in its LDS area, and keeps its own
 // online-softmax state; the waves are merged through LDS at the end.  A group
-// of an even number of 16-head blocks (plain calls) takes two blocks per
-// workgroup: the waves share each step's tiles through LDS, half of them
+// of an even number of 16-head blocks takes two blocks per workgroup: the waves share each step's tiles through LDS, half of them
 // computing for each block (NB = 2 below).
 //
 // Per 32-row 16-bit tile, with n = lane % 16 and grp = lane / 16:
@@ -217,9 +216,9 @@ __device__ inline void issue_tile(KVTile<MfmaGeom<E, D>::NI> &T, const DecodePar
 // carries none of their per-score work).
 //
 // NB: 16-column head blocks per workgroup.  NB = 1: every wave serves the
-// workgroup's one block and streams its own tiles.  NB = 2 (plain calls whose
-// query group splits into an even number of blocks, e.g. G = 32): the waves
-// still load one tile each per step into their LDS areas, and after a
+// workgroup's one block and streams its own tiles.  NB = 2 (a query group of
+// an even number of blocks, e.g. G = 32): the waves still load one tile each
+// per step into their LDS areas, and after a
 // workgroup barrier the first NW / 2 waves compute every tile of the step for
 // block 0 and the others for block 1, each wave for its own 16 heads -- so
 // K and V leave HBM once for 32 query heads, with the per-wave registers of
@@ -232,7 +231,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   using v8 = typename M::v8;
   constexpr int KK = G::KK, MB = G::MB, NW = G::NW, TT = G::TT, JB = G::JB, QC = G::QC;
   constexpr bool kF32 = G::kF32;
-  static_assert(NB == 1 || (NB == 2 && NW % 2 == 0 && !kMods), "head blocks per workgroup");
+  static_assert(NB == 1 || (NB == 2 && NW % 2 == 0), "head blocks per workgroup");
   constexpr int WPB = NW / NB;  // waves per head block
 
   __shared__ __attribute__((aligned(16))) char lds[G::LDS];
@@ -241,6 +240,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   __shared__ float s_stat[2 * kStatHeads];
   __shared__ int s_last;
   __shared__ int s_work;
+  __shared__ uint32_t s_mask[NW];  // NB = 2: each wave's tile mask word
 
   // work item = unit * planes + head block: a unit's head blocks are adjacent,
   // and work items run in (longest-first) unit order.  The first resident
@@ -344,8 +344,9 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   // span bytes B/8 .. B/8 + 4.  mask_load issues one load instruction for
   // them with the tile's K/V loads (lanes 0-4, a byte each; bytes past the
   // mask's end read as 0); mask_bits, at compute time, assembles the wave's
-  // bytes and returns the lane's rows: bit 4j + i for row t0 + 16j + 4grp + i
-  // (j < JB).
+  // bytes into the tile's word (mask_word: bit r for row t0 + r, the same in
+  // every lane) and returns the lane's rows (lane_bits: bit 4j + i for row
+  // t0 + 16j + 4grp + i, j < JB).
   // Rows past the request (a prefetched tile, the tail of the last one) see
   // other bits and are cut by t_end.
   auto mask_load = [&](int t0) -> uint32_t {
@@ -358,11 +359,13 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
     }
     return v;
   };
-  auto mask_bits = [&](int t0, uint32_t v) -> uint32_t {
+  auto mask_word = [&](int t0, uint32_t v) -> uint32_t {
     uint64_t w = 0;
 #pragma unroll
     for (int k = 0; k < 5; ++k) w |= (uint64_t)__builtin_amdgcn_readlane(v, k) << (8 * k);
-    const uint32_t tile = (uint32_t)(w >> ((uint32_t)(u.row0 + t0) & 7));  // bit r: row t0 + r
+    return (uint32_t)(w >> ((uint32_t)(u.row0 + t0) & 7));  // bit r: row t0 + r
+  };
+  auto lane_bits = [&](uint32_t tile) -> uint32_t {
     const uint32_t lo = (tile >> (4 * grp)) & 0xFu;
     return JB == 2 ? lo | (((tile >> (16 + 4 * grp)) & 0xFu) << 4) : lo;
   };
@@ -379,11 +382,9 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
 
   // One tile (rows t0 .. t0 + TT) for this wave's heads, from the LDS area at
   // ck (K rows, then V rows).
-  auto compute_tile = [&](const char *ck, int t0, uint32_t mraw) {
+  // mbits: the lane's mask bits of the tile (lane_bits; unused without a mask).
+  auto compute_tile = [&](const char *ck, int t0, uint32_t mbits) {
     const char *vt = ck + TT * G::ROWK + vt_off;
-    uint32_t mbits = 0;
-    if constexpr (kMods)
-      if (p.mask) mbits = mask_bits(t0, mraw);
     // scores; A = K row 16j + n: features 32kk + 8grp .. + 8 (16-bit), or the
     // lane group's quarter of D, one feature per product (f32)
     f32x4 s[JB];
@@ -477,7 +478,10 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    compute_tile(wk, t0, mraw);
+    uint32_t mbits = 0;
+    if constexpr (kMods)
+      if (p.mask) mbits = lane_bits(mask_word(t0, mraw));
+    compute_tile(wk, t0, mbits);
     // the reads above complete before the next tile overwrites the area
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -523,39 +527,54 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
     // workgroup's), loading clamped rows where its tile lies past the unit.
     const int steps = t_begin < t_end ? (t_end - t_begin + stride - 1) / stride : 0;
     const int cw = (wave % WPB) * NB;
-    auto shared_step = [&](const KVTile<G::NI> &T, int s) {
+    // A custom mask's word of each tile is assembled by the wave that loaded
+    // the tile and published in s_mask with it.
+    auto shared_step = [&](const KVTile<G::NI> &T, int s, uint32_t mraw) {
       store_tile(T);
+      if constexpr (kMods)
+        if (p.mask && lane == 0) s_mask[wave] = mask_word(t0 + s * stride, mraw);
       __syncthreads();
       const int ts = t_begin + s * stride;
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         const int tc = ts + (cw + i) * TT;
-        if (tc < t_end) compute_tile(lds + (cw + i) * G::WAVE_LDS, tc, 0u);
+        uint32_t mbits = 0;
+        if constexpr (kMods)
+          if (p.mask) mbits = lane_bits(s_mask[cw + i]);
+        if (tc < t_end) compute_tile(lds + (cw + i) * G::WAVE_LDS, tc, mbits);
       }
       __syncthreads();  // the step's tiles are read by every wave before they are replaced
     };
     if (steps > 0) {
       KVTile<G::NI> A;
       issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, t0, t_end, lane);
+      uint32_t mA = mask_load(t0);
       if constexpr (G::kPipelined) {
         KVTile<G::NI> B;
+        uint32_t mB = 0;
         for (int s = 0; s < steps; s += 2) {
-          if (s + 1 < steps)
+          if (s + 1 < steps) {
             issue_tile<E, D, kNhd>(B, p, page_base, s_pages, slot0, kvh, t0 + (s + 1) * stride,
                                    t_end, lane);
-          shared_step(A, s);
+            mB = mask_load(t0 + (s + 1) * stride);
+          }
+          shared_step(A, s, mA);
           if (s + 1 >= steps) break;
-          if (s + 2 < steps)
+          if (s + 2 < steps) {
             issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, t0 + (s + 2) * stride,
                                    t_end, lane);
-          shared_step(B, s + 1);
+            mA = mask_load(t0 + (s + 2) * stride);
+          }
+          shared_step(B, s + 1, mB);
         }
       } else {
         for (int s = 0; s < steps; ++s) {
-          shared_step(A, s);
-          if (s + 1 < steps)
+          shared_step(A, s, mA);
+          if (s + 1 < steps) {
             issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, t0 + (s + 1) * stride,
                                    t_end, lane);
+            mA = mask_load(t0 + (s + 1) * stride);
+          }
         }
       }
     }

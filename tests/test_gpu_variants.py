@@ -63,6 +63,9 @@ CASES = [
     ("f32", 128, 2, 8, 32, [1, 300, 1500]),
     ("f32", 256, 1, 4, 16, [3, 700, 2049]),
     ("bf16", 128, 1, 32, 16, [5, 900, 2100]),
+    # two 16-head blocks per workgroup (an even number of blocks)
+    ("f16", 256, 2, 32, 16, [1, 48, 1500]),
+    ("f32", 64, 1, 64, 8, [7, 600, 1100]),
 ]
 VARIANTS = [(1, 0.0, False), (5, 0.0, False), (16, 0.0, False), (17, 0.0, False),
             (257, 0.0, False), (0, 1.0, False), (0, 30.0, False), (100, 5.0, False),
