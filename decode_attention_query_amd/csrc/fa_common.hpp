@@ -57,8 +57,9 @@ struct DecodeParams {
   int total_used_pages;
   int group;          // Hq / Hkv
   int n_gblocks;      // workgroups per KV head along the query group
-  int heads_per_unit; // query heads per workgroup (group / n_gblocks)
-  int planes;         // Hkv * n_gblocks: head blocks per split unit
+  int heads_per_unit; // query heads per head block (the group, or 16; the last
+                      // block of a group may hold fewer)
+  int planes;         // Hkv * n_gblocks: workgroups per split unit
   float scale_log2;   // scale * log2(e): scores live in the base-2 domain
   FastDiv page_div;   // row -> (page slot, row in page)
   // split-KV plan

@@ -30,14 +30,6 @@ constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Query heads per workgroup: the largest power of two dividing the group that
-// the kernel's head block holds (16, the MFMA column block).
-int heads_per_unit(int group, int max_heads) {
-  for (int gt = max_heads; gt > 1; gt /= 2)
-    if (group % gt == 0) return gt;
-  return 1;
-}
-
 // The attention kernel of a call: 1, the matrix-core kernel, for every element
 // type and head dim (the value fa_debug_plan reports).
 constexpr int kKernelMfma = 1;
@@ -65,11 +57,17 @@ HostPlan make_plan(fa_dtype_t dt, int batch, int hq, int hkv, int d, int page_si
   HostPlan hp;
   hp.kind = kKernelMfma;
   hp.group = hq / hkv;
-  hp.gt = heads_per_unit(hp.group, 16);
-  // a group of an even number of head blocks: two blocks per workgroup, so
-  // K/V are read once per 2 * gt query heads
-  hp.nb = (hp.group / hp.gt) % 2 == 0 ? 2 : 1;
-  hp.n_gblocks = hp.group / (hp.gt * hp.nb);
+  // Head blocks: the whole group when it fits the 16-column MFMA block (one
+  // workgroup per split unit and KV head); else blocks of 16 with a shorter
+  // last one, two per workgroup, so K/V are read once per 32 query heads.
+  if (hp.group <= 16) {
+    hp.gt = hp.group;
+    hp.nb = 1;
+  } else {
+    hp.gt = 16;
+    hp.nb = 2;
+  }
+  hp.n_gblocks = (hp.group + hp.gt * hp.nb - 1) / (hp.gt * hp.nb);
   hp.planes = hkv * hp.n_gblocks;
   // The split size depends on the KV heads only (not on the kernel's head
   // blocking), so the workspace size is the same for every element type.
@@ -751,7 +749,7 @@ fa_status_t fa_debug_plan(fa_dtype_t dtype, int batch, int num_qo_heads, int num
                                 total_used_pages, false);
   if (chunk_rows) *chunk_rows = hp.chunk;
   if (units_bound) *units_bound = hp.units_bound;
-  if (heads_per_unit_out) *heads_per_unit_out = hp.gt * hp.nb;
+  if (heads_per_unit_out) *heads_per_unit_out = std::min(hp.group, hp.gt * hp.nb);
   if (kernel_kind) *kernel_kind = hp.kind;
   return FA_OK;
 }

@@ -2,12 +2,13 @@
 // on gfx950.
 //
 // One workgroup = one split unit of one KV head and a block of up to 16 query
-// heads of its group (the whole group when G <= 16), so K and V are read from
-// HBM once for all those heads.  Four waves (two at D = 256); each wave
+// heads of its group (the whole group when G <= 16, any G), so K and V are
+// read from HBM once for all those heads.  Four waves (two at D = 256); each wave
 // streams its own tiles of the unit (32 rows for 16-bit K/V, 16 for f32),
 // loads whole rows from HBM, stages K and V in its LDS area, and keeps its own
 // online-softmax state; the waves are merged through LDS at the end.  A group
-// of an even number of 16-head blocks takes two blocks per workgroup: the waves share each step's tiles through LDS, half of them
+// of more than 16 heads is cut into blocks of 16 (the last one shorter, or
+// empty) and takes two blocks per workgroup: the waves share each step's tiles through LDS, half of them
 // computing for each block (NB = 2 below).
 //
 // Per 32-row 16-bit tile, with n = lane % 16 and grp = lane / 16:
@@ -217,7 +218,7 @@ __device__ inline void issue_tile(KVTile<MfmaGeom<E, D>::NI> &T, const DecodePar
 //
 // NB: 16-column head blocks per workgroup.  NB = 1: every wave serves the
 // workgroup's one block and streams its own tiles.  NB = 2 (a query group of
-// an even number of blocks, e.g. G = 32): the waves still load one tile each
+// more than 16 heads, e.g. G = 32): the waves still load one tile each
 // per step into their LDS areas, and after a
 // workgroup barrier the first NW / 2 waves compute every tile of the step for
 // block 0 and the others for block 1, each wave for its own 16 heads -- so
@@ -257,9 +258,14 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   const int plane = w - unit * p.planes;
   UnitInfo u;
   if (!find_unit<kMods>(p, unit, u)) return;  // row0 (for a custom mask) in the kMods instance
-  const int gt = p.heads_per_unit;  // valid columns of each 16-wide head block
+  // Head blocks of bs = heads_per_unit query heads (the whole group when it
+  // has at most 16, else 16 with a shorter last block); the workgroup serves
+  // blocks NB * gblock .. + NB - 1 of its KV head's group, gt_wg heads in all.
+  const int bs = p.heads_per_unit;
   const int kvh = plane / p.n_gblocks;
-  const int h0 = kvh * p.group + (plane % p.n_gblocks) * gt * NB;  // the workgroup's first head
+  const int gblock = plane - kvh * p.n_gblocks;
+  const int h0 = kvh * p.group + gblock * NB * bs;  // the workgroup's first head
+  const int gt_wg = min(NB * bs, p.group - gblock * NB * bs);
   // workgroup-uniform values, kept in scalar registers
   const int t_begin = __builtin_amdgcn_readfirstlane(u.lo + u.c * p.chunk);
   const int t_end = __builtin_amdgcn_readfirstlane(min(u.L, t_begin + p.chunk));
@@ -272,7 +278,12 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15;
   const int grp = lane >> 4;
-  const int hb = h0 + (wave / WPB) * gt;  // first head of this wave's block
+  // first head of this wave's block: past the group when the block is empty,
+  // so only lanes with a valid column (n < gt) may use it in an address
+  const int hb = h0 + (wave / WPB) * bs;
+  // valid columns of this wave's block (0 for the empty second block of a
+  // workgroup at the end of an odd number of blocks)
+  const int gt = max(0, min(bs, gt_wg - (wave / WPB) * bs));
 
   // B operand of the score MFMA: Q^T, head n, loaded before the page ids are
   // staged so that the two memory round trips overlap.  16-bit: features
@@ -285,7 +296,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   {
     const bool live = n < gt;
     const char *qrow = static_cast<const char *>(p.q) +
-                       ((int64_t)u.b * p.num_qo_heads + hb + (live ? n : 0)) * D * E::kBytes;
+                       ((int64_t)u.b * p.num_qo_heads + (live ? hb + n : h0)) * D * E::kBytes;
     if constexpr (kF32) {
 #pragma unroll
       for (int q4 = 0; q4 < QC; ++q4) {
@@ -541,7 +552,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
         uint32_t mbits = 0;
         if constexpr (kMods)
           if (p.mask) mbits = lane_bits(s_mask[cw + i]);
-        if (tc < t_end) compute_tile(lds + (cw + i) * G::WAVE_LDS, tc, mbits);
+        if (tc < t_end && gt > 0) compute_tile(lds + (cw + i) * G::WAVE_LDS, tc, mbits);
       }
       __syncthreads();  // the step's tiles are read by every wave before they are replaced
     };
@@ -596,13 +607,13 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
     }
   }
   __syncthreads();
-  // workgroup head hh = block k's head g (k = hh / gt): merged over the WPB
+  // workgroup head hh = block k's head g (k = hh / bs): merged over the WPB
   // waves of block k
-  for (int idx = tid; idx < NB * gt * D; idx += NW * 64) {
+  for (int idx = tid; idx < gt_wg * D; idx += NW * 64) {
     const int hh = idx / D;
     const int d = idx % D;
-    const int k = NB == 1 ? 0 : hh / gt;
-    const int g = hh - k * gt;
+    const int k = NB == 1 ? 0 : hh / bs;
+    const int g = hh - k * bs;
     float Mx = -INFINITY;
 #pragma unroll
     for (int w = 0; w < WPB; ++w) Mx = fmaxf(Mx, s_m[k * WPB + w][g]);
@@ -619,7 +630,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   }
   // merge depth 16 where the main loop's register peak already covers it
   // (D >= 128); 8 at D = 64, where 16 would cost occupancy
-  finish_split<E, (D >= 128 ? 16 : 8)>(p, u, plane, h0, NB * gt, NW, s_stat, &s_last,
+  finish_split<E, (D >= 128 ? 16 : 8)>(p, u, plane, h0, gt_wg, NW, s_stat, &s_last,
                                         reinterpret_cast<float *>(lds), G::LDS / 4);
 }
 

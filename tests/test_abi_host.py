@@ -66,10 +66,14 @@ def test_plan_covers_units():
                                           (2, 32, 64, 8, 128, 32, 32768),
                                           (1, 128, 16, 4, 256, 16, 33000),
                                           (0, 1, 8, 2, 64, 256, 1),
-                                          (2, 3, 12, 4, 64, 3, 7)]:
+                                          (2, 3, 12, 4, 64, 3, 7),
+                                          (2, 4, 28, 4, 128, 16, 90),   # G = 7
+                                          (1, 2, 71, 1, 128, 16, 40),   # G = 71
+                                          (1, 2, 96, 2, 64, 16, 40)]:   # G = 48
         chunk, bound, gt, kind = fad.fa_debug_plan(dtype, b, hq, hkv, d, p, used)
         assert chunk > 0 and chunk % 128 == 0
-        assert (hq // hkv) % gt == 0 and gt in (1, 2, 4, 8, 16, 32)
+        # heads per workgroup: the whole group up to 16, else two blocks of 16
+        assert gt == min(hq // hkv, 32)
         # worst case: every row in one request, or spread so each request wastes a unit
         rows = used * p
         assert bound >= -(-rows // chunk) + (b - 1)

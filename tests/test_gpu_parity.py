@@ -133,6 +133,15 @@ EDGE = [
     ("f32", 256, 1, 32, 5, [77, 3000], ()),
     ("bf16", 128, 2, 64, 16, [5000, 16, 0], (1,)),
     ("f16", 128, 1, 96, 32, [31, 640], ()),
+    # groups that are not powers of two: one block of the whole group up to
+    # 16 heads, else blocks of 16 with a shorter last one (G = 48: the last
+    # workgroup's second block is empty; G = 71: 16 + 16 | 16 + 16 | 7)
+    ("bf16", 128, 4, 7, 16, [0, 1, 700, 2500], ()),
+    ("f16", 64, 2, 6, 8, [33, 900], ()),
+    ("f32", 256, 1, 13, 16, [17, 1300], ()),
+    ("bf16", 128, 1, 48, 16, [600, 2, 3100], ()),
+    ("f16", 128, 1, 71, 16, [1, 1030], ()),
+    ("bf16", 64, 2, 24, 32, [2048, 5], (0,)),
 ]
 
 
@@ -172,6 +181,8 @@ CONTIG_EDGE = [
     ("f32", 64, 1, 20, 300, 299),
     ("f16", 256, 2, 64, 2000, 1999),
     ("f32", 64, 1, 32, 100, 0),
+    ("bf16", 128, 4, 7, 4096, 4096),
+    ("f16", 256, 1, 40, 700, 699),
 ]
 
 

@@ -66,6 +66,9 @@ CASES = [
     # two 16-head blocks per workgroup (an even number of blocks)
     ("f16", 256, 2, 32, 16, [1, 48, 1500]),
     ("f32", 64, 1, 64, 8, [7, 600, 1100]),
+    # a group that is not a power of two, and a ragged last head block
+    ("bf16", 128, 2, 7, 16, [3, 800]),
+    ("f16", 128, 1, 40, 16, [300, 1700]),
 ]
 VARIANTS = [(1, 0.0, False), (5, 0.0, False), (16, 0.0, False), (17, 0.0, False),
             (257, 0.0, False), (0, 1.0, False), (0, 30.0, False), (100, 5.0, False),
