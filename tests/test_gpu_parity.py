@@ -362,11 +362,12 @@ def test_binding_checks_shapes(dev):
                             o, lse, ws[:16])
 
 
-@pytest.mark.parametrize("name,qo_heads", [("c3", 8), ("c3", 16), ("c3", 128), ("c5", 4)])
+@pytest.mark.parametrize("name,qo_heads", [("c3", 8), ("c3", 16), ("c3", 56), ("c3", 128),
+                                            ("c3", 192), ("c3", 256), ("c3", 384), ("c5", 4)])
 def test_full_shapes_other_group(dev, name, qo_heads):
     """Full-size K/V and page tables with another number of query heads per KV
-    head (G = 1, 2 and 16 on C3's store, G = 1 on C5's), as bench.py
-    --qo-heads times them: sampled pairs against the oracle."""
+    head (G = 1, 2, 7, 16, 24, 32 and 48 on C3's store, G = 1 on C5's), as
+    bench.py --qo-heads times them: sampled pairs against the oracle."""
     p = W.FULL[name](qo_heads=qo_heads)
     announce(f"full {name} with {qo_heads} query heads: {p.name}")
     d = to_dev(p, dev)
