@@ -123,7 +123,7 @@ def _launch_size(p):
     _, bound, gt, _ = fad.fa_debug_plan(fad.DTYPE_CODES[p.dtype], p.batch, p.num_qo_heads,
                                         p.num_kv_heads, p.head_dim, p.page_size,
                                         p.total_used_pages)
-    return bound * p.num_kv_heads * ((p.num_qo_heads // p.num_kv_heads) // gt)
+    return bound * p.num_kv_heads * -(-(p.num_qo_heads // p.num_kv_heads) // gt)
 
 
 def test_garbage_workspace(dev):
@@ -171,10 +171,16 @@ def test_workspace_shared_across_shapes(dev):
         compare(q.dtype, ref[0], ref[1], ro, rl, q.name)
 
 
-def test_graph_replay(dev):
+@pytest.mark.parametrize("qo_heads", [16, 64], ids=["G4", "G32-two-blocks"])
+def test_graph_replay(dev, qo_heads):
     """A captured call replays correctly again and again (each merge leaves its
-    arrival counter at rest), with eager work in between."""
+    arrival counter at rest), with eager work in between; G = 32 takes the
+    two-block workgroups."""
     p = _split_problem(seed=78)
+    if qo_heads != p.num_qo_heads:
+        lens = _lens_of(p)
+        p = W.make_paged("split-mix-g32", p.dtype, p.batch, qo_heads, 2, 128, 16, 78,
+                         lens=lens, pool_slack=0.1)
     d = to_dev(p, dev)
     ws = fad.workspace_paged(p.batch, p.num_qo_heads, p.num_kv_heads, p.head_dim,
                              p.page_size, p.total_used_pages, dev)
@@ -202,6 +208,45 @@ def test_graph_replay(dev):
         torch.cuda.synchronize()
         assert torch.equal(o, eo) and torch.equal(lse, el), f"replay {r}"
     announce("graph replays match eager")
+
+
+def _lens_of(p):
+    return np.asarray(p.kv_lens, dtype=np.int64)
+
+
+def test_graph_replay_merge(dev):
+    """The separate merge captured in a graph: every replay, with new partials
+    copied in and eager work in between, equals the eager call bit for bit."""
+    rng = np.random.default_rng(12)
+    s_, rows, d = 6, 300, 128
+    o_p = torch.from_numpy(rng.standard_normal((s_, rows, d)).astype(np.float32)).to(dev)
+    l_p = torch.from_numpy((rng.standard_normal((s_, rows)) * 3).astype(np.float32)).to(dev)
+    l_p[2, ::7] = -float("inf")
+    o = torch.empty((rows, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((rows,), dtype=torch.float32, device=dev)
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        fad.merge_states(o_p, l_p, o=o, lse=lse)
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fad.merge_states(o_p, l_p, o=o, lse=lse)
+    torch.cuda.synchronize()
+    o0, l0 = o_p.clone(), l_p.clone()
+    for r in range(4):
+        o_p.copy_(o0 * (1.0 - 0.2 * r))
+        l_p.copy_(l0 + 0.5 * r)
+        eo, el = fad.merge_states(o_p, l_p, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        o.zero_()
+        lse.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), eo.view(torch.int16)), f"replay {r}"
+        assert torch.equal(lse.view(torch.int32), el.view(torch.int32)), f"replay {r}"
+    announce("merge graph replays match eager")
 
 
 def test_read_probe_runs(dev):
