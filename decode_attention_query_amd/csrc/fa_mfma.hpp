@@ -145,7 +145,9 @@ struct MfmaGeom {
   static constexpr int ACC_ROW = D + 4;
   static constexpr int LDS_ACC = NW * 16 * ACC_ROW * 4;
   static constexpr int LDS = LDS_KV > LDS_ACC ? LDS_KV : LDS_ACC;
-  static constexpr bool kPipelined = D <= 128;   // prefetch one tile ahead
+  // two register tiles, ping-pong (D <= 128); at D = 256 one, reloaded as
+  // soon as it is in LDS
+  static constexpr bool kPipelined = D <= 128;
 };
 
 // K and V of one tile as loaded: instruction i, lane l holds row
@@ -522,12 +524,29 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
         if (t0 >= t_end) break;
       }
     } else {
+      // One register tile (D = 256): once it is in LDS its registers are free,
+      // so the next tile's loads are issued before the current one is
+      // computed and stream meanwhile.
       while (true) {
-        compute(A, t0, mA);
-        t0 += stride;
+        store_tile(A);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        uint32_t mbits = 0;
+        if constexpr (kMods)
+          if (p.mask) mbits = lane_bits(mask_word(t0, mA));
+        const int tn = t0 + stride;
+        if (tn < t_end) {
+          issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, tn, t_end, lane);
+          mA = mask_load(tn);
+        }
+        compute_tile(wk, t0, mbits);
+        // the reads above complete before the next tile overwrites the area
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        t0 = tn;
         if (t0 >= t_end) break;
-        issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, t0, t_end, lane);
-        mA = mask_load(t0);
       }
     }
   }
