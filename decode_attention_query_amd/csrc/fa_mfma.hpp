@@ -559,10 +559,12 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
     const int cw = (wave % WPB) * NB;
     // A custom mask's word of each tile is assembled by the wave that loaded
     // the tile and published in s_mask with it.
-    auto shared_step = [&](const KVTile<G::NI> &T, int s, uint32_t mraw) {
+    auto shared_store = [&](const KVTile<G::NI> &T, int s, uint32_t mraw) {
       store_tile(T);
       if constexpr (kMods)
         if (p.mask && lane == 0) s_mask[wave] = mask_word(t0 + s * stride, mraw);
+    };
+    auto shared_compute = [&](int s) {
       __syncthreads();
       const int ts = t_begin + s * stride;
 #pragma unroll
@@ -574,6 +576,10 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
         if (tc < t_end && gt > 0) compute_tile(lds + (cw + i) * G::WAVE_LDS, tc, mbits);
       }
       __syncthreads();  // the step's tiles are read by every wave before they are replaced
+    };
+    auto shared_step = [&](const KVTile<G::NI> &T, int s, uint32_t mraw) {
+      shared_store(T, s, mraw);
+      shared_compute(s);
     };
     if (steps > 0) {
       KVTile<G::NI> A;
@@ -598,13 +604,16 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
           shared_step(B, s + 1, mB);
         }
       } else {
+        // one register tile (D = 256): reloaded as soon as it is in LDS, so
+        // the next step's loads stream while this step is computed
         for (int s = 0; s < steps; ++s) {
-          shared_step(A, s, mA);
+          shared_store(A, s, mA);
           if (s + 1 < steps) {
             issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, t0 + (s + 1) * stride,
                                    t_end, lane);
             mA = mask_load(t0 + (s + 1) * stride);
           }
+          shared_compute(s);
         }
       }
     }
