@@ -138,3 +138,27 @@ def test_context_parallel_decode(dev, parts):
     torch.cuda.synchronize()
     ro, rl = oracle_of(p)
     compare("f32", o, lse, ro, rl, what=f"context-parallel {parts}")
+
+
+def test_merge_many_rows(dev):
+    """600,000 rows x 2 parts at D = 128: 75,000 workgroups, so the launch and
+    the kernel's 64-bit row offsets go well past 16-bit grid sizes; sampled
+    rows against the oracle, every row finite."""
+    announce("merge 600k rows")
+    rows, s_, d = 600_000, 2, 128
+    g = torch.Generator(device="cpu").manual_seed(31)
+    o_p = torch.randn((s_, rows, d), generator=g).to(dev)
+    l_p = (torch.randn((s_, rows), generator=g) * 3.0).to(dev)
+    l_p[1, ::5] = -float("inf")
+    o, lse = fad.merge_states(o_p, l_p, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    pick = np.unique(np.concatenate([np.arange(4), rows - 1 - np.arange(4),
+                                     np.random.default_rng(3).integers(0, rows, 200)]))
+    idx = torch.from_numpy(pick).to(dev)
+    op = o_p[:, idx, :].cpu().numpy()
+    lp = l_p[:, idx].cpu().numpy()
+    ro, rl = _oracle_rows(op, lp)
+    compare("f32", o[idx], lse[idx], ro, rl, what="merge 600k rows")
+    del o_p, l_p, o, lse
+    torch.cuda.empty_cache()
