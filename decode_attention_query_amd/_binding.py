@@ -23,11 +23,13 @@ CODE_TORCH_DTYPES = {v: k for k, v in TORCH_DTYPE_CODES.items()}
 
 FA_OK, FA_ERR_INVALID_PROBLEM, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE_TOO_SMALL, FA_ERR_LAUNCH = \
     range(5)
+FA_NOALLOC_SCRATCH_BYTES = 32 << 20  # include/fa_decode.h
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_INVALID_PROBLEM", 2: "FA_ERR_UNSUPPORTED",
                 3: "FA_ERR_WORKSPACE_TOO_SMALL", 4: "FA_ERR_LAUNCH"}
 
 # every symbol the public headers declare
 EXPORTED = ("fa_decode_workspace_size", "fa_decode_contig", "fa_decode_paged",
+            "fa_decode_paged_noalloc",
             "fa_decode_contig_nhd", "fa_decode_paged_nhd", "fa_append_paged",
             "fa_append_paged_nhd", "fa_decode_paged_opts", "fa_decode_contig_opts",
             "fa_merge_states", "fa_status_string",
@@ -79,6 +81,9 @@ def load_library():
         getattr(lib, name).argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P,
                                        _P, _P, _P, _P, _SZ, _P]
         getattr(lib, name).restype = _I
+    lib.fa_decode_paged_noalloc.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P,
+                                            _P, _P, _P, _P, _P, _P]
+    lib.fa_decode_paged_noalloc.restype = _I
     lib.fa_status_string.argtypes = [_I]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_decode_contig_opts.argtypes = [_P] + list(lib.fa_decode_contig.argtypes)
@@ -237,6 +242,36 @@ def fa_decode_paged(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_siz
     _paged("fa_decode_paged", dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
            num_total_pages, total_used_pages, sm_scale, q, k_data, v_data, indices, indptr,
            last_page_len, o, lse, workspace, stream)
+
+
+def fa_decode_paged_noalloc(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                            num_total_pages, total_used_pages, sm_scale, q, k_data, v_data,
+                            indices, indptr, last_page_len, o, lse, stream=None):
+    """fa_decode_paged without a workspace: the library's static scratch array
+    (FA_NOALLOC_SCRATCH_BYTES per GPU) holds the split partials."""
+    lib = load_library()
+    fn = "fa_decode_paged_noalloc"
+    tdt = CODE_TORCH_DTYPES.get(dtype)
+    if tdt is None:
+        _check(fn, lib.fa_decode_paged_noalloc(dtype, batch, num_qo_heads, num_kv_heads,
+                                               head_dim, page_size, num_total_pages,
+                                               total_used_pages, sm_scale, *([None] * 8),
+                                               None))
+    pool = num_total_pages * num_kv_heads * page_size * head_dim
+    args = (
+        _dev_buf(q, "q", batch * num_qo_heads * head_dim, tdt),
+        _dev_buf(k_data, "k_data", pool, tdt),
+        _dev_buf(v_data, "v_data", pool, tdt),
+        _dev_buf(indices, "indices", total_used_pages, torch.int32,
+                 allow_none=total_used_pages == 0),
+        _dev_buf(indptr, "indptr", batch + 1, torch.int32),
+        _dev_buf(last_page_len, "last_page_len", batch, torch.int32),
+        _dev_buf(o, "o", batch * num_qo_heads * head_dim, tdt),
+        _dev_buf(lse, "lse", batch * num_qo_heads, torch.float32),
+    )
+    _check(fn, lib.fa_decode_paged_noalloc(dtype, batch, num_qo_heads, num_kv_heads, head_dim,
+                                           page_size, num_total_pages, total_used_pages,
+                                           float(sm_scale), *args, _stream(stream)))
 
 
 def fa_decode_paged_opts(opts, dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,

@@ -370,13 +370,14 @@ fa_status_t decode_contig(const Variant &var, fa_dtype_t dtype, int num_qo_heads
   return FA_OK;
 }
 
-fa_status_t decode_paged(const Variant &var, fa_dtype_t dtype, int batch, int num_qo_heads,
-                         int num_kv_heads, int head_dim, int page_size, int num_total_pages,
-                         int total_used_pages, float sm_scale, const void *q,
-                         const void *k_data, const void *v_data, const int32_t *indices,
-                         const int32_t *indptr, const int32_t *last_page_len, void *o,
-                         float *lse, void *workspace, size_t workspace_bytes,
-                         hipStream_t stream) {
+// Every check of a paged call that comes before the workspace check, in the
+// documented order (the workspace pointer's alignment included).
+fa_status_t paged_checks(fa_dtype_t dtype, int batch, int num_qo_heads, int num_kv_heads,
+                         int head_dim, int page_size, int num_total_pages, int total_used_pages,
+                         const void *q, const void *k_data, const void *v_data,
+                         const int32_t *indices, const int32_t *indptr,
+                         const int32_t *last_page_len, const void *o, const float *lse,
+                         const void *workspace) {
   if (!dtype_ok(dtype)) return FA_ERR_UNSUPPORTED;
   if (!extents_ok(batch, num_qo_heads, num_kv_heads, page_size) || num_total_pages <= 0)
     return FA_ERR_INVALID_PROBLEM;
@@ -394,6 +395,22 @@ fa_status_t decode_paged(const Variant &var, fa_dtype_t dtype, int batch, int nu
   const HostPlan hp = make_plan(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
                                 total_used_pages, false);
   if (!launch_ok(hp)) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+fa_status_t decode_paged(const Variant &var, fa_dtype_t dtype, int batch, int num_qo_heads,
+                         int num_kv_heads, int head_dim, int page_size, int num_total_pages,
+                         int total_used_pages, float sm_scale, const void *q,
+                         const void *k_data, const void *v_data, const int32_t *indices,
+                         const int32_t *indptr, const int32_t *last_page_len, void *o,
+                         float *lse, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  const fa_status_t st = paged_checks(dtype, batch, num_qo_heads, num_kv_heads, head_dim,
+                                      page_size, num_total_pages, total_used_pages, q, k_data,
+                                      v_data, indices, indptr, last_page_len, o, lse, workspace);
+  if (st != FA_OK) return st;
+  const HostPlan hp = make_plan(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                                total_used_pages, false);
   const size_t need = fa_decode_workspace_size(batch, num_qo_heads, num_kv_heads, head_dim,
                                                page_size, total_used_pages);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
@@ -531,6 +548,43 @@ fa_status_t merge_states(fa_dtype_t dtype, int num_rows, int num_parts, int head
 
 }  // namespace
 
+// ------------------------------------------------ allocation-free entry point
+//
+// The split partials and counters of fa_decode_paged_noalloc live here: one
+// copy of this array on every GPU the library runs on, held until the process
+// ends.  In host code `scratch` only names the array (a host-side stand-in, not
+// a device address): its device address on a GPU comes from
+// hipGetSymbolAddress with that GPU current, and only that address is passed
+// to kernels.
+__device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current GPU's copy of `scratch`, looked up on the
+// first call on that GPU and kept; nullptr if the lookup fails.
+void *scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void *addr = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (addr) return addr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  addr = g_scratch_addr[dev].load(std::memory_order_relaxed);
+  if (!addr) {
+    void *found = nullptr;
+    if (hipGetSymbolAddress(&found, HIP_SYMBOL(scratch)) != hipSuccess || !found)
+      return nullptr;
+    g_scratch_addr[dev].store(found, std::memory_order_release);
+    addr = found;
+  }
+  return addr;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t fa_decode_workspace_size(int batch, int num_qo_heads, int num_kv_heads, int head_dim,
@@ -604,6 +658,28 @@ fa_status_t fa_decode_paged_nhd(fa_dtype_t dtype, int batch, int num_qo_heads,
   return decode_paged(Variant{1, 0, 0.0f, nullptr}, dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
                       num_total_pages, total_used_pages, sm_scale, q, k_data, v_data, indices,
                       indptr, last_page_len, o, lse, workspace, workspace_bytes, stream);
+}
+
+fa_status_t fa_decode_paged_noalloc(fa_dtype_t dtype, int batch, int num_qo_heads,
+                                    int num_kv_heads, int head_dim, int page_size,
+                                    int num_total_pages, int total_used_pages, float sm_scale,
+                                    const void *q, const void *k_data, const void *v_data,
+                                    const int32_t *indices, const int32_t *indptr,
+                                    const int32_t *last_page_len, void *o, float *lse,
+                                    hipStream_t stream) {
+  const fa_status_t st = paged_checks(dtype, batch, num_qo_heads, num_kv_heads, head_dim,
+                                      page_size, num_total_pages, total_used_pages, q, k_data,
+                                      v_data, indices, indptr, last_page_len, o, lse, nullptr);
+  if (st != FA_OK) return st;
+  const size_t need = fa_decode_workspace_size(batch, num_qo_heads, num_kv_heads, head_dim,
+                                               page_size, total_used_pages);
+  if (need > size_t(FA_NOALLOC_SCRATCH_BYTES)) return FA_ERR_WORKSPACE_TOO_SMALL;
+  void *ws = scratch_address();
+  if (!ws) return FA_ERR_LAUNCH;
+  return decode_paged(Variant{}, dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                      num_total_pages, total_used_pages, sm_scale, q, k_data, v_data, indices,
+                      indptr, last_page_len, o, lse, ws, size_t(FA_NOALLOC_SCRATCH_BYTES),
+                      stream);
 }
 
 fa_status_t fa_decode_contig_opts(const fa_decode_options_t *opts, fa_dtype_t dtype,

@@ -25,7 +25,8 @@
  *     (round-to-nearest-even).
  *   - Ownership: the caller allocates and frees every buffer (inputs, outputs,
  *     workspace).  The library allocates no device memory and keeps no state
- *     between calls.
+ *     between calls, except the static scratch array of
+ *     fa_decode_paged_noalloc (below).
  *   - Streams: work is enqueued on `stream` (0 = the null stream) and the call
  *     returns without synchronising; outputs are ready when the stream reaches
  *     that point.  No host<->device copies are made.
@@ -173,6 +174,40 @@ fa_status_t fa_decode_paged(fa_dtype_t dtype, int batch, int num_qo_heads, int n
                             const int32_t *indptr, const int32_t *last_page_len, void *o,
                             float *lse, void *workspace, size_t workspace_bytes,
                             hipStream_t stream);
+
+/* Size in bytes of the library's static scratch array used by
+ * fa_decode_paged_noalloc (one copy per GPU). */
+#define FA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* fa_decode_paged for callers that cannot allocate device memory: code under
+ * HIP graph capture that has no buffer to hand over as a workspace, tight
+ * serving loops, and harnesses that forbid hipMalloc.  Same arguments, checks,
+ * conventions and results as fa_decode_paged (bit-identical outputs), minus
+ * workspace and workspace_bytes.  The split partials and counters live in a
+ * static device array of FA_NOALLOC_SCRATCH_BYTES bytes inside the library:
+ * each GPU the library runs on holds one copy until the process ends, and no
+ * call allocates or frees anything.
+ *   - The problem's fa_decode_workspace_size(batch, Hq, Hkv, D, page_size,
+ *     total_used_pages) must not exceed FA_NOALLOC_SCRATCH_BYTES; a larger one
+ *     -> FA_ERR_WORKSPACE_TOO_SMALL (checked after every check of
+ *     fa_decode_paged before its workspace check; nothing is enqueued).
+ *   - The first call on a GPU looks up the device address of that GPU's copy
+ *     of the array (hipGetSymbolAddress, with that GPU current) and keeps it;
+ *     if the lookup fails -> FA_ERR_LAUNCH.  A caller that captures calls
+ *     should make its first call on each GPU outside capture.
+ *   - Every call on one GPU uses that GPU's one array, which keeps what the
+ *     last call left there.  Calls that may overlap on one GPU (on different
+ *     streams, or concurrent replays of captured calls) race on it and give
+ *     undefined results; calls on one stream are ordered and safe.  Nothing in
+ *     the array needs clearing between calls (as for a workspace, its contents
+ *     before a call do not matter). */
+fa_status_t fa_decode_paged_noalloc(fa_dtype_t dtype, int batch, int num_qo_heads,
+                                    int num_kv_heads, int head_dim, int page_size,
+                                    int num_total_pages, int total_used_pages, float sm_scale,
+                                    const void *q, const void *k_data, const void *v_data,
+                                    const int32_t *indices, const int32_t *indptr,
+                                    const int32_t *last_page_len, void *o, float *lse,
+                                    hipStream_t stream);
 
 /* Token-major variants (ferrox-cuda 0.15.2, src/attn.rs: the gqa_decode kernel
  * source and the k_cache / v_cache shape in its doc comment put row t of KV

@@ -152,6 +152,37 @@ def test_paged_rejects(kw, status, fn):
     assert _paged(**kw, fn=fn) == status
 
 
+def _noalloc(*, dtype=2, batch=2, hq=8, hkv=2, d=128, page=16, pages=10, used=4, ptrs=None):
+    lib = fad.load_library()
+    q = k = v = ind = ptr = lpl = o = lse = FAKE
+    if ptrs:
+        q, k, v, ind, ptr, lpl, o, lse = [ptrs.get(n, FAKE) for n in
+                                          ("q", "k", "v", "ind", "ptr", "lpl", "o", "lse")]
+    return lib.fa_decode_paged_noalloc(dtype, batch, hq, hkv, d, page, pages, used, 0.125, q, k,
+                                       v, ind, ptr, lpl, o, lse, None)
+
+
+def test_noalloc_rejects_like_paged():
+    """The allocation-free entry point makes fa_decode_paged's checks in the
+    same order (no workspace argument), and refuses a problem whose workspace
+    would not fit its static array -- all before any device call."""
+    cases = [
+        (dict(dtype=3), UNS), (dict(batch=0), INV), (dict(hq=12, hkv=8), INV),
+        (dict(d=96), UNS), (dict(used=-1), INV), (dict(ptrs={"q": None}), INV),
+        (dict(ptrs={"ind": None}), INV), (dict(ptrs={"lse": None}), INV),
+        (dict(ptrs={"k": MIS8}), INV), (dict(ptrs={"ptr": MIS2}), INV),
+        (dict(page=1 << 20, used=1 << 11, pages=1 << 11), UNS),
+        (dict(hq=70000, hkv=70000), UNS), (dict(batch=1 << 21, hq=32768, hkv=1), UNS),
+        (dict(dtype=7, batch=0), UNS), (dict(d=96, ptrs={"q": None}), UNS),
+    ]
+    for kw, status in cases:
+        assert _noalloc(**kw) == status, kw
+        assert _paged(**kw) == status, kw
+    big = dict(batch=2048, hq=64, hkv=8, d=256, used=0)
+    assert fad.fa_decode_workspace_size(2048, 64, 8, 256, 16, 0) > fad.FA_NOALLOC_SCRATCH_BYTES
+    assert _noalloc(**big) == WS
+
+
 def test_paged_workspace_exact_boundary():
     need = fad.fa_decode_workspace_size(2, 8, 2, 128, 16, 4)
     assert _paged(ws_bytes=need - 1) == WS
