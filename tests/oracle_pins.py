@@ -280,6 +280,29 @@ def _bruteforce(rng, layout, dims, page_sizes):
                         assert abs(lse[b, h] - float(ml)) <= 1e-13 * max(1.0, abs(float(ml)))
 
 
+def pin_attend_f64_mpmath():
+    """The oracle's attention over explicit f64 rows (what a split's partial
+    is) against the 50-digit evaluation of the definition, on random
+    double-precision rows of assorted lengths, head dims and scales; no rows
+    gives o = 0 and lse = -inf."""
+    rng = np.random.default_rng(29)
+    for trial in range(40):
+        d = int(rng.choice([1, 2, 3, 8, 16]))
+        L = int(rng.integers(1, 9))
+        q = rng.standard_normal(d) * 1.5
+        k = rng.standard_normal((L, d)) * 1.5
+        v = rng.standard_normal((L, d)) * float(rng.choice([0.25, 1.0, 4.0]))
+        scale = float(rng.uniform(0.05, 2.0))
+        o, lse = O.attend_f64(q, k, v, scale)
+        mo, ml = _mp_attend(q.tolist(), k.tolist(), v.tolist(), scale)
+        for dd in range(d):
+            ref = float(mo[dd])
+            assert abs(o[dd] - ref) <= 1e-13 * max(1.0, abs(ref)), (trial, dd)
+        assert abs(lse - float(ml)) <= 1e-13 * max(1.0, abs(float(ml))), trial
+    o, lse = O.attend_f64(np.ones(4), np.zeros((0, 4)), np.zeros((0, 4)), 0.5)
+    assert np.all(o == 0.0) and np.isneginf(lse)
+
+
 # ------------------------------------------------------------- head mapping
 
 def pin_head_mapping():

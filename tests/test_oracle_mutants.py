@@ -77,6 +77,10 @@ MUTANTS = [
     ("mask_renumbers_positions", "dist[kept++] = j - (L - 1);",
      "dist[kept] = kept - (L - 1);\n        kept++;"),
     ("validate_skips_upper_bound", "indices[i] >= num_total_pages", "indices[i] > num_total_pages"),
+    # the attention over explicit rows (a split's partial)
+    ("attend_drops_scale", "    x[j] = scale * dot;\n", "    x[j] = dot;\n"),
+    ("attend_k_transposed", "dot += q[d] * k[j * head_dim + d];", "dot += q[d] * k[d * L + j];"),
+    ("attend_v_first_row", "o[d] += w * v[j * head_dim + d];", "o[d] += w * v[d];"),
 ]
 
 
