@@ -19,7 +19,8 @@ from ._binding import (CODE_TORCH_DTYPES, DTYPE_CODES, EXPORTED, FA_DTYPE_BF16, 
                        fa_append_paged, fa_append_paged_nhd, fa_merge_states, fa_status_string,
                        load_library,
                        DecodeOptions, fa_decode_paged_opts, fa_decode_contig_opts,
-                       fa_decode_paged_noalloc, FA_NOALLOC_SCRATCH_BYTES)
+                       fa_decode_paged_noalloc, FA_NOALLOC_SCRATCH_BYTES,
+                       fa_debug_counters_in_use)
 
 
 def _code(t):

@@ -35,7 +35,7 @@ EXPORTED = ("fa_decode_workspace_size", "fa_decode_contig", "fa_decode_paged",
             "fa_merge_states", "fa_status_string",
             "fa_debug_gather_paged", "fa_debug_gather_paged_nhd", "fa_debug_timing_enable",
             "fa_debug_timing_read", "fa_debug_plan", "fa_debug_schedule",
-            "fa_debug_read_probe")
+            "fa_debug_read_probe", "fa_debug_counters_in_use")
 
 
 class DecodeOptions(ctypes.Structure):
@@ -110,6 +110,8 @@ def load_library():
     lib.fa_debug_plan.restype = _I
     lib.fa_debug_schedule.argtypes = [_I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I64, _P]
     lib.fa_debug_schedule.restype = _I
+    lib.fa_debug_counters_in_use.argtypes = [_I, _I, _I, _I, _I, _I, _P, _SZ, _P, _P]
+    lib.fa_debug_counters_in_use.restype = _I
     lib.fa_debug_read_probe.argtypes = [_P, _SZ, _P, _P]
     lib.fa_debug_read_probe.restype = _I
     _lib = lib
@@ -355,6 +357,19 @@ def fa_debug_schedule(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_s
         _dev_buf(indptr, "indptr", batch + 1, torch.int32),
         _dev_buf(last_page_len, "last_page_len", batch, torch.int32),
         out.data_ptr(), out.numel(), _stream(stream)))
+
+
+def fa_debug_counters_in_use(batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                             total_used_pages, workspace, stream=None):
+    """How many of the workspace's counters a paged call of these dimensions
+    uses were left part counted (synchronises the stream to read the answer)."""
+    lib = load_library()
+    ws_ptr, ws_bytes = _workspace(workspace, None)
+    out = torch.zeros(1, dtype=torch.int32, device=workspace.device)
+    _check("fa_debug_counters_in_use", lib.fa_debug_counters_in_use(
+        batch, num_qo_heads, num_kv_heads, head_dim, page_size, total_used_pages, ws_ptr,
+        ws_bytes, out.data_ptr(), _stream(stream)))
+    return int(out.item())
 
 
 def fa_debug_read_probe(buf, sink, stream=None):

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_limits.hpp"
+
 namespace fa {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -94,14 +96,8 @@ struct DecodeParams {
 // by the first unit that meets it, so the workspace needs no clearing.  The
 // mark's upper 32 bits are a NaN with a payload no arithmetic produces, so
 // left-over partial results (finite floats) never look like a counter.
-constexpr int kCountBits = 24;  // a request has fewer than 2^24 split units
 constexpr unsigned long long kArrivalMark = 0x7FF3A5C35Aull;  // 40 bits
 
-// 64-bit words from one arrival counter to the next: 128 bytes, one cache line
-// each.  Atomics on one line are serialised where they are performed, and the
-// units of one request finish close together, so counters that shared a line
-// queued behind each other (a 16-unit request on 8 head blocks: 128 atomics).
-constexpr int kArrivalStride = 16;
 
 // Query heads a decode workgroup serves at most (two 16-column head blocks):
 // the split merge keeps a maximum and a normaliser per head in LDS.

@@ -1,13 +1,12 @@
-// fa_decode.hip -- the C ABI of the decode library: argument checks, the
-// launch plan, workspace carve-up and kernel dispatch.  See include/fa_decode.h.
+// fa_decode.hip -- the C ABI of the decode library: workspace carve-up, kernel
+// dispatch and the entry points (argument checks and the launch plan are in
+// fa_plan.hpp).  See include/fa_decode.h.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <array>
 #include <atomic>
-#include <cmath>
 #include <cstdint>
-#include <initializer_list>
 #include <mutex>
 #include <vector>
 
@@ -16,98 +15,13 @@
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
 #include "fa_mfma.hpp"
+#include "fa_plan.hpp"
 
 namespace {
 
 using fa::DecodeParams;
 
-// Split sizing: aim for about this many decode workgroups per call, so the
-// 256 CUs each get several and the tail is short.
-constexpr int64_t kTargetWorkgroups = 1024;
-constexpr int64_t kChunkQuantum = 128;  // KV rows; a multiple of every tile (32 rows)
-constexpr int64_t kMaxChunk = int64_t(1) << 30;
-constexpr size_t kAlign = 256;
-
-size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
-
-// The attention kernel of a call: 1, the matrix-core kernel, for every element
-// type and head dim (the value fa_debug_plan reports).
-constexpr int kKernelMfma = 1;
-
-struct HostPlan {
-  int group = 0, gt = 0, nb = 1, n_gblocks = 0, planes = 0;
-  int chunk = 0, units_bound = 0, kind = 0;
-  // workspace byte offsets
-  size_t part_lse = 0, part_o = 0, arrivals = 0, tickets = 0, total = 0;
-};
-
-bool extents_ok(int batch, int hq, int hkv, int page_size) {
-  return batch > 0 && hq > 0 && hkv > 0 && page_size > 0 && hq % hkv == 0;
-}
-
-bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
-
-// grid.y is Hkv * (workgroups per KV head) and must stay within the launch limit
-bool grid_ok(int hq, int hkv) { return hq / hkv > 0 && hkv * (hq / hkv) <= 65535; }
-
-// The plan for a call; `page_size` is max_kv_len and total_used_pages 1 for a
-// contiguous cache.  Pure host arithmetic.
-HostPlan make_plan(fa_dtype_t dt, int batch, int hq, int hkv, int d, int page_size,
-                   int total_used_pages, bool contig) {
-  HostPlan hp;
-  hp.kind = kKernelMfma;
-  hp.group = hq / hkv;
-  // Head blocks: the whole group when it fits the 16-column MFMA block (one
-  // workgroup per split unit and KV head); else blocks of 16 with a shorter
-  // last one, two per workgroup, so K/V are read once per 32 query heads.
-  if (hp.group <= 16) {
-    hp.gt = hp.group;
-    hp.nb = 1;
-  } else {
-    hp.gt = 16;
-    hp.nb = 2;
-  }
-  hp.n_gblocks = (hp.group + hp.gt * hp.nb - 1) / (hp.gt * hp.nb);
-  hp.planes = hkv * hp.n_gblocks;
-  // The split size depends on the KV heads only (not on the kernel's head
-  // blocking), so the workspace size is the same for every element type.
-  const int64_t rows_ub = int64_t(std::max(total_used_pages, 0)) * page_size;
-  int64_t want = (rows_ub * hkv + kTargetWorkgroups - 1) / kTargetWorkgroups;
-  want = std::max<int64_t>(want, kChunkQuantum);
-  int64_t chunk = (want + kChunkQuantum - 1) / kChunkQuantum * kChunkQuantum;
-  chunk = std::min(chunk, kMaxChunk);
-  if (!contig && page_size % 16 == 0) {
-    // the matrix-core kernel stages a unit's page ids in LDS: at most 1024
-    // whole pages per unit (plus a partial page at each end)
-    static_assert(1024 + 2 <= fa::kPageTable, "page table slice");
-    const int64_t cap = std::max<int64_t>(
-        kChunkQuantum, 1024 * int64_t(page_size) / kChunkQuantum * kChunkQuantum);
-    chunk = std::min(chunk, cap);
-  }
-  hp.chunk = int(chunk);
-  // Units: a request of L rows has max(1, ceil(L / chunk)) of them, which is at
-  // most 1 + floor(L / chunk); summed, at most batch + floor(sum L / chunk).
-  if (contig)
-    hp.units_bound = int(std::max<int64_t>(1, (int64_t(page_size) + chunk - 1) / chunk));
-  else
-    hp.units_bound = int(batch + rows_ub / chunk);
-  size_t off = 0;
-  hp.part_lse = off;    off = align_up(off + sizeof(float) * size_t(hp.units_bound) * hq);
-  hp.part_o = off;      off = align_up(off + sizeof(float) * size_t(hp.units_bound) * hq * d);
-  // one counter line per (request, head block); Hq per request bounds the blocks
-  hp.arrivals = off;
-  off = align_up(off + sizeof(uint64_t) * fa::kArrivalStride * size_t(batch) * hq);
-  // and one line for the counter that hands out work items past the first round
-  hp.tickets = off;
-  off = align_up(off + sizeof(uint64_t) * fa::kArrivalStride);
-  hp.total = off;
-  return hp;
-}
-
-// Work indices (split units times head blocks) must fit a launch and an int.
-bool launch_ok(const HostPlan &hp) {
-  return int64_t(hp.units_bound) * hp.planes < (int64_t(1) << 31);
-}
+using namespace fa_plan;
 
 void carve(DecodeParams &p, const HostPlan &hp, void *ws) {
   char *w = static_cast<char *>(ws);
@@ -234,32 +148,6 @@ hipError_t dispatch_decode(fa_dtype_t dt, const DecodeParams &p, const HostPlan 
   }
 }
 
-bool dtype_ok(fa_dtype_t dt) {
-  return dt == FA_DTYPE_F32 || dt == FA_DTYPE_F16 || dt == FA_DTYPE_BF16;
-}
-
-// The kernels move q, K, V, o and workspace data 16 bytes per access and
-// int32 / f32 arrays 4 bytes per access; row strides (D * element size >= 128
-// bytes) keep every row at the alignment of its base.  NULL counts as aligned.
-bool aligned(const void *ptr, uintptr_t a) {
-  return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0;
-}
-
-bool all_aligned(std::initializer_list<const void *> wide,
-                 std::initializer_list<const void *> narrow) {
-  for (const void *ptr : wide)
-    if (!aligned(ptr, 16)) return false;
-  for (const void *ptr : narrow)
-    if (!aligned(ptr, 4)) return false;
-  return true;
-}
-
-// Elements of a [pages, Hkv, P, D] pool must stay far inside int64 offsets.
-bool pool_size_ok(int pages, int hkv, int page_size, int d) {
-  const double n = double(pages) * hkv * page_size * d;
-  return n < 1.0e15;
-}
-
 DecodeParams base_params(int batch, int hq, int hkv, int d, int page_size, int pages,
                          int total_used_pages, float scale, const HostPlan &hp) {
   DecodeParams p{};
@@ -283,34 +171,6 @@ DecodeParams base_params(int batch, int hq, int hkv, int d, int page_size, int p
 }
 
 
-// Layout and score variants of one call (fa_decode_options_t, validated).
-struct Variant {
-  int nhd = 0;
-  int window = 0;
-  float softcap = 0.0f;
-  const float *alibi = nullptr;
-  const uint8_t *mask = nullptr;
-  uint32_t mask_bytes = 0;
-};
-
-// FA_OK, or why opts is rejected; fills v.
-fa_status_t read_options(const fa_decode_options_t *opts, Variant &v) {
-  if (!opts) return FA_OK;
-  if (opts->kv_layout != 0 && opts->kv_layout != 1) return FA_ERR_UNSUPPORTED;
-  if (opts->window < 0 || !(opts->logits_soft_cap >= 0.0f) ||
-      !std::isfinite(opts->logits_soft_cap) || !aligned(opts->alibi_slopes, 4) ||
-      (opts->custom_mask && opts->custom_mask_bytes == 0))
-    return FA_ERR_INVALID_PROBLEM;
-  v.nhd = opts->kv_layout;
-  v.window = opts->window;
-  v.softcap = opts->logits_soft_cap;
-  v.alibi = opts->alibi_slopes;
-  v.mask = opts->custom_mask;
-  // rows are int-indexed, so no bit past 2^31 is ever asked for
-  v.mask_bytes = uint32_t(std::min<size_t>(opts->custom_mask_bytes, size_t(1) << 28));
-  return FA_OK;
-}
-
 void apply_variant(DecodeParams &p, const Variant &v) {
   p.nhd = v.nhd;
   p.window = v.window;
@@ -328,21 +188,15 @@ fa_status_t decode_contig(const Variant &var, fa_dtype_t dtype, int num_qo_heads
                           float scale, const void *q, const void *k_cache, const void *v_cache,
                           void *o, float *lse, void *workspace, size_t workspace_bytes,
                           hipStream_t stream) {
-  if (!dtype_ok(dtype)) return FA_ERR_UNSUPPORTED;
-  if (!extents_ok(1, num_qo_heads, num_kv_heads, max_kv_len)) return FA_ERR_INVALID_PROBLEM;
-  if (!head_dim_ok(head_dim)) return FA_ERR_UNSUPPORTED;
-  if (!grid_ok(num_qo_heads, num_kv_heads)) return FA_ERR_UNSUPPORTED;
-  if (!q || !k_cache || !v_cache || !o) return FA_ERR_INVALID_PROBLEM;
-  if (!all_aligned({q, k_cache, v_cache, o, workspace}, {lse})) return FA_ERR_INVALID_PROBLEM;
-  if (valid_kv_len < 0 || valid_kv_len > max_kv_len) return FA_ERR_INVALID_PROBLEM;
-  if (!pool_size_ok(1, num_kv_heads, max_kv_len, head_dim)) return FA_ERR_UNSUPPORTED;
-  const size_t need =
-      fa_decode_workspace_size(1, num_qo_heads, num_kv_heads, head_dim, max_kv_len, 1);
+  const fa_status_t st = contig_checks(dtype, num_qo_heads, num_kv_heads, head_dim, max_kv_len,
+                                       valid_kv_len, q, k_cache, v_cache, o, lse, workspace);
+  if (st != FA_OK) return st;
+  const size_t need = workspace_size(1, num_qo_heads, num_kv_heads, head_dim, max_kv_len, 1);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
 
   // Sized like the workspace query (a single page of max_kv_len rows) so the
   // split units fit what the caller allocated.
-  const HostPlan hp = make_plan(dtype, 1, num_qo_heads, num_kv_heads, head_dim, max_kv_len, 1,
+  const HostPlan hp = make_plan(1, num_qo_heads, num_kv_heads, head_dim, max_kv_len, 1,
                                 /*contig=*/true);
   DecodeParams p = base_params(1, num_qo_heads, num_kv_heads, head_dim, max_kv_len, 1, 1,
                                scale, hp);
@@ -370,34 +224,6 @@ fa_status_t decode_contig(const Variant &var, fa_dtype_t dtype, int num_qo_heads
   return FA_OK;
 }
 
-// Every check of a paged call that comes before the workspace check, in the
-// documented order (the workspace pointer's alignment included).
-fa_status_t paged_checks(fa_dtype_t dtype, int batch, int num_qo_heads, int num_kv_heads,
-                         int head_dim, int page_size, int num_total_pages, int total_used_pages,
-                         const void *q, const void *k_data, const void *v_data,
-                         const int32_t *indices, const int32_t *indptr,
-                         const int32_t *last_page_len, const void *o, const float *lse,
-                         const void *workspace) {
-  if (!dtype_ok(dtype)) return FA_ERR_UNSUPPORTED;
-  if (!extents_ok(batch, num_qo_heads, num_kv_heads, page_size) || num_total_pages <= 0)
-    return FA_ERR_INVALID_PROBLEM;
-  if (!head_dim_ok(head_dim)) return FA_ERR_UNSUPPORTED;
-  if (total_used_pages < 0) return FA_ERR_INVALID_PROBLEM;
-  if (!grid_ok(num_qo_heads, num_kv_heads)) return FA_ERR_UNSUPPORTED;
-  if (!q || !k_data || !v_data || !indptr || !last_page_len || !o || !lse ||
-      (!indices && total_used_pages > 0))
-    return FA_ERR_INVALID_PROBLEM;
-  if (!all_aligned({q, k_data, v_data, o, workspace}, {indices, indptr, last_page_len, lse}))
-    return FA_ERR_INVALID_PROBLEM;
-  if (int64_t(total_used_pages) * page_size >= (int64_t(1) << 31)) return FA_ERR_UNSUPPORTED;
-  if (!pool_size_ok(num_total_pages, num_kv_heads, page_size, head_dim))
-    return FA_ERR_UNSUPPORTED;
-  const HostPlan hp = make_plan(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
-                                total_used_pages, false);
-  if (!launch_ok(hp)) return FA_ERR_UNSUPPORTED;
-  return FA_OK;
-}
-
 fa_status_t decode_paged(const Variant &var, fa_dtype_t dtype, int batch, int num_qo_heads,
                          int num_kv_heads, int head_dim, int page_size, int num_total_pages,
                          int total_used_pages, float sm_scale, const void *q,
@@ -409,10 +235,10 @@ fa_status_t decode_paged(const Variant &var, fa_dtype_t dtype, int batch, int nu
                                       page_size, num_total_pages, total_used_pages, q, k_data,
                                       v_data, indices, indptr, last_page_len, o, lse, workspace);
   if (st != FA_OK) return st;
-  const HostPlan hp = make_plan(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+  const HostPlan hp = make_plan(batch, num_qo_heads, num_kv_heads, head_dim, page_size,
                                 total_used_pages, false);
-  const size_t need = fa_decode_workspace_size(batch, num_qo_heads, num_kv_heads, head_dim,
-                                               page_size, total_used_pages);
+  const size_t need = workspace_size(batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                                     total_used_pages);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
 
   DecodeParams p = base_params(batch, num_qo_heads, num_kv_heads, head_dim, page_size,
@@ -441,21 +267,11 @@ fa_status_t append_paged(int nhd, fa_dtype_t dtype, int batch, int num_kv_heads,
                          const void *k_new, const void *v_new, const int32_t *indices,
                          const int32_t *indptr, const int32_t *last_page_len, void *k_data,
                          void *v_data, hipStream_t stream) {
-  if (!dtype_ok(dtype)) return FA_ERR_UNSUPPORTED;
-  if (!extents_ok(batch, num_kv_heads, num_kv_heads, page_size) || num_total_pages <= 0)
-    return FA_ERR_INVALID_PROBLEM;
-  if (!head_dim_ok(head_dim)) return FA_ERR_UNSUPPORTED;
-  if (total_used_pages < 0) return FA_ERR_INVALID_PROBLEM;
-  if (!k_new || !v_new || !indptr || !last_page_len || !k_data || !v_data ||
-      (!indices && total_used_pages > 0))
-    return FA_ERR_INVALID_PROBLEM;
-  if (!all_aligned({k_new, v_new, k_data, v_data}, {indices, indptr, last_page_len}))
-    return FA_ERR_INVALID_PROBLEM;
-  if (int64_t(total_used_pages) * page_size >= (int64_t(1) << 31)) return FA_ERR_UNSUPPORTED;
-  if (!pool_size_ok(num_total_pages, num_kv_heads, page_size, head_dim))
-    return FA_ERR_UNSUPPORTED;
-  if (int64_t(batch) * num_kv_heads >= (int64_t(1) << 31)) return FA_ERR_UNSUPPORTED;
-  const HostPlan hp = make_plan(dtype, batch, num_kv_heads, num_kv_heads, head_dim, page_size,
+  const fa_status_t st = append_checks(dtype, batch, num_kv_heads, head_dim, page_size,
+                                       num_total_pages, total_used_pages, k_new, v_new,
+                                       indices, indptr, last_page_len, k_data, v_data);
+  if (st != FA_OK) return st;
+  const HostPlan hp = make_plan(batch, num_kv_heads, num_kv_heads, head_dim, page_size,
                                 total_used_pages, false);
   DecodeParams p = base_params(batch, num_kv_heads, num_kv_heads, head_dim, page_size,
                                num_total_pages, total_used_pages, 1.0f, hp);
@@ -471,41 +287,63 @@ fa_status_t append_paged(int nhd, fa_dtype_t dtype, int batch, int num_kv_heads,
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+// The gather hook runs the decode kernel's own tile loads (gather_tiles_kernel),
+// with the same workgroup size and split units as the decode launch.
+template <class E, int D>
+hipError_t launch_gather(const DecodeParams &p, const HostPlan &hp, void *out, int64_t out_rows,
+                         hipStream_t s) {
+  const dim3 grid(unsigned(hp.units_bound) * unsigned(hp.planes));
+  const dim3 block(fa::MfmaGeom<E, D>::NW * 64);
+  char *dst = static_cast<char *>(out);
+  if (p.nhd)
+    hipLaunchKernelGGL((fa::gather_tiles_kernel<E, D, true>), grid, block, 0, s, p, dst,
+                       out_rows);
+  else
+    hipLaunchKernelGGL((fa::gather_tiles_kernel<E, D, false>), grid, block, 0, s, p, dst,
+                       out_rows);
+  return hipGetLastError();
+}
+
+template <class E>
+hipError_t launch_gather_dim(const DecodeParams &p, const HostPlan &hp, void *out,
+                             int64_t out_rows, hipStream_t s) {
+  switch (p.head_dim) {
+    case 64: return launch_gather<E, 64>(p, hp, out, out_rows, s);
+    case 128: return launch_gather<E, 128>(p, hp, out, out_rows, s);
+    default: return launch_gather<E, 256>(p, hp, out, out_rows, s);
+  }
+}
+
 fa_status_t gather_paged(int nhd, fa_dtype_t dtype, int batch, int num_kv_heads, int head_dim,
                          int page_size, int num_total_pages, int total_used_pages,
                          const void *data, const int32_t *indices, const int32_t *indptr,
                          const int32_t *last_page_len, void *out, int64_t out_rows,
                          void *workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (!dtype_ok(dtype)) return FA_ERR_UNSUPPORTED;
-  if (!extents_ok(batch, num_kv_heads, num_kv_heads, page_size) || num_total_pages <= 0)
-    return FA_ERR_INVALID_PROBLEM;
-  if (!head_dim_ok(head_dim)) return FA_ERR_UNSUPPORTED;
-  if (total_used_pages < 0 || out_rows < 0) return FA_ERR_INVALID_PROBLEM;
-  if (!data || !indptr || !last_page_len || !out || (!indices && total_used_pages > 0))
-    return FA_ERR_INVALID_PROBLEM;
-  if (!all_aligned({data, out, workspace}, {indices, indptr, last_page_len}))
-    return FA_ERR_INVALID_PROBLEM;
-  if (int64_t(total_used_pages) * page_size >= (int64_t(1) << 31)) return FA_ERR_UNSUPPORTED;
-  if (!pool_size_ok(num_total_pages, num_kv_heads, page_size, head_dim))
-    return FA_ERR_UNSUPPORTED;
-  const size_t need = fa_decode_workspace_size(batch, num_kv_heads, num_kv_heads, head_dim,
-                                               page_size, total_used_pages);
+  const fa_status_t st = gather_checks(dtype, batch, num_kv_heads, head_dim, page_size,
+                                       num_total_pages, total_used_pages, data, indices,
+                                       indptr, last_page_len, out, out_rows, workspace);
+  if (st != FA_OK) return st;
+  const size_t need = workspace_size(batch, num_kv_heads, num_kv_heads, head_dim, page_size,
+                                     total_used_pages);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE_TOO_SMALL;
-  const HostPlan hp = make_plan(dtype, batch, num_kv_heads, num_kv_heads, head_dim, page_size,
+  const HostPlan hp = make_plan(batch, num_kv_heads, num_kv_heads, head_dim, page_size,
                                 total_used_pages, false);
   DecodeParams p = base_params(batch, num_kv_heads, num_kv_heads, head_dim, page_size,
                                num_total_pages, total_used_pages, 1.0f, hp);
   p.k = data;
+  p.v = data;
   p.indices = indices;
   p.indptr = indptr;
   p.last_page_len = last_page_len;
   p.nhd = nhd;
   carve(p, hp, workspace);
-  const int elem = dtype == FA_DTYPE_F32 ? 4 : 2;
-  hipLaunchKernelGGL(fa::gather_kernel, dim3(hp.units_bound, num_kv_heads), dim3(256), 0,
-                     stream, p, out, out_rows, elem);
-  if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
-  return FA_OK;
+  hipError_t e;
+  switch (dtype) {
+    case FA_DTYPE_F32: e = launch_gather_dim<fa::F32>(p, hp, out, out_rows, stream); break;
+    case FA_DTYPE_F16: e = launch_gather_dim<fa::F16>(p, hp, out, out_rows, stream); break;
+    default: e = launch_gather_dim<fa::BF16>(p, hp, out, out_rows, stream); break;
+  }
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 template <class E>
@@ -521,13 +359,10 @@ hipError_t launch_merge_states(const float *o_parts, const float *lse_parts, voi
 fa_status_t merge_states(fa_dtype_t dtype, int num_rows, int num_parts, int head_dim,
                          const float *o_parts, const float *lse_parts, void *o, float *lse,
                          hipStream_t stream) {
-  if (!dtype_ok(dtype)) return FA_ERR_UNSUPPORTED;
-  if (num_rows < 0 || num_parts <= 0) return FA_ERR_INVALID_PROBLEM;
-  if (!head_dim_ok(head_dim)) return FA_ERR_UNSUPPORTED;
-  if (num_rows == 0) return FA_OK;
-  if (!o_parts || !lse_parts || !o) return FA_ERR_INVALID_PROBLEM;
-  if (!all_aligned({o_parts, o}, {lse_parts, lse})) return FA_ERR_INVALID_PROBLEM;
-  if (double(num_parts) * num_rows * head_dim >= 1.0e15) return FA_ERR_UNSUPPORTED;
+  bool empty = false;
+  const fa_status_t st = merge_checks(dtype, num_rows, num_parts, head_dim, o_parts, lse_parts,
+                                      o, lse, &empty);
+  if (st != FA_OK || empty) return st;
   hipError_t e;
   switch (dtype) {
     case FA_DTYPE_F32:
@@ -589,13 +424,8 @@ extern "C" {
 
 size_t fa_decode_workspace_size(int batch, int num_qo_heads, int num_kv_heads, int head_dim,
                                 int page_size, int total_used_pages) {
-  if (!extents_ok(batch, num_qo_heads, num_kv_heads, page_size) || !head_dim_ok(head_dim) ||
-      total_used_pages < 0)
-    return 0;
-  if (int64_t(total_used_pages) * page_size >= (int64_t(1) << 31)) return 0;
-  return make_plan(FA_DTYPE_BF16, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
-                   total_used_pages, false)
-      .total;
+  return workspace_size(batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                        total_used_pages);
 }
 
 fa_status_t fa_append_paged(fa_dtype_t dtype, int batch, int num_kv_heads, int head_dim,
@@ -671,8 +501,8 @@ fa_status_t fa_decode_paged_noalloc(fa_dtype_t dtype, int batch, int num_qo_head
                                       page_size, num_total_pages, total_used_pages, q, k_data,
                                       v_data, indices, indptr, last_page_len, o, lse, nullptr);
   if (st != FA_OK) return st;
-  const size_t need = fa_decode_workspace_size(batch, num_qo_heads, num_kv_heads, head_dim,
-                                               page_size, total_used_pages);
+  const size_t need = workspace_size(batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+                                     total_used_pages);
   if (need > size_t(FA_NOALLOC_SCRATCH_BYTES)) return FA_ERR_WORKSPACE_TOO_SMALL;
   void *ws = scratch_address();
   if (!ws) return FA_ERR_LAUNCH;
@@ -762,15 +592,39 @@ fa_status_t fa_debug_schedule(fa_dtype_t dtype, int batch, int num_qo_heads, int
   if (total_used_pages < 0) return FA_ERR_INVALID_PROBLEM;
   if (!indptr || !last_page_len || !out) return FA_ERR_INVALID_PROBLEM;
   if (!all_aligned({}, {indptr, last_page_len, out})) return FA_ERR_INVALID_PROBLEM;
-  if (int64_t(total_used_pages) * page_size >= (int64_t(1) << 31)) return FA_ERR_UNSUPPORTED;
-  const HostPlan hp = make_plan(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+  if (!grid_ok(num_qo_heads, num_kv_heads) || !rows_ok(total_used_pages, page_size))
+    return FA_ERR_UNSUPPORTED;
+  const HostPlan hp = make_plan(batch, num_qo_heads, num_kv_heads, head_dim, page_size,
                                 total_used_pages, false);
+  if (!launch_ok(hp)) return FA_ERR_UNSUPPORTED;
   if (out_entries < 8 * int64_t(hp.units_bound)) return FA_ERR_WORKSPACE_TOO_SMALL;
   DecodeParams p = base_params(batch, num_qo_heads, num_kv_heads, head_dim, page_size, 1,
                                total_used_pages, 1.0f, hp);
   p.indptr = indptr;
   p.last_page_len = last_page_len;
   hipLaunchKernelGGL(fa::schedule_kernel, dim3(hp.units_bound), dim3(256), 0, stream, p, out);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+fa_status_t fa_debug_counters_in_use(int batch, int num_qo_heads, int num_kv_heads,
+                                     int head_dim, int page_size, int total_used_pages,
+                                     const void *workspace, size_t workspace_bytes,
+                                     int32_t *out, hipStream_t stream) {
+  if (!extents_ok(batch, num_qo_heads, num_kv_heads, page_size) || total_used_pages < 0)
+    return FA_ERR_INVALID_PROBLEM;
+  if (!head_dim_ok(head_dim)) return FA_ERR_UNSUPPORTED;
+  if (!out || !all_aligned({workspace}, {out})) return FA_ERR_INVALID_PROBLEM;
+  if (!grid_ok(num_qo_heads, num_kv_heads) || !rows_ok(total_used_pages, page_size))
+    return FA_ERR_UNSUPPORTED;
+  const HostPlan hp = make_plan(batch, num_qo_heads, num_kv_heads, head_dim,
+                                page_size, total_used_pages, false);
+  if (!launch_ok(hp)) return FA_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < hp.total) return FA_ERR_WORKSPACE_TOO_SMALL;
+  const char *w = static_cast<const char *>(workspace);
+  hipLaunchKernelGGL(fa::counter_check_kernel, dim3(1), dim3(256), 0, stream,
+                     reinterpret_cast<const uint64_t *>(w + hp.arrivals),
+                     int64_t(batch) * num_qo_heads,
+                     reinterpret_cast<const uint64_t *>(w + hp.tickets), out);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -821,7 +675,7 @@ fa_status_t fa_debug_plan(fa_dtype_t dtype, int batch, int num_qo_heads, int num
   if (!extents_ok(batch, num_qo_heads, num_kv_heads, page_size) || total_used_pages < 0)
     return FA_ERR_INVALID_PROBLEM;
   if (!head_dim_ok(head_dim)) return FA_ERR_UNSUPPORTED;
-  const HostPlan hp = make_plan(dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+  const HostPlan hp = make_plan(batch, num_qo_heads, num_kv_heads, head_dim, page_size,
                                 total_used_pages, false);
   if (chunk_rows) *chunk_rows = hp.chunk;
   if (units_bound) *units_bound = hp.units_bound;

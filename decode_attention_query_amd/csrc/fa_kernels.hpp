@@ -1,5 +1,5 @@
-// fa_kernels.hpp -- split-unit schedule, LSE merge, and the append, gather,
-// schedule and read-probe kernels.
+// fa_kernels.hpp -- split-unit schedule, LSE merge, and the append,
+// standalone-merge, schedule and read-probe kernels.
 //
 // Work decomposition (all kernels): a *split unit* is one request's KV rows
 // [c * chunk, min(L_b, (c + 1) * chunk)).  A decode workgroup handles one split
@@ -56,16 +56,11 @@ struct Request {
   int L, full, part, p0, lo, start;
 };
 
-// L_b and the unit counts of request b (zeros past the batch).  The page table
-// is clamped so a table that breaks its contract cannot send a kernel outside
-// the buffers.
-__device__ inline Request request_of(const DecodeParams &p, int b) {
-  const int bb = min(b, p.batch - 1);  // loads stay in bounds
-  const int T = p.total_used_pages;
-  const int i0 = p.indptr[bb], i1 = p.indptr[bb + 1], lpl_raw = p.last_page_len[bb];
+// L_b and the unit counts of a request whose pages are indices[p0 .. p0 + n)
+// and whose last page holds lpl_raw rows (clamped to [0, P]).
+__device__ inline Request make_request(const DecodeParams &p, int p0, int n, int lpl_raw) {
   Request r;
-  r.p0 = min(max(i0, 0), T);
-  const int n = min(max(i1, r.p0), T) - r.p0;
+  r.p0 = p0;
   const int lpl = min(max(lpl_raw, 0), p.page_size);
   r.L = n == 0 ? 0 : (n - 1) * p.page_size + lpl;  // < 2^31: the host checks T * P
   r.start = (p.window > 0 && r.L > p.window) ? r.L - p.window : 0;
@@ -73,8 +68,29 @@ __device__ inline Request request_of(const DecodeParams &p, int b) {
   const int rows = r.L - r.lo;  // rows the units cover
   r.full = rows / p.chunk;
   r.part = (rows % p.chunk != 0 || rows == 0) ? 1 : 0;  // an empty request is one empty unit
-  if (b >= p.batch) r = Request{0, 0, 0, 0, 0, 0};
   return r;
+}
+
+// Request b on its own (the append kernel): its page range clamped into
+// [0, T], so a table that breaks its contract cannot send a kernel outside
+// the buffers.
+__device__ inline Request request_of(const DecodeParams &p, int b) {
+  const int T = p.total_used_pages;
+  const int p0 = min(max(p.indptr[b], 0), T);
+  const int n = min(max(p.indptr[b + 1], p0), T) - p0;
+  return make_request(p, p0, n, p.last_page_len[b]);
+}
+
+// Inclusive prefix maximum over the 64 lanes of a wave, for x >= 0 (lanes
+// shifted in from outside a row read 0), by the steps of wave_incl_scan.
+__device__ inline int wave_incl_max(int x) {
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true));   // row_shr:1
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true));   // row_shr:2
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true));   // row_shr:4
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true));   // row_shr:8
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return x;
 }
 
 // Length class of a request's last unit, -1 if it has none (chunk is a
@@ -124,11 +140,31 @@ __device__ bool find_unit(const DecodeParams &p, int w, UnitInfo &u) {
   constexpr int kGroup = kRegChunks * kWave;  // requests per register group
   const int groups = (p.batch + kGroup - 1) / kGroup;
   Request rq[kRegChunks];
+  // Page ranges: with pm_b = max over k <= b of clamp(indptr[k], 0, T),
+  // request b owns indices[pm_b .. pm_{b+1}).  A table that keeps its
+  // contract (indptr non-decreasing, indptr[B] <= T) gives exactly
+  // [indptr[b], indptr[b+1]).  Any other table gets ranges that neither
+  // overlap nor leave [0, T), so the requests' split units never number more
+  // than units_bound: every unit of a request runs (no counter is left part
+  // counted) and no partial lands past the workspace.  pm_carry holds the
+  // maximum over the requests of earlier chunks; each pass starts it at 0.
+  int pm_carry = 0;
   auto load_group = [&](int g) {
+    const int T = p.total_used_pages;
 #pragma unroll
-    for (int j = 0; j < kRegChunks; ++j)
-      if ((g * kRegChunks + j) * kWave < p.batch)
-        rq[j] = request_of(p, (g * kRegChunks + j) * kWave + lane);
+    for (int j = 0; j < kRegChunks; ++j) {
+      const int b0 = (g * kRegChunks + j) * kWave;
+      if (b0 < p.batch) {
+        const int bb = min(b0 + lane, p.batch - 1);  // loads stay in bounds
+        const int c0 = min(max(p.indptr[bb], 0), T);
+        const int c1 = min(max(p.indptr[bb + 1], 0), T);
+        const int pm0 = max(pm_carry, wave_incl_max(c0));
+        const int pm1 = max(pm0, c1);
+        pm_carry = lane_value(pm1, kWave - 1);
+        rq[j] = b0 + lane < p.batch ? make_request(p, pm0, pm1 - pm0, p.last_page_len[bb])
+                                    : Request{0, 0, 0, 0, 0, 0};
+      }
+    }
   };
   auto take = [&](const Request &r, int src, int b0, int c, int n_units, int u0, int row0) {
     u.b = b0 + src;
@@ -176,6 +212,7 @@ __device__ bool find_unit(const DecodeParams &p, int w, UnitInfo &u) {
   // the lane order is the work order
   const bool resident = groups == 1;  // rq[] still holds every request
   int hist = 0;
+  pm_carry = 0;
   for (int g = 0; g < groups; ++g) {
     if (!resident) load_group(g);
 #pragma unroll
@@ -199,6 +236,7 @@ __device__ bool find_unit(const DecodeParams &p, int w, UnitInfo &u) {
   int carry_sel = 0;
   carry_units = 0;
   carry_rows = 0;
+  pm_carry = 0;
   for (int g = 0; g < groups; ++g) {
     if (!resident) load_group(g);
 #pragma unroll
@@ -617,6 +655,30 @@ __global__ __launch_bounds__(64) void append_kernel(const DecodeParams p, const 
   }
 }
 
+// --------------------------------------------------------- counter check
+//
+// Test-only: how many of a workspace's counters (n arrival counters kStride
+// words apart, then the work-ticket counter) carry the rest mark with a
+// non-zero count, i.e. were left part counted.  A call on a workspace leaves
+// every counter it used at rest; one left part counted would make the next
+// call's merge start early.  One workgroup; out[0] = the count.
+__global__ __launch_bounds__(256) void counter_check_kernel(const uint64_t *arrivals, int64_t n,
+                                                            const uint64_t *ticket,
+                                                            int32_t *out) {
+  __shared__ int s_count;
+  if (threadIdx.x == 0) s_count = 0;
+  __syncthreads();
+  int mine = 0;
+  for (int64_t i = threadIdx.x; i <= n; i += blockDim.x) {
+    const uint64_t c = i < n ? arrivals[i * kArrivalStride] : ticket[0];
+    const uint64_t count = c & ((1ull << kCountBits) - 1);
+    mine += (c >> kCountBits) == kArrivalMark && count != 0;
+  }
+  atomicAdd(&s_count, mine);
+  __syncthreads();
+  if (threadIdx.x == 0) out[0] = s_count;
+}
+
 // ------------------------------------------------------------- read probe
 //
 // Measurement only: streams a buffer of whole 8 KiB blocks with the decode
@@ -641,33 +703,6 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const char *buf, int64_
     for (int i = 0; i < kProbeBlock / 1024; ++i) acc ^= r[i].x ^ r[i].y ^ r[i].z ^ r[i].w;
   }
   if (acc == 0x9e3779b9u) sink[0] = acc;
-}
-
-// ------------------------------------------------------------ gather hook
-//
-// Test-only: copies every valid row t of one KV head of one split unit of
-// request b to out[(row0_b + t) * Hkv + kvh, :], where row0_b = L_0 + .. +
-// L_{b-1}, using kv_row_offset, the same address code as the decode kernels,
-// and the same unit schedule.  16 bytes per lane.
-__global__ __launch_bounds__(256) void gather_kernel(const DecodeParams p, void *out,
-                                                     int64_t out_rows, int elem_bytes) {
-  UnitInfo u;
-  if (!find_unit<true>(p, blockIdx.x, u)) return;
-  const int kvh = blockIdx.y;
-  const int t_begin = u.lo + u.c * p.chunk;
-  const int t_end = min(u.L, t_begin + p.chunk);
-  const int vecs = p.head_dim * elem_bytes / 16;  // 16-byte vectors per row
-  for (int idx = threadIdx.x; idx < (t_end - t_begin) * vecs; idx += blockDim.x) {
-    const int t = t_begin + idx / vecs;
-    const int vi = idx % vecs;
-    const int64_t orow = u.row0 + t;
-    if (orow >= out_rows) continue;
-    const int64_t off = kv_row_offset(p, u.page_base, kvh, t);
-    const uint4 r =
-        *reinterpret_cast<const uint4 *>(static_cast<const char *>(p.k) + off * elem_bytes + vi * 16);
-    *reinterpret_cast<uint4 *>(static_cast<char *>(out) +
-                               ((orow * p.num_kv_heads + kvh) * p.head_dim) * elem_bytes + vi * 16) = r;
-  }
 }
 
 }  // namespace fa

@@ -102,9 +102,6 @@ __device__ inline void pack_probs(const float *p, typename Mfma<E>::v8 &hi,
   }
 }
 
-// Page slots of one split unit staged in LDS (the host caps the split size so
-// a unit spans at most 1024 whole pages plus a partial one at each end).
-constexpr int kPageTable = 1040;
 
 // Waves per workgroup: four, but two at D = 256, whose K/V tiles would fill
 // 137 KB of LDS at four waves; at two, two workgroups share a compute unit, so
@@ -149,6 +146,28 @@ struct MfmaGeom {
   // soon as it is in LDS
   static constexpr bool kPipelined = D <= 128;
 };
+
+// The page ids of the unit's rows [t_begin, t_end), once, into LDS
+// (s_pages[i] = page id of page slot slot0 + i, clamped into the pool), so
+// that each tile's lookups are LDS reads instead of memory loads it would wait
+// for; returns slot0.  Only when every 16-row block lies in one page (else
+// issue_tile resolves rows itself).  The host keeps a unit within kPageTable
+// page slots.  Every thread of the workgroup calls it (it ends in a barrier).
+__device__ inline int stage_unit_pages(const DecodeParams &p, int32_t *s_pages,
+                                       int32_t page_base, int t_begin, int t_end,
+                                       int nthreads) {
+  int slot0 = 0;
+  if (p.uniform_blocks && !p.contig && t_begin < t_end) {
+    slot0 = (int)fastdiv((uint32_t)t_begin, p.page_div);
+    const int count = (int)fastdiv((uint32_t)(t_end - 1), p.page_div) - slot0 + 1;
+    for (int i = threadIdx.x; i < count; i += nthreads) {
+      const int32_t id = p.indices[page_base + slot0 + i];
+      s_pages[i] = min(max(id, 0), p.num_total_pages - 1);
+    }
+    __syncthreads();
+  }
+  return slot0;
+}
 
 // K and V of one tile as loaded: instruction i, lane l holds row
 // RPI * i + l / LPR, bytes 16 (l % LPR) .. + 16.
@@ -316,20 +335,8 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
     }
   }
 
-  // The unit's page ids, once, into LDS: later lookups are LDS reads instead
-  // of memory loads that each tile would wait for.  The host keeps a unit
-  // within kPageTable page slots.
   __shared__ int32_t s_pages[kPageTable];
-  int slot0 = 0;
-  if (p.uniform_blocks && !p.contig && t_begin < t_end) {
-    slot0 = (int)fastdiv((uint32_t)t_begin, p.page_div);
-    const int count = (int)fastdiv((uint32_t)(t_end - 1), p.page_div) - slot0 + 1;
-    for (int i = threadIdx.x; i < count; i += NW * 64) {
-      const int32_t id = p.indices[page_base + slot0 + i];
-      s_pages[i] = min(max(id, 0), p.num_total_pages - 1);
-    }
-    __syncthreads();
-  }
+  const int slot0 = stage_unit_pages(p, s_pages, page_base, t_begin, t_end, NW * 64);
 
   // ALiBi slope of head n (base-2 units): row t's score gains slope2 * (t - (L - 1))
   const float slope2 = (kMods && p.alibi && n < gt) ? p.alibi[hb + n] * kLog2e : 0.0f;
@@ -660,6 +667,49 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   // (D >= 128); 8 at D = 64, where 16 would cost occupancy
   finish_split<E, (D >= 128 ? 16 : 8)>(p, u, plane, h0, gt_wg, NW, s_stat, &s_last,
                                         reinterpret_cast<float *>(lds), G::LDS / 4);
+}
+
+// ------------------------------------------------------------ gather hook
+//
+// Test-only: the page-table gather exactly as the decode kernel performs it,
+// so a test can compare the rows the kernel loads with an independent gather
+// bit for bit.  Same work decomposition (one workgroup per split unit and KV
+// head, units from find_unit), same LDS page staging (stage_unit_pages), same
+// per-wave tile walk (tile t0 = t_begin + wave * TT, then every NW * TT rows)
+// and the same loads (issue_tile, rows past the unit clamped to its last
+// row).  Instead of computing, each wave writes the rows it loaded that lie
+// inside the unit to out[(row0_b + t) * Hkv + kvh, :], row0_b = L_0 + .. +
+// L_{b-1}.  p.k and p.v both point at the store being gathered.
+template <class E, int D, bool kNhd>
+__global__ __launch_bounds__(mfma_waves(D) * 64) void gather_tiles_kernel(const DecodeParams p,
+                                                                          char *out,
+                                                                          int64_t out_rows) {
+  using G = MfmaGeom<E, D>;
+  constexpr int NW = G::NW, TT = G::TT;
+  const int unit = blockIdx.x / p.planes;
+  const int kvh = blockIdx.x - unit * p.planes;  // one query head per KV head: planes = Hkv
+  UnitInfo u;
+  if (!find_unit<true>(p, unit, u)) return;
+  const int t_begin = __builtin_amdgcn_readfirstlane(u.lo + u.c * p.chunk);
+  const int t_end = __builtin_amdgcn_readfirstlane(min(u.L, t_begin + p.chunk));
+  const int32_t page_base = __builtin_amdgcn_readfirstlane(u.page_base);
+  __shared__ int32_t s_pages[kPageTable];
+  const int slot0 = stage_unit_pages(p, s_pages, page_base, t_begin, t_end, NW * 64);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int r0 = lane / G::LPR, col = (lane % G::LPR) * 16;
+  for (int t0 = t_begin + wave * TT; t0 < t_end; t0 += NW * TT) {
+    KVTile<G::NI> T;
+    issue_tile<E, D, kNhd>(T, p, page_base, s_pages, slot0, kvh, t0, t_end, lane);
+#pragma unroll
+    for (int i = 0; i < G::NI; ++i) {
+      const int t = t0 + G::RPI * i + r0;
+      const int64_t orow = (int64_t)u.row0 + t;
+      if (t < t_end && orow < out_rows)
+        *reinterpret_cast<uint4 *>(out + ((orow * p.num_kv_heads + kvh) * D) * E::kBytes +
+                                   col) = T.k[i];
+    }
+  }
 }
 
 }  // namespace fa

@@ -78,8 +78,8 @@ typedef enum {
  * A pure function of its arguments; it makes no device query.
  *   paged calls:       fa_decode_workspace_size(batch, Hq, Hkv, D, page_size, total_used_pages)
  *   contiguous calls:  fa_decode_workspace_size(1, Hq, Hkv, D, max_kv_len, 1)
- * Returns 0 when the arguments are not a valid problem (the entry point then
- * reports why); otherwise a positive size.  The workspace holds the split
+ * Returns 0 when the arguments are not a valid problem or one no entry point
+ * launches (the entry point then reports why); otherwise a positive size.  The workspace holds the split
  * partial results, one arrival counter per (request, head block) and one
  * counter that hands out work items to the workgroups of a launch that start
  * after its first resident round.  A counter at rest carries a fixed mark and

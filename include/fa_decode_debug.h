@@ -16,10 +16,11 @@ extern "C" {
 #endif
 
 /* Resolve a paged store through its page table (baracuda-kernels 0.0.1-alpha.68,
- * src/attention/batch_paged_decode.rs, module doc "Layout") with the same
- * row-address code the decode kernels use, and write the valid rows, as raw
- * element bits, to out laid out [sum_b L_b, Hkv, D]: request 0's rows first,
- * each request's rows in order.
+ * src/attention/batch_paged_decode.rs, module doc "Layout") exactly as the
+ * decode kernels do -- the same split units and workgroup size, the same page
+ * ids staged in LDS, the same tile loads (one KV head per workgroup) -- and
+ * write the valid rows, as raw element bits, to out laid out
+ * [sum_b L_b, Hkv, D]: request 0's rows first, each request's rows in order.
  *
  *   data           [num_total_pages, Hkv, page_size, D]  element size from dtype
  *   indices, indptr, last_page_len   as for fa_decode_paged (same contract)
@@ -28,7 +29,7 @@ extern "C" {
  *                                              total_used_pages)
  * Checks are those of fa_decode_paged that apply (dtype, extents, head_dim,
  * NULL pointers, alignment -- data, out and workspace 16 bytes, the int32
- * arrays 4 --, row range, workspace), plus out_rows < 0 ->
+ * arrays 4 --, row range, launch size, workspace), plus out_rows < 0 ->
  * FA_ERR_INVALID_PROBLEM.
  * Asynchronous on stream, like the decode calls. */
 fa_status_t fa_debug_gather_paged(fa_dtype_t dtype, int batch, int num_kv_heads, int head_dim,
@@ -43,20 +44,44 @@ fa_status_t fa_debug_gather_paged(fa_dtype_t dtype, int batch, int num_kv_heads,
  * w < units_bound (see fa_debug_plan), 8 int32 values at out[8 w .. 8 w + 7]:
  * the request b (-1 for indices past the real unit count, the rest 0), the
  * unit's index c within the request, the request's unit count, L_b, the
- * request's first partial-result slot, its page base (indptr[b], clamped),
- * and the low and high 32-bit words of L_0 + .. + L_{b-1}.
+ * request's first partial-result slot, its page base, and the low and high
+ * 32-bit words of L_0 + .. + L_{b-1}.  Request b's pages are indices[s_b ..
+ * s_{b+1}) with s_b the largest of indptr[0 .. b] clamped into [0,
+ * total_used_pages]: indptr[b] for a table that keeps its contract; for any
+ * other, ranges that do not overlap, so the units never exceed units_bound.
  *   indptr, last_page_len   as for fa_decode_paged (same contract)
  *   out                     device int32 [out_entries], at least 8 * units_bound
  * Checks: dtype, extents, head_dim and total_used_pages as fa_decode_paged;
  * indptr, last_page_len or out NULL or not 4-byte aligned ->
- * FA_ERR_INVALID_PROBLEM; rows beyond
- * the index range -> FA_ERR_UNSUPPORTED; out_entries short ->
+ * FA_ERR_INVALID_PROBLEM; more query heads, rows or work items than
+ * fa_decode_paged takes -> FA_ERR_UNSUPPORTED; out_entries short ->
  * FA_ERR_WORKSPACE_TOO_SMALL; a failed launch -> FA_ERR_LAUNCH.
  * Asynchronous on stream. */
 fa_status_t fa_debug_schedule(fa_dtype_t dtype, int batch, int num_qo_heads, int num_kv_heads,
                               int head_dim, int page_size, int total_used_pages,
                               const int32_t *indptr, const int32_t *last_page_len,
                               int32_t *out, int64_t out_entries, hipStream_t stream);
+
+/* Counters of a workspace left part counted: writes to out[0] how many of the
+ * arrival counters a paged call with these arguments uses (one per request
+ * and query head, the bound on head blocks), plus the work-ticket counter,
+ * hold the rest mark with a non-zero count.  Every decode call leaves the
+ * counters it used at rest (count 0), so after calls that ran to completion
+ * this is 0; a counter left part counted would make the next call on the
+ * workspace merge a request's partials too early.  Counters without the mark
+ * (a fresh workspace) are not counted: the next call resets them.
+ *   workspace   >= fa_decode_workspace_size(batch, Hq, Hkv, D, page_size,
+ *                                           total_used_pages) bytes
+ *   out         device int32, at least 1
+ * Extents, head_dim, total_used_pages as fa_decode_paged; out NULL or not
+ * 4-byte aligned, or workspace not 16-byte aligned -> FA_ERR_INVALID_PROBLEM;
+ * more query heads, rows or work items than fa_decode_paged takes ->
+ * FA_ERR_UNSUPPORTED; workspace NULL or short -> FA_ERR_WORKSPACE_TOO_SMALL.
+ * Asynchronous: read out after the stream reaches the call. */
+fa_status_t fa_debug_counters_in_use(int batch, int num_qo_heads, int num_kv_heads,
+                                     int head_dim, int page_size, int total_used_pages,
+                                     const void *workspace, size_t workspace_bytes,
+                                     int32_t *out, hipStream_t stream);
 
 /* Read-bandwidth probe: reads every byte of buf (device memory, bytes > 0 and a
  * multiple of 8192) once with the load shape of the attention kernels (1 KiB

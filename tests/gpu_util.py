@@ -15,15 +15,24 @@ LSE_TOL = 1e-4
 MANT_BITS = {"f32": 23, "f16": 10, "bf16": 7}
 
 
+# relative error of the f32 arithmetic before o is rounded to a 16-bit type
+# (scores, exponentials and the P.V sums in f32, bf16 probabilities split into
+# two parts): well under 2^-12 of |o|
+F32_MARGIN = 2.0 ** -12
+
+
 def o_tolerance(dtype, o_ref):
-    """Per-element bound on |o - o_ref|: the stated tolerance, or one unit in
-    the last place of the element type at |o_ref| where that is larger.  Even
-    the correctly rounded exact result is half an ulp away from o_ref, and for
-    |o| >= 1 half a bf16 ulp already exceeds 4e-3; below 1 (every configured
-    workload) the bound is the stated tolerance itself."""
+    """Per-element bound on |o - o_ref|: the stated tolerance, or, for a 16-bit
+    output where it is larger, half an ulp of the element type at |o_ref| (the
+    error of rounding even the exact result to nearest) plus the f32 margin.
+    That takes over at |o| >= 1 for bf16 (half an ulp on [1, 2) is 3.9e-3) and
+    |o| >= 8 for f16; below, the bound is the stated tolerance itself, as for
+    every output of the five configured workloads."""
+    if dtype == "f32":
+        return np.full(np.shape(o_ref), O_TOL[dtype])
     mag = np.maximum(np.abs(o_ref), np.finfo(np.float64).tiny)
-    ulp = np.exp2(np.floor(np.log2(mag)) - MANT_BITS[dtype])
-    return np.maximum(O_TOL[dtype], ulp)
+    half_ulp = np.exp2(np.floor(np.log2(mag)) - MANT_BITS[dtype] - 1)
+    return np.maximum(O_TOL[dtype], half_ulp + F32_MARGIN * mag)
 
 
 def device():
@@ -86,13 +95,47 @@ def compare(dtype, o_gpu, lse_gpu, o_ref, lse_ref, what="", strict=False):
     return err_o, err_l
 
 
-def sample_pairs(p, n, rng):
-    """(b, h) pairs: every head of the first two requests and of the longest one,
-    then random pairs, n in total at least."""
-    lens = oracle.seq_lens(p.page_size, p.indptr.numpy(), p.last_page_len.numpy())
-    picks = []
-    for b in sorted({0, min(1, p.batch - 1), int(np.argmax(lens)), p.batch - 1}):
-        picks += [(b, h) for h in range(p.num_qo_heads)]
-    while len(picks) < n:
-        picks.append((int(rng.integers(p.batch)), int(rng.integers(p.num_qo_heads))))
-    return np.array(picks, dtype=np.int32)
+def compare_all(p, o, lse, what=None, strict=True, **oracle_kw):
+    """Every (request, head) output of a call against the oracle's whole call
+    (on every host core); returns (max |do|, max |dlse|)."""
+    torch.cuda.synchronize()
+    if isinstance(p, W.PagedProblem):
+        ro, rl = oracle.decode_paged(p.dtype, W.bits(p.q), W.bits(p.k_data), W.bits(p.v_data),
+                                     p.indices.numpy(), p.indptr.numpy(),
+                                     p.last_page_len.numpy(), p.scale, layout=p.layout,
+                                     **oracle_kw)
+    else:
+        ro, rl = oracle.decode_contig(p.dtype, W.bits(p.q), W.bits(p.k_cache),
+                                      W.bits(p.v_cache), p.valid_kv_len, p.scale,
+                                      layout=p.layout, **oracle_kw)
+    return compare(p.dtype, o, lse, ro, rl, what or p.name, strict=strict)
+
+
+def check_gather(p, dev):
+    """The decode kernel's own loads of the page-table-resolved K and V rows
+    (fa_debug_gather_paged runs its split units, LDS page staging and tile
+    loads) against the oracle's gather, byte for byte."""
+    import oracle as O
+    lens = O.seq_lens(p.page_size, p.indptr.numpy(), p.last_page_len.numpy())
+    rows = int(lens.sum())
+    ws = fad.workspace_paged(p.batch, p.num_kv_heads, p.num_kv_heads, p.head_dim, p.page_size,
+                             p.total_used_pages, dev)
+    ind, ptr, lpl = p.indices.to(dev), p.indptr.to(dev), p.last_page_len.to(dev)
+    for which, data in (("k", p.k_data), ("v", p.v_data)):
+        out = torch.zeros((rows, p.num_kv_heads, p.head_dim), dtype=data.dtype, device=dev)
+        dd = data.to(dev)
+        fad.fa_debug_gather_paged(fad.DTYPE_CODES[p.dtype], p.batch, p.num_kv_heads,
+                                  p.head_dim, p.page_size, p.num_total_pages,
+                                  p.total_used_pages, dd, ind if p.total_used_pages else None,
+                                  ptr, lpl, out, rows, ws, layout=p.layout)
+        torch.cuda.synchronize()
+        del dd
+        want = O.gather_paged(p.dtype, W.bits(data), p.indices.numpy(), p.indptr.numpy(),
+                              p.last_page_len.numpy(), layout=p.layout)
+        got = W.bits(out.cpu())
+        del out
+        assert got.shape == want.shape, (p.name, which)
+        same = got.view(np.uint8).reshape(rows, -1) == want.view(np.uint8).reshape(rows, -1)
+        bad = np.nonzero(~same.all(axis=1))[0]
+        assert bad.size == 0, (f"{p.name} {which}: {bad.size} of {rows} gathered rows differ, "
+                               f"first at row {bad[0]}")

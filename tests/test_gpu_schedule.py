@@ -275,3 +275,104 @@ def test_many_unit_merge(dev, dtype, d, hq, length):
     torch.cuda.synchronize()
     ro, rl = oracle_of(p)
     compare(dtype, o, lse, ro, rl, p.name)
+
+
+# ------------------------------------------------ tables that break the contract
+
+def _broken_tables(T, batch_hint=None):
+    """(name, indptr, last_page_len offsets) of page tables that break the
+    contract: overlapping ranges, a non-monotone indptr, values outside
+    [0, T]."""
+    return [
+        ("overlap", np.array([0, T, 0, T, 0, T], dtype=np.int64)),
+        ("non-monotone", np.array([0, T // 2, T // 5, T, T // 3, T - 1, 2], dtype=np.int64)),
+        ("out-of-range", np.array([-40, 10, T + 50, 1 << 30, -(1 << 30), T], dtype=np.int64)),
+    ]
+
+
+def _envelope(indptr, T):
+    """Page range of each request as the schedule defines it for any table:
+    request b owns [s_b, s_{b+1}) with s_b = max over k <= b of
+    clamp(indptr[k], 0, T)."""
+    c = np.clip(indptr, 0, T)
+    s = np.maximum.accumulate(c)
+    return s[:-1], s[1:] - s[:-1]
+
+
+@pytest.mark.parametrize("which", [0, 1, 2], ids=["overlap", "non-monotone", "out-of-range"])
+def test_schedule_broken_table(dev, which):
+    """Whatever the table holds, every split unit of every request appears once
+    below units_bound and no request's partial slots reach past it; page
+    ranges follow the running maximum of the clamped indptr."""
+    page_size, hq, hkv, d, T = 16, 32, 8, 128, 3000
+    name, indptr = _broken_tables(T)[which]
+    batch = indptr.size - 1
+    rng = np.random.default_rng(which)
+    lpl = rng.integers(-3, page_size + 5, batch)
+    chunk, bound, _, _ = fad.fa_debug_plan(fad.FA_DTYPE_BF16, batch, hq, hkv, d, page_size, T)
+    out = torch.full((bound * 8,), 12345, dtype=torch.int32, device=dev)
+    fad.fa_debug_schedule(fad.FA_DTYPE_BF16, batch, hq, hkv, d, page_size, T,
+                          torch.from_numpy(indptr.astype(np.int32)).to(dev),
+                          torch.from_numpy(lpl.astype(np.int32)).to(dev), out)
+    got = out.cpu().numpy().reshape(bound, 8)
+    starts, n = _envelope(indptr, T)
+    lens = np.where(n > 0, (n - 1) * page_size + np.clip(lpl, 0, page_size), 0)
+    announce(f"broken table {name}: lens {lens.tolist()}, chunk {chunk}, bound {bound}")
+    assert int(n.sum()) <= T
+    seen = {}
+    for row in got:
+        b = int(row[0])
+        if b < 0:
+            continue
+        assert row[3] == lens[b] and row[5] == starts[b], (name, row.tolist())
+        assert row[4] + row[2] <= bound, (name, row.tolist())
+        seen.setdefault(b, []).append(int(row[1]))
+    for b in range(batch):
+        units = max(1, -(-int(lens[b]) // chunk))
+        assert sorted(seen.get(b, [])) == list(range(units)), (name, b)
+
+
+def test_valid_call_after_broken_table(dev):
+    """A call with a broken table (overlapping page ranges of long requests)
+    stays inside its buffers and leaves no counter part counted, so the next,
+    valid call on the same workspace equals a call on a fresh one bit for bit
+    and matches the oracle."""
+    p = _split_problem(seed=83)
+    d = to_dev(p, dev)
+    ws = fad.workspace_paged(p.batch, p.num_qo_heads, p.num_kv_heads, p.head_dim,
+                             p.page_size, p.total_used_pages, dev)
+    T = p.total_used_pages
+    for name, ptr in _broken_tables(T):
+        bad = ptr[:p.batch + 1] if ptr.size >= p.batch + 1 else \
+            np.concatenate([ptr, np.full(p.batch + 1 - ptr.size, T)])
+        announce(f"broken table {name}: indptr {bad.tolist()}")
+        bad_d = dict(d, indptr=torch.from_numpy(bad.astype(np.int32)).to(dev),
+                     lpl=torch.from_numpy(np.full(p.batch, p.page_size + 7,
+                                                  dtype=np.int32)).to(dev))
+        run(p, bad_d, workspace=ws)
+        torch.cuda.synchronize()
+        assert fad.fa_debug_counters_in_use(p.batch, p.num_qo_heads, p.num_kv_heads,
+                                            p.head_dim, p.page_size, T, ws) == 0, name
+        o, lse = run(p, d, workspace=ws)
+        ref_o, ref_l = run(p, d)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), ref_o.view(torch.int16)), name
+        assert torch.equal(lse.view(torch.int32), ref_l.view(torch.int32)), name
+    ro, rl = oracle_of(p)
+    compare(p.dtype, o, lse, ro, rl, p.name)
+
+
+def test_counters_at_rest_after_calls(dev):
+    """After split calls (eager, on garbage and on reused workspaces) no counter
+    is left part counted."""
+    p = _split_problem(seed=84)
+    d = to_dev(p, dev)
+    ws = fad.workspace_paged(p.batch, p.num_qo_heads, p.num_kv_heads, p.head_dim,
+                             p.page_size, p.total_used_pages, dev)
+    ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8))
+    args = (p.batch, p.num_qo_heads, p.num_kv_heads, p.head_dim, p.page_size,
+            p.total_used_pages)
+    for _ in range(3):
+        run(p, d, workspace=ws)
+        torch.cuda.synchronize()
+        assert fad.fa_debug_counters_in_use(*args, ws) == 0
