@@ -13,7 +13,7 @@ import decode_attention_query_amd as fad
 import oracle
 import workloads as W
 from _helpers import rand_t, scatter_paged
-from gpu_util import announce, compare, device, sample_pairs, to_dev
+from gpu_util import announce, compare, compare_all, device, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -118,19 +118,15 @@ def test_contig_variants(dev, variant):
 
 
 def test_variants_full_c3(dev):
-    """The full C3 workload with a 1000-row window and a soft-cap of 30,
-    sampled against the oracle; no window and a cap far beyond every score
+    """The full C3 workload with a 1000-row window and a soft-cap of 30, every
+    output against the oracle; no window and a cap far beyond every score
     match the plain call within the tolerance."""
     p = W.FULL["c3"]()
     announce("variants full c3")
     d = to_dev(p, dev)
     o, lse = _run(p, d, 1000, 30.0)
     torch.cuda.synchronize()
-    pairs = sample_pairs(p, 64, np.random.default_rng(8))
-    ro, rl = _oracle(p, 1000, 30.0, samples=pairs)
-    idx = (torch.from_numpy(pairs[:, 0].astype(np.int64)),
-           torch.from_numpy(pairs[:, 1].astype(np.int64)))
-    compare(p.dtype, o.cpu()[idx], lse.cpu()[idx], ro, rl, "c3 w1000 cap30", strict=True)
+    compare_all(p, o, lse, "c3 w1000 cap30", window=1000, softcap=30.0)
     o0, l0 = _run(p, d, 0, 0.0)
     o1, l1 = _run(p, d, 0, 1.0e6)
     torch.cuda.synchronize()
@@ -223,15 +219,12 @@ def test_contig_mask(dev, keep_p, blocks):
 
 
 def test_mask_full_c3(dev):
-    """The full C3 workload under a random half mask, sampled against the oracle."""
+    """The full C3 workload under a random half mask, every output against the
+    oracle."""
     p = W.FULL["c3"]()
     announce("mask full c3")
     lens = oracle.seq_lens(p.page_size, p.indptr.numpy(), p.last_page_len.numpy())
     packed = W.pack_mask(W.random_mask(13, lens, keep=0.5))
     o, lse = _run(p, to_dev(p, dev), 0, 0.0, mask=packed)
     torch.cuda.synchronize()
-    pairs = sample_pairs(p, 64, np.random.default_rng(9))
-    ro, rl = _oracle(p, 0, 0.0, samples=pairs, mask=packed)
-    idx = (torch.from_numpy(pairs[:, 0].astype(np.int64)),
-           torch.from_numpy(pairs[:, 1].astype(np.int64)))
-    compare(p.dtype, o.cpu()[idx], lse.cpu()[idx], ro, rl, "c3 mask", strict=True)
+    compare_all(p, o, lse, "c3 mask", mask=packed)
