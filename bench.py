@@ -3,15 +3,26 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3|c4|c5|c2|c1]
 
 One step is one call of the library's decode entry point over the whole batch
-(split plan, attention kernel and split merge), with inputs resident in HBM.
-Prints one JSON line.  value = algorithmic bytes per call / wall time per call
-(GB/s, 1e9 B/s), where the algorithmic bytes are the valid K and V rows, q, o,
-lse and the page table, counted once each.  roofline.achieved divides the same
-bytes by the attention kernel's own average duration, timed with HIP events the
-library records on its stream during a second run of the same steps.
-per_call gives p10 / median / p90 of single calls, each in its own event pair
-(--flush: with the caches flushed before each call).  cpu_baseline runs the
-float64 oracle on the host over the same workload.
+(one launch of the attention kernel, which also finds its split units and
+merges them), with inputs resident in HBM.  Prints one JSON line.
+
+value = algorithmic bytes per call / time per call (GB/s, 1e9 B/s) over K
+back-to-back calls bracketed by HIP events on the stream the kernel is
+launched on; the algorithmic bytes are the valid K and V rows, q, o, lse and
+the page table, counted once each.  Since a call is one kernel launch, that
+bracket also gives the kernel's average launch period (roofline.kernel_us,
+which includes the gap between back-to-back launches, so it never exceeds the
+call); roofline.trace_kernel_us is the kernel's own mean duration from the
+committed rocprofv3 trace of the same command while the kernel sources still
+hash as they did then.
+
+Also in the line, by default: per_call (p10 / median / p90 of single calls,
+each in its own event pair) unflushed and with the caches flushed before each
+call (a 512 MiB write); `rotated`, the calls cycled over 4 device copies of
+the K/V store so no call finds the previous call's rows in the last-level
+cache; hbm_probe (the library's read probe and a device copy); for the
+default workload, a sub-record for the second primary workload (C4); and
+cpu_baseline, the float64 oracle on this host's cores.
 """
 import argparse
 import json
@@ -111,9 +122,29 @@ def describe(p):
             "sum_kv_len": int(lens.sum()), "max_kv_len": int(lens.max())}
 
 
-def cpu_baseline(p, nbytes, window=0, softcap=0.0, mask=None, min_seconds=2.0, max_runs=5):
-    """The float64 oracle over the whole workload on this host's cores: whole
-    calls repeated until min_seconds have passed (at most max_runs), median."""
+def cpu_model():
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(p, nbytes, window=0, softcap=0.0, mask=None, min_seconds=10.0, max_runs=200):
+    """The float64 oracle, as it stands, over the whole workload on this host's
+    cores: whole calls repeated until min_seconds of wall time have passed (a
+    bounded sample of about 10 s), median per call."""
     import oracle
     threads = len(os.sched_getaffinity(0))
     times = []
@@ -131,9 +162,24 @@ def cpu_baseline(p, nbytes, window=0, softcap=0.0, mask=None, min_seconds=2.0, m
         times.append(time.perf_counter() - t0)
     dt = float(np.median(times))
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "seconds_per_call": round(dt, 3),
-            "sample": f"the whole {p.name} call (every request and head), "
-                      f"median of {len(times)} runs"}
+            "kind": "oracle", "cpu_model": cpu_model(), "seconds_per_call": round(dt, 3),
+            "sample": f"whole {p.name} calls (every request and head) repeated for "
+                      f"{sum(times):.1f} s: median of {len(times)} calls"}
+
+
+def trace_record(workload_name):
+    """The attention kernel's mean duration from a committed rocprofv3 kernel
+    trace of this workload (profiles/*_kernel_trace.md, line `trace-record:`),
+    or None if there is none or the kernel sources changed since."""
+    import glob
+    sha = kernel_source_sha()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_kernel_trace.md"))):
+        for line in open(path):
+            if line.startswith("trace-record:"):
+                rec = json.loads(line.split(":", 1)[1])
+                if rec.get("workload") == workload_name and rec.get("kernel_source_sha") == sha:
+                    return dict(rec, file=os.path.relpath(path, ROOT))
+    return None
 
 
 def hbm_probe(dev, nbytes=4 << 30, reps=10):
@@ -276,6 +322,106 @@ def graph_call_time(step, n_calls, reps):
     return a.elapsed_time(b) * 1e3 / (reps * n_calls)
 
 
+def timed_us(step, steps):
+    """Mean µs per call of `steps` back-to-back calls, bracketed by HIP events on
+    the current stream (the stream the library launches on)."""
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e3 / steps
+
+
+def graph_flushed_time(step, dev, n_calls, reps):
+    """Mean µs per call inside a HIP graph with the caches flushed before every
+    call: a graph of n_calls (512 MiB flush, call) pairs minus a graph of the
+    n_calls flushes alone, per call."""
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    both = graph_call_time(lambda: (scratch.fill_(1), step()), n_calls, reps)
+    flush = graph_call_time(lambda: scratch.fill_(1), n_calls, reps)
+    del scratch
+    return both - flush
+
+
+class Bench:
+    """One workload on the device: its inputs, a step (one library call), and
+    the measurements of the line."""
+
+    def __init__(self, p, dev, args, mask=None):
+        self.p, self.dev, self.args = p, dev, args
+        self.mask = mask
+        if isinstance(p, W.ContigProblem):
+            self.q, self.k, self.v = p.q.to(dev), p.k_cache.to(dev), p.v_cache.to(dev)
+            self.lse = torch.empty(p.num_qo_heads, dtype=torch.float32, device=dev)
+            self.ws = fad.workspace_paged(1, p.num_qo_heads, p.num_kv_heads, p.head_dim,
+                                          p.max_kv_len, 1, dev)
+        else:
+            self.q, self.k, self.v = p.q.to(dev), p.k_data.to(dev), p.v_data.to(dev)
+            self.ind, self.ptr = p.indices.to(dev), p.indptr.to(dev)
+            self.lpl = p.last_page_len.to(dev)
+            self.lse = torch.empty((p.batch, p.num_qo_heads), dtype=torch.float32, device=dev)
+            self.ws = fad.workspace_paged(p.batch, p.num_qo_heads, p.num_kv_heads, p.head_dim,
+                                          p.page_size, p.total_used_pages, dev)
+        self.o = torch.empty_like(self.q)
+        self.stores = [(self.k, self.v)]
+        self.turn = 0
+
+    def call(self, k, v):
+        p, a = self.p, self.args
+        if isinstance(p, W.ContigProblem):
+            fad.decode_contig(self.q, k, v, p.valid_kv_len, p.scale, o=self.o, lse=self.lse,
+                              workspace=self.ws, layout=p.layout, window=a.window,
+                              softcap=a.softcap, mask=self.mask)
+        else:
+            fad.decode_paged(self.q, k, v, self.ind, self.ptr, self.lpl, p.scale, o=self.o,
+                             lse=self.lse, workspace=self.ws, layout=p.layout, window=a.window,
+                             softcap=a.softcap, mask=self.mask)
+
+    def step(self):
+        """One call on the resident store."""
+        self.call(self.k, self.v)
+
+    def rotated_step(self):
+        """One call on the next of the store's copies."""
+        k, v = self.stores[self.turn % len(self.stores)]
+        self.turn += 1
+        self.call(k, v)
+
+    def rotated(self, copies, steps, nbytes):
+        """Back-to-back calls cycling over `copies` device copies of the K/V
+        store, so no call finds the previous call's rows in the last-level
+        cache (as successive layers of a model would)."""
+        self.stores = [(self.k, self.v)] + [(self.k.clone(), self.v.clone())
+                                            for _ in range(copies - 1)]
+        for _ in range(copies):
+            self.rotated_step()
+        us = timed_us(self.rotated_step, steps)
+        self.stores = [(self.k, self.v)]
+        torch.cuda.empty_cache()
+        return {"kv_copies": copies, "us_per_call": round(us, 2),
+                "GBps": round(nbytes / (us * 1e-6) / 1e9, 2),
+                "pct_of_hbm_peak": round(100.0 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
+
+
+def measure(b, nbytes, steps, warmup, flush, rotate):
+    """The headline measurement of a workload (warm-up, then `steps` timed calls)
+    and its per-call, flushed and rotated figures."""
+    for _ in range(warmup):
+        b.step()
+    torch.cuda.synchronize()
+    us = timed_us(b.step, steps)
+    out = {"us_per_call": us, "GBps": nbytes / (us * 1e-6) / 1e9,
+           "per_call": per_call_times(b.step, steps, b.dev, flush=False)}
+    if flush:
+        out["per_call_flushed"] = per_call_times(b.step, steps, b.dev, flush=True)
+    if rotate > 1 and not isinstance(b.p, W.ContigProblem):
+        out["rotated"] = b.rotated(rotate, steps, nbytes)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -291,7 +437,7 @@ def main():
                     help="K/V storage: heads-major (default) or token-major")
     ap.add_argument("--graph-calls", type=int, default=0,
                     help="also time N calls captured in one HIP graph (no host or launch "
-                         "overhead between calls)")
+                         "overhead between calls), plain and with the caches flushed")
     ap.add_argument("--append", action="store_true",
                     help="also time the decode-time KV append (paged workloads)")
     ap.add_argument("--merge-parts", type=int, default=0,
@@ -304,15 +450,16 @@ def main():
     ap.add_argument("--mask-keep", type=float, default=0.0,
                     help="custom mask: keep each K/V row with this probability (seeded; "
                          "0: no mask); bytes count the kept rows only")
-    ap.add_argument("--rotate", type=int, default=1,
-                    help="cycle the calls over this many distinct device copies of the K/V "
-                         "store (paged), as successive layers of a model would, so no call "
-                         "finds the previous call's rows in the 256 MB last-level cache")
+    ap.add_argument("--rotate", type=int, default=4,
+                    help="paged workloads: also time calls cycling over this many device "
+                         "copies of the K/V store (1: off)")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="leave out the per-call figures with the caches flushed")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="leave out the read probe and device copy")
+    ap.add_argument("--no-second", action="store_true",
+                    help="leave out the second primary workload's sub-record")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--probe", action="store_true",
-                    help="also measure the read probe and a device copy for context")
-    ap.add_argument("--flush", action="store_true",
-                    help="per-call timings with the caches flushed before each call")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -343,77 +490,39 @@ def main():
         mask = W.pack_mask(keep)
         dev_mask = torch.from_numpy(mask).to(dev)
     nbytes = algorithmic_bytes(p, args.window, keep)
+    b = Bench(p, dev, args, dev_mask)
 
-    if isinstance(p, W.ContigProblem):
-        q, k, v = p.q.to(dev), p.k_cache.to(dev), p.v_cache.to(dev)
-        o = torch.empty_like(q)
-        lse = torch.empty(p.num_qo_heads, dtype=torch.float32, device=dev)
-        ws = fad.workspace_paged(1, p.num_qo_heads, p.num_kv_heads, p.head_dim, p.max_kv_len, 1,
-                                 dev)
-
-        def step():
-            fad.decode_contig(q, k, v, p.valid_kv_len, p.scale, o=o, lse=lse, workspace=ws,
-                              layout=p.layout, window=args.window, softcap=args.softcap,
-                              mask=dev_mask)
-    else:
-        q, k, v = p.q.to(dev), p.k_data.to(dev), p.v_data.to(dev)
-        ind, ptr, lpl = p.indices.to(dev), p.indptr.to(dev), p.last_page_len.to(dev)
-        o = torch.empty_like(q)
-        lse = torch.empty((p.batch, p.num_qo_heads), dtype=torch.float32, device=dev)
-        ws = fad.workspace_paged(p.batch, p.num_qo_heads, p.num_kv_heads, p.head_dim,
-                                 p.page_size, p.total_used_pages, dev)
-        stores = [(k, v)] + [(k.clone(), v.clone()) for _ in range(args.rotate - 1)]
-        turn = [0]
-
-        def step():
-            ks, vs = stores[turn[0] % len(stores)]
-            turn[0] += 1
-            fad.decode_paged(q, ks, vs, ind, ptr, lpl, p.scale, o=o, lse=lse, workspace=ws,
-                             layout=p.layout, window=args.window, softcap=args.softcap,
-                             mask=dev_mask)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} calls)", file=sys.stderr, flush=True)
-
-    # timed region: K whole calls, nothing else on the stream
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        step()
-    end.record()
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / args.steps
-    # the same K calls again with the library's HIP events around its attention
-    # kernel (the event markers themselves add a little to each call, so this
-    # region is kept out of `value`)
-    fad.fa_debug_timing_enable(1)
-    fad.fa_debug_timing_read()  # reset
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    main_ms, call_ms, calls = fad.fa_debug_timing_read()
-    fad.fa_debug_timing_enable(0)
-    per_call = per_call_times(step, args.steps, dev, flush=False)
-    per_call_cold = per_call_times(step, args.steps, dev, flush=True) if args.flush else None
-    value = nbytes / (ms_per_step * 1e-3) / 1e9
-    kernel_ms = main_ms / max(calls, 1)
-    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    # timed region: K whole calls (one attention-kernel launch each), nothing
+    # else on the stream, between HIP events on that stream
+    m = measure(b, nbytes, args.steps, args.warmup, not args.no_flush, args.rotate)
+    us = m["us_per_call"]
+    ms_per_step = us * 1e-3
+    value = m["GBps"]
     chunk, bound, gt, kind = fad.fa_debug_plan(fad.DTYPE_CODES[p.dtype],
                                                getattr(p, "batch", 1), p.num_qo_heads,
                                                p.num_kv_heads, p.head_dim,
                                                getattr(p, "page_size", getattr(p, "max_kv_len", 1)),
                                                getattr(p, "total_used_pages", 1))
-    print(f"[bench] {args.steps} calls: {ms_per_step * 1e3:.1f} us/call, attention kernel "
-          f"{kernel_ms * 1e3:.1f} us (call with event markers {call_ms / max(calls, 1) * 1e3:.1f} "
-          f"us), {value:.0f} GB/s call, {achieved:.0f} GB/s kernel", file=sys.stderr, flush=True)
+    print(f"[bench] {args.steps} calls: {us:.1f} us/call, {value:.0f} GB/s "
+          f"({100.0 * value / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f})", file=sys.stderr,
+          flush=True)
 
-    # the committed counter figures were taken on plain calls (no window, cap or mask)
+    # the committed counter and trace figures were taken on plain calls
     plain = not (args.window or args.softcap or mask is not None)
     traffic = committed_traffic(p.name) if plain else None
+    trace = trace_record(p.name) if plain else None
+    roofline = {"bound": "hbm", "achieved": round(value, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(value / HBM_PEAK_GBS, 4),
+                "traffic": traffic["traffic_bytes"] if traffic else None,
+                "traffic_over_algorithmic":
+                    traffic["traffic_over_algorithmic"] if traffic else None,
+                "kernel_us": round(us, 2),
+                "kernel_us_source": "HIP events on the launch stream around the timed "
+                                    "calls, one kernel launch per call (launch period)",
+                "trace_kernel_us": trace["mean_us"] if trace else None,
+                "trace_frac": round(nbytes / (trace["mean_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                if trace else None,
+                "kernel": "decode attention with fused split merge (fa::decode_mfma_kernel)"}
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -422,7 +531,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
-        "us_per_call": round(ms_per_step * 1e3, 2),
+        "us_per_call": round(us, 2),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "higher_is_better": True,
         "scaling": "weak",
@@ -431,31 +540,53 @@ def main():
         "data": "synthetic (seeded N(0,1) values, seeded page tables; no dataset)",
         "config": {**describe(p), "window": args.window, "softcap": args.softcap,
                    "mask_keep": args.mask_keep,
-                   "kv_copies_rotated": args.rotate,
                    "algorithmic_bytes_per_call": int(nbytes),
                    "chunk_rows": chunk, "heads_per_workgroup": gt,
                    "attention_kernel": "mfma" if kind == 1 else f"kind {kind}"},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic["traffic_bytes"] if traffic else None,
-                     "traffic_over_algorithmic":
-                         traffic["traffic_over_algorithmic"] if traffic else None,
-                     "kernel_us": round(kernel_ms * 1e3, 2),
-                     "kernel": "decode attention with fused split merge (fa::decode_*_kernel)"},
+        "roofline": roofline,
+        "per_call": m["per_call"],
     }
+    for key in ("per_call_flushed", "rotated"):
+        if key in m:
+            line[key] = m[key]
     if args.append and not isinstance(p, W.ContigProblem):
-        line["append"] = time_append(p, {"k": k, "v": v, "ind": ind, "ptr": ptr, "lpl": lpl},
-                                     dev, args.steps, args.warmup)
+        line["append"] = time_append(p, {"k": b.k, "v": b.v, "ind": b.ind, "ptr": b.ptr,
+                                         "lpl": b.lpl}, dev, args.steps, args.warmup)
     if args.merge_parts > 0:
         line["merge"] = time_merge(p, dev, args.merge_parts, args.steps, args.warmup)
     if args.graph_calls > 0:
-        us = graph_call_time(step, args.graph_calls, max(1, args.steps // args.graph_calls) + 4)
-        line["graph_per_call"] = {"calls_per_graph": args.graph_calls, "us_per_call": round(us, 2),
-                                  "GBps": round(nbytes / (us * 1e-6) / 1e9, 2)}
-    line["per_call"] = per_call
-    if per_call_cold:
-        line["per_call_flushed"] = per_call_cold
-    if args.probe:
+        reps = max(1, args.steps // args.graph_calls) + 4
+        g_us = graph_call_time(b.step, args.graph_calls, reps)
+        line["graph_per_call"] = {"calls_per_graph": args.graph_calls, "us_per_call": round(g_us, 2),
+                                  "GBps": round(nbytes / (g_us * 1e-6) / 1e9, 2)}
+        if not args.no_flush:
+            f_us = graph_flushed_time(b.step, dev, args.graph_calls, reps)
+            line["graph_per_call_flushed"] = {
+                "calls_per_graph": args.graph_calls, "us_per_call": round(f_us, 2),
+                "GBps": round(nbytes / (f_us * 1e-6) / 1e9, 2),
+                "method": "graph of (512 MiB flush, call) pairs minus a graph of the flushes"}
+    second = None
+    if args.workload == "c3" and not args.no_second and args.qo_heads is None and \
+            args.dtype is None and args.layout == "hnd" and plain:
+        del b
+        torch.cuda.empty_cache()
+        print("[bench] second primary workload: c4", file=sys.stderr, flush=True)
+        p2 = W.FULL["c4"]()
+        n2 = algorithmic_bytes(p2)
+        b2 = Bench(p2, dev, args)
+        m2 = measure(b2, n2, args.steps, args.warmup, not args.no_flush, args.rotate)
+        t2 = trace_record(p2.name)
+        second = {"config": describe(p2), "algorithmic_bytes_per_call": int(n2),
+                  "us_per_call": round(m2["us_per_call"], 2), "GBps": round(m2["GBps"], 2),
+                  "pct_of_hbm_peak": round(100.0 * m2["GBps"] / HBM_PEAK_GBS, 2),
+                  "trace_kernel_us": t2["mean_us"] if t2 else None,
+                  **{k: m2[k] for k in ("per_call", "per_call_flushed", "rotated") if k in m2}}
+        line["second_primary"] = second
+        print(f"[bench] c4: {m2['us_per_call']:.1f} us/call, {m2['GBps']:.0f} GB/s",
+              file=sys.stderr, flush=True)
+        del b2, p2
+        torch.cuda.empty_cache()
+    if not args.no_probe:
         line["hbm_probe"] = hbm_probe(dev)
     if not args.no_cpu_baseline:
         print("[bench] timing the float64 oracle on the host", file=sys.stderr, flush=True)
