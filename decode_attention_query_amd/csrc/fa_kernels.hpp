@@ -121,8 +121,11 @@ __device__ inline int lanes_below(uint64_t mask) {
 
 // The split unit of work index w; false for indices past the real unit count.
 // Every lane of the calling wave takes part; the result is wave-uniform.
+// (Forced inline, as are the tile loads and the split merge: with many call
+// sites the compiler may otherwise emit them as real calls, whose arguments
+// and results then travel through scratch memory.)
 template <bool kRows>
-__device__ bool find_unit(const DecodeParams &p, int w, UnitInfo &u) {
+__device__ __forceinline__ bool find_unit(const DecodeParams &p, int w, UnitInfo &u) {
   if (p.contig) {  // one request of contig_len rows, known on the host
     if (w >= p.contig_units) return false;
     u.b = 0;
@@ -352,7 +355,7 @@ __device__ inline void store4(typename E::raw *out, const f32x4 &v) {
 }
 
 template <class E, int kDepth>
-__device__ void merge_partials(const DecodeParams &p, int b, int u0, int n, int h0, int gt, int nw,
+__device__ __forceinline__ void merge_partials(const DecodeParams &p, int b, int u0, int n, int h0, int gt, int nw,
                                float *s_stat /* LDS [2 kStatHeads] */, float *s_w,
                                int w_cap) {
   const int tid = threadIdx.x;
@@ -525,7 +528,7 @@ __device__ inline int draw_ticket(unsigned long long *counter, int n) {
 }
 
 template <class E, int kDepth>
-__device__ void finish_split(const DecodeParams &p, const UnitInfo &u, int plane, int h0, int gt, int nw,
+__device__ __forceinline__ void finish_split(const DecodeParams &p, const UnitInfo &u, int plane, int h0, int gt, int nw,
                              float *s_stat, int *s_last, float *s_w, int w_cap) {
   if (u.n_units <= 1) return;
   __builtin_amdgcn_s_waitcnt(0);

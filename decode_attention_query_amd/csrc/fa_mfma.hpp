@@ -201,7 +201,7 @@ __device__ inline int64_t staged_block_offset(const DecodeParams &p, const int32
 // the layout's row stride (D heads-major, Hkv * D token-major); otherwise
 // (page sizes that are not multiples of 16) every lane resolves its own rows.
 template <class E, int D, bool kNhd>
-__device__ inline void issue_tile(KVTile<MfmaGeom<E, D>::NI> &T, const DecodeParams &p,
+__device__ __forceinline__ void issue_tile(KVTile<MfmaGeom<E, D>::NI> &T, const DecodeParams &p,
                                   int32_t page_base, const int32_t *s_pages, int slot0, int kvh,
                                   int t0, int t_end, int lane) {
   using G = MfmaGeom<E, D>;
