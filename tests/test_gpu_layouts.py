@@ -109,9 +109,9 @@ def test_token_major_gather_bit_exact(dev):
             assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), (p.name, which)
 
 
-@pytest.mark.parametrize("name", ["c3", "c4", "c5"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
 def test_token_major_full(dev, name):
-    """The full paged workloads stored token-major, in the benchmark's launch
+    """The full workloads stored token-major, in the benchmark's launch
     configuration: bit-identical to heads-major, and every output against the
     oracle's token-major path."""
     p = W.FULL[name]()
