@@ -8,8 +8,8 @@
 // loads whole rows from HBM, stages K and V in its LDS area, and keeps its own
 // online-softmax state; the waves are merged through LDS at the end.  A group
 // of more than 16 heads is cut into blocks of 16 (the last one shorter, or
-// empty) and takes two blocks per workgroup: the waves share each step's tiles through LDS, half of them
-// computing for each block (NB = 2 below).
+// empty) and takes two blocks per workgroup: every wave computes each of its
+// tiles for both blocks (NB = 2 below).
 //
 // Per 32-row 16-bit tile, with n = lane % 16 and grp = lane / 16:
 //   scores   S^T[t][g] = sum_d K[t][d] Q[g][d]        v_mfma_f32_16x16x32 (bf16|f16)
@@ -237,14 +237,20 @@ __device__ __forceinline__ void issue_tile(KVTile<MfmaGeom<E, D>::NI> &T, const 
 // kMods: a sliding window, soft-cap or ALiBi is in use (the plain instance
 // carries none of their per-score work).
 //
-// NB: 16-column head blocks per workgroup.  NB = 1: every wave serves the
-// workgroup's one block and streams its own tiles.  NB = 2 (a query group of
-// more than 16 heads, e.g. G = 32): the waves still load one tile each
-// per step into their LDS areas, and after a
-// workgroup barrier the first NW / 2 waves compute every tile of the step for
-// block 0 and the others for block 1, each wave for its own 16 heads -- so
-// K and V leave HBM once for 32 query heads, with the per-wave registers of
-// the one-block kernel.
+// NB: 16-column head blocks per workgroup.  NB = 1: the workgroup's one block
+// (the whole group when G <= 16).  NB = 2 (a query group of more than 16
+// heads, e.g. G = 32), D <= 128: every wave computes each tile it loads for
+// both blocks -- one K operand read from LDS feeds both blocks' score
+// products and one V^T read both blocks' P.V products -- so K and V leave HBM
+// once for 32 query heads and the waves stream independently, with no
+// workgroup barrier inside the main loop.  The second block's query operands,
+// accumulators and softmax state take the registers of the second K/V tile,
+// so one register tile is in flight while the other is computed (the D = 256
+// loop).  NB = 2 where a wave's registers do not hold two blocks' state
+// beside a tile (D = 256; f32 at D = 128 with the per-score options): the
+// waves share each step's tiles through LDS instead, and after a workgroup
+// barrier the first half of the waves computes every tile of the step for
+// block 0 and the second half for block 1.
 template <class E, int D, bool kNhd, bool kMods, int NB>
 __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1))) void decode_mfma_kernel(
     const DecodeParams p) {
@@ -253,16 +259,27 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   using v8 = typename M::v8;
   constexpr int KK = G::KK, MB = G::MB, NW = G::NW, TT = G::TT, JB = G::JB, QC = G::QC;
   constexpr bool kF32 = G::kF32;
-  static_assert(NB == 1 || (NB == 2 && NW % 2 == 0), "head blocks per workgroup");
-  constexpr int WPB = NW / NB;  // waves per head block
+  static_assert(NB == 1 || NB == 2, "head blocks per workgroup");
+  // head blocks per wave (NBW), and whether the waves share tiles (kShared:
+  // wave w serves block w / WPB of the workgroup's NB) -- where two blocks'
+  // state does not fit a wave's registers beside a tile: D = 256, and f32 at
+  // D = 128 with the per-score options
+  constexpr bool kShared = NB == 2 && (D > 128 || (kF32 && D == 128 && kMods));
+  constexpr int NBW = kShared ? 1 : NB;
+  constexpr int WPB = kShared ? NW / NB : NW;
+  static_assert(!kShared || NW % NB == 0, "waves per head block");
+  // two register tiles in flight only where the registers allow it
+  constexpr bool kPipe = G::kPipelined && NBW == 1;
+  // the wave-merge area (per wave NBW * 16 head rows) fits the K/V area
+  static_assert(NW * 16 * NBW * G::ACC_ROW * 4 <= G::LDS, "wave-merge area");
 
   __shared__ __attribute__((aligned(16))) char lds[G::LDS];
-  __shared__ float s_m[NW][16];
-  __shared__ float s_l[NW][16];
+  __shared__ float s_m[NW][16 * NBW];
+  __shared__ float s_l[NW][16 * NBW];
   __shared__ float s_stat[2 * kStatHeads];
   __shared__ int s_last;
   __shared__ int s_work;
-  __shared__ uint32_t s_mask[NW];  // NB = 2: each wave's tile mask word
+  __shared__ uint32_t s_mask[NW];  // shared tiles: each wave's tile mask word
 
   // work item = unit * planes + head block: a unit's head blocks are adjacent,
   // and work items run in (longest-first) unit order.  The first resident
@@ -299,38 +316,45 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15;
   const int grp = lane >> 4;
-  // first head of this wave's block: past the group when the block is empty,
-  // so only lanes with a valid column (n < gt) may use it in an address
-  const int hb = h0 + (wave / WPB) * bs;
-  // valid columns of this wave's block (0 for the empty second block of a
-  // workgroup at the end of an odd number of blocks)
-  const int gt = max(0, min(bs, gt_wg - (wave / WPB) * bs));
+  // the wave's k-th block (block wb0 + k of the workgroup): first head hb[k]
+  // (past the group when the block is empty, so only lanes with a valid
+  // column, n < gt[k], may use it in an address) and its valid columns gt[k]
+  // (0 for the empty second block of a workgroup at the end of an odd number
+  // of blocks)
+  const int wb0 = kShared ? wave / WPB : 0;
+  int hb[NBW], gt[NBW];
+#pragma unroll
+  for (int k = 0; k < NBW; ++k) {
+    hb[k] = h0 + (wb0 + k) * bs;
+    gt[k] = max(0, min(bs, gt_wg - (wb0 + k) * bs));
+  }
 
-  // B operand of the score MFMA: Q^T, head n, loaded before the page ids are
-  // staged so that the two memory round trips overlap.  16-bit: features
-  // 32kk + 8grp .. + 8 (qb).  f32: lane group grp takes features grp D/4 ..
-  // + D/4 as its share of every product, four per 16-byte chunk (qf); any
-  // split of the contraction works as long as the A operand (K) uses the
-  // same one.
-  v8 qb[kF32 ? 1 : KK];
-  f32x4 qf[kF32 ? QC : 1];
-  {
-    const bool live = n < gt;
+  // B operand of the score MFMA: Q^T, head n of each block, loaded before the
+  // page ids are staged so that the two memory round trips overlap.  16-bit:
+  // features 32kk + 8grp .. + 8 (qb).  f32: lane group grp takes features
+  // grp D/4 .. + D/4 as its share of every product, four per 16-byte chunk
+  // (qf); any split of the contraction works as long as the A operand (K)
+  // uses the same one.
+  v8 qb[NBW][kF32 ? 1 : KK];
+  f32x4 qf[NBW][kF32 ? QC : 1];
+#pragma unroll
+  for (int k = 0; k < NBW; ++k) {
+    const bool live = n < gt[k];
     const char *qrow = static_cast<const char *>(p.q) +
-                       ((int64_t)u.b * p.num_qo_heads + (live ? hb + n : h0)) * D * E::kBytes;
+                       ((int64_t)u.b * p.num_qo_heads + (live ? hb[k] + n : h0)) * D * E::kBytes;
     if constexpr (kF32) {
 #pragma unroll
       for (int q4 = 0; q4 < QC; ++q4) {
         uint4 r = *reinterpret_cast<const uint4 *>(qrow + (grp * (D / 4) + 4 * q4) * 4);
         if (!live) r = make_uint4(0, 0, 0, 0);
-        qf[q4] = __builtin_bit_cast(f32x4, r);
+        qf[k][q4] = __builtin_bit_cast(f32x4, r);
       }
     } else {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         uint4 r = *reinterpret_cast<const uint4 *>(qrow + (8 * grp) * 2 + kk * 64);
         if (!live) r = make_uint4(0, 0, 0, 0);
-        qb[kk] = __builtin_bit_cast(v8, r);
+        qb[k][kk] = __builtin_bit_cast(v8, r);
       }
     }
   }
@@ -338,14 +362,23 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   __shared__ int32_t s_pages[kPageTable];
   const int slot0 = stage_unit_pages(p, s_pages, page_base, t_begin, t_end, NW * 64);
 
-  // ALiBi slope of head n (base-2 units): row t's score gains slope2 * (t - (L - 1))
-  const float slope2 = (kMods && p.alibi && n < gt) ? p.alibi[hb + n] * kLog2e : 0.0f;
-
-  f32x4 acc[MB];
+  // ALiBi slope of head n of each block (base-2 units): row t's score gains
+  // slope2 * (t - (L - 1))
+  float slope2[NBW];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float m_run = -INFINITY;  // running max (base 2) of head n; same in all 4 lane groups
-  float l_run = 0.0f;       // this lane's share of the normaliser of head n
+  for (int k = 0; k < NBW; ++k)
+    slope2[k] = (kMods && p.alibi && n < gt[k]) ? p.alibi[hb[k] + n] * kLog2e : 0.0f;
+
+  f32x4 acc[NBW][MB];
+  float m_run[NBW];  // running max (base 2) of head n; same in all 4 lane groups
+  float l_run[NBW];  // this lane's share of the normaliser of head n
+#pragma unroll
+  for (int k = 0; k < NBW; ++k) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[k][mb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    m_run[k] = -INFINITY;
+    l_run[k] = 0.0f;
+  }
 
   char *wk = lds + wave * G::WAVE_LDS;   // this wave's K tile
   char *wv = wk + TT * G::ROWK;           // and V tile
@@ -400,68 +433,78 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
     }
   };
 
-  // One tile (rows t0 .. t0 + TT) for this wave's heads, from the LDS area at
-  // ck (K rows, then V rows).
+  // One tile (rows t0 .. t0 + TT) for this wave's heads (each block's), from
+  // the LDS area at ck (K rows, then V rows).
   // mbits: the lane's mask bits of the tile (lane_bits; unused without a mask).
   auto compute_tile = [&](const char *ck, int t0, uint32_t mbits) {
     const char *vt = ck + TT * G::ROWK + vt_off;
     // scores; A = K row 16j + n: features 32kk + 8grp .. + 8 (16-bit), or the
-    // lane group's quarter of D, one feature per product (f32)
-    f32x4 s[JB];
+    // lane group's quarter of D, one feature per product (f32); each A
+    // operand serves every block
+    f32x4 s[NBW][JB];
 #pragma unroll
     for (int j = 0; j < JB; ++j) {
-      s[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int k = 0; k < NBW; ++k) s[k][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       if constexpr (kF32) {
 #pragma unroll
         for (int q4 = 0; q4 < QC; ++q4) {
           const f32x4 ka = *reinterpret_cast<const f32x4 *>(
               ck + (16 * j + n) * G::ROWK + (grp * (D / 4) + 4 * q4) * 4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) s[j] = Mfma<F32>::mma4(ka[e], qf[q4][e], s[j]);
+          for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int k = 0; k < NBW; ++k) s[k][j] = Mfma<F32>::mma4(ka[e], qf[k][q4][e], s[k][j]);
         }
       } else {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           const uint4 ka = *reinterpret_cast<const uint4 *>(ck + (16 * j + n) * G::ROWK +
                                                             (32 * kk + 8 * grp) * 2);
-          s[j] = M::mma(__builtin_bit_cast(v8, ka), qb[kk], s[j]);
+#pragma unroll
+          for (int k = 0; k < NBW; ++k)
+            s[k][j] = M::mma(__builtin_bit_cast(v8, ka), qb[k][kk], s[k][j]);
         }
       }
     }
-    // online softmax for head n over the tile's rows 16j + 4grp + i
-    float x[4 * JB];
-    float tmax = -INFINITY;
+    // online softmax for head n of each block over the tile's rows
+    // 16j + 4grp + i
+    float pr[NBW][4 * JB];
 #pragma unroll
-    for (int j = 0; j < JB; ++j)
+    for (int k = 0; k < NBW; ++k) {
+      float x[4 * JB];
+      float tmax = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 16 * j + 4 * grp + i;
-        float v = s[j][i] * c;
-        if constexpr (kMods) {
-          if (p.alibi) v += slope2 * (float)(t - last_row);
-          if (p.softcap2 > 0.0f) v = p.softcap2 * tanhf(v * p.softcap2_inv);
-          if (t < t_lo) v = -INFINITY;
-          if (p.mask && !((mbits >> (4 * j + i)) & 1u)) v = -INFINITY;
+      for (int j = 0; j < JB; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = t0 + 16 * j + 4 * grp + i;
+          float v = s[k][j][i] * c;
+          if constexpr (kMods) {
+            if (p.alibi) v += slope2[k] * (float)(t - last_row);
+            if (p.softcap2 > 0.0f) v = p.softcap2 * tanhf(v * p.softcap2_inv);
+            if (t < t_lo) v = -INFINITY;
+            if (p.mask && !((mbits >> (4 * j + i)) & 1u)) v = -INFINITY;
+          }
+          if (t >= t_end) v = -INFINITY;
+          x[4 * j + i] = v;
+          tmax = fmaxf(tmax, v);
         }
-        if (t >= t_end) v = -INFINITY;
-        x[4 * j + i] = v;
-        tmax = fmaxf(tmax, v);
+      tmax = rows4_max(tmax);
+      const float m_new = fmaxf(m_run[k], tmax);
+      const float ref = safe_ref(m_new);
+      const float alpha = fast_exp2(m_run[k] - ref);
+      float psum = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4 * JB; ++e) {
+        pr[k][e] = fast_exp2(x[e] - ref);
+        psum += pr[k][e];
       }
-    tmax = rows4_max(tmax);
-    const float m_new = fmaxf(m_run, tmax);
-    const float ref = safe_ref(m_new);
-    const float alpha = fast_exp2(m_run - ref);
-    float pr[4 * JB];
-    float psum = 0.0f;
+      l_run[k] = l_run[k] * alpha + psum;
+      m_run[k] = m_new;
 #pragma unroll
-    for (int e = 0; e < 4 * JB; ++e) {
-      pr[e] = fast_exp2(x[e] - ref);
-      psum += pr[e];
+      for (int mb = 0; mb < MB; ++mb) acc[k][mb] *= alpha;
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[mb] *= alpha;
     if constexpr (kF32) {
       // O^T += V^T P^T over the 16 rows, 4 at a time: in product i, lane group
       // grp contributes row 4grp + i, so B is the lane's own probability pr[i]
@@ -471,11 +514,13 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float a = *reinterpret_cast<const float *>(vt + i * G::ROWV + 64 * mb);
-          acc[mb] = Mfma<F32>::mma4(a, pr[i], acc[mb]);
+#pragma unroll
+          for (int k = 0; k < NBW; ++k) acc[k][mb] = Mfma<F32>::mma4(a, pr[k][i], acc[k][mb]);
         }
     } else {
-      v8 ph, pl;
-      pack_probs<E>(pr, ph, pl);
+      v8 ph[NBW], pl[NBW];
+#pragma unroll
+      for (int k = 0; k < NBW; ++k) pack_probs<E>(pr[k], ph[k], pl[k]);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         // A = V^T: rows 16h + 4grp + r (r < 4) of feature 16mb + n, for h = 0, 1
@@ -486,13 +531,16 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
         typedef short s16x8 __attribute__((ext_vector_type(8)));
         const s16x8 a16 = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
         const v8 a = __builtin_bit_cast(v8, a16);
-        acc[mb] = M::mma(a, ph, acc[mb]);
-        if constexpr (M::kSplitP) acc[mb] = M::mma(a, pl, acc[mb]);
+#pragma unroll
+        for (int k = 0; k < NBW; ++k) {
+          acc[k][mb] = M::mma(a, ph[k], acc[k][mb]);
+          if constexpr (M::kSplitP) acc[k][mb] = M::mma(a, pl[k], acc[k][mb]);
+        }
       }
     }
   };
 
-  // One-block workgroups: each wave stores its tile and computes it alone.
+  // Each wave stores its tile and computes it alone.
   auto compute = [&](const KVTile<G::NI> &T, int t0, uint32_t mraw) {
     store_tile(T);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -510,12 +558,48 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
 
   const int stride = NW * TT;
   int t0 = t_begin + wave * TT;
-  if constexpr (NB == 1) {
-  if (t0 < t_end) {
+  if constexpr (kShared) {
+    // Shared tiles: step s covers rows t_begin + s * stride ..; wave w loads
+    // the step's tile w into its LDS area and computes tiles cw .. cw + NB - 1
+    // for its block's heads.  Every wave runs every step (the barriers are the
+    // workgroup's), loading clamped rows where its tile lies past the unit.
+    // A custom mask's word of each tile is assembled by the wave that loaded
+    // the tile and published in s_mask with it.  One register tile, reloaded
+    // as soon as it is in LDS, so the next step's loads stream while this
+    // step is computed.
+    const int steps = t_begin < t_end ? (t_end - t_begin + stride - 1) / stride : 0;
+    const int cw = (wave % WPB) * NB;
+    if (steps > 0) {
+      KVTile<G::NI> A;
+      issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, t0, t_end, lane);
+      uint32_t mA = mask_load(t0);
+      for (int st = 0; st < steps; ++st) {
+        store_tile(A);
+        if constexpr (kMods)
+          if (p.mask && lane == 0) s_mask[wave] = mask_word(t0 + st * stride, mA);
+        if (st + 1 < steps) {
+          issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, t0 + (st + 1) * stride,
+                                 t_end, lane);
+          mA = mask_load(t0 + (st + 1) * stride);
+        }
+        __syncthreads();
+        const int ts = t_begin + st * stride;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          const int tc = ts + (cw + i) * TT;
+          uint32_t mbits = 0;
+          if constexpr (kMods)
+            if (p.mask) mbits = lane_bits(s_mask[cw + i]);
+          if (tc < t_end && gt[0] > 0) compute_tile(lds + (cw + i) * G::WAVE_LDS, tc, mbits);
+        }
+        __syncthreads();  // the step's tiles are read by every wave before they are replaced
+      }
+    }
+  } else if (t0 < t_end) {
     KVTile<G::NI> A;
     issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, t0, t_end, lane);
     uint32_t mA = mask_load(t0);
-    if constexpr (G::kPipelined) {
+    if constexpr (kPipe) {
       KVTile<G::NI> B;
       uint32_t mB;
       while (true) {
@@ -531,9 +615,9 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
         if (t0 >= t_end) break;
       }
     } else {
-      // One register tile (D = 256): once it is in LDS its registers are free,
-      // so the next tile's loads are issued before the current one is
-      // computed and stream meanwhile.
+      // One register tile (D = 256, or two head blocks): once it is in LDS its
+      // registers are free, so the next tile's loads are issued before the
+      // current one is computed and stream meanwhile.
       while (true) {
         store_tile(A);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -557,109 +641,47 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
       }
     }
   }
-  } else {
-    // Shared tiles: step s covers rows t_begin + s * stride ..; wave w loads
-    // the step's tile w into its LDS area and computes tiles cw .. cw + NB - 1
-    // for its block's heads.  Every wave runs every step (the barriers are the
-    // workgroup's), loading clamped rows where its tile lies past the unit.
-    const int steps = t_begin < t_end ? (t_end - t_begin + stride - 1) / stride : 0;
-    const int cw = (wave % WPB) * NB;
-    // A custom mask's word of each tile is assembled by the wave that loaded
-    // the tile and published in s_mask with it.
-    auto shared_store = [&](const KVTile<G::NI> &T, int s, uint32_t mraw) {
-      store_tile(T);
-      if constexpr (kMods)
-        if (p.mask && lane == 0) s_mask[wave] = mask_word(t0 + s * stride, mraw);
-    };
-    auto shared_compute = [&](int s) {
-      __syncthreads();
-      const int ts = t_begin + s * stride;
-#pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const int tc = ts + (cw + i) * TT;
-        uint32_t mbits = 0;
-        if constexpr (kMods)
-          if (p.mask) mbits = lane_bits(s_mask[cw + i]);
-        if (tc < t_end && gt > 0) compute_tile(lds + (cw + i) * G::WAVE_LDS, tc, mbits);
-      }
-      __syncthreads();  // the step's tiles are read by every wave before they are replaced
-    };
-    auto shared_step = [&](const KVTile<G::NI> &T, int s, uint32_t mraw) {
-      shared_store(T, s, mraw);
-      shared_compute(s);
-    };
-    if (steps > 0) {
-      KVTile<G::NI> A;
-      issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, t0, t_end, lane);
-      uint32_t mA = mask_load(t0);
-      if constexpr (G::kPipelined) {
-        KVTile<G::NI> B;
-        uint32_t mB = 0;
-        for (int s = 0; s < steps; s += 2) {
-          if (s + 1 < steps) {
-            issue_tile<E, D, kNhd>(B, p, page_base, s_pages, slot0, kvh, t0 + (s + 1) * stride,
-                                   t_end, lane);
-            mB = mask_load(t0 + (s + 1) * stride);
-          }
-          shared_step(A, s, mA);
-          if (s + 1 >= steps) break;
-          if (s + 2 < steps) {
-            issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, t0 + (s + 2) * stride,
-                                   t_end, lane);
-            mA = mask_load(t0 + (s + 2) * stride);
-          }
-          shared_step(B, s + 1, mB);
-        }
-      } else {
-        // one register tile (D = 256): reloaded as soon as it is in LDS, so
-        // the next step's loads stream while this step is computed
-        for (int s = 0; s < steps; ++s) {
-          shared_store(A, s, mA);
-          if (s + 1 < steps) {
-            issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, t0 + (s + 1) * stride,
-                                   t_end, lane);
-            mA = mask_load(t0 + (s + 1) * stride);
-          }
-          shared_compute(s);
-        }
-      }
-    }
-  }
 
   // ---- merge the four lane groups' normalisers, then the waves
-  l_run = rows4_sum(l_run);
+#pragma unroll
+  for (int k = 0; k < NBW; ++k) l_run[k] = rows4_sum(l_run[k]);
   __syncthreads();  // every wave is done with its V area; reuse it for the merge
-  float *s_acc = reinterpret_cast<float *>(lds);  // [NW][16][ACC_ROW]
-  if (n < gt) {
+  float *s_acc = reinterpret_cast<float *>(lds);  // [NW][NBW * 16][ACC_ROW]
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+  for (int k = 0; k < NBW; ++k) {
+    if (n < gt[k]) {
+      const int row = wave * NBW * 16 + k * 16 + n;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        s_acc[(wave * 16 + n) * G::ACC_ROW + 16 * mb + 4 * grp + i] = acc[mb][i];
-    if (grp == 0) {
-      s_m[wave][n] = m_run;
-      s_l[wave][n] = l_run;
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          s_acc[row * G::ACC_ROW + 16 * mb + 4 * grp + i] = acc[k][mb][i];
+      if (grp == 0) {
+        s_m[wave][k * 16 + n] = m_run[k];
+        s_l[wave][k * 16 + n] = l_run[k];
+      }
     }
   }
   __syncthreads();
-  // workgroup head hh = block k's head g (k = hh / bs): merged over the WPB
-  // waves of block k
+  // workgroup head hh = head g of block kb = hh / bs: merged over the WPB
+  // waves that hold it (waves kb * WPB .. with shared tiles, where each wave
+  // holds one block; else every wave, as its block kb)
   for (int idx = tid; idx < gt_wg * D; idx += NW * 64) {
     const int hh = idx / D;
     const int d = idx % D;
-    const int k = NB == 1 ? 0 : hh / bs;
-    const int g = hh - k * bs;
+    const int kb = NB == 1 ? 0 : hh / bs;
+    const int w0 = kShared ? kb * WPB : 0;
+    const int col = (kShared ? 0 : kb) * 16 + (hh - kb * bs);
     float Mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < WPB; ++w) Mx = fmaxf(Mx, s_m[k * WPB + w][g]);
+    for (int w = 0; w < WPB; ++w) Mx = fmaxf(Mx, s_m[w0 + w][col]);
     const float ref = safe_ref(Mx);
     float lsum = 0.0f, a = 0.0f;
 #pragma unroll
     for (int w = 0; w < WPB; ++w) {
-      const int ww = k * WPB + w;
-      const float sw = fast_exp2(s_m[ww][g] - ref);
-      lsum += s_l[ww][g] * sw;
-      a += s_acc[(ww * 16 + g) * G::ACC_ROW + d] * sw;
+      const float sw = fast_exp2(s_m[w0 + w][col] - ref);
+      lsum += s_l[w0 + w][col] * sw;
+      a += s_acc[((w0 + w) * NBW * 16 + col) * G::ACC_ROW + d] * sw;
     }
     emit<E>(p, u, h0 + hh, d, Mx, lsum, a);
   }
