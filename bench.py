@@ -450,6 +450,9 @@ def main():
     ap.add_argument("--mask-keep", type=float, default=0.0,
                     help="custom mask: keep each K/V row with this probability (seeded; "
                          "0: no mask); bytes count the kept rows only")
+    ap.add_argument("--mask-run", type=int, default=0,
+                    help="custom mask in runs of this many rows kept or dropped together "
+                         "(a block-sparse mask; 0: rows drawn one by one)")
     ap.add_argument("--rotate", type=int, default=4,
                     help="paged workloads: also time calls cycling over this many device "
                          "copies of the K/V store (1: off)")
@@ -486,7 +489,8 @@ def main():
     keep = mask = dev_mask = None
     if args.mask_keep > 0.0:
         lens = [p.valid_kv_len] if isinstance(p, W.ContigProblem) else p.kv_lens
-        keep = W.random_mask(4242, lens, keep=args.mask_keep)
+        keep = W.random_mask(4242, lens, keep=args.mask_keep,
+                             blocks=args.mask_run if args.mask_run > 0 else False)
         mask = W.pack_mask(keep)
         dev_mask = torch.from_numpy(mask).to(dev)
     nbytes = algorithmic_bytes(p, args.window, keep)
@@ -539,7 +543,7 @@ def main():
         "dtype": p.dtype,
         "data": "synthetic (seeded N(0,1) values, seeded page tables; no dataset)",
         "config": {**describe(p), "window": args.window, "softcap": args.softcap,
-                   "mask_keep": args.mask_keep,
+                   "mask_keep": args.mask_keep, "mask_run": args.mask_run,
                    "algorithmic_bytes_per_call": int(nbytes),
                    "chunk_rows": chunk, "heads_per_workgroup": gt,
                    "attention_kernel": "mfma" if kind == 1 else f"kind {kind}"},

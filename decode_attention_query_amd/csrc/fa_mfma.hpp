@@ -595,49 +595,114 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
         __syncthreads();  // the step's tiles are read by every wave before they are replaced
       }
     }
-  } else if (t0 < t_end) {
-    KVTile<G::NI> A;
-    issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, t0, t_end, lane);
-    uint32_t mA = mask_load(t0);
-    if constexpr (kPipe) {
-      KVTile<G::NI> B;
-      uint32_t mB;
-      while (true) {
-        issue_tile<E, D, kNhd>(B, p, page_base, s_pages, slot0, kvh, t0 + stride, t_end, lane);
-        mB = mask_load(t0 + stride);
-        compute(A, t0, mA);
-        t0 += stride;
-        if (t0 >= t_end) break;
-        issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, t0 + stride, t_end, lane);
-        mA = mask_load(t0 + stride);
-        compute(B, t0, mB);
-        t0 += stride;
-        if (t0 >= t_end) break;
-      }
-    } else {
-      // One register tile (D = 256, or two head blocks): once it is in LDS its
-      // registers are free, so the next tile's loads are issued before the
-      // current one is computed and stream meanwhile.
-      while (true) {
-        store_tile(A);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        uint32_t mbits = 0;
-        if constexpr (kMods)
-          if (p.mask) mbits = lane_bits(mask_word(t0, mA));
-        const int tn = t0 + stride;
-        if (tn < t_end) {
-          issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, tn, t_end, lane);
-          mA = mask_load(tn);
+  } else {
+    // The wave's tiles: tile k starts at row t0 + k * stride, k < n_tiles.
+    // Under a custom mask only the tiles holding a kept row are loaded and
+    // computed (live_tile); a skipped tile would leave the state as it is.
+    const int n_tiles = t0 < t_end ? (t_end - t0 + stride - 1) / stride : 0;
+    uint64_t live = ~0ull;  // bit i: tile win0 + i may hold a kept row
+    int win0 = 0;
+    // the live bits of tiles k0 .. k0 + 63 (a superset: each lane ORs the
+    // five mask bytes that cover its tile's 32 bits; bytes past the mask's
+    // end read as 0)
+    auto scan_mask = [&](int k0) -> uint64_t {
+      uint32_t any = 0;
+      if constexpr (kMods) {
+        const int t = t0 + (k0 + lane) * stride;
+        if (k0 + lane < n_tiles) {
+          const uint32_t b0 = (uint32_t)(u.row0 + t) >> 3;
+#pragma unroll
+          for (int e = 0; e < 5; ++e)
+            if (b0 + e < p.mask_bytes) any |= p.mask[b0 + e];
         }
-        compute_tile(wk, t0, mbits);
-        // the reads above complete before the next tile overwrites the area
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        t0 = tn;
-        if (t0 >= t_end) break;
+      }
+      return __ballot(any != 0);
+    };
+    if constexpr (kMods)
+      if (p.mask) live = scan_mask(0);
+    // the first live tile at or after k (k <= n_tiles; n_tiles if none)
+    auto live_tile = [&](int k) -> int {
+      if constexpr (kMods) {
+        if (p.mask) {
+          while (k < n_tiles) {
+            if (k >= win0 + 64) {
+              win0 = k;
+              live = scan_mask(k);
+            }
+            const uint64_t m = live >> (k - win0);
+            if (m) return min(k + (int)__builtin_ctzll(m), n_tiles);
+            k = win0 + 64;
+          }
+          return n_tiles;
+        }
+      }
+      return k;
+    };
+    auto row_of = [&](int k) { return t0 + k * stride; };
+    int ka = live_tile(0);
+    if (ka < n_tiles) {
+      KVTile<G::NI> A;
+      issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, row_of(ka), t_end, lane);
+      uint32_t mA = mask_load(row_of(ka));
+      if constexpr (kPipe && !kMods) {
+        // every tile, two in flight, at a fixed stride (the live-tile form
+        // below measured ~1% slower here); the next tile's loads go out
+        // unconditionally: past the wave's last tile they read the unit's
+        // last row again (clamped, in bounds, from cache), which keeps every
+        // wait for a tile's data exact
+        KVTile<G::NI> B;
+        int ta = t0;
+        while (true) {
+          issue_tile<E, D, kNhd>(B, p, page_base, s_pages, slot0, kvh, ta + stride, t_end, lane);
+          compute(A, ta, 0);
+          ta += stride;
+          if (ta >= t_end) break;
+          issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, ta + stride, t_end, lane);
+          compute(B, ta, 0);
+          ta += stride;
+          if (ta >= t_end) break;
+        }
+      } else if constexpr (kPipe) {
+        // the live tiles, two in flight, loaded the same way
+        KVTile<G::NI> B;
+        uint32_t mB = 0;
+        while (true) {
+          const int kb = live_tile(ka + 1);
+          issue_tile<E, D, kNhd>(B, p, page_base, s_pages, slot0, kvh, row_of(kb), t_end, lane);
+          mB = mask_load(row_of(kb));
+          compute(A, row_of(ka), mA);
+          if (kb >= n_tiles) break;
+          ka = live_tile(kb + 1);
+          issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, row_of(ka), t_end, lane);
+          mA = mask_load(row_of(ka));
+          compute(B, row_of(kb), mB);
+          if (ka >= n_tiles) break;
+        }
+      } else {
+        // One register tile (D = 256, or two head blocks): once it is in LDS
+        // its registers are free, so the next tile's loads are issued before
+        // the current one is computed and stream meanwhile.
+        while (true) {
+          store_tile(A);
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          uint32_t mbits = 0;
+          if constexpr (kMods)
+            if (p.mask) mbits = lane_bits(mask_word(row_of(ka), mA));
+          const int kn = live_tile(ka + 1);
+          if (kn < n_tiles) {
+            issue_tile<E, D, kNhd>(A, p, page_base, s_pages, slot0, kvh, row_of(kn), t_end, lane);
+            mA = mask_load(row_of(kn));
+          }
+          compute_tile(wk, row_of(ka), mbits);
+          // the reads above complete before the next tile overwrites the area
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          ka = kn;
+          if (ka >= n_tiles) break;
+        }
       }
     }
   }

@@ -143,10 +143,15 @@ MASKS = [  # keep probability, blocks of rows, window, cap, alibi
     (0.5, True, 0, 0.0, False),
     (0.7, False, 40, 0.0, True),
     (0.5, True, 0, 10.0, True),
+    # block-sparse masks: whole 32-row tiles dropped, whose loads are skipped
+    (0.3, 64, 0, 0.0, False),
+    (0.5, 256, 0, 0.0, False),
+    (0.4, 96, 40, 10.0, True),
 ]
 
 
-@pytest.mark.parametrize("mvar", MASKS, ids=lambda m: f"keep{m[0]}" + ("-blocks" if m[1] else "")
+@pytest.mark.parametrize("mvar", MASKS, ids=lambda m: f"keep{m[0]}"
+                         + ("" if m[1] is False else "-blocks" if m[1] is True else f"-runs{m[1]}")
                          + (f"-w{m[2]}" if m[2] else "") + (f"-cap{m[3]:g}" if m[3] else "")
                          + ("-alibi" if m[4] else ""))
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}-D{c[1]}-G{c[3]}-P{c[4]}")
@@ -208,7 +213,7 @@ def test_mask_all_ones_and_short(dev):
     compare(p.dtype, got[0], got[1], ro, rl, "short mask")
 
 
-@pytest.mark.parametrize("keep_p,blocks", [(0.5, False), (0.3, True)])
+@pytest.mark.parametrize("keep_p,blocks", [(0.5, False), (0.3, True), (0.3, 128), (0.6, 33)])
 def test_contig_mask(dev, keep_p, blocks):
     p = W.make_contig("mask", "f16", 16, 4, 128, 5000, 4999, seed=78, q_std=2.0)
     keep = W.random_mask(12, [p.valid_kv_len], keep=keep_p, blocks=blocks)
@@ -218,13 +223,42 @@ def test_contig_mask(dev, keep_p, blocks):
     compare("f16", o, lse, ro, rl, f"contig mask {keep_p} {blocks}")
 
 
-def test_mask_full_c3(dev):
-    """The full C3 workload under a random half mask, every output against the
-    oracle."""
+@pytest.mark.parametrize("blocks", [False, 256])
+def test_mask_full_c3(dev, blocks):
+    """The full C3 workload under a random half mask (rows one by one, or
+    256-row runs, whose dropped tiles are not loaded), every output against
+    the oracle."""
     p = W.FULL["c3"]()
-    announce("mask full c3")
+    announce(f"mask full c3 blocks={blocks}")
     lens = oracle.seq_lens(p.page_size, p.indptr.numpy(), p.last_page_len.numpy())
-    packed = W.pack_mask(W.random_mask(13, lens, keep=0.5))
+    packed = W.pack_mask(W.random_mask(13, lens, keep=0.5, blocks=blocks))
     o, lse = _run(p, to_dev(p, dev), 0, 0.0, mask=packed)
     torch.cuda.synchronize()
     compare_all(p, o, lse, "c3 mask", mask=packed)
+
+
+def test_mask_long_units(dev):
+    """Block-sparse mask over split units of more than 64 tiles per wave, so
+    each wave looks up which of its tiles hold a kept row in more than one
+    64-tile window (a contiguous cache of 9M rows, D = 64: units of ~8,800
+    rows against 64 x 128 = 8,192 rows per window); every output against the
+    oracle, and against the same call without the mask's dropped runs cut
+    out of the rows (an all-ones mask) for the plain path."""
+    n = 9_000_000
+    chunk, _, _, _ = fad.fa_debug_plan(fad.FA_DTYPE_BF16, 1, 2, 1, 64, n, 1)
+    assert chunk > 64 * 128, chunk
+    p = W.make_contig("long-mask", "bf16", 2, 1, 64, n, n - 1, seed=515, q_std=2.0)
+    announce(f"mask long units: chunk {chunk}")
+    keep = W.random_mask(16, [p.valid_kv_len], keep=0.3, blocks=512)
+    packed = W.pack_mask(keep)
+    d = to_dev(p, dev)
+    o, lse = _run(p, d, 0, 0.0, mask=packed)
+    torch.cuda.synchronize()
+    ro, rl = _oracle(p, 0, 0.0, mask=packed)
+    compare("bf16", o, lse, ro, rl, "long units, block-sparse mask")
+    ones = _run(p, d, 0, 0.0, mask=W.pack_mask(np.ones(p.valid_kv_len, bool)))
+    plain = _run(p, d, 0, 0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(ones[0], plain[0]) and torch.equal(ones[1], plain[1])
+    del d
+    torch.cuda.empty_cache()

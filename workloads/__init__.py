@@ -110,12 +110,18 @@ def pack_mask(keep) -> np.ndarray:
 
 def random_mask(seed, lens, keep=0.5, blocks=False) -> np.ndarray:
     """Seeded keep-booleans for requests of the given lengths, concatenated in
-    request order: independent rows kept with probability `keep`, or
-    (blocks=True) runs of 1-40 rows kept or dropped together."""
+    request order: independent rows kept with probability `keep`; with
+    blocks=True, runs of 1-40 rows kept or dropped together; with an integer
+    blocks=R, runs of R rows (a block-sparse mask) kept or dropped together."""
     rng = np.random.default_rng(seed)
     total = int(np.sum(lens))
-    if not blocks:
+    if blocks is False:
         return rng.random(total) < keep
+    if blocks is not True:
+        run = int(blocks)
+        assert run > 0
+        flags = rng.random((total + run - 1) // run) < keep
+        return np.repeat(flags, run)[:total]
     out = np.empty(total, dtype=bool)
     i = 0
     while i < total:
