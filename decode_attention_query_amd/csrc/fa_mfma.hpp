@@ -396,9 +396,9 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   // Custom mask of the tile at t0: its 32 bits start at bit B = row0 + t0 and
   // span bytes B/8 .. B/8 + 4.  mask_load issues one load instruction for
   // them with the tile's K/V loads (lanes 0-4, a byte each; bytes past the
-  // mask's end read as 0); mask_bits, at compute time, assembles the wave's
-  // bytes into the tile's word (mask_word: bit r for row t0 + r, the same in
-  // every lane) and returns the lane's rows (lane_bits: bit 4j + i for row
+  // mask's end read as 0); at compute time mask_word assembles the wave's
+  // bytes into the tile's word (bit r for row t0 + r, the same in every
+  // lane) and lane_bits picks the lane's rows (bit 4j + i for row
   // t0 + 16j + 4grp + i, j < JB).
   // Rows past the request (a prefetched tile, the tail of the last one) see
   // other bits and are cut by t_end.
