@@ -264,8 +264,8 @@ fa_status_t fa_decode_paged_nhd(fa_dtype_t dtype, int batch, int num_qo_heads,
  *                    for one query row per request.  K/V rows are read in
  *                    32-row tiles (16 for f32), per wave of the kernel: a tile
  *                    with no kept row is not read; a tile with one is read
- *                    whole (two head blocks per workgroup at head_dim 256
- *                    read every tile).
+ *                    whole.  Groups of more than 16 query heads at head_dim
+ *                    256 (f32 K/V: 128 and 256) read every tile.
  *   custom_mask_bytes  size of custom_mask in bytes (ignored when it is NULL):
  *                    ceil(sum L_b / 8) covers every row (ceil(valid_kv_len / 8)
  *                    for a contiguous cache).  Bits at or past 8 *
