@@ -37,3 +37,20 @@ def test_multi_gpu_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_block_sparse_mask_runs():
+    """random_mask(blocks=R): runs of exactly R rows kept or dropped together
+    (the last run cut at the total), seeded, with about the asked share kept."""
+    lens = [1000, 37, 2600]
+    keep = W.random_mask(21, lens, keep=0.3, blocks=64)
+    assert keep.shape == (3637,) and keep.dtype == bool
+    runs = keep[: 3637 // 64 * 64].reshape(-1, 64)
+    assert (runs.all(axis=1) | ~runs.any(axis=1)).all()  # every run uniform
+    tail = keep[3637 // 64 * 64:]
+    assert tail.all() or not tail.any()
+    assert 0.15 < keep.mean() < 0.45
+    assert np.array_equal(keep, W.random_mask(21, lens, keep=0.3, blocks=64))
+    # runs of 1-40 rows (blocks=True) and independent rows stay as they were
+    assert W.random_mask(21, lens, keep=0.3, blocks=True).shape == (3637,)
+    assert W.random_mask(21, lens, keep=0.3).shape == (3637,)
