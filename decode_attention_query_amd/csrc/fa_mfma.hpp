@@ -234,8 +234,9 @@ __device__ __forceinline__ void issue_tile(KVTile<MfmaGeom<E, D>::NI> &T, const 
   }
 }
 
-// kMods: a sliding window, soft-cap or ALiBi is in use (the plain instance
-// carries none of their per-score work).
+// kMods: a sliding window, soft-cap, ALiBi or custom mask is in use (the
+// plain instance carries none of their per-score work, nor the mask's tile
+// lookups).
 //
 // NB: 16-column head blocks per workgroup.  NB = 1: the workgroup's one block
 // (the whole group when G <= 16).  NB = 2 (a query group of more than 16
