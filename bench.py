@@ -467,8 +467,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(requests and KV heads shard across GPUs with no exchange; see DESIGN.md)",
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(requests and KV heads would shard across GPUs with no exchange)",
               file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
