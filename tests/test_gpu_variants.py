@@ -66,6 +66,7 @@ CASES = [
     # two 16-head blocks per workgroup (an even number of blocks)
     ("f16", 256, 2, 32, 16, [1, 48, 1500]),
     ("f32", 64, 1, 64, 8, [7, 600, 1100]),
+    ("f32", 128, 1, 32, 16, [77, 1200]),  # shared tiles with the per-score options
     # a group that is not a power of two, and a ragged last head block
     ("bf16", 128, 2, 7, 16, [3, 800]),
     ("f16", 128, 1, 40, 16, [300, 1700]),
