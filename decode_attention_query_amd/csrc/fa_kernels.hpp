@@ -278,29 +278,6 @@ __device__ inline bool mask_keeps(const DecodeParams &p, int row0, int t) {
   return (bit >> 3) < p.mask_bytes && ((p.mask[byte] >> (bit & 7)) & 1);
 }
 
-// Writes the combined result of one (request, query head, feature) of a unit:
-// the final o / lse if the request has a single unit, else the partial.
-template <class E>
-__device__ inline void emit(const DecodeParams &p, const UnitInfo &u, int h, int d, float m2,
-                            float l, float a) {
-  const bool any = l > 0.0f;
-  if (u.n_units == 1) {
-    const int64_t row = (int64_t)u.b * p.num_qo_heads + h;
-    static_cast<typename E::raw *>(p.o)[row * p.head_dim + d] = E::narrow(any ? a / l : 0.0f);
-    if (d == 0 && p.lse) p.lse[row] = any ? (m2 + fast_log2(l)) * kLn2 : -INFINITY;
-  } else {
-    // Partials are read by whichever workgroup merges the request, possibly on
-    // another XCD: store them device-coherent (agent-scope atomic stores write
-    // through to memory) so no L2 write-back of the whole cache is needed.
-    const int64_t row = (int64_t)(u.u0 + u.c) * p.num_qo_heads + h;
-    __hip_atomic_store(p.part_o + row * p.head_dim + d, any ? a / l : 0.0f, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-    if (d == 0)
-      __hip_atomic_store(p.part_lse + row, any ? m2 + fast_log2(l) : -INFINITY,
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
 // ------------------------------------------------------------- LSE merge
 
 // Device-coherent load of data another workgroup wrote (see finish_split).
@@ -324,6 +301,55 @@ __device__ inline f32x4 coherent_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
   return __builtin_bit_cast(
       f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCachePolicySc1));
 }
+
+// The store counterpart: 16 bytes with the sc1 bit (write-through, device
+// coherent).
+__device__ inline void coherent_store4(__amdgpu_buffer_rsrc_t r, uint32_t voff, f32x4 v) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, voff, 0,
+                                         kCachePolicySc1);
+}
+
+// Writes the combined result of features d .. d + 3 (d a multiple of 4) of one
+// (request, query head) of a unit: the final o / lse if the request has a
+// single unit (one vector store of the four outputs), else the partial.
+template <class E>
+__device__ inline void emit(const DecodeParams &p, const UnitInfo &u, int h, int d, float m2,
+                            float l, const float (&a)[4]) {
+  const bool any = l > 0.0f;
+  if (u.n_units == 1) {
+    const int64_t row = (int64_t)u.b * p.num_qo_heads + h;
+    typename E::raw *dst = static_cast<typename E::raw *>(p.o) + row * p.head_dim + d;
+    if constexpr (E::kBytes == 4) {
+      *reinterpret_cast<float4 *>(dst) = make_float4(any ? a[0] / l : 0.0f, any ? a[1] / l : 0.0f,
+                                                     any ? a[2] / l : 0.0f, any ? a[3] / l : 0.0f);
+    } else {
+      uint32_t w[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        w[i] = (uint32_t)E::narrow(any ? a[2 * i] / l : 0.0f) |
+               ((uint32_t)E::narrow(any ? a[2 * i + 1] / l : 0.0f) << 16);
+      *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1]);
+    }
+    if (d == 0 && p.lse) p.lse[row] = any ? (m2 + fast_log2(l)) * kLn2 : -INFINITY;
+  } else {
+    // Partials are read by whichever workgroup merges the request, possibly on
+    // another XCD: store them device-coherent (sc1 stores, what agent-scope
+    // atomic stores compile to, write through to memory) so no L2 write-back
+    // of the whole cache is needed.  One 16-byte store per four features,
+    // relative to the unit's partial block (a workgroup-uniform base).
+    const int64_t row = (int64_t)(u.u0 + u.c) * p.num_qo_heads + h;
+    const __amdgpu_buffer_rsrc_t r =
+        coherent_rsrc(p.part_o + (int64_t)(u.u0 + u.c) * p.num_qo_heads * p.head_dim);
+    coherent_store4(r, (uint32_t)((h * p.head_dim + d) * 4),
+                    f32x4{any ? a[0] / l : 0.0f, any ? a[1] / l : 0.0f, any ? a[2] / l : 0.0f,
+                          any ? a[3] / l : 0.0f});
+    if (d == 0)
+      __hip_atomic_store(p.part_lse + row, any ? m2 + fast_log2(l) : -INFINITY,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 //
 // Combines request b's split partials (o_s normalised over its rows, lse_s in
 // base 2) for query heads h0 .. h0 + gt - 1; every thread of the nw-wave

@@ -731,10 +731,12 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
   __syncthreads();
   // workgroup head hh = head g of block kb = hh / bs: merged over the WPB
   // waves that hold it (waves kb * WPB .. with shared tiles, where each wave
-  // holds one block; else every wave, as its block kb)
-  for (int idx = tid; idx < gt_wg * D; idx += NW * 64) {
-    const int hh = idx / D;
-    const int d = idx % D;
+  // holds one block; else every wave, as its block kb); each thread takes
+  // four adjacent features, read from LDS and stored at once
+  constexpr int D4 = D / 4;
+  for (int idx = tid; idx < gt_wg * D4; idx += NW * 64) {
+    const int hh = idx / D4;
+    const int d = (idx - hh * D4) * 4;
     const int kb = NB == 1 ? 0 : hh / bs;
     const int w0 = kShared ? kb * WPB : 0;
     const int col = (kShared ? 0 : kb) * 16 + (hh - kb * bs);
@@ -742,12 +744,18 @@ __global__ __launch_bounds__(mfma_waves(D) * 64) __attribute__((amdgpu_waves_per
 #pragma unroll
     for (int w = 0; w < WPB; ++w) Mx = fmaxf(Mx, s_m[w0 + w][col]);
     const float ref = safe_ref(Mx);
-    float lsum = 0.0f, a = 0.0f;
+    float lsum = 0.0f;
+    float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int w = 0; w < WPB; ++w) {
       const float sw = fast_exp2(s_m[w0 + w][col] - ref);
       lsum += s_l[w0 + w][col] * sw;
-      a += s_acc[((w0 + w) * NBW * 16 + col) * G::ACC_ROW + d] * sw;
+      const float4 v = *reinterpret_cast<const float4 *>(
+          &s_acc[((w0 + w) * NBW * 16 + col) * G::ACC_ROW + d]);
+      a[0] += v.x * sw;
+      a[1] += v.y * sw;
+      a[2] += v.z * sw;
+      a[3] += v.w * sw;
     }
     emit<E>(p, u, h0 + hh, d, Mx, lsum, a);
   }
