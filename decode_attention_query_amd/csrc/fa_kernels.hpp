@@ -310,6 +310,18 @@ __device__ inline void coherent_store4(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
                                          kCachePolicySc1);
 }
 
+// Four outputs at out .. out + 3 in the element type, one vector store.
+template <class E>
+__device__ inline void store4(typename E::raw *out, const f32x4 &v) {
+  if constexpr (E::kBytes == 4) {
+    *reinterpret_cast<f32x4 *>(out) = v;
+  } else {
+    const uint32_t lo = (uint32_t)E::narrow(v[0]) | ((uint32_t)E::narrow(v[1]) << 16);
+    const uint32_t hi = (uint32_t)E::narrow(v[2]) | ((uint32_t)E::narrow(v[3]) << 16);
+    *reinterpret_cast<uint2 *>(out) = make_uint2(lo, hi);
+  }
+}
+
 // Writes the combined result of features d .. d + 3 (d a multiple of 4) of one
 // (request, query head) of a unit: the final o / lse if the request has a
 // single unit (one vector store of the four outputs), else the partial.
@@ -319,18 +331,9 @@ __device__ inline void emit(const DecodeParams &p, const UnitInfo &u, int h, int
   const bool any = l > 0.0f;
   if (u.n_units == 1) {
     const int64_t row = (int64_t)u.b * p.num_qo_heads + h;
-    typename E::raw *dst = static_cast<typename E::raw *>(p.o) + row * p.head_dim + d;
-    if constexpr (E::kBytes == 4) {
-      *reinterpret_cast<float4 *>(dst) = make_float4(any ? a[0] / l : 0.0f, any ? a[1] / l : 0.0f,
-                                                     any ? a[2] / l : 0.0f, any ? a[3] / l : 0.0f);
-    } else {
-      uint32_t w[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        w[i] = (uint32_t)E::narrow(any ? a[2 * i] / l : 0.0f) |
-               ((uint32_t)E::narrow(any ? a[2 * i + 1] / l : 0.0f) << 16);
-      *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1]);
-    }
+    store4<E>(static_cast<typename E::raw *>(p.o) + row * p.head_dim + d,
+              f32x4{any ? a[0] / l : 0.0f, any ? a[1] / l : 0.0f, any ? a[2] / l : 0.0f,
+                    any ? a[3] / l : 0.0f});
     if (d == 0 && p.lse) p.lse[row] = any ? (m2 + fast_log2(l)) * kLn2 : -INFINITY;
   } else {
     // Partials are read by whichever workgroup merges the request, possibly on
@@ -350,7 +353,6 @@ __device__ inline void emit(const DecodeParams &p, const UnitInfo &u, int h, int
   }
 }
 
-//
 // Combines request b's split partials (o_s normalised over its rows, lse_s in
 // base 2) for query heads h0 .. h0 + gt - 1; every thread of the nw-wave
 // workgroup takes part.  Per head:
@@ -369,17 +371,6 @@ __device__ inline void emit(const DecodeParams &p, const UnitInfo &u, int h, int
 // are then read 16 bytes per load, one 4-feature column per thread, kDepth
 // units in flight (kDepth is what the kernel's register budget leaves room
 // for) and the last units four at a time.
-template <class E>
-__device__ inline void store4(typename E::raw *out, const f32x4 &v) {
-  if constexpr (E::kBytes == 4) {
-    *reinterpret_cast<f32x4 *>(out) = v;
-  } else {
-    const uint32_t lo = (uint32_t)E::narrow(v[0]) | ((uint32_t)E::narrow(v[1]) << 16);
-    const uint32_t hi = (uint32_t)E::narrow(v[2]) | ((uint32_t)E::narrow(v[3]) << 16);
-    *reinterpret_cast<uint2 *>(out) = make_uint2(lo, hi);
-  }
-}
-
 template <class E, int kDepth>
 __device__ __forceinline__ void merge_partials(const DecodeParams &p, int b, int u0, int n, int h0, int gt, int nw,
                                float *s_stat /* LDS [2 kStatHeads] */, float *s_w,
