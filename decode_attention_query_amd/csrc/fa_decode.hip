@@ -82,10 +82,10 @@ struct CallEvents {
 
 // --------------------------------------------------------------- dispatch
 
-// Workgroups of the first resident round (two per compute unit) take their
-// work item from their launch index; the rest of a launch of n draw theirs
-// from a counter.  The compute-unit count is read once per device.
-int first_round(int64_t n) {
+// Workgroups of the first resident round (per_cu per compute unit) take
+// their work item from their launch index; the rest of a launch of n draw
+// theirs from a counter.  The compute-unit count is read once per device.
+int first_round(int64_t n, int per_cu) {
   static std::atomic<int> cus_of[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return int(n);
@@ -96,7 +96,7 @@ int first_round(int64_t n) {
       return int(n);
     cus_of[dev].store(cus, std::memory_order_relaxed);
   }
-  const int64_t r = 2 * int64_t(cus);
+  const int64_t r = int64_t(per_cu) * int64_t(cus);
   if (n <= r || n - r >= (int64_t(1) << fa::kCountBits)) return int(n);
   return int(r);
 }
@@ -118,12 +118,32 @@ hipError_t launch_mfma_nb(const DecodeParams &p, bool mods, dim3 grid, dim3 bloc
   return hipGetLastError();
 }
 
+// Workgroups of the kernel instance for (E, D, NB) that one compute unit
+// holds at once (two at D = 128 and 256, three at D = 64), from the runtime's
+// occupancy calculator; read once per instance (the same on every device of
+// one architecture), 2 if the query fails.
+template <class E, int D, int NB>
+int resident_per_cu(dim3 block) {
+  static std::atomic<int> cached{0};
+  int n = cached.load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, reinterpret_cast<const void *>(&fa::decode_mfma_kernel<E, D, false, false, NB>),
+            int(block.x), 0) != hipSuccess ||
+        n <= 0)
+      n = 2;
+    cached.store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <class E, int D>
 hipError_t launch_mfma(const DecodeParams &params, const HostPlan &hp, hipStream_t s) {
   dim3 grid(unsigned(hp.units_bound) * unsigned(hp.planes));
   dim3 block(fa::MfmaGeom<E, D>::NW * 64);
   DecodeParams p = params;
-  p.ticket_from = first_round(int64_t(hp.units_bound) * hp.planes);
+  const int per_cu = hp.nb == 2 ? resident_per_cu<E, D, 2>(block) : resident_per_cu<E, D, 1>(block);
+  p.ticket_from = first_round(int64_t(hp.units_bound) * hp.planes, per_cu);
   const bool mods = p.window > 0 || p.softcap2 > 0.0f || p.alibi != nullptr || p.mask != nullptr;
   if (hp.nb == 2)
     return launch_mfma_nb<E, D, 2>(p, mods, grid, block, s);
